@@ -1,0 +1,21 @@
+"""fp64 CPU oracle for the attention forward pass.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the library.  It shares no code with
+the HIP path.
+"""
+from .reference import (  # noqa: F401
+    CAUSAL,
+    CAUSAL_WINDOW,
+    FULL,
+    LOCAL_GLOBAL,
+    MASK_KINDS,
+    attention,
+    effective_flops,
+    global_set,
+    kv_head,
+    softmax_rows,
+    visibility,
+    visible_pair_count,
+    weights,
+)

@@ -1,0 +1,137 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws numbers and lays them out; it holds none of the
+attention arithmetic.  It is the one piece shared by the fp64 oracle's tests,
+the GPU parity tests and the benchmark, so that both sides see identical
+inputs.
+
+Workloads (shapes follow the examples on the pages):
+
+* ``causal_mha_fp32_s256``   -- causal multi-head, fp32, B=1 H=4 S=256 D=64,
+  scale 1/8.
+* ``causal_mha_bf16_s2048``  -- causal multi-head, bf16, B=4 H=32 S=2048 D=128.
+* ``causal_gqa_bf16_s8192``  -- causal grouped-query (32 query heads over 8
+  key/value heads), bf16, B=1 S=8192 D=128.
+* ``window_gqa_bf16_s16384`` -- causal sliding window of 4096 keys (key j is
+  visible from query i when i-4096 < j <= i), grouped-query, bf16,
+  B=1 S=16384 D=128; window and length follow the Mistral and Longformer
+  figures on "Transformer 演进与变体", section 稀疏注意力.
+* ``local_global_bf16_s8192`` -- bidirectional band |i-j| <= 512 plus global
+  tokens {0, 1000, 3000, 6000}, 12 heads, B=1 S=8192 D=64: the document example
+  of "Transformer 演进与变体", section 稀疏注意力 (Longformer paragraph).
+
+Values are iid N(0, 1) from ``numpy.random.default_rng(seed)``, drawn as
+float32 in the order Q, K, V, each shaped [B][H][S][D].  bf16 workloads round
+those draws to nearest-even bf16; the rounded values are what every consumer
+(kernel and oracle) sees.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Tuple
+
+import numpy as np
+
+MASK_FULL = "full"
+MASK_CAUSAL = "causal"
+MASK_CAUSAL_WINDOW = "causal_window"
+MASK_LOCAL_GLOBAL = "local_global"
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    S: int
+    D: int
+    dtype: str  # "fp32" or "bf16"
+    mask: str
+    window: int = 0
+    global_idx: Tuple[int, ...] = ()
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+    def describe(self) -> dict:
+        d = dataclasses.asdict(self)
+        d["global_idx"] = list(self.global_idx)
+        return d
+
+
+WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("causal_mha_fp32_s256", 1, 4, 4, 256, 64, "fp32", MASK_CAUSAL, seed=1),
+        Workload("causal_mha_bf16_s2048", 4, 32, 32, 2048, 128, "bf16", MASK_CAUSAL, seed=2),
+        Workload("causal_gqa_bf16_s8192", 1, 32, 8, 8192, 128, "bf16", MASK_CAUSAL, seed=3),
+        Workload("window_gqa_bf16_s16384", 1, 32, 8, 16384, 128, "bf16", MASK_CAUSAL_WINDOW,
+                 window=4096, seed=4),
+        Workload("local_global_bf16_s8192", 1, 12, 12, 8192, 64, "bf16", MASK_LOCAL_GLOBAL,
+                 window=512, global_idx=(0, 1000, 3000, 6000), seed=5),
+    )
+}
+
+# The workload the headline throughput is quoted on.
+HEADLINE = "causal_gqa_bf16_s8192"
+
+
+def bf16_round_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); return uint16 bit patterns.
+
+    Inputs are finite normal draws, so no NaN handling is needed.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    bias = ((bits >> 16) & 1) + 0x7FFF
+    return ((bits + bias) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def draw(shape, rng: np.random.Generator) -> np.ndarray:
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+def make_inputs(B, Hq, Hkv, S, D, dtype, seed):
+    """Return dict with float32 arrays 'q','k','v' holding the values the kernel sees,
+    plus (for bf16) the uint16 bit patterns under 'q_bits','k_bits','v_bits'."""
+    rng = np.random.default_rng(seed)
+    q = draw((B, Hq, S, D), rng)
+    k = draw((B, Hkv, S, D), rng)
+    v = draw((B, Hkv, S, D), rng)
+    out = {}
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if dtype == "bf16":
+            bits = bf16_round_bits(x)
+            out[name + "_bits"] = bits
+            out[name] = bf16_bits_to_float(bits)
+        elif dtype == "fp32":
+            out[name] = x
+        else:
+            raise ValueError(f"unknown dtype {dtype!r}")
+    return out
+
+
+def workload_inputs(w: Workload):
+    return make_inputs(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype, w.seed)
+
+
+def to_torch(inputs: dict, dtype: str, device):
+    """Move generated inputs into torch tensors of the kernel dtype (no arithmetic)."""
+    import torch
+
+    res = []
+    for name in ("q", "k", "v"):
+        if dtype == "bf16":
+            t = torch.from_numpy(inputs[name + "_bits"].view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(inputs[name])
+        res.append(t.to(device).contiguous())
+    return tuple(res)
