@@ -1,0 +1,206 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--no-parity]
+
+A step is one attn_fwd call over the whole workload (default: causal
+grouped-query bf16, B=1 Hq=32 Hkv=8 S=8192 D=128) with the inputs already
+resident in HBM.  K steps are timed with HIP events recorded on the stream the
+kernel is launched on.  Prints one JSON line:
+
+  value     effective TFLOP/s = unmasked FLOPs (4*D per visible (query, key)
+            pair per query head) / time per step
+  roofline  matrix-core bound: achieved TFLOP/s of the attention kernel (its
+            algorithmic FLOPs per launch / its average launch duration) vs the
+            MI355X dense bf16 peak; traffic = HBM bytes per launch from the
+            committed rocprofv3 counter summary, or null when the kernel
+            source changed since the counters were taken
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload,
+            timed on the host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_FP32_TFLOPS = 157.3   # vector fp32
+KERNEL_SOURCES = ("kernel_bf16.hip", "attn_kernels.h", "attn_sched.h")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_causal_gqa_s8192_hbm_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "transformer_attention_attn_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source for this workload."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    txt = open(TRAFFIC_SUMMARY, encoding="utf-8").read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", txt)
+    m_wl = re.search(r"workload:\s*(\S+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not (m_hash and m_wl and m_b):
+        return None
+    if m_hash.group(1) != kernel_source_hash() or m_wl.group(1) != workload:
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(w, inputs, n_heads: int):
+    """Time the oracle on the first n_heads query heads of batch 0 (all rows)."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((x.get("num_threads", 1) for x in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    G = w.Hq // w.Hkv
+    n_heads = min(n_heads, w.Hq)
+    n_kv = (n_heads + G - 1) // G
+    q = inputs["q"][:1, :n_heads]
+    k = inputs["k"][:1, :n_kv]
+    v = inputs["v"][:1, :n_kv]
+    # keep the head map: query head a of the sample still reads kv head a // G
+    Hs = n_kv * G
+    if Hs != n_heads:
+        q = inputs["q"][:1, :Hs]
+        n_heads = Hs
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, w.mask, w.window, w.global_idx, scale=w.scale)
+    dt = time.perf_counter() - t0
+    flops = oracle.effective_flops(1, n_heads, w.S, w.D, w.mask, w.window, w.global_idx)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"batch 0, query heads 0..{n_heads - 1} of {w.Hq}, all {w.S} rows "
+                  f"({flops:.3e} effective FLOPs in {dt:.2f} s, fp64 NumPy)",
+        "seconds": dt,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the kernel shards by key/value head, see DESIGN.md", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import transformer_attention_attn_amd as attn
+    import workloads
+
+    name = args.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    print(f"bench: workload {name} {w.describe()}", file=sys.stderr, flush=True)
+    inputs = workloads.workload_inputs(w)
+    q, k, v = workloads.to_torch(inputs, w.dtype, dev)
+    out = torch.empty_like(q)
+    g = list(w.global_idx) or None
+    plan = attn.plan(w.B, w.Hq, w.Hkv, w.S, w.D, w.mask, w.window, g, w.dtype)
+    flops = plan["effective_flops"]
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        attn.fwd(q, k, v, mask=w.mask, window=w.window, global_idx=g, scale=w.scale, out=out,
+                 stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(f"bench: {ms * 1e3:.1f} us/step, {tflops:.1f} effective TFLOP/s", file=sys.stderr,
+          flush=True)
+
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    traffic = committed_traffic(name)
+    result = {
+        "metric": "effective attention TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, 1 GPU",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
+                   "mask": w.mask, "window": w.window, "global_idx": list(w.global_idx),
+                   "effective_flops": flops, "parallelism": "none"},
+        "pct_peak": round(100.0 * tflops / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4),
+            "traffic": traffic,
+        },
+        "gpu": torch.cuda.get_device_name(dev),
+        "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
+    }
+
+    if not args.no_parity:
+        import oracle
+
+        rows = sorted({0, 1, 127, 128, w.S // 2, w.S - 1})
+        ref = oracle.attention(inputs["q"][:1], inputs["k"][:1], inputs["v"][:1], w.mask,
+                               w.window, w.global_idx, scale=w.scale, rows=rows)
+        got = out[:1].float().cpu().numpy()[:, :, rows]
+        result["parity"] = {"rows": rows, "batch": 0,
+                            "max_abs_err": float(np.max(np.abs(got - ref)))}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_heads)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,125 @@
+/*
+ * attn.h -- C ABI of libattn.so: fused masked / grouped-query scaled
+ * dot-product attention forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * Operation ("Trasformer 浅析", section 缩放点积注意力; shapes and head map from
+ * "Transformer 架构及其变体", section 带显式形状的因果自注意力):
+ *
+ *   for every batch b, query head a, query position i:
+ *     h      = a / (Hq / Hkv)                       key/value head of query head a
+ *     s_ij   = scale * sum_d q[b][a][i][d] * k[b][h][j][d]      for visible j
+ *     p_ij   = exp(s_ij - max_j s_ij) / sum_j exp(s_ij - max_j s_ij)
+ *     o[b][a][i][:] = sum_j p_ij * v[b][h][j][:]
+ *
+ * Masked pairs are excluded exactly (their weight is zero), as with the -inf
+ * mask entries of "Trasformer 浅析", section 掩码与三种架构范式.
+ *
+ * Layout: q and o are [B][Hq][S][D], k and v are [B][Hkv][S][D], dense
+ * row-major (D fastest), all four in the same element type, all in device
+ * memory owned by the caller.  The n x n score matrix is never stored: the
+ * library allocates no device memory at all.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Which (query i, key j) pairs are visible. */
+typedef enum {
+  ATTN_MASK_FULL = 0,          /* every key (bidirectional)                        */
+  ATTN_MASK_CAUSAL = 1,        /* j <= i  ("Trasformer 浅析", causal-mask equation) */
+  ATTN_MASK_CAUSAL_WINDOW = 2, /* i - window < j <= i: the last `window` keys up to
+                                  and including i; window >= 1                     */
+  ATTN_MASK_LOCAL_GLOBAL = 3   /* |i - j| <= window, or i is a global token, or j is
+                                  a global token ("Transformer 演进与变体", section
+                                  稀疏注意力, sliding window of radius w plus global
+                                  tokens); window >= 0                            */
+} attn_mask_kind;
+
+/* Element type of q, k, v and o.  Arithmetic: bf16 products accumulate in fp32
+ * on the matrix cores; softmax statistics are fp32; the attention weights are
+ * rounded to bf16 (nearest even) before the P.V product; o is rounded once to
+ * bf16 at the end.  fp32 inputs are computed entirely in fp32. */
+typedef enum { ATTN_DTYPE_FP32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  ATTN_ERR_SHAPE = 2,       /* B, Hq, Hkv or S < 1, or sizes overflow              */
+  ATTN_ERR_HEADS = 3,       /* Hq is not a multiple of Hkv                         */
+  ATTN_ERR_UNSUPPORTED = 4, /* D not in {64, 128}, unknown dtype or mask kind      */
+  ATTN_ERR_WINDOW = 5,      /* window out of range for the mask kind               */
+  ATTN_ERR_GLOBAL = 6,      /* bad global tokens: n_global out of [0, 64], index out
+                               of [0, S), or globals given with another mask kind  */
+  ATTN_ERR_ALIGN = 7,       /* a tensor pointer is not 16-byte aligned             */
+  ATTN_ERR_HIP = 8,         /* the kernel launch failed (hipGetLastError)          */
+  ATTN_ERR_ALIAS = 9,       /* o overlaps q, k or v                                */
+  ATTN_ERR_SCALE = 10       /* scale is NaN or infinite                            */
+} attn_status;
+
+#define ATTN_MAX_GLOBAL 64
+
+/*
+ * attn_fwd -- enqueue the attention forward pass on `stream`.
+ *
+ *   q, k, v     device pointers, layouts above, read only
+ *   o           device pointer [B][Hq][S][D], written; must not overlap q, k, v
+ *   B, Hq, Hkv  batch, query heads, key/value heads (Hq % Hkv == 0;
+ *               Hkv == Hq is multi-head, Hkv == 1 is multi-query attention)
+ *   S           sequence length (any S >= 1; partial tiles are handled)
+ *   D           head width, 64 or 128
+ *   mask_kind   attn_mask_kind
+ *   window      ignored for FULL and CAUSAL; see attn_mask_kind otherwise
+ *   global_idx  HOST pointer to n_global int32 positions (LOCAL_GLOBAL only);
+ *               treated as a set (order and duplicates do not matter), read
+ *               during the call and not kept; may be NULL when n_global == 0
+ *   n_global    number of entries in global_idx, 0..ATTN_MAX_GLOBAL
+ *   scale       multiplies q.k; used exactly as given (0 gives uniform weights;
+ *               the usual choice is 1/sqrt(D), "Trasformer 浅析", section
+ *               缩放因子的必要性)
+ *   dtype       attn_dtype of all four tensors
+ *   stream      hipStream_t to launch on (NULL = the default stream)
+ *
+ * Returns ATTN_OK after enqueuing one kernel; the call does not synchronise.
+ * Argument errors are detected on the host before any launch and leave o
+ * untouched.  Faults during execution surface at the caller's next
+ * synchronisation.  NaN/Inf inputs propagate.  Stateless and re-entrant; for a
+ * given input the output is bitwise reproducible (no atomics in the numerics).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o,
+             int B, int Hq, int Hkv, int S, int D,
+             int mask_kind, int window, const int* global_idx, int n_global,
+             float scale, int dtype, void* stream);
+
+/* Host-only description of the work attn_fwd would launch for these arguments
+ * (the same validation as attn_fwd, no device access).  Counts are per call. */
+typedef struct {
+  long long work_items;      /* workgroups launched                                */
+  long long tile_visits;     /* (work item, key tile) pairs processed               */
+  long long partial_tiles;   /* tile visits that need the per-element mask          */
+  long long visible_pairs;   /* exact visible (query, key) pairs of one query head  */
+  double effective_flops;    /* 4 * D * visible_pairs * B * Hq                       */
+  int rows_per_item;         /* query rows per head per work item                   */
+  int heads_per_item;        /* query heads of one key/value head per work item     */
+  int keys_per_tile;         /* keys per tile                                       */
+  int kernel;                /* 0 = fp32 kernel, 1 = bf16 matrix-core kernel         */
+} attn_plan_info;
+
+/* Fills *info for the given arguments; returns the same status attn_fwd would
+ * return for them (pointers are not needed and not checked). */
+int attn_plan(int B, int Hq, int Hkv, int S, int D, int mask_kind, int window,
+              const int* global_idx, int n_global, int dtype, attn_plan_info* info);
+
+/* Static, NUL-terminated name of a status code. */
+const char* attn_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

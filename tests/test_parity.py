@@ -1,0 +1,105 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle,
+element by element on the same seeded inputs.
+
+Tolerances (max-abs over every compared element): 1e-5 for fp32 inputs and
+outputs, 2e-2 for bf16 inputs with fp32 accumulation and a bf16 output.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+
+
+def run_case(device, B, Hq, Hkv, S, D, dtype, mask, window=0, g=(), seed=0, scale=None,
+             rows=None):
+    import torch
+    import transformer_attention_attn_amd as attn
+
+    print(f"case B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} {dtype} {mask} w={window} g={list(g)} "
+          f"seed={seed} scale={scale}", flush=True)
+    inp = workloads.make_inputs(B, Hq, Hkv, S, D, dtype, seed)
+    q, k, v = workloads.to_torch(inp, dtype, device)
+    o = attn.fwd(q, k, v, mask=mask, window=window, global_idx=list(g) if g else None,
+                 scale=scale)
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy()
+    if rows is not None:
+        got = got[:, :, rows]
+    ref = oracle.attention(inp["q"], inp["k"], inp["v"], mask, window, g, scale=scale, rows=rows)
+    assert np.all(np.isfinite(got))
+    err = float(np.max(np.abs(got.astype(np.float64) - ref)))
+    return err
+
+
+SWEEP = []
+_rng = np.random.default_rng(2024)
+for dtype in ("bf16", "fp32"):
+    for D in (64, 128):
+        for S in (1, 7, 63, 64, 65, 127, 129, 1000):
+            for mask in ("full", "causal", "causal_window", "local_global"):
+                heads = [(1, 1), (2, 1), (4, 2), (8, 2), (4, 4), (3, 1), (6, 3), (12, 1)]
+                Hq, Hkv = heads[int(_rng.integers(len(heads)))]
+                window, g = 0, ()
+                if mask == "causal_window":
+                    window = int(_rng.choice([1, 63, 64, 65, max(1, S - 1), S, S + 5]))
+                if mask == "local_global":
+                    window = int(_rng.choice([0, 1, 63, 64, 65, S]))
+                    cand = [0, 63, 64, 127, 128, S - 1, S // 2, S // 2]
+                    g = tuple(int(x) for x in _rng.choice(cand, size=int(_rng.integers(0, 5)))
+                              if x < S)
+                SWEEP.append((1 + int(_rng.integers(2)), Hq, Hkv, S, D, dtype, mask, window, g))
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"{c[5]}-D{c[4]}-S{c[3]}-{c[6]}-H{c[1]}x{c[2]}")
+def test_sweep(device, case):
+    B, Hq, Hkv, S, D, dtype, mask, window, g = case
+    err = run_case(device, B, Hq, Hkv, S, D, dtype, mask, window, g, seed=S * 7 + D)
+    assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2, 0.05, 1.0])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_scales(device, scale, dtype):
+    err = run_case(device, 1, 4, 2, 200, 64, dtype, "causal", scale=scale, seed=11)
+    assert err <= TOL[dtype], err
+
+
+def test_many_globals(device):
+    g = tuple(range(0, 1000, 16))  # 63 globals, several per tile
+    err = run_case(device, 1, 4, 4, 1000, 128, "bf16", "local_global", 20, g, seed=5)
+    assert err <= TOL["bf16"], err
+    g = tuple(range(0, 64))  # 64 globals, the maximum, one full strip tile
+    err = run_case(device, 1, 2, 1, 300, 64, "fp32", "local_global", 3, g, seed=6)
+    assert err <= TOL["fp32"], err
+
+
+def sample_rows(w: workloads.Workload, n=48):
+    S = w.S
+    rng = np.random.default_rng(w.seed + 100)
+    rows = {0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, S - 1, S - 2, S - 33, S // 2}
+    if w.window:
+        for x in (w.window - 1, w.window, w.window + 1, 2 * w.window):
+            rows.add(min(S - 1, x))
+    for gp in w.global_idx:
+        for d in (-w.window - 1, -w.window, -1, 0, 1, w.window, w.window + 1):
+            if 0 <= gp + d < S:
+                rows.add(gp + d)
+    rows |= set(int(x) for x in rng.integers(0, S, size=n))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_workload_full_size(device, name):
+    """The workloads at full size, in the launch configuration the benchmark
+    times; every element of the sampled query rows (all heads) is compared."""
+    w = workloads.WORKLOADS[name]
+    rows = None if w.S <= 256 else sample_rows(w)
+    err = run_case(device, w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype, w.mask, w.window, w.global_idx,
+                   seed=w.seed, scale=w.scale, rows=rows)
+    print(f"{name}: max abs err {err:.3e}", flush=True)
+    assert err <= TOL[w.dtype], err

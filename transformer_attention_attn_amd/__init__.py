@@ -1,0 +1,28 @@
+"""MI355X-native fused attention forward: masked, grouped-query
+scaled dot-product attention in hand-written gfx950 HIP kernels.
+
+The library is libattn.so (C ABI in include/attn.h); this package is a thin
+ctypes binding over it.  Build it with
+``python -m transformer_attention_attn_amd.build``.
+"""
+from ._binding import (  # noqa: F401
+    DTYPE_BF16,
+    DTYPE_FP32,
+    EXPORTS,
+    LIB_PATH,
+    MASK_CAUSAL,
+    MASK_CAUSAL_WINDOW,
+    MASK_FULL,
+    MASK_LOCAL_GLOBAL,
+    MASKS,
+    MAX_GLOBAL,
+    STATUS,
+    AttnError,
+    fwd,
+    fwd_raw,
+    load,
+    plan,
+    plan_status,
+    status_string,
+    version,
+)

@@ -1,0 +1,176 @@
+"""ctypes binding of libattn.so (argument marshalling only).
+
+Every step of the attention forward runs inside the library's HIP kernels;
+torch only provides device memory and the stream.  If the library is missing
+this module raises: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+MASK_FULL, MASK_CAUSAL, MASK_CAUSAL_WINDOW, MASK_LOCAL_GLOBAL = 0, 1, 2, 3
+DTYPE_FP32, DTYPE_BF16 = 0, 1
+MAX_GLOBAL = 64
+
+MASKS = {
+    "full": MASK_FULL,
+    "causal": MASK_CAUSAL,
+    "causal_window": MASK_CAUSAL_WINDOW,
+    "local_global": MASK_LOCAL_GLOBAL,
+}
+
+STATUS = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_HEADS",
+    4: "ATTN_ERR_UNSUPPORTED", 5: "ATTN_ERR_WINDOW", 6: "ATTN_ERR_GLOBAL",
+    7: "ATTN_ERR_ALIGN", 8: "ATTN_ERR_HIP", 9: "ATTN_ERR_ALIAS", 10: "ATTN_ERR_SCALE",
+}
+
+EXPORTS = ("attn_fwd", "attn_plan", "attn_status_string", "attn_version")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"attn call failed: {STATUS.get(status, status)}")
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("work_items", ctypes.c_longlong),
+        ("tile_visits", ctypes.c_longlong),
+        ("partial_tiles", ctypes.c_longlong),
+        ("visible_pairs", ctypes.c_longlong),
+        ("effective_flops", ctypes.c_double),
+        ("rows_per_item", ctypes.c_int),
+        ("heads_per_item", ctypes.c_int),
+        ("keys_per_tile", ctypes.c_int),
+        ("kernel", ctypes.c_int),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libattn.so (built by transformer_attention_attn_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m transformer_attention_attn_amd.build`")
+    lib = ctypes.CDLL(path)
+    i, p, f = ctypes.c_int, ctypes.c_void_p, ctypes.c_float
+    lib.attn_fwd.argtypes = [p, p, p, p, i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int), i,
+                             f, i, p]
+    lib.attn_fwd.restype = i
+    lib.attn_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int), i, i,
+                              ctypes.POINTER(PlanInfo)]
+    lib.attn_plan.restype = i
+    lib.attn_status_string.argtypes = [i]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = i
+    _lib = lib
+    return lib
+
+
+def _mask_id(mask) -> int:
+    if isinstance(mask, str):
+        return MASKS[mask]
+    return int(mask)
+
+
+def _globals(global_idx: Optional[Sequence[int]]):
+    if global_idx is None:
+        return None, 0
+    vals = [int(x) for x in global_idx]
+    arr = (ctypes.c_int * max(1, len(vals)))(*vals)
+    return arr, len(vals)
+
+
+def fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, B: int, Hq: int, Hkv: int, S: int,
+            D: int, mask, window: int, global_idx, scale: float, dtype: int, stream: int) -> int:
+    """Direct call of attn_fwd with raw device addresses; returns the status."""
+    lib = load()
+    garr, ng = _globals(global_idx)
+    return lib.attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, B, Hq, Hkv, S, D, _mask_id(mask), window,
+                        garr, ng, float(scale), dtype, stream)
+
+
+def fwd(q, k, v, mask="causal", window: int = 0, global_idx=None, scale: Optional[float] = None,
+        out=None, stream=None):
+    """Attention forward on torch device tensors.
+
+    q: [B, Hq, S, D], k, v: [B, Hkv, S, D], contiguous, bf16 or fp32, on the GPU.
+    Returns o shaped like q (allocated with torch unless `out` is given).
+    The kernel runs on `stream` (default: torch's current stream).
+    """
+    import torch
+
+    if q.dtype == torch.bfloat16:
+        dt = DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dt = DTYPE_FP32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for t in (q, k, v):
+        if t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v must be contiguous 4-D GPU tensors of one dtype")
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, S, D) or tuple(v.shape) != (B, Hkv, S, D):
+        raise ValueError("k, v must be [B, Hkv, S, D] matching q")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped like q")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, S, D,
+                     mask, window, global_idx, scale, dt, handle)
+    if st != 0:
+        raise AttnError(st)
+    return out
+
+
+def plan(B: int, Hq: int, Hkv: int, S: int, D: int, mask="causal", window: int = 0,
+         global_idx=None, dtype: str = "bf16") -> dict:
+    """Host-only work plan of attn_fwd for these arguments (no GPU needed)."""
+    lib = load()
+    garr, ng = _globals(global_idx)
+    info = PlanInfo()
+    st = lib.attn_plan(B, Hq, Hkv, S, D, _mask_id(mask), window, garr, ng,
+                       DTYPE_BF16 if dtype == "bf16" else DTYPE_FP32, ctypes.byref(info))
+    if st != 0:
+        raise AttnError(st)
+    return info.as_dict()
+
+
+def plan_status(B, Hq, Hkv, S, D, mask, window=0, global_idx=None, dtype=DTYPE_BF16) -> int:
+    """Status attn_plan returns for these arguments (validation only)."""
+    lib = load()
+    garr, ng = _globals(global_idx)
+    info = PlanInfo()
+    return lib.attn_plan(B, Hq, Hkv, S, D, _mask_id(mask), window, garr, ng, dtype,
+                         ctypes.byref(info))
+
+
+def status_string(status: int) -> str:
+    return load().attn_status_string(status).decode()
+
+
+def version() -> int:
+    return load().attn_version()

@@ -1,0 +1,188 @@
+// attn_api.cpp -- the C ABI of libattn.so: argument validation, normalisation
+// of the global-token set, work planning and kernel dispatch.  No device
+// memory is allocated; all launch data travels in the kernel argument block.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/attn.h"
+#include "attn_kernels.h"
+
+namespace {
+
+using attn::KParams;
+using attn::Sched;
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr long long kMaxS = 1LL << 30;
+
+struct Checked {
+  int status;
+  Sched s;
+  int gpos[attn::kMaxGlobal];
+  int n_global;  // distinct
+};
+
+Checked check_args(int B, int Hq, int Hkv, int S, int D, int mask_kind, int window,
+                   const int* global_idx, int n_global, int dtype) {
+  Checked c{};
+  c.status = ATTN_OK;
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || (long long)S > kMaxS) { c.status = ATTN_ERR_SHAPE; return c; }
+  if (dtype != ATTN_DTYPE_FP32 && dtype != ATTN_DTYPE_BF16) { c.status = ATTN_ERR_UNSUPPORTED; return c; }
+  if (D != 64 && D != 128) { c.status = ATTN_ERR_UNSUPPORTED; return c; }
+  if (mask_kind < ATTN_MASK_FULL || mask_kind > ATTN_MASK_LOCAL_GLOBAL) { c.status = ATTN_ERR_UNSUPPORTED; return c; }
+  if (Hq % Hkv != 0) { c.status = ATTN_ERR_HEADS; return c; }
+  // total elements and the flat index of the last element must fit in 63 bits
+  const long double elems = (long double)B * Hq * S * D;
+  if (elems > 4.0e18L) { c.status = ATTN_ERR_SHAPE; return c; }
+  if (mask_kind == ATTN_MASK_CAUSAL_WINDOW && window < 1) { c.status = ATTN_ERR_WINDOW; return c; }
+  if (mask_kind == ATTN_MASK_LOCAL_GLOBAL && window < 0) { c.status = ATTN_ERR_WINDOW; return c; }
+  if (n_global < 0 || n_global > ATTN_MAX_GLOBAL) { c.status = ATTN_ERR_GLOBAL; return c; }
+  if (n_global > 0 && (mask_kind != ATTN_MASK_LOCAL_GLOBAL || global_idx == nullptr)) {
+    c.status = ATTN_ERR_GLOBAL;
+    return c;
+  }
+  int tmp[ATTN_MAX_GLOBAL];
+  for (int i = 0; i < n_global; ++i) {
+    if (global_idx[i] < 0 || global_idx[i] >= S) { c.status = ATTN_ERR_GLOBAL; return c; }
+    tmp[i] = global_idx[i];
+  }
+  std::sort(tmp, tmp + n_global);
+  const int nd = (int)(std::unique(tmp, tmp + n_global) - tmp);
+  std::copy(tmp, tmp + nd, c.gpos);
+  c.n_global = nd;
+
+  if (dtype == ATTN_DTYPE_FP32)
+    c.s = attn::make_sched(B, Hq, Hkv, S, mask_kind, window, nd, attn::kF32Rows, attn::kF32Keys, 0);
+  else
+    c.s = attn::make_sched(B, Hq, Hkv, S, mask_kind, window, nd, attn::kBf16Rows,
+                           attn::bf16_keys_per_tile(D), 1);
+  if (c.s.n_items > 0x7fffffffLL) { c.status = ATTN_ERR_SHAPE; return c; }
+  return c;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// Exact visible (query, key) pairs of one head, from per-row closed forms.
+long long visible_pairs(int S, int mask, int window, const int* g, int ng) {
+  const long long n = S;
+  switch (mask) {
+    case ATTN_MASK_FULL: return n * n;
+    case ATTN_MASK_CAUSAL: return n * (n + 1) / 2;
+    case ATTN_MASK_CAUSAL_WINDOW: {
+      const long long w = std::min<long long>(window, n);
+      return w * (w + 1) / 2 + (n - w) * w;  // rows i < w see i+1 keys, the rest w
+    }
+    default: {
+      long long tot = 0;
+      const long long w = window;
+      for (long long i = 0; i < n; ++i) {
+        bool is_g = std::binary_search(g, g + ng, (int)i);
+        if (is_g) { tot += n; continue; }
+        long long band = std::min(i, w) + std::min(n - 1 - i, w) + 1;
+        for (int t = 0; t < ng; ++t) {
+          long long d = i - g[t];
+          if (d > w || -d > w) ++band;
+        }
+        tot += band;
+      }
+      return tot;
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int S,
+             int D, int mask_kind, int window, const int* global_idx, int n_global, float scale,
+             int dtype, void* stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  Checked c = check_args(B, Hq, Hkv, S, D, mask_kind, window, global_idx, n_global, dtype);
+  if (c.status != ATTN_OK) return c.status;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  for (const void* ptr : {q, k, v, (const void*)o})
+    if ((uintptr_t)ptr % 16 != 0) return ATTN_ERR_ALIGN;
+  const size_t esz = dtype == ATTN_DTYPE_BF16 ? 2 : 4;
+  const size_t nq = (size_t)B * Hq * S * D * esz, nkv = (size_t)B * Hkv * S * D * esz;
+  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
+    return ATTN_ERR_ALIAS;
+
+  KParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o;
+  p.s = c.s;
+  p.scale = scale;
+  p.c = std::fabs(scale) * 1.4426950408889634f;
+  p.qmode = scale > 0.f ? 0 : (scale < 0.f ? 1 : 2);
+  if (p.qmode == 2) p.c = 1.f;  // all visible scores equal: weights are uniform
+  std::copy(c.gpos, c.gpos + c.n_global, p.gpos);
+
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t err = dtype == ATTN_DTYPE_BF16 ? attn::launch_bf16(p, D, st) : attn::launch_fp32(p, D, st);
+  return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_plan(int B, int Hq, int Hkv, int S, int D, int mask_kind, int window,
+              const int* global_idx, int n_global, int dtype, attn_plan_info* info) {
+  if (!info) return ATTN_ERR_NULL;
+  Checked c = check_args(B, Hq, Hkv, S, D, mask_kind, window, global_idx, n_global, dtype);
+  if (c.status != ATTN_OK) return c.status;
+  const Sched& s = c.s;
+  attn_plan_info r{};
+  r.work_items = s.n_items;
+  r.rows_per_item = s.BMh;
+  r.heads_per_item = s.HP;
+  r.keys_per_tile = s.BN;
+  r.kernel = dtype == ATTN_DTYPE_BF16 ? 1 : 0;
+  // Walk one pair's items (all pairs are alike) and scale by the pair count.
+  long long visits = 0, partial = 0;
+  for (long long id = 0; id < s.n_items; id += s.P) {
+    attn::Item it = attn::decode_item(s, id);
+    int r0 = 0, r1 = 0;
+    if (!it.is_global) { r0 = it.blk * s.BMh; r1 = std::min(r0 + s.BMh, s.S) - 1; }
+    int klo, khi;
+    attn::key_range(s, it.is_global, r0, r1, &klo, &khi);
+    const int kt_lo = klo / s.BN, kt_hi = khi / s.BN;
+    const int strip = (!it.is_global && s.n_global > 0) ? attn::cdiv(s.n_global, s.BN) : 0;
+    visits += (kt_hi - kt_lo + 1) + strip;
+    partial += strip;
+    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+      int cls = it.is_global ? ((long long)kt * s.BN + s.BN > s.S ? attn::TILE_PARTIAL : attn::TILE_FULL)
+                             : attn::classify_tile(s.mask, s.window, s.S, r0, r1, kt * s.BN, s.BN);
+      if (cls == attn::TILE_PARTIAL) ++partial;
+    }
+  }
+  r.tile_visits = visits * s.P;
+  r.partial_tiles = partial * s.P;
+  r.visible_pairs = visible_pairs(S, mask_kind, window, c.gpos, c.n_global);
+  r.effective_flops = 4.0 * D * (double)r.visible_pairs * B * Hq;
+  *info = r;
+  return ATTN_OK;
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_NULL: return "ATTN_ERR_NULL";
+    case ATTN_ERR_SHAPE: return "ATTN_ERR_SHAPE";
+    case ATTN_ERR_HEADS: return "ATTN_ERR_HEADS";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_WINDOW: return "ATTN_ERR_WINDOW";
+    case ATTN_ERR_GLOBAL: return "ATTN_ERR_GLOBAL";
+    case ATTN_ERR_ALIGN: return "ATTN_ERR_ALIGN";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+    case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS";
+    case ATTN_ERR_SCALE: return "ATTN_ERR_SCALE";
+    default: return "ATTN_ERR_UNKNOWN";
+  }
+}
+
+int attn_version(void) { return kVersion; }
+
+}  // extern "C"

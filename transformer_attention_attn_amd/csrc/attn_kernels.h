@@ -1,0 +1,35 @@
+// attn_kernels.h -- parameters shared by the host dispatcher and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "attn_sched.h"
+
+namespace attn {
+
+constexpr int kMaxGlobal = 64;
+constexpr int kThreads = 256;  // four wave64 per workgroup
+
+// Passed by value as the kernel argument block.
+struct KParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  Sched s;
+  float scale;   // fp32 kernel: the caller's scale
+  float c;       // bf16 kernel: |scale| * log2(e) (> 0), see qmode
+  int qmode;     // bf16 kernel: 0 use q, 1 use -q (negative scale), 2 use 0 (zero scale)
+  int gpos[kMaxGlobal];  // sorted distinct global-token positions (n_global of them)
+};
+
+// Workgroup shapes used by the two kernels.
+constexpr int kF32Rows = 64;   // query rows per fp32 work item (one head)
+constexpr int kF32Keys = 32;   // keys per fp32 tile
+constexpr int kBf16Rows = 128; // query rows per bf16 work item (32 per wave, heads packed)
+ATTN_HD int bf16_keys_per_tile(int D) { return 8192 / D; }  // 16 KiB bf16 K tile
+
+hipError_t launch_fp32(const KParams& p, int D, hipStream_t stream);
+hipError_t launch_bf16(const KParams& p, int D, hipStream_t stream);
+
+}  // namespace attn
