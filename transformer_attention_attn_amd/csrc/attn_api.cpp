@@ -143,7 +143,7 @@ int attn_plan(int B, int Hq, int Hkv, int S, int D, int mask_kind, int window,
   // Walk one pair's items (all pairs are alike) and scale by the pair count.
   long long visits = 0, partial = 0;
   for (long long id = 0; id < s.n_items; id += s.P) {
-    attn::Item it = attn::decode_item(s, id);
+    attn::Item it = attn::decode_item(s, (int)id);
     int r0 = 0, r1 = 0;
     if (!it.is_global) { r0 = it.blk * s.BMh; r1 = std::min(r0 + s.BMh, s.S) - 1; }
     int klo, khi;

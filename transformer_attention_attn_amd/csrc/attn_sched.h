@@ -83,26 +83,27 @@ ATTN_HD Sched make_sched(int B, int Hq, int Hkv, int S, int mask, int window, in
 // the same XCD (workgroups are dealt to the 8 XCDs round-robin by id) and the
 // pair's K/V stays in that XCD's L2.  Causal masks visit row blocks from the
 // last (most key tiles) to the first, so the longest items start first.
-ATTN_HD Item decode_item(const Sched& s, long long id) {
+ATTN_HD Item decode_item(const Sched& s, int id) {
+  // 32-bit arithmetic: the host rejects launches with more than 2^31 - 1 items
   Item it;
-  long long pair, rank;
-  if (id < s.n_global_items) {
+  int pair, rank;
+  const int ngi = (int)s.n_global_items;
+  if (id < ngi) {
     it.is_global = 1;
     pair = id % s.P;
     rank = id / s.P;
-    it.blk = (int)rank;
+    it.blk = rank;
   } else {
     it.is_global = 0;
-    long long w = id - s.n_global_items;
+    const int w = id - ngi;
     pair = w % s.P;
     rank = w / s.P;
-    int heavy_last = (s.mask == MASK_CAUSAL || s.mask == MASK_CAUSAL_WINDOW);
-    it.blk = heavy_last ? (s.T - 1 - (int)rank) : (int)rank;
+    const int heavy_last = (s.mask == MASK_CAUSAL || s.mask == MASK_CAUSAL_WINDOW);
+    it.blk = heavy_last ? (s.T - 1 - rank) : rank;
   }
-  int p = (int)pair;
-  int per_b = s.Hkv * s.NHG;
-  it.b = p / per_b;
-  int rem = p % per_b;
+  const int per_b = s.Hkv * s.NHG;
+  it.b = pair / per_b;
+  const int rem = pair % per_b;
   it.kvh = rem / s.NHG;
   it.hg = rem % s.NHG;
   return it;
@@ -134,6 +135,17 @@ ATTN_HD bool visible_band(int mask, int window, int i, int j) {
     case MASK_CAUSAL_WINDOW: return j <= i && j > i - window;
     case MASK_LOCAL_GLOBAL: { int d = i - j; return d <= window && -d <= window; }
     default: return true;
+  }
+}
+
+// Visible keys of band row i, as an inclusive interval [*lo, *hi] of absolute
+// key positions (globals excluded; the tail j < S is applied by the caller).
+ATTN_HD void row_interval(int mask, int window, int S, int i, long long* lo, long long* hi) {
+  switch (mask) {
+    case MASK_CAUSAL: *lo = 0; *hi = i; break;
+    case MASK_CAUSAL_WINDOW: *lo = (long long)i - window + 1; *hi = i; break;
+    case MASK_LOCAL_GLOBAL: *lo = (long long)i - window; *hi = (long long)i + window; break;
+    default: *lo = 0; *hi = (long long)S - 1; break;
   }
 }
 

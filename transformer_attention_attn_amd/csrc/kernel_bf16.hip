@@ -72,7 +72,7 @@ void attn_fwd_bf16(KParams p) {
   const Sched& s = p.s;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31;
   const int hf = lane >> 5;  // lane half: selects the k sub-range of an MFMA operand
   const Item it = decode_item(s, blockIdx.x);
@@ -133,38 +133,53 @@ void attn_fwd_bf16(KParams p) {
   const int has_strip = (MASK == MASK_LOCAL_GLOBAL && !it.is_global && s.n_global > 0) ? 1 : 0;
   const int n_it = (kt_hi - kt_lo + 1) + has_strip;
 
-  // Loader assignment.  K: chunk f = n*256 + tid -> key f / KCH, chunk f % KCH
-  // (16 consecutive lanes read one 256-byte row).  V: thread owns 8 keys x 4
-  // dims: key group vg = tid / (D/4) -> (c, h) = (vg >> 1, vg & 1), keys
-  // 16c + 4h + {0..3} and 16c + 8 + 4h + {0..3} (the key order of the P^T
-  // operand), dims 4 * (tid % (D/4)) + [0, 4).
+  // Loader assignment.  K: 16-byte chunk f = n*256 + tid of the tile, i.e. key
+  // f / KCH, chunk f % KCH (16 consecutive lanes read one row), byte offset
+  // f * 16 within the tile.  V: thread owns 8 keys x 4 dims: key group
+  // vg = tid / (D/4) -> (c, h) = (vg >> 1, vg & 1), keys 16c + 4h + {0..3} and
+  // 16c + 8 + 4h + {0..3} (the key order of the P^T operand), dims
+  // 4 * (tid % (D/4)) + [0, 4).
   const int vg = tid / (D / 4);
   const int vdg = tid % (D / 4);
   const int vc = vg >> 1, vh = vg & 1;
+  const int v_off = (16 * vc + 4 * vh) * D * 2 + vdg * 8;  // + key step (t&3) + 8 (t>>2) rows
 
   u32x4 kreg[KLOADS];
   u32x2 vreg[8];
 
-  auto key_row = [&](int iter, int key) -> int {
-    if (MASK == MASK_LOCAL_GLOBAL && has_strip && iter == 0)
-      return key < s.n_global ? gpos_s[key] : -1;
-    const int pos = (kt_lo + iter - has_strip) * BN + key;
-    return pos < s.S ? pos : -1;
+  // Band tile kt through raw buffer loads: the descriptor covers only the
+  // rows [kt*BN, min(S, kt*BN + BN)), so rows past the end read as zero and no
+  // per-lane address arithmetic or branch is needed.
+  auto load_band = [&](int kt) {
+    const int row0 = kt * BN;
+    const int nbytes = imin(BN, s.S - row0) * D * 2;
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kp + (size_t)row0 * D), (short)0, nbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vp + (size_t)row0 * D), (short)0, nbytes, 0x00020000);
+#pragma unroll
+    for (int n = 0; n < KLOADS; ++n)
+      kreg[n] = __builtin_amdgcn_raw_buffer_load_b128(kr, tid * 16, n * kThreads * 16, 0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      vreg[t] = __builtin_amdgcn_raw_buffer_load_b64(vr, v_off + ((t & 3) + 8 * (t >> 2)) * D * 2, 0, 0);
   };
 
-  auto load_tile = [&](int iter) {
+  // Strip tile: the global tokens' rows, gathered; slots past n_global repeat
+  // a valid row (their scores are masked, so they carry zero weight).
+  auto load_strip = [&]() {
 #pragma unroll
     for (int n = 0; n < KLOADS; ++n) {
       const int f = n * kThreads + tid;
       const int key = f / KCH, ch = f % KCH;
-      const int row = key_row(iter, key);
-      kreg[n] = row >= 0 ? *(const u32x4*)(kp + (size_t)row * D + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+      const int row = gpos_s[imin(key, s.n_global - 1)];
+      kreg[n] = *(const u32x4*)(kp + (size_t)row * D + ch * 8);
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int key = 16 * vc + 4 * vh + (t & 3) + 8 * (t >> 2);
-      const int row = key_row(iter, key);
-      vreg[t] = row >= 0 ? *(const u32x2*)(vp + (size_t)row * D + vdg * 4) : u32x2{0u, 0u};
+      const int row = gpos_s[imin(key, s.n_global - 1)];
+      vreg[t] = *(const u32x2*)(vp + (size_t)row * D + vdg * 4);
     }
   };
 
@@ -198,24 +213,32 @@ void attn_fwd_bf16(KParams p) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY;  // running max of the log2-unit scores of query q_row
-  float l_run = 0.f;        // this lane's share of the denominator (its 16 of each 32 keys)
+  // m_run: the reference maximum (in units of q.k) the weights of query q_row
+  // are exponentiated against.  It is raised only when a tile's maximum
+  // exceeds it by more than 2^kLazy in weight, so the output rescale is rare;
+  // weights are then at most 2^kLazy, far inside fp32 and bf16 range, and
+  // O / l is unchanged (numerator and denominator share the reference).
+  constexpr float kLazy = 8.f;
+  float m_run = -INFINITY;
+  float l_run = 0.f;  // this lane's share of the denominator (its 16 of each 32 keys)
   const float c = p.c;
   const int lswz = l32 ^ ((l32 >> 3) & 3);  // V^T read slot within a 32-dim block
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
-  load_tile(0);
+  if (has_strip) load_strip(); else load_band(kt_lo);
   store_tile(0);
 
   for (int iter = 0; iter < n_it; ++iter) {
     __syncthreads();  // tile iter is in LDS; buffer (iter+1)&1 is free
     const bool more = iter + 1 < n_it;
-    if (more) load_tile(iter + 1);
+    const int kt = kt_lo + iter - has_strip;
+    if (more) load_band(kt + 1);
 
     const int buf = iter & 1;
     const unsigned char* kb = smem + buf * BUF;
     const unsigned char* vb = kb + KTILE;
     const bool strip = has_strip && iter == 0;
-    const int kt = kt_lo + iter - has_strip;
 
     int cls;
     if (!wave_active) cls = TILE_EMPTY;
@@ -238,27 +261,40 @@ void attn_fwd_bf16(KParams p) {
         }
       }
       // per-element mask on partial tiles; register r of block kbk holds key
-      // 32*kbk + 8*(r/4) + 4*hf + r%4 for query q_row
+      // 32*kbk + 8*(r/4) + 4*hf + r%4 of the tile for query q_row
       if (cls == TILE_PARTIAL) {
+        asm volatile("");  // keep this a branch: full tiles skip it
+        if (MASK == MASK_LOCAL_GLOBAL && strip) {
 #pragma unroll
-        for (int kbk = 0; kbk < NKB; ++kbk)
+          for (int kbk = 0; kbk < NKB; ++kbk)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbk * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            bool vis;
-            if (MASK == MASK_LOCAL_GLOBAL && strip) {
-              if (key < s.n_global) {
-                const int dist = q_row - gpos_s[key];
-                vis = dist > s.window || -dist > s.window;
-              } else {
-                vis = false;
-              }
-            } else {
-              const int kpos = kt * BN + key;
-              vis = kpos < s.S && (it.is_global || visible_band(MASK, s.window, q_row, kpos));
+            for (int r = 0; r < 16; ++r) {
+              const int key = kbk * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+              const int dist = q_row - gpos_s[key < kMaxGlobal ? key : 0];
+              const bool vis = key < s.n_global && (dist > s.window || -dist > s.window);
+              sacc[kbk][r] = vis ? sacc[kbk][r] : -INFINITY;
             }
-            sacc[kbk][r] = vis ? sacc[kbk][r] : -INFINITY;
-          }
+        } else {
+          // visible keys of this lane's query as an interval of tile-relative
+          // indices, shifted by the lane half so each test is against an
+          // immediate: lo <= 32*kbk + 8*(r/4) + r%4 <= hi
+          long long lo, hi;
+          if (it.is_global) { lo = 0; hi = (long long)s.S - 1; }
+          else row_interval(MASK, s.window, s.S, q_row, &lo, &hi);
+          const long long base = (long long)kt * BN + 4 * hf;
+          const long long tail = (long long)s.S - 1;
+          const int lo_r = (int)(lo - base < -1 ? -1 : (lo - base > BN ? BN : lo - base));
+          const long long hi_a = hi < tail ? hi : tail;
+          const int hi_r = (int)(hi_a - base < -1 ? -1 : (hi_a - base > BN ? BN : hi_a - base));
+#pragma unroll
+          for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kbk * 32 + 8 * (r >> 2) + (r & 3);
+              const bool vis = key >= lo_r && key <= hi_r;
+              sacc[kbk][r] = vis ? sacc[kbk][r] : -INFINITY;
+            }
+        }
       }
       // online softmax (scores in units of q.k; c = |scale| log2 e)
       float mx = -INFINITY;
@@ -267,29 +303,32 @@ void attn_fwd_bf16(KParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kbk][r]);
       mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
-      m_run = m_new;
-      l_run *= alpha;
+      if (__builtin_amdgcn_ballot_w64(mx * c > m_run * c + kLazy)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      const float mc = m_use * c;
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
       bf16x8 pb[NPC];
 #pragma unroll
       for (int kbk = 0; kbk < NKB; ++kbk)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          float pv[8];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            pv[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kbk][half * 8 + t], c, -mc));
-            l_run += pv[t];
+          for (int t = 0; t < 8; t += 2) {
+            bf16x2 pr;
+            pr[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kbk][half * 8 + t], c, -mc));
+            pr[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kbk][half * 8 + t + 1], c, -mc));
+            // the denominator sums exactly the rounded weights used in P.V
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+            pb[kbk * 2 + half][t] = pr[0];
+            pb[kbk * 2 + half][t + 1] = pr[1];
           }
-#pragma unroll
-          for (int t = 0; t < 8; ++t) pb[kbk * 2 + half][t] = (__bf16)pv[t];
         }
       // O^T += V^T P^T
 #pragma unroll
