@@ -65,6 +65,13 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
+    # a kernel template whose host pass failed silently leaves its launch stub undefined
+    nm = shutil.which("nm")
+    if nm:
+        undef = subprocess.run([nm, "-u", tmp], capture_output=True, text=True).stdout
+        bad = [line for line in undef.splitlines() if "__device_stub__" in line]
+        if bad:
+            raise RuntimeError("undefined kernel launch stubs in libattn.so:\n" + "\n".join(bad))
     os.replace(tmp, LIB)
     return LIB
 

@@ -27,7 +27,7 @@ struct KParams {
 constexpr int kF32Rows = 64;   // query rows per fp32 work item (one head)
 constexpr int kF32Keys = 32;   // keys per fp32 tile
 constexpr int kBf16Rows = 128; // query rows per bf16 work item (32 per wave, heads packed)
-ATTN_HD int bf16_keys_per_tile(int D) { return 8192 / D; }  // 16 KiB bf16 K tile
+ATTN_HD int bf16_keys_per_tile(int) { return 64; }
 
 hipError_t launch_fp32(const KParams& p, int D, hipStream_t stream);
 hipError_t launch_bf16(const KParams& p, int D, hipStream_t stream);

@@ -18,14 +18,22 @@
 //     registers (converted to bf16, round to nearest even), A = V^T from a
 //     transposed LDS tile.  The accumulator lane again owns one query, so the
 //     rescale factor is a per-lane scalar.
-//   * K and V tiles (16 KiB each) are double-buffered in LDS; the next tile's
-//     global loads are issued before the current tile's matrix work and land
-//     in LDS after it, so HBM latency hides behind the MFMAs.
+//   * Software pipeline over key tiles j: while the matrix cores compute
+//     S(j+1) = K(j+1) Q^T, the vector ALUs run the softmax of S(j); while they
+//     compute O += V(j) P(j), the vector ALUs finish P(j).  The order is pinned
+//     with sched_group_barrier.  K is fetched two tiles ahead and V one tile
+//     ahead, straight from HBM into LDS (buffer/global loads with the LDS
+//     flag: no staging registers), double-buffered, one barrier per tile.
+//     V^T operands come from row-major V tiles through ds_read_b64_tr_b16.
+//     MFMA accumulation chains are interleaved (a dependent MFMA waits ~44
+//     cycles, an independent one issues every 32).
+//   * The output rescale runs only when a row maximum grows by more than a
+//     factor 2^8 (weights stay <= 2^8, far inside bf16/fp32 range); O / l is
+//     unchanged by the choice of reference maximum.
 //   * Query heads that share a key/value head are packed into one workgroup
 //     (up to four, one per wave), so each K/V tile is staged once per group.
-//   * Fully masked tiles are never visited (mask-aware key-tile ranges), and
-//     a wave skips the matrix work of tiles that are empty for its own rows;
-//     only partial tiles evaluate the per-element mask.
+//   * Fully masked tiles are never visited (mask-aware key-tile ranges); only
+//     partial tiles evaluate the per-element mask.
 #include "attn_kernels.h"
 
 namespace attn {
@@ -33,10 +41,15 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int BN = 64;           // keys per tile
+constexpr int NKB = BN / 32;     // 32-key blocks of S^T
+constexpr int NPC = BN / 16;     // 16-key reduction steps of O^T
+constexpr float kLazy = 8.f;     // rescale threshold, log2 units
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -49,24 +62,49 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(x, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 
+// LDS-DMA and transpose-read wrappers (plain device functions, so that the
+// host pass of the template kernel sees ordinary calls)
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// 16 bytes per lane from global memory into LDS at dst + 16 * lane (dst wave-uniform)
+__device__ __forceinline__ void dma16_global(const void* src, unsigned char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+}
+// same through a buffer descriptor (byte offsets voff per lane + soff uniform)
+__device__ __forceinline__ void dma16_buffer(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int voff,
+                                             int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, voff, soff, 0, 0);
+}
+// two transposed 8-byte reads (see the V^T operand comment in the kernel)
+__device__ __forceinline__ bf16x8 lds_read_tr_pair(const unsigned char* p0, const unsigned char* p1) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p0);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p1);
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int D>
+struct Cfg {
+  static constexpr int NDC = D / 16;            // 16-dim reduction steps of S^T
+  static constexpr int NDB = D / 32;            // 32-dim blocks of O^T
+  static constexpr int ROWB = D * 2;            // bytes per K or V row
+  static constexpr int REG = BN * ROWB;         // bytes of one K or V tile
+  static constexpr int BUF = 2 * REG;           // K tile then V tile
+  static constexpr int NI = REG / 1024 / 4;     // 1 KiB direct loads per wave per tile
+  static_assert(NI >= 1 && NI * 4 * 1024 == REG, "tile split into 1 KiB wave loads");
+};
+
 template <int D, int MASK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(KParams p) {
-  constexpr int BN = 8192 / D;          // keys per tile (16 KiB of K)
-  constexpr int NKB = BN / 32;          // 32-key blocks of S^T
-  constexpr int NDC = D / 16;           // reduction steps of S^T (16 dims each)
-  constexpr int NDB = D / 32;           // 32-dim blocks of O^T
-  constexpr int NPC = BN / 16;          // reduction steps of O^T (16 keys each)
-  constexpr int KCH = D / 8;            // 16-byte chunks per K row
-  constexpr int KSTRIDE = D * 2 + 16;   // padded K row in LDS: rows r..r+7 hit distinct banks
-  constexpr int KTILE = BN * KSTRIDE;
-  constexpr int VTILE = BN * D * 2;
-  constexpr int BUF = KTILE + VTILE;
-  constexpr int KLOADS = BN * KCH / kThreads;  // 16-byte K chunks per thread per tile
-  static_assert(KLOADS * kThreads == BN * KCH, "K tile split");
-  static_assert((BN / 8) * (D / 4) == kThreads, "V tile split: 8 keys x 4 dims per thread");
+  using C = Cfg<D>;
+  constexpr int NDC = C::NDC, NDB = C::NDB, ROWB = C::ROWB, REG = C::REG, BUF = C::BUF,
+                NI = C::NI;
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * BUF];
   __shared__ int gpos_s[kMaxGlobal];
 
   const Sched& s = p.s;
@@ -132,79 +170,130 @@ void attn_fwd_bf16(KParams p) {
   const int kt_lo = klo / BN, kt_hi = khi / BN;
   const int has_strip = (MASK == MASK_LOCAL_GLOBAL && !it.is_global && s.n_global > 0) ? 1 : 0;
   const int n_it = (kt_hi - kt_lo + 1) + has_strip;
+  auto tile_kt = [&](int iter) { return kt_lo + iter - has_strip; };
+  auto is_strip = [&](int iter) { return MASK == MASK_LOCAL_GLOBAL && has_strip && iter == 0; };
 
-  // Loader assignment.  K: 16-byte chunk f = n*256 + tid of the tile, i.e. key
-  // f / KCH, chunk f % KCH (16 consecutive lanes read one row), byte offset
-  // f * 16 within the tile.  V: thread owns 8 keys x 4 dims: key group
-  // vg = tid / (D/4) -> (c, h) = (vg >> 1, vg & 1), keys 16c + 4h + {0..3} and
-  // 16c + 8 + 4h + {0..3} (the key order of the P^T operand), dims
-  // 4 * (tid % (D/4)) + [0, 4).
-  const int vg = tid / (D / 4);
-  const int vdg = tid % (D / 4);
-  const int vc = vg >> 1, vh = vg & 1;
-  const int v_off = (16 * vc + 4 * vh) * D * 2 + vdg * 8;  // + key step (t&3) + 8 (t>>2) rows
+  // ---- LDS layout and direct (global -> LDS) tile loads ---------------------
+  // A tile region holds BN rows of ROWB bytes, row-major, with the 16-byte
+  // chunks of row r permuted: physical chunk = logical chunk ^ swz(r).
+  //   K: swz = r & 7         -> the K operand reads (8 consecutive rows, one
+  //                              chunk) hit 8 distinct bank groups
+  //   V: swz = (r & 3) << 1  -> the transposed reads (4 consecutive rows, two
+  //                              chunks) hit distinct banks
+  // A direct load writes 1 KiB: lane l of instruction n of wave w fills slot
+  // s = (4n + w)*64 + l, i.e. row s*16/ROWB and physical chunk (s*16 % ROWB)/16;
+  // its source is that row's logical chunk.  Because rows advance by
+  // 4096/ROWB per n (a multiple of 8), the source offset is a per-lane base
+  // plus n*4096.
+  const int slot_b = (wave * 64 + lane) * 16;
+  const int srow = slot_b / ROWB, sphys = (slot_b % ROWB) / 16;
+  const int k_src = srow * ROWB + (sphys ^ (srow & 7)) * 16;
+  const int v_src = srow * ROWB + (sphys ^ ((srow & 3) << 1)) * 16;
 
-  u32x4 kreg[KLOADS];
-  u32x2 vreg[8];
-
-  // Band tile kt through raw buffer loads: the descriptor covers only the
-  // rows [kt*BN, min(S, kt*BN + BN)), so rows past the end read as zero and no
-  // per-lane address arithmetic or branch is needed.
-  auto load_band = [&](int kt) {
+  auto rsrc = [&](const __bf16* base, int kt) {
+    // descriptor over rows [kt*BN, S): whole tiles only (tail tiles clamp rows)
     const int row0 = kt * BN;
-    const int nbytes = imin(BN, s.S - row0) * D * 2;
-    const __amdgpu_buffer_rsrc_t kr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kp + (size_t)row0 * D), (short)0, nbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vp + (size_t)row0 * D), (short)0, nbytes, 0x00020000);
+    const int nbytes = imin(BN, s.S - row0) * ROWB;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)row0 * D), (short)0, nbytes,
+                                             0x00020000);
+  };
+  // rows past S (tail tile) or past n_global (strip) repeat a valid row: their
+  // scores are masked, so they carry zero weight
+  auto load_region = [&](const __bf16* base, int src_lane, int iter, int dst) {
+    if (is_strip(iter)) {
 #pragma unroll
-    for (int n = 0; n < KLOADS; ++n)
-      kreg[n] = __builtin_amdgcn_raw_buffer_load_b128(kr, tid * 16, n * kThreads * 16, 0);
+      for (int n = 0; n < NI; ++n) {
+        const int row = gpos_s[imin(srow + n * (4096 / ROWB), s.n_global - 1)];
+        const int off = row * ROWB + (src_lane - srow * ROWB);
+        dma16_global((const char*)base + off, smem + dst + (n * 4 + wave) * 1024);
+      }
+      return;
+    }
+    const int kt = tile_kt(iter);
+    if (kt * BN + BN <= s.S) {
+      const __amdgpu_buffer_rsrc_t r = rsrc(base, kt);
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      vreg[t] = __builtin_amdgcn_raw_buffer_load_b64(vr, v_off + ((t & 3) + 8 * (t >> 2)) * D * 2, 0, 0);
+      for (int n = 0; n < NI; ++n)
+        dma16_buffer(r, smem + dst + (n * 4 + wave) * 1024, src_lane, n * 4096);
+    } else {
+#pragma unroll
+      for (int n = 0; n < NI; ++n) {
+        const int row = imin(kt * BN + srow + n * (4096 / ROWB), s.S - 1);
+        const size_t off = (size_t)row * ROWB + (src_lane - srow * ROWB);
+        dma16_global((const char*)base + off, smem + dst + (n * 4 + wave) * 1024);
+      }
+    }
+  };
+  auto load_k = [&](int iter, int buf) { load_region(kp, k_src, iter, buf * BUF); };
+  auto load_v = [&](int iter, int buf) { load_region(vp, v_src, iter, buf * BUF + REG); };
+
+  // Per-wave tile class.  Tiles EMPTY for this wave (only at the ends of its
+  // range, or when it holds no rows) are processed as fully masked.
+  auto tile_partial = [&](int iter) -> bool {
+    if (!wave_active || is_strip(iter)) return true;
+    const int kt = tile_kt(iter);
+    if (it.is_global) return kt * BN + BN > s.S;
+    return classify_tile(MASK, s.window, s.S, wqa, wqb, kt * BN, BN) != TILE_FULL;
   };
 
-  // Strip tile: the global tokens' rows, gathered; slots past n_global repeat
-  // a valid row (their scores are masked, so they carry zero weight).
-  auto load_strip = [&]() {
-#pragma unroll
-    for (int n = 0; n < KLOADS; ++n) {
-      const int f = n * kThreads + tid;
-      const int key = f / KCH, ch = f % KCH;
-      const int row = gpos_s[imin(key, s.n_global - 1)];
-      kreg[n] = *(const u32x4*)(kp + (size_t)row * D + ch * 8);
-    }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int key = 16 * vc + 4 * vh + (t & 3) + 8 * (t >> 2);
-      const int row = gpos_s[imin(key, s.n_global - 1)];
-      vreg[t] = *(const u32x2*)(vp + (size_t)row * D + vdg * 4);
-    }
+  // ---- operand reads -------------------------------------------------------
+  // K operand (key 32*kbk + l32, dims 16*dc + 8*hf + [0,8)): logical chunk
+  // 2*dc + hf, physical (2*dc + hf) ^ (l32 & 7) = 2*((dc & 3) ^ (x >> 1)) +
+  // (hf ^ (x & 1)) + 8*(dc >> 2) with x = l32 & 7.
+  const int kx = l32 & 7;
+  const int k_rd = l32 * ROWB + 16 * (hf ^ (kx & 1));
+  auto k_frag = [&](int buf, int kbk, int dc) -> bf16x8 {
+    const int off = buf * BUF + kbk * 32 * ROWB + k_rd + 32 * ((dc & 3) ^ (kx >> 1)) + 128 * (dc >> 2);
+    return *(const bf16x8*)(smem + off);
+  };
+  // V^T operand (dim 32*db + l32, keys 16*pc + 4*hf + [0,4) then +8) from two
+  // ds_read_b64_tr_b16: within each 16-lane group, lane 4t + u addresses the
+  // 4 dims 32*db + 16*g + 4u of key 16*pc + 4*hf + t (g = lane bit 4), and the
+  // transpose hands lane i element (i & 3) of lanes 4t + (i >> 2), t = 0..3,
+  // i.e. dim 32*db + l32 of keys 4*hf + t.  Physical chunk of the 4 dims:
+  // (4*db + 2*g + (u >> 1)) ^ (2*t).
+  const int tt = (lane >> 2) & 3, uu = lane & 3, gg = (lane >> 4) & 1;
+  const int v_rd = (4 * hf + tt) * ROWB + 8 * (uu & 1) + 16 * (2 * (gg ^ (tt & 1)) + (uu >> 1));
+  auto v_frag = [&](int buf, int db, int pc) -> bf16x8 {
+    const int off = buf * BUF + REG + v_rd + 64 * ((db & 1) ^ (tt >> 1)) + 128 * (db >> 1) +
+                    16 * pc * ROWB;
+    return lds_read_tr_pair(smem + off, smem + off + 8 * ROWB);
   };
 
-  auto store_tile = [&](int buf) {
-    unsigned char* kb = smem + buf * BUF;
-    unsigned char* vb = kb + KTILE;
+  // Mask S^T of iteration iter in place.  Register r of block kbk holds key
+  // 32*kbk + 8*(r/4) + 4*hf + r%4 of the tile for query q_row.
+  auto apply_mask = [&](f32x16* sc, int iter) {
+    if (is_strip(iter)) {
 #pragma unroll
-    for (int n = 0; n < KLOADS; ++n) {
-      const int f = n * kThreads + tid;
-      const int key = f / KCH, ch = f % KCH;
-      *(u32x4*)(kb + key * KSTRIDE + ch * 16) = kreg[n];
-    }
-    // transpose 8 keys x 4 dims into 4 slots of 8 keys (one per dim)
+      for (int kbk = 0; kbk < NKB; ++kbk)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 w;
-      w.x = __builtin_amdgcn_perm(vreg[1][j >> 1], vreg[0][j >> 1], sel);
-      w.y = __builtin_amdgcn_perm(vreg[3][j >> 1], vreg[2][j >> 1], sel);
-      w.z = __builtin_amdgcn_perm(vreg[5][j >> 1], vreg[4][j >> 1], sel);
-      w.w = __builtin_amdgcn_perm(vreg[7][j >> 1], vreg[6][j >> 1], sel);
-      const int d = vdg * 4 + j;
-      const int phys = d ^ ((d >> 3) & 3);  // bank-conflict-free for both writes and reads
-      *(u32x4*)(vb + ((vc * 2 + vh) * D + phys) * 16) = w;
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbk * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const int dist = q_row - gpos_s[key];
+          const bool vis = key < s.n_global && (dist > s.window || -dist > s.window);
+          sc[kbk][r] = vis ? sc[kbk][r] : -INFINITY;
+        }
+      return;
     }
+    // visible keys of this lane's query as an interval of tile-relative
+    // indices, shifted by the lane half so each test is against an immediate:
+    // lo <= 32*kbk + 8*(r/4) + r%4 <= hi
+    long long lo, hi;
+    if (it.is_global) { lo = 0; hi = (long long)s.S - 1; }
+    else row_interval(MASK, s.window, s.S, q_row, &lo, &hi);
+    if (!wave_active) hi = lo - 1;
+    const long long base = (long long)tile_kt(iter) * BN + 4 * hf;
+    const long long tail = (long long)s.S - 1;
+    const long long hi_a = hi < tail ? hi : tail;
+    const int lo_r = (int)(lo - base < -1 ? -1 : (lo - base > BN ? BN : lo - base));
+    const int hi_r = (int)(hi_a - base < -1 ? -1 : (hi_a - base > BN ? BN : hi_a - base));
+#pragma unroll
+    for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kbk * 32 + 8 * (r >> 2) + (r & 3);
+        sc[kbk][r] = (key >= lo_r && key <= hi_r) ? sc[kbk][r] : -INFINITY;
+      }
   };
 
   // ---- accumulators --------------------------------------------------------
@@ -213,138 +302,142 @@ void attn_fwd_bf16(KParams p) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  // m_run: the reference maximum (in units of q.k) the weights of query q_row
-  // are exponentiated against.  It is raised only when a tile's maximum
-  // exceeds it by more than 2^kLazy in weight, so the output rescale is rare;
-  // weights are then at most 2^kLazy, far inside fp32 and bf16 range, and
-  // O / l is unchanged (numerator and denominator share the reference).
-  constexpr float kLazy = 8.f;
-  float m_run = -INFINITY;
-  float l_run = 0.f;  // this lane's share of the denominator (its 16 of each 32 keys)
+  float m_run = -INFINITY;  // reference maximum (units of q.k) of query q_row
+  float l_run0 = 0.f, l_run1 = 0.f;  // this lane's share of the denominator (two chains)
   const float c = p.c;
-  const int lswz = l32 ^ ((l32 >> 3) & 3);  // V^T read slot within a 32-dim block
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
-  if (has_strip) load_strip(); else load_band(kt_lo);
-  store_tile(0);
+  // ---- prologue: K(0), V(0) -> buffer 0, K(1) -> buffer 1; S(0) -------------
+  f32x16 scur[NKB], snxt[NKB];
+  load_k(0, 0);
+  load_v(0, 0);
+  if (n_it > 1) load_k(1, 1);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's direct loads have landed
+  __syncthreads();
+#pragma unroll
+  for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) scur[kbk][r] = 0.f;
+#pragma unroll
+  for (int dc = 0; dc < NDC; ++dc)
+#pragma unroll
+    for (int kbk = 0; kbk < NKB; ++kbk) scur[kbk] = mfma32(k_frag(0, kbk, dc), qf[dc], scur[kbk]);
 
   for (int iter = 0; iter < n_it; ++iter) {
-    __syncthreads();  // tile iter is in LDS; buffer (iter+1)&1 is free
-    const bool more = iter + 1 < n_it;
-    const int kt = kt_lo + iter - has_strip;
-    if (more) load_band(kt + 1);
+    // Every wave has left the previous tile (its LDS reads are done) and the
+    // direct loads issued during it have landed.
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    const int cur = iter & 1, nxt = cur ^ 1;
+    if (iter + 2 < n_it) load_k(iter + 2, cur);  // K(j+2) replaces K(j), consumed in tile j-1
+    if (iter + 1 < n_it) load_v(iter + 1, nxt);  // V(j+1) replaces V(j-1)
 
-    const int buf = iter & 1;
-    const unsigned char* kb = smem + buf * BUF;
-    const unsigned char* vb = kb + KTILE;
-    const bool strip = has_strip && iter == 0;
+    if (tile_partial(iter)) {
+      asm volatile("");  // keep this a branch: full tiles skip it
+      apply_mask(scur, iter);
+    }
 
-    int cls;
-    if (!wave_active) cls = TILE_EMPTY;
-    else if (strip) cls = TILE_PARTIAL;
-    else if (it.is_global) cls = (kt * BN + BN > s.S) ? TILE_PARTIAL : TILE_FULL;
-    else cls = classify_tile(MASK, s.window, s.S, wqa, wqb, kt * BN, BN);
-
-    if (cls != TILE_EMPTY) {
-      // S^T = K Q^T
-      f32x16 sacc[NKB];
+    // -- block A: first half of S(j+1) = K(j+1) Q^T beside the row max of S(j).
+    //    S(j+1) is always computed; after the last tile it is unused.
 #pragma unroll
-      for (int kbk = 0; kbk < NKB; ++kbk) {
+    for (int kbk = 0; kbk < NKB; ++kbk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kbk][r] = 0.f;
-        const unsigned char* krow = kb + (kbk * 32 + l32) * KSTRIDE + hf * 16;
+      for (int r = 0; r < 16; ++r) snxt[kbk][r] = 0.f;
+    float mx;
+    {
+      float t[8];
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) {
-          const bf16x8 ka = *(const bf16x8*)(krow + dc * 32);
-          sacc[kbk] = mfma32(ka, qf[dc], sacc[kbk]);
-        }
-      }
-      // per-element mask on partial tiles; register r of block kbk holds key
-      // 32*kbk + 8*(r/4) + 4*hf + r%4 of the tile for query q_row
-      if (cls == TILE_PARTIAL) {
-        asm volatile("");  // keep this a branch: full tiles skip it
-        if (MASK == MASK_LOCAL_GLOBAL && strip) {
-#pragma unroll
-          for (int kbk = 0; kbk < NKB; ++kbk)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kbk * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-              const int dist = q_row - gpos_s[key < kMaxGlobal ? key : 0];
-              const bool vis = key < s.n_global && (dist > s.window || -dist > s.window);
-              sacc[kbk][r] = vis ? sacc[kbk][r] : -INFINITY;
-            }
-        } else {
-          // visible keys of this lane's query as an interval of tile-relative
-          // indices, shifted by the lane half so each test is against an
-          // immediate: lo <= 32*kbk + 8*(r/4) + r%4 <= hi
-          long long lo, hi;
-          if (it.is_global) { lo = 0; hi = (long long)s.S - 1; }
-          else row_interval(MASK, s.window, s.S, q_row, &lo, &hi);
-          const long long base = (long long)kt * BN + 4 * hf;
-          const long long tail = (long long)s.S - 1;
-          const int lo_r = (int)(lo - base < -1 ? -1 : (lo - base > BN ? BN : lo - base));
-          const long long hi_a = hi < tail ? hi : tail;
-          const int hi_r = (int)(hi_a - base < -1 ? -1 : (hi_a - base > BN ? BN : hi_a - base));
-#pragma unroll
-          for (int kbk = 0; kbk < NKB; ++kbk)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kbk * 32 + 8 * (r >> 2) + (r & 3);
-              const bool vis = key >= lo_r && key <= hi_r;
-              sacc[kbk][r] = vis ? sacc[kbk][r] : -INFINITY;
-            }
-        }
-      }
-      // online softmax (scores in units of q.k; c = |scale| log2 e)
-      float mx = -INFINITY;
+      for (int i = 0; i < 8; ++i) t[i] = -INFINITY;
 #pragma unroll
       for (int kbk = 0; kbk < NKB; ++kbk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kbk][r]);
-      mx = pair_max(mx);
-      if (__builtin_amdgcn_ballot_w64(mx * c > m_run * c + kLazy)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
-        m_run = m_new;
-        l_run *= alpha;
+        for (int r = 0; r < 16; r += 2)
+          t[(kbk * 8 + r / 2) & 7] =
+              fmaxf(t[(kbk * 8 + r / 2) & 7], fmaxf(scur[kbk][r], scur[kbk][r + 1]));
+      mx = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
+                 fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
+    }
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+    for (int dc = 0; dc < NDC / 2; ++dc)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-      const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-      bf16x8 pb[NPC];
+      for (int kbk = 0; kbk < NKB; ++kbk) snxt[kbk] = mfma32(k_frag(nxt, kbk, dc), qf[dc], snxt[kbk]);
+    mx = pair_max(mx);
+    const bool need_rescale = __builtin_amdgcn_ballot_w64(mx * c > m_run * c + kLazy) != 0;
+    // schedule: operand reads run ahead of their MFMA; the max tree fills the gaps
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // DS read
 #pragma unroll
-      for (int kbk = 0; kbk < NKB; ++kbk)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-#pragma unroll
-          for (int t = 0; t < 8; t += 2) {
-            bf16x2 pr;
-            pr[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kbk][half * 8 + t], c, -mc));
-            pr[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kbk][half * 8 + t + 1], c, -mc));
-            // the denominator sums exactly the rounded weights used in P.V
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
-            pb[kbk * 2 + half][t] = pr[0];
-            pb[kbk * 2 + half][t + 1] = pr[1];
-          }
-        }
-      // O^T += V^T P^T
+    for (int i = 0; i < NDC / 2 * NKB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+
+    // rare: a row maximum grew by more than 2^kLazy
+    if (need_rescale) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
+      m_run = m_new;
+      l_run0 *= alpha;
+      l_run1 *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int pc = 0; pc < NPC; ++pc) {
-          const bf16x8 va = *(const bf16x8*)(vb + ((pc * 2 + hf) * D + db * 32 + lswz) * 16);
-          oacc[db] = mfma32(va, pb[pc], oacc[db]);
-        }
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+
+    // weights of the 8 registers of one P^T operand -> bf16, added to l
+    bf16x8 pb[NPC];
+    auto make_p = [&](int pc) {
+      const int kbk = pc >> 1, rb = (pc & 1) * 8;
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        bf16x2 pr;
+        pr[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(scur[kbk][rb + t], c, -mc));
+        pr[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(scur[kbk][rb + t + 1], c, -mc));
+        // the denominator sums exactly the rounded weights used in P.V
+        if (t & 2) l_run1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run1, false);
+        else l_run0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run0, false);
+        pb[pc][t] = pr[0];
+        pb[pc][t + 1] = pr[1];
+      }
+    };
+
+    // -- block B: second half of S(j+1) beside the first half of P(j); O +=
+    //    V(j) P(j) beside the second half of P(j).
+    make_p(0);
+    make_p(1);
+#pragma unroll
+    for (int dc = NDC / 2; dc < NDC; ++dc)
+#pragma unroll
+      for (int kbk = 0; kbk < NKB; ++kbk) snxt[kbk] = mfma32(k_frag(nxt, kbk, dc), qf[dc], snxt[kbk]);
+#pragma unroll
+    for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(v_frag(cur, db, pc), pb[pc], oacc[db]);
+    make_p(2);
+    make_p(3);
+#pragma unroll
+    for (int pc = 2; pc < NPC; ++pc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(v_frag(cur, db, pc), pb[pc], oacc[db]);
+    // schedule: 24 MFMAs (8 of S(j+1), 16 of P.V), each followed by ~4 VALU of
+    // the weights and by the operand reads of the MFMAs two steps ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < NDC / 2 * NKB + NPC * NDB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
 
-    if (more) store_tile((iter + 1) & 1);
+#pragma unroll
+    for (int kbk = 0; kbk < NKB; ++kbk) scur[kbk] = snxt[kbk];
   }
 
   // ---- epilogue: O = O^T / l, round to bf16, store --------------------------
   {
+    const float l_run = l_run0 + l_run1;
     const unsigned lu = __float_as_uint(l_run);
     const float l_other = __uint_as_float(__shfl_xor((int)lu, 32));
     const float l_tot = l_run + l_other;
