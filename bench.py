@@ -106,7 +106,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--prewarm", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     args = ap.parse_args(argv)
@@ -139,6 +141,15 @@ def main(argv=None):
         attn.fwd(q, k, v, mask=w.mask, window=w.window, global_idx=g, scale=w.scale, out=out,
                  stream=stream)
 
+    # Untimed warm-up: first about one second of steps (the GPU clocks ramp up
+    # over the first ~100 ms of load), then the requested W warmup steps.
+    t_warm = time.perf_counter()
+    prewarm_steps = 0
+    while time.perf_counter() - t_warm < args.prewarm:
+        for _ in range(5):
+            step()
+        prewarm_steps += 5
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -181,6 +192,7 @@ def main(argv=None):
             "frac": round(tflops / peak, 4),
             "traffic": traffic,
         },
+        "prewarm_steps": prewarm_steps,
         "gpu": torch.cuda.get_device_name(dev),
         "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
     }

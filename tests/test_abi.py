@@ -104,8 +104,9 @@ def test_plan_matches_oracle_counts(case):
     assert info["tile_visits"] * info["keys_per_tile"] * rows * info["heads_per_item"] >= pairs * B * Hq
     if dt == "bf16":
         G = Hq // Hkv
-        assert info["heads_per_item"] == (4 if G % 4 == 0 else 2 if G % 2 == 0 else 1)
-        assert rows * info["heads_per_item"] == 128
+        assert info["heads_per_item"] == (8 if G % 8 == 0 else 4 if G % 4 == 0 else
+                                          2 if G % 2 == 0 else 1)
+        assert rows * info["heads_per_item"] == 256
     else:
         assert (rows, info["heads_per_item"], info["keys_per_tile"]) == (64, 1, 32)
 

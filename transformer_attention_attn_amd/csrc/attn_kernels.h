@@ -8,7 +8,9 @@
 namespace attn {
 
 constexpr int kMaxGlobal = 64;
-constexpr int kThreads = 256;  // four wave64 per workgroup
+constexpr int kThreads = 256;  // fp32 kernel: four wave64 per workgroup
+constexpr int kBf16Waves = 8;  // bf16 kernel: eight wave64 per workgroup, 32 query rows each
+constexpr int kBf16Threads = 64 * kBf16Waves;
 
 // Passed by value as the kernel argument block.
 struct KParams {
@@ -26,7 +28,7 @@ struct KParams {
 // Workgroup shapes used by the two kernels.
 constexpr int kF32Rows = 64;   // query rows per fp32 work item (one head)
 constexpr int kF32Keys = 32;   // keys per fp32 tile
-constexpr int kBf16Rows = 128; // query rows per bf16 work item (32 per wave, heads packed)
+constexpr int kBf16Rows = 32 * kBf16Waves;  // query rows per bf16 work item (heads packed)
 ATTN_HD int bf16_keys_per_tile(int) { return 64; }
 
 hipError_t launch_fp32(const KParams& p, int D, hipStream_t stream);

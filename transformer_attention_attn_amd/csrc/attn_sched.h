@@ -52,11 +52,13 @@ ATTN_HD int cdiv(int a, int b) { return (a + b - 1) / b; }
 ATTN_HD int imin(int a, int b) { return a < b ? a : b; }
 ATTN_HD int imax(int a, int b) { return a > b ? a : b; }
 
-// Heads packed per work item: the largest of {4, 2, 1} dividing G.  Packing the
+// Heads packed per work item: the largest of {8, 4, 2, 1} dividing G.  Packing the
 // query heads of one key/value head into one workgroup lets every staged K/V
 // tile serve all of them ("Transformer 演进与变体", section GQA：分组查询注意力:
 // a group of query heads shares one key/value head).
-ATTN_HD int heads_per_item(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
+ATTN_HD int heads_per_item(int G) {
+  return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+}
 
 ATTN_HD Sched make_sched(int B, int Hq, int Hkv, int S, int mask, int window, int n_global,
                          int rows_per_wg, int BN, int pack_heads) {

@@ -9,7 +9,8 @@
 // units (s = q.k * scale * log2(e)), so exp becomes one v_exp_f32.  Only O is
 // written to HBM.
 //
-// gfx950 mapping (one workgroup = four wave64, 32 query rows per wave):
+// gfx950 mapping (one workgroup = eight wave64, 32 query rows per wave, one
+// workgroup per CU: 256 query rows share every K/V tile staged in LDS):
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q^T
 //     from registers.  In the 32x32 accumulator each lane owns one query
 //     (lane % 32) and 16 of the 32 keys, so the row max and row sum are mostly
@@ -20,10 +21,10 @@
 //     rescale factor is a per-lane scalar.
 //   * Software pipeline over key tiles j: while the matrix cores compute
 //     S(j+1) = K(j+1) Q^T, the vector ALUs run the softmax of S(j); while they
-//     compute O += V(j) P(j), the vector ALUs finish P(j).  The order is pinned
-//     with sched_group_barrier.  K is fetched two tiles ahead and V one tile
-//     ahead, straight from HBM into LDS (buffer/global loads with the LDS
-//     flag: no staging registers), double-buffered, one barrier per tile.
+//     compute O += V(j) P(j), the vector ALUs finish P(j).  K and V go
+//     straight from HBM into LDS (buffer/global loads with the LDS flag: no
+//     staging registers) through a three-stage ring, issued two tiles ahead
+//     of use, with one barrier per tile.
 //     V^T operands come from row-major V tiles through ds_read_b64_tr_b16.
 //     MFMA accumulation chains are interleaved (a dependent MFMA waits ~44
 //     cycles, an independent one issues every 32).
@@ -31,7 +32,7 @@
 //     factor 2^8 (weights stay <= 2^8, far inside bf16/fp32 range); O / l is
 //     unchanged by the choice of reference maximum.
 //   * Query heads that share a key/value head are packed into one workgroup
-//     (up to four, one per wave), so each K/V tile is staged once per group.
+//     (up to eight), so each K/V tile is staged once per group.
 //   * Fully masked tiles are never visited (mask-aware key-tile ranges); only
 //     partial tiles evaluate the per-element mask.
 #include "attn_kernels.h"
@@ -53,6 +54,15 @@ constexpr float kLazy = 8.f;     // rescale threshold, log2 units
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// max(a, b, c) in one v_max3_f32.  fmaxf would add a NaN-quieting v_max per
+// operand (IEEE mode); the scores are max-reduced only to pick the reference
+// maximum, so quieting is not needed.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // max of x over the lane pair (l, l ^ 32)
@@ -93,18 +103,21 @@ struct Cfg {
   static constexpr int ROWB = D * 2;            // bytes per K or V row
   static constexpr int REG = BN * ROWB;         // bytes of one K or V tile
   static constexpr int BUF = 2 * REG;           // K tile then V tile
-  static constexpr int NI = REG / 1024 / 4;     // 1 KiB direct loads per wave per tile
-  static_assert(NI >= 1 && NI * 4 * 1024 == REG, "tile split into 1 KiB wave loads");
+  static constexpr int NSTAGE = 3;              // LDS stages: K(j+1), K(j+2) / V(j), V(j+1) in flight
+  static constexpr int NI = REG / 1024 / kBf16Waves;  // 1 KiB direct loads per wave per tile
+  static_assert(NI >= 1 && NI * kBf16Waves * 1024 == REG, "tile split into 1 KiB wave loads");
+  static_assert(NSTAGE * BUF <= 160 * 1024, "LDS budget of one CU");
 };
 
 template <int D, int MASK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kBf16Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(KParams p) {
   using C = Cfg<D>;
   constexpr int NDC = C::NDC, NDB = C::NDB, ROWB = C::ROWB, REG = C::REG, BUF = C::BUF,
-                NI = C::NI;
+                NI = C::NI, NSTAGE = C::NSTAGE;
+  constexpr int WSTEP = kBf16Waves * 1024;  // bytes one direct load of every wave covers
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * BUF];
   __shared__ int gpos_s[kMaxGlobal];
 
   const Sched& s = p.s;
@@ -121,7 +134,7 @@ void attn_fwd_bf16(KParams p) {
   }
 
   // ---- rows of this wave -------------------------------------------------
-  const int wph = 4 / s.HP;                       // waves per query head
+  const int wph = kBf16Waves / s.HP;              // waves per query head
   const int a = it.kvh * s.G + it.hg * s.HP + wave / wph;
   const int rpart = wave % wph;
   int q_row, wqa = 0, wqb = -1, r0 = 0, r1 = 0;
@@ -180,11 +193,11 @@ void attn_fwd_bf16(KParams p) {
   //                              chunk) hit 8 distinct bank groups
   //   V: swz = (r & 3) << 1  -> the transposed reads (4 consecutive rows, two
   //                              chunks) hit distinct banks
-  // A direct load writes 1 KiB: lane l of instruction n of wave w fills slot
-  // s = (4n + w)*64 + l, i.e. row s*16/ROWB and physical chunk (s*16 % ROWB)/16;
-  // its source is that row's logical chunk.  Because rows advance by
-  // 4096/ROWB per n (a multiple of 8), the source offset is a per-lane base
-  // plus n*4096.
+  // A direct load writes 1 KiB: lane l of instruction n of wave w (of W
+  // waves) fills slot s = (W*n + w)*64 + l, i.e. row s*16/ROWB and physical
+  // chunk (s*16 % ROWB)/16; its source is that row's logical chunk.  Rows
+  // advance by W*1024/ROWB per n (a multiple of 8), so the source offset is a
+  // per-lane base plus n*W*1024.
   const int slot_b = (wave * 64 + lane) * 16;
   const int srow = slot_b / ROWB, sphys = (slot_b % ROWB) / 16;
   const int k_src = srow * ROWB + (sphys ^ (srow & 7)) * 16;
@@ -203,9 +216,9 @@ void attn_fwd_bf16(KParams p) {
     if (is_strip(iter)) {
 #pragma unroll
       for (int n = 0; n < NI; ++n) {
-        const int row = gpos_s[imin(srow + n * (4096 / ROWB), s.n_global - 1)];
+        const int row = gpos_s[imin(srow + n * (WSTEP / ROWB), s.n_global - 1)];
         const int off = row * ROWB + (src_lane - srow * ROWB);
-        dma16_global((const char*)base + off, smem + dst + (n * 4 + wave) * 1024);
+        dma16_global((const char*)base + off, smem + dst + (n * kBf16Waves + wave) * 1024);
       }
       return;
     }
@@ -214,13 +227,13 @@ void attn_fwd_bf16(KParams p) {
       const __amdgpu_buffer_rsrc_t r = rsrc(base, kt);
 #pragma unroll
       for (int n = 0; n < NI; ++n)
-        dma16_buffer(r, smem + dst + (n * 4 + wave) * 1024, src_lane, n * 4096);
+        dma16_buffer(r, smem + dst + (n * kBf16Waves + wave) * 1024, src_lane, n * WSTEP);
     } else {
 #pragma unroll
       for (int n = 0; n < NI; ++n) {
-        const int row = imin(kt * BN + srow + n * (4096 / ROWB), s.S - 1);
+        const int row = imin(kt * BN + srow + n * (WSTEP / ROWB), s.S - 1);
         const size_t off = (size_t)row * ROWB + (src_lane - srow * ROWB);
-        dma16_global((const char*)base + off, smem + dst + (n * 4 + wave) * 1024);
+        dma16_global((const char*)base + off, smem + dst + (n * kBf16Waves + wave) * 1024);
       }
     }
   };
@@ -241,10 +254,11 @@ void attn_fwd_bf16(KParams p) {
   // 2*dc + hf, physical (2*dc + hf) ^ (l32 & 7) = 2*((dc & 3) ^ (x >> 1)) +
   // (hf ^ (x & 1)) + 8*(dc >> 2) with x = l32 & 7.
   const int kx = l32 & 7;
-  const int k_rd = l32 * ROWB + 16 * (hf ^ (kx & 1));
-  auto k_frag = [&](int buf, int kbk, int dc) -> bf16x8 {
-    const int off = buf * BUF + kbk * 32 * ROWB + k_rd + 32 * ((dc & 3) ^ (kx >> 1)) + 128 * (dc >> 2);
-    return *(const bf16x8*)(smem + off);
+  int k_rd[4];  // per-lane part for dc & 3; the rest of the offset is an immediate
+#pragma unroll
+  for (int d4 = 0; d4 < 4; ++d4) k_rd[d4] = l32 * ROWB + 16 * (hf ^ (kx & 1)) + 32 * (d4 ^ (kx >> 1));
+  auto k_frag = [&](const unsigned char* kbuf, int kbk, int dc) -> bf16x8 {
+    return *(const bf16x8*)(kbuf + k_rd[dc & 3] + kbk * 32 * ROWB + 128 * (dc >> 2));
   };
   // V^T operand (dim 32*db + l32, keys 16*pc + 4*hf + [0,4) then +8) from two
   // ds_read_b64_tr_b16: within each 16-lane group, lane 4t + u addresses the
@@ -253,11 +267,14 @@ void attn_fwd_bf16(KParams p) {
   // i.e. dim 32*db + l32 of keys 4*hf + t.  Physical chunk of the 4 dims:
   // (4*db + 2*g + (u >> 1)) ^ (2*t).
   const int tt = (lane >> 2) & 3, uu = lane & 3, gg = (lane >> 4) & 1;
-  const int v_rd = (4 * hf + tt) * ROWB + 8 * (uu & 1) + 16 * (2 * (gg ^ (tt & 1)) + (uu >> 1));
-  auto v_frag = [&](int buf, int db, int pc) -> bf16x8 {
-    const int off = buf * BUF + REG + v_rd + 64 * ((db & 1) ^ (tt >> 1)) + 128 * (db >> 1) +
-                    16 * pc * ROWB;
-    return lds_read_tr_pair(smem + off, smem + off + 8 * ROWB);
+  int v_rd[2];  // per-lane part for db & 1; the rest of the offset is an immediate
+#pragma unroll
+  for (int d2 = 0; d2 < 2; ++d2)
+    v_rd[d2] = (4 * hf + tt) * ROWB + 8 * (uu & 1) + 16 * (2 * (gg ^ (tt & 1)) + (uu >> 1)) +
+               64 * (d2 ^ (tt >> 1));
+  auto v_frag = [&](const unsigned char* vbuf, int db, int pc) -> bf16x8 {
+    const unsigned char* p0 = vbuf + v_rd[db & 1] + 128 * (db >> 1) + 16 * pc * ROWB;
+    return lds_read_tr_pair(p0, p0 + 8 * ROWB);
   };
 
   // Mask S^T of iteration iter in place.  Register r of block kbk holds key
@@ -307,12 +324,28 @@ void attn_fwd_bf16(KParams p) {
   const float c = p.c;
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
-  // ---- prologue: K(0), V(0) -> buffer 0, K(1) -> buffer 1; S(0) -------------
+  // ---- pipeline ---------------------------------------------------------
+  // Tile j lives in stage j % NSTAGE.  Iteration j issues the batch
+  // {K(j+3), V(j+2)} (those that exist) into the stages of K(j) and V(j-1),
+  // both consumed during iteration j-1.  At the top of iteration j the batch of
+  // iteration j-2 (K(j+1), V(j)) must have landed; the batch of iteration j-1
+  // may still be in flight, so vmcnt waits down to its size.
+  auto wait_batch = [&](int j) {
+    // in flight may remain: the batch issued just before iteration j
+    if (j + 2 < n_it) __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * NI));  // vmcnt(2*NI)
+    else if (j + 1 < n_it) __builtin_amdgcn_s_waitcnt(0x0f70 | NI);   // vmcnt(NI)
+    else __builtin_amdgcn_s_waitcnt(0x0f70);                           // vmcnt(0)
+  };
+  auto issue_batch = [&](int j) {
+    if (j + 3 < n_it) load_k(j + 3, (j + 3) % NSTAGE);
+    if (j + 2 < n_it) load_v(j + 2, (j + 2) % NSTAGE);
+  };
   f32x16 scur[NKB], snxt[NKB];
   load_k(0, 0);
   load_v(0, 0);
   if (n_it > 1) load_k(1, 1);
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's direct loads have landed
+  issue_batch(-1);  // K(2), V(1)
+  wait_batch(0);
   __syncthreads();
 #pragma unroll
   for (int kbk = 0; kbk < NKB; ++kbk)
@@ -321,16 +354,17 @@ void attn_fwd_bf16(KParams p) {
 #pragma unroll
   for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
-    for (int kbk = 0; kbk < NKB; ++kbk) scur[kbk] = mfma32(k_frag(0, kbk, dc), qf[dc], scur[kbk]);
+    for (int kbk = 0; kbk < NKB; ++kbk) scur[kbk] = mfma32(k_frag(smem, kbk, dc), qf[dc], scur[kbk]);
 
   for (int iter = 0; iter < n_it; ++iter) {
-    // Every wave has left the previous tile (its LDS reads are done) and the
-    // direct loads issued during it have landed.
-    __builtin_amdgcn_s_waitcnt(0x0f70);
+    // Every wave has left the previous tile (its LDS reads are done), and
+    // K(j+1), V(j) have landed.
+    wait_batch(iter);
     __syncthreads();
-    const int cur = iter & 1, nxt = cur ^ 1;
-    if (iter + 2 < n_it) load_k(iter + 2, cur);  // K(j+2) replaces K(j), consumed in tile j-1
-    if (iter + 1 < n_it) load_v(iter + 1, nxt);  // V(j+1) replaces V(j-1)
+    const int cur = iter % NSTAGE, nxt = (iter + 1) % NSTAGE;
+    issue_batch(iter);
+    const unsigned char* kbuf_nxt = smem + nxt * BUF;      // K(j+1)
+    const unsigned char* vbuf_cur = smem + cur * BUF + REG;  // V(j)
 
     if (tile_partial(iter)) {
       asm volatile("");  // keep this a branch: full tiles skip it
@@ -345,32 +379,24 @@ void attn_fwd_bf16(KParams p) {
       for (int r = 0; r < 16; ++r) snxt[kbk][r] = 0.f;
     float mx;
     {
-      float t[8];
+      // four independent v_max3 chains over the 32 scores of this lane, then join
+      float t[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) t[i] = -INFINITY;
-#pragma unroll
-      for (int kbk = 0; kbk < NKB; ++kbk)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2)
-          t[(kbk * 8 + r / 2) & 7] =
-              fmaxf(t[(kbk * 8 + r / 2) & 7], fmaxf(scur[kbk][r], scur[kbk][r + 1]));
-      mx = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
-                 fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int kbk = c4 >> 1, rb = (c4 & 1) * 8;
+        float x = max3f(scur[kbk][rb], scur[kbk][rb + 1], scur[kbk][rb + 2]);
+        x = max3f(x, scur[kbk][rb + 3], scur[kbk][rb + 4]);
+        x = max3f(x, scur[kbk][rb + 5], scur[kbk][rb + 6]);
+        t[c4] = max3f(x, scur[kbk][rb + 7], scur[kbk][rb + 7]);
+      }
+      mx = max3f(max3f(t[0], t[1], t[2]), t[3], t[3]);
     }
 #pragma unroll
     for (int dc = 0; dc < NDC / 2; ++dc)
 #pragma unroll
-      for (int kbk = 0; kbk < NKB; ++kbk) snxt[kbk] = mfma32(k_frag(nxt, kbk, dc), qf[dc], snxt[kbk]);
+      for (int kbk = 0; kbk < NKB; ++kbk) snxt[kbk] = mfma32(k_frag(kbuf_nxt, kbk, dc), qf[dc], snxt[kbk]);
     mx = pair_max(mx);
     const bool need_rescale = __builtin_amdgcn_ballot_w64(mx * c > m_run * c + kLazy) != 0;
-    // schedule: operand reads run ahead of their MFMA; the max tree fills the gaps
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // DS read
-#pragma unroll
-    for (int i = 0; i < NDC / 2 * NKB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    }
 
     // rare: a row maximum grew by more than 2^kLazy
     if (need_rescale) {
@@ -410,27 +436,17 @@ void attn_fwd_bf16(KParams p) {
 #pragma unroll
     for (int dc = NDC / 2; dc < NDC; ++dc)
 #pragma unroll
-      for (int kbk = 0; kbk < NKB; ++kbk) snxt[kbk] = mfma32(k_frag(nxt, kbk, dc), qf[dc], snxt[kbk]);
+      for (int kbk = 0; kbk < NKB; ++kbk) snxt[kbk] = mfma32(k_frag(kbuf_nxt, kbk, dc), qf[dc], snxt[kbk]);
 #pragma unroll
     for (int pc = 0; pc < 2; ++pc)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(v_frag(cur, db, pc), pb[pc], oacc[db]);
+      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(v_frag(vbuf_cur, db, pc), pb[pc], oacc[db]);
     make_p(2);
     make_p(3);
 #pragma unroll
     for (int pc = 2; pc < NPC; ++pc)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(v_frag(cur, db, pc), pb[pc], oacc[db]);
-    // schedule: 24 MFMAs (8 of S(j+1), 16 of P.V), each followed by ~4 VALU of
-    // the weights and by the operand reads of the MFMAs two steps ahead
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int i = 0; i < NDC / 2 * NKB + NPC * NDB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-
+      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(v_frag(vbuf_cur, db, pc), pb[pc], oacc[db]);
 #pragma unroll
     for (int kbk = 0; kbk < NKB; ++kbk) scur[kbk] = snxt[kbk];
   }
@@ -463,7 +479,7 @@ void attn_fwd_bf16(KParams p) {
 
 template <int D>
 hipError_t launch_d(const KParams& p, hipStream_t stream) {
-  dim3 grid((unsigned)p.s.n_items), block(kThreads);
+  dim3 grid((unsigned)p.s.n_items), block(kBf16Threads);
   switch (p.s.mask) {
     case MASK_FULL: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_FULL>), grid, block, 0, stream, p); break;
     case MASK_CAUSAL: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL>), grid, block, 0, stream, p); break;
