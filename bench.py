@@ -111,6 +111,9 @@ def main(argv=None):
                     help="seconds of untimed steps before the warmup steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one plain elementwise copy of this many MiB (fp32 in, fp32 "
+                         "out), whose HBM counters scale the attention kernel's")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -136,6 +139,16 @@ def main(argv=None):
     flops = plan["effective_flops"]
 
     stream = torch.cuda.current_stream(dev)
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 18  # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)  # reads and writes exactly n * 4 bytes
+        torch.cuda.synchronize()
+        print(f"bench: calibration copy of {n * 4} bytes done", file=sys.stderr, flush=True)
+        del src, dst
 
     def step():
         attn.fwd(q, k, v, mask=w.mask, window=w.window, global_idx=g, scale=w.scale, out=out,

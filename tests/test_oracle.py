@@ -321,6 +321,52 @@ def pin_sampled_rows_match_full():
     assert np.array_equal(part, full[:, :, rows])
 
 
+def online_softmax_attention(q, k, v, mask, scale, block, lazy):
+    """Blockwise online softmax in float64 ("Transformer 演进与变体", section
+    Flash Attention: per key block update the running maximum m, rescale the
+    running denominator l and the accumulator by exp(m_old - m_new), add the
+    block's exp(s - m_new)).  With lazy > 0 the reference maximum moves only
+    when the block maximum exceeds it by more than lazy (natural-log units),
+    the variant the GPU kernels use; the result must not change."""
+    B, Hq, S, D = q.shape
+    G = Hq // k.shape[1]
+    out = np.empty_like(q)
+    for b in range(B):
+        for a in range(Hq):
+            qa, ka, va = q[b, a], k[b, a // G], v[b, a // G]
+            m = np.full(S, -np.inf)
+            l = np.zeros(S)
+            acc = np.zeros((S, D))
+            for j0 in range(0, S, block):
+                s = scale * (qa @ ka[j0:j0 + block].T)
+                s[~mask[:, j0:j0 + block]] = -np.inf
+                bmax = s.max(axis=1)
+                move = bmax > m + lazy
+                m_new = np.where(move, bmax, m)
+                with np.errstate(invalid="ignore"):  # -inf - -inf, discarded by the where
+                    alpha = np.where(np.isneginf(m_new), 1.0, np.exp(m - m_new))
+                    p = np.where(np.isneginf(s), 0.0, np.exp(s - m_new[:, None]))
+                l = alpha * l + p.sum(axis=1)
+                acc = alpha[:, None] * acc + p @ va[j0:j0 + block]
+                m = m_new
+            out[b, a] = acc / l[:, None]
+    return out
+
+
+def pin_online_softmax_recurrence():
+    for kind, w, g in (("full", 0, ()), ("causal", 0, ()), ("causal_window", 5, ()),
+                       ("local_global", 3, (0, 17, 30))):
+        S, D = 37, 8
+        q, k, v = randn(2, 4, S, D), randn(2, 2, S, D), randn(2, 2, S, D)
+        q[0, 1, 5] *= 40.0  # a row whose block maxima jump far above the first block's
+        mask = torch_mask(S, kind, w, g).numpy()
+        ref = oracle.attention(q, k, v, kind, w, g, scale=0.35)
+        for block in (1, 7, 16, 64):
+            for lazy in (0.0, 8.0 * math.log(2.0)):
+                got = online_softmax_attention(q, k, v, mask, 0.35, block, lazy)
+                assert np.allclose(got, ref, atol=1e-12, rtol=0), (kind, block, lazy)
+
+
 PINS = [
     pin_page_softmax_example,
     pin_page_ranking_example,
@@ -339,6 +385,7 @@ PINS = [
     pin_torch_sdpa_crosscheck,
     pin_brute_force_tiny,
     pin_sampled_rows_match_full,
+    pin_online_softmax_recurrence,
 ]
 
 
