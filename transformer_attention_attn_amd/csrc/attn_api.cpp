@@ -55,10 +55,11 @@ Checked check_args(int B, int Hq, int Hkv, int S, int D, int mask_kind, int wind
   c.n_global = nd;
 
   if (dtype == ATTN_DTYPE_FP32)
-    c.s = attn::make_sched(B, Hq, Hkv, S, mask_kind, window, nd, attn::kF32Rows, attn::kF32Keys, 0);
+    c.s = attn::make_sched(B, Hq, Hkv, S, mask_kind, window, nd, attn::kF32Rows, attn::kF32Keys, 0,
+                           attn::kF32Rows);
   else
     c.s = attn::make_sched(B, Hq, Hkv, S, mask_kind, window, nd, attn::kBf16Rows,
-                           attn::bf16_keys_per_tile(D), 1);
+                           attn::bf16_keys_per_tile(D), 1, attn::kBf16GlobalRows);
   if (c.s.n_items > 0x7fffffffLL) { c.status = ATTN_ERR_SHAPE; return c; }
   return c;
 }

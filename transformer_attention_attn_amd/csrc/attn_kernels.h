@@ -29,6 +29,7 @@ struct KParams {
 constexpr int kF32Rows = 64;   // query rows per fp32 work item (one head)
 constexpr int kF32Keys = 32;   // keys per fp32 tile
 constexpr int kBf16Rows = 32 * kBf16Waves;  // query rows per bf16 work item (heads packed)
+constexpr int kBf16GlobalRows = 32;          // global rows per query head in a bf16 global item
 ATTN_HD int bf16_keys_per_tile(int) { return 64; }
 
 hipError_t launch_fp32(const KParams& p, int D, hipStream_t stream);

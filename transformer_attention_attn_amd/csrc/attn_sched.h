@@ -11,7 +11,8 @@
 //   * band items: rows of one block, key tiles covering |i - j| <= w;
 //   * one extra "strip" tile per band item holding the global tokens' keys
 //     (columns j in G outside the band of row i);
-//   * global items: the rows i in G, gathered, each seeing all S keys.
+//   * global items: the rows i in G, gathered (GR per query head per item),
+//     each seeing all S keys.
 // Band items compute global rows too but never store them; the global items
 // own those rows.
 #pragma once
@@ -35,9 +36,10 @@ struct Sched {
   int BMh;      // query rows per head per work item
   int BN;       // keys per tile
   int T;        // row blocks per head: ceil(S / BMh)
+  int GR;       // global rows per query head in a global item
   int P;        // B * Hkv * NHG (item "pairs")
   int mask, window, n_global;
-  int n_gblocks;           // global-row blocks per pair: ceil(n_global / BMh) (local+global only)
+  int n_gblocks;           // global-row blocks per pair: ceil(n_global / GR) (local+global only)
   long long n_global_items;  // P * n_gblocks, numbered first
   long long n_items;         // total workgroups
 };
@@ -61,7 +63,7 @@ ATTN_HD int heads_per_item(int G) {
 }
 
 ATTN_HD Sched make_sched(int B, int Hq, int Hkv, int S, int mask, int window, int n_global,
-                         int rows_per_wg, int BN, int pack_heads) {
+                         int rows_per_wg, int BN, int pack_heads, int global_rows) {
   Sched s;
   s.B = B; s.Hq = Hq; s.Hkv = Hkv; s.S = S;
   s.G = Hq / Hkv;
@@ -73,7 +75,8 @@ ATTN_HD Sched make_sched(int B, int Hq, int Hkv, int S, int mask, int window, in
   s.P = B * Hkv * s.NHG;
   s.mask = mask; s.window = window;
   s.n_global = (mask == MASK_LOCAL_GLOBAL) ? n_global : 0;
-  s.n_gblocks = s.n_global > 0 ? cdiv(s.n_global, s.BMh) : 0;
+  s.GR = global_rows;
+  s.n_gblocks = s.n_global > 0 ? cdiv(s.n_global, s.GR) : 0;
   s.n_global_items = (long long)s.P * s.n_gblocks;
   s.n_items = s.n_global_items + (long long)s.P * s.T;
   return s;

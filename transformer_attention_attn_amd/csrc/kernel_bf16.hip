@@ -48,6 +48,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BN = 64;           // keys per tile
+constexpr int GK = 32;           // keys per private tile of the global-row path
 constexpr int NKB = BN / 32;     // 32-key blocks of S^T
 constexpr int NPC = BN / 16;     // 16-key reduction steps of O^T
 constexpr float kLazy = 8.f;     // rescale threshold, log2 units
@@ -117,7 +118,9 @@ void attn_fwd_bf16(KParams p) {
                 NI = C::NI, NSTAGE = C::NSTAGE;
   constexpr int WSTEP = kBf16Waves * 1024;  // bytes one direct load of every wave covers
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * BUF];
+  // the global-row path needs a K and a V tile of GK keys per wave
+  constexpr int LDS_G = (MASK == MASK_LOCAL_GLOBAL) ? kBf16Waves * 2 * GK * ROWB : 0;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * BUF > LDS_G ? NSTAGE * BUF : LDS_G];
   __shared__ int gpos_s[kMaxGlobal];
 
   const Sched& s = p.s;
@@ -148,12 +151,11 @@ void attn_fwd_bf16(KParams p) {
     wqa = q0;
     wqb = imin(q0 + 31, s.S - 1);
   } else {
-    const int slot = it.blk * s.BMh + rpart * 32 + l32;
+    // every wave of a head holds the head's (up to) 32 global rows; the waves
+    // split the keys instead (see the global-row path below)
+    const int slot = it.blk * kBf16GlobalRows + l32;
     row_valid = slot < s.n_global;
     q_row = row_valid ? gpos_s[slot] : 0;
-    const int first = it.blk * s.BMh + rpart * 32;
-    wqa = 0;
-    wqb = first < s.n_global ? 0 : -1;  // wave active iff it holds a global row
   }
   const bool wave_active = wqa <= wqb;
 
@@ -340,6 +342,145 @@ void attn_fwd_bf16(KParams p) {
     if (j + 3 < n_it) load_k(j + 3, (j + 3) % NSTAGE);
     if (j + 2 < n_it) load_v(j + 2, (j + 2) % NSTAGE);
   };
+  if (MASK == MASK_LOCAL_GLOBAL && it.is_global) {
+    // ---- global rows: keys split over the waves of a head -----------------
+    // The wph waves of a query head hold the same 32 global rows and walk
+    // disjoint, contiguous chunks of the S keys, each through its own LDS
+    // region (one 32-key K tile and one V tile, same layout and swizzles as
+    // the shared ring), so no workgroup barrier is needed inside the walk.
+    // K(t+1) is loaded while S(t) is in the softmax, V(t+1) while PV(t) runs.
+    constexpr int GREG = GK * ROWB;     // one private K or V tile
+    constexpr int NIG = GREG / 1024;    // 1 KiB direct loads per private tile
+    constexpr int RPI = 1024 / ROWB;    // tile rows per 1 KiB load
+    unsigned char* kreg = smem + wave * 2 * GREG;
+    unsigned char* vreg = kreg + GREG;
+    const int ntile = cdiv(s.S, GK);
+    const int t_lo = (int)((long long)ntile * rpart / wph);
+    const int t_hi = (int)((long long)ntile * (rpart + 1) / wph);
+    const int lrow = lane * 16 / ROWB, lphys = (lane * 16 % ROWB) / 16;
+    auto gload = [&](const __bf16* base, int t, unsigned char* dst, bool is_v) {
+#pragma unroll
+      for (int n = 0; n < NIG; ++n) {
+        const int row = n * RPI + lrow;
+        const int key = imin(t * GK + row, s.S - 1);  // tail rows repeat a valid row (masked)
+        const int sw = is_v ? ((row & 3) << 1) : (row & 7);
+        dma16_global((const char*)base + (size_t)key * ROWB + (lphys ^ sw) * 16, dst + n * 1024);
+      }
+    };
+    if (t_lo < t_hi) {
+      gload(kp, t_lo, kreg, false);
+      gload(vp, t_lo, vreg, true);
+    }
+    for (int t = t_lo; t < t_hi; ++t) {
+      const bool more = t + 1 < t_hi;
+      __builtin_amdgcn_s_waitcnt(0x0f70 | NIG);  // K(t) landed; V(t) may be in flight
+      f32x16 sc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) sc = mfma32(k_frag(kreg, 0, dc), qf[dc], sc);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // K operand reads done: the region may be refilled
+      if (more) gload(kp, t + 1, kreg, false);
+      if ((t + 1) * GK > s.S) {
+        // tail tile: keys at or beyond S carry no weight
+        const int lim = s.S - t * GK - 4 * hf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = (8 * (r >> 2) + (r & 3) < lim) ? sc[r] : -INFINITY;
+      }
+      float mx = max3f(sc[0], sc[1], sc[2]);
+      mx = max3f(mx, sc[3], sc[4]);
+      mx = max3f(mx, sc[5], sc[6]);
+      mx = max3f(mx, sc[7], sc[8]);
+      mx = max3f(mx, sc[9], sc[10]);
+      mx = max3f(mx, sc[11], sc[12]);
+      mx = max3f(mx, sc[13], sc[14]);
+      mx = max3f(mx, sc[15], sc[15]);
+      mx = pair_max(mx);
+      if (__builtin_amdgcn_ballot_w64(mx * c > m_run * c + kLazy) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
+        m_run = m_new;
+        l_run0 *= alpha;
+        l_run1 *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+      bf16x8 pb[2];
+#pragma unroll
+      for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+        for (int u = 0; u < 8; u += 2) {
+          bf16x2 pr;
+          pr[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * pc + u], c, -mc));
+          pr[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * pc + u + 1], c, -mc));
+          if (u & 2) l_run1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run1, false);
+          else l_run0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run0, false);
+          pb[pc][u] = pr[0];
+          pb[pc][u + 1] = pr[1];
+        }
+      if (more) __builtin_amdgcn_s_waitcnt(0x0f70 | NIG);  // V(t) landed; K(t+1) in flight
+      else __builtin_amdgcn_s_waitcnt(0x0f70);
+#pragma unroll
+      for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(v_frag(vreg, db, pc), pb[pc], oacc[db]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // V operand reads done
+      if (more) gload(vp, t + 1, vreg, true);
+    }
+
+    // ---- merge the partial (m, l, O) of the waves of each head ------------
+    // Fixed pairing (chunk c takes chunk c + half, half = wph/2, wph/4, ...),
+    // so results are bitwise reproducible.  In the O^T accumulator lane l of
+    // every wave owns the same (query, dims), so partials combine lane by lane:
+    //   m = max(m1, m2),  X = X1 * 2^((m1 - m) c) + X2 * 2^((m2 - m) c)  for X in {l, O}.
+    // A slot holds one wave's partial: O as 16-byte chunks [chunk][lane], then
+    // (m, l) per lane.
+    constexpr int SLOT = 4 * NDB * 64 * 16 + 64 * 8;
+    static_assert(MASK != MASK_LOCAL_GLOBAL || kBf16Waves / 2 * SLOT <= LDS_G,
+                  "merge slots of half the waves fit in LDS");
+    const int hh = wave / wph;
+    for (int half = wph >> 1; half >= 1; half >>= 1) {
+      __syncthreads();  // the private regions (first pass) or slots (later passes) are free
+      if (rpart >= half && rpart < 2 * half) {
+        unsigned char* sl = smem + (hh * (wph >> 1) + rpart - half) * SLOT;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 x = {oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2],
+                              oacc[db][4 * g4 + 3]};
+            *(float4*)(sl + ((4 * db + g4) * 64 + lane) * 16) = x;
+          }
+        *(float2*)(sl + 4 * NDB * 64 * 16 + lane * 8) = float2{m_run, l_run0 + l_run1};
+      }
+      __syncthreads();
+      if (rpart < half) {
+        const unsigned char* sl = smem + (hh * (wph >> 1) + rpart) * SLOT;
+        const float2 ml = *(const float2*)(sl + 4 * NDB * 64 * 16 + lane * 8);
+        const float m_new = fmaxf(m_run, ml.x);
+        if (m_new != -INFINITY) {
+          const float fa = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+          const float fb = __builtin_amdgcn_exp2f((ml.x - m_new) * c);
+          l_run0 = (l_run0 + l_run1) * fa + ml.y * fb;
+          l_run1 = 0.f;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const float4 x = *(const float4*)(sl + ((4 * db + g4) * 64 + lane) * 16);
+              oacc[db][4 * g4] = oacc[db][4 * g4] * fa + x.x * fb;
+              oacc[db][4 * g4 + 1] = oacc[db][4 * g4 + 1] * fa + x.y * fb;
+              oacc[db][4 * g4 + 2] = oacc[db][4 * g4 + 2] * fa + x.z * fb;
+              oacc[db][4 * g4 + 3] = oacc[db][4 * g4 + 3] * fa + x.w * fb;
+            }
+          m_run = m_new;
+        }
+      }
+    }
+  } else {
   f32x16 scur[NKB], snxt[NKB];
   load_k(0, 0);
   load_v(0, 0);
@@ -450,6 +591,7 @@ void attn_fwd_bf16(KParams p) {
 #pragma unroll
     for (int kbk = 0; kbk < NKB; ++kbk) scur[kbk] = snxt[kbk];
   }
+  }  // shared-ring path
 
   // ---- epilogue: O = O^T / l, round to bf16, store --------------------------
   {
@@ -457,7 +599,8 @@ void attn_fwd_bf16(KParams p) {
     const unsigned lu = __float_as_uint(l_run);
     const float l_other = __uint_as_float(__shfl_xor((int)lu, 32));
     const float l_tot = l_run + l_other;
-    bool store = row_valid && wave_active;
+    // global items: the first wave of each head holds the merged result
+    bool store = row_valid && (it.is_global ? rpart == 0 : wave_active);
     if (MASK == MASK_LOCAL_GLOBAL && !it.is_global && store) {
       for (int g = 0; g < s.n_global; ++g) store = store && (gpos_s[g] != q_row);
     }
