@@ -50,6 +50,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int BN = 64;           // keys per tile
 constexpr int GK = 32;           // keys per private tile of the global-row path
 constexpr int NKB = BN / 32;     // 32-key blocks of S^T
+static_assert(NKB == 2, "the S^T steps hold two 32-key blocks");
 constexpr int NPC = BN / 16;     // 16-key reduction steps of O^T
 constexpr float kLazy = 8.f;     // rescale threshold, log2 units
 
@@ -89,12 +90,92 @@ __device__ __forceinline__ void dma16_buffer(__amdgpu_buffer_rsrc_t r, unsigned 
                                              int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, voff, soff, 0, 0);
 }
-// two transposed 8-byte reads (see the V^T operand comment in the kernel)
-__device__ __forceinline__ bf16x8 lds_read_tr_pair(const unsigned char* p0, const unsigned char* p1) {
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p0);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p1);
+// LDS byte address of a pointer into shared memory
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One V^T operand from two transposed 8-byte reads at LDS byte addresses
+// base + OFF and base + OFF + HI (see the V^T operand comment in the kernel).
+// Issued as inline asm: the compiler treats the transposed-read builtin as
+// possibly aliasing in-flight LDS-DMA writes and would wait for every
+// outstanding global load before it, which defeats the tile prefetch.  The
+// caller guarantees the tile has landed, and waits for the result with
+// lds_wait_frags before any use.
+template <int OFF, int HI>
+__device__ __forceinline__ bf16x8 lds_tr_pair(unsigned base) {
+  i16x4 lo, hi;
+  asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\tds_read_b64_tr_b16 %1, %2 offset:%4"
+               : "=&v"(lo), "=&v"(hi)
+               : "v"(base), "i"(OFF), "i"(OFF + HI));
   const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// The NDB V^T operands (dims 32*db + l32) of 16-key step PC of a V tile whose
+// per-lane read bases are vb0 (db even) and vb1 (db odd).
+template <int ROWB, int NDB, int PC>
+__device__ __forceinline__ void v_frags(bf16x8 (&f)[NDB], unsigned vb0, unsigned vb1) {
+  constexpr int STEP = 16 * PC * ROWB, HI = 8 * ROWB;
+  f[0] = lds_tr_pair<STEP, HI>(vb0);
+  f[1] = lds_tr_pair<STEP, HI>(vb1);
+  if constexpr (NDB > 2) {
+    f[2] = lds_tr_pair<STEP + 128, HI>(vb0);
+    f[3] = lds_tr_pair<STEP + 128, HI>(vb1);
+  }
+}
+
+// Wait until at most N LDS reads are outstanding; the operands are tied to the
+// wait so that no use of them is scheduled above it.
+template <int N, int NDB>
+__device__ __forceinline__ void lds_wait_frags(bf16x8 (&f)[NDB]) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f[0]) : "i"(N));
+  asm volatile("" : "+v"(f[1]));
+  if constexpr (NDB > 2) {
+    asm volatile("" : "+v"(f[2]));
+    asm volatile("" : "+v"(f[3]));
+  }
+}
+
+// One 16-byte LDS read at LDS byte address base + OFF, as inline asm (its
+// completion is waited for explicitly, like the transposed reads).
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_read16(unsigned base) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=&v"(r) : "v"(base), "i"(OFF));
+  return r;
+}
+
+// The two K operands (keys 32*kbk + l32, kbk = 0, 1) of 16-dim step DC, from
+// per-lane bases kbd[DC & 3] (the swizzle repeats every four steps).
+template <int ROWB, int DC>
+__device__ __forceinline__ void k_frags(bf16x8 (&f)[2], const unsigned (&kbd)[4]) {
+  f[0] = lds_read16<128 * (DC >> 2)>(kbd[DC & 3]);
+  f[1] = lds_read16<32 * ROWB + 128 * (DC >> 2)>(kbd[DC & 3]);
+}
+
+// LDS reads issued after the K operands of step dc when the S(j+1) MFMAs of
+// step dc wait for them: the operands of steps dc+1 and dc+2 (read two steps
+// ahead), and the V^T operands of the first 16-key step of P.V, which are
+// issued between steps NDC/2 + 1 and NDC/2 + 2.
+constexpr int k_younger(int dc, int ndc, int ndb) {
+  return (dc + 1 < ndc ? 2 : 0) + (dc + 2 < ndc ? 2 : 0) +
+         (dc >= ndc / 2 && dc <= ndc / 2 + 1 ? 2 * ndb : 0);
+}
+
+// Steps [DC, END) of S(j+1) = K(j+1) Q^T on a three-slot ring of K operands:
+// read step DC+2, wait for step DC, two MFMAs (one per 32-key block).
+template <int ROWB, int NDC, int NDB, int DC, int END>
+__device__ __forceinline__ void s_steps(bf16x8 (&kf)[3][2], const unsigned (&kbd)[4],
+                                        const bf16x8 (&qf)[NDC], f32x16 (&sn)[2]) {
+  if constexpr (DC < END) {
+    if constexpr (DC + 2 < NDC) k_frags<ROWB, DC + 2>(kf[(DC + 2) % 3], kbd);
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(kf[DC % 3][0]), "+v"(kf[DC % 3][1])
+                 : "i"(k_younger(DC, NDC, NDB)));
+    sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[DC % 3][0], qf[DC], sn[0], 0, 0, 0);
+    sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[DC % 3][1], qf[DC], sn[1], 0, 0, 0);
+    s_steps<ROWB, NDC, NDB, DC + 1, END>(kf, kbd, qf, sn);
+  }
 }
 
 template <int D>
@@ -263,7 +344,7 @@ void attn_fwd_bf16(KParams p) {
     return *(const bf16x8*)(kbuf + k_rd[dc & 3] + kbk * 32 * ROWB + 128 * (dc >> 2));
   };
   // V^T operand (dim 32*db + l32, keys 16*pc + 4*hf + [0,4) then +8) from two
-  // ds_read_b64_tr_b16: within each 16-lane group, lane 4t + u addresses the
+  // ds_read_b64_tr_b16 (v_frags): within each 16-lane group, lane 4t + u addresses the
   // 4 dims 32*db + 16*g + 4u of key 16*pc + 4*hf + t (g = lane bit 4), and the
   // transpose hands lane i element (i & 3) of lanes 4t + (i >> 2), t = 0..3,
   // i.e. dim 32*db + l32 of keys 4*hf + t.  Physical chunk of the 4 dims:
@@ -274,10 +355,6 @@ void attn_fwd_bf16(KParams p) {
   for (int d2 = 0; d2 < 2; ++d2)
     v_rd[d2] = (4 * hf + tt) * ROWB + 8 * (uu & 1) + 16 * (2 * (gg ^ (tt & 1)) + (uu >> 1)) +
                64 * (d2 ^ (tt >> 1));
-  auto v_frag = [&](const unsigned char* vbuf, int db, int pc) -> bf16x8 {
-    const unsigned char* p0 = vbuf + v_rd[db & 1] + 128 * (db >> 1) + 16 * pc * ROWB;
-    return lds_read_tr_pair(p0, p0 + 8 * ROWB);
-  };
 
   // Mask S^T of iteration iter in place.  Register r of block kbk holds key
   // 32*kbk + 8*(r/4) + 4*hf + r%4 of the tile for query q_row.
@@ -423,11 +500,18 @@ void attn_fwd_bf16(KParams p) {
         }
       if (more) __builtin_amdgcn_s_waitcnt(0x0f70 | NIG);  // V(t) landed; K(t+1) in flight
       else __builtin_amdgcn_s_waitcnt(0x0f70);
+      {
+        const unsigned vb = lds_addr(vreg);
+        bf16x8 fx[NDB], fy[NDB];
+        v_frags<ROWB, NDB, 0>(fx, vb + v_rd[0], vb + v_rd[1]);
+        v_frags<ROWB, NDB, 1>(fy, vb + v_rd[0], vb + v_rd[1]);
+        lds_wait_frags<2 * NDB>(fx);
 #pragma unroll
-      for (int pc = 0; pc < 2; ++pc)
+        for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fx[db], pb[0], oacc[db]);
+        lds_wait_frags<0>(fy);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(v_frag(vreg, db, pc), pb[pc], oacc[db]);
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // V operand reads done
+        for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fy[db], pb[1], oacc[db]);
+      }
       if (more) gload(vp, t + 1, vreg, true);
     }
 
@@ -506,6 +590,12 @@ void attn_fwd_bf16(KParams p) {
     issue_batch(iter);
     const unsigned char* kbuf_nxt = smem + nxt * BUF;      // K(j+1)
     const unsigned char* vbuf_cur = smem + cur * BUF + REG;  // V(j)
+    // K(j+1) operands: read two 16-dim steps ahead of their MFMAs
+    const unsigned kb = lds_addr(kbuf_nxt);
+    const unsigned kbd[4] = {kb + k_rd[0], kb + k_rd[1], kb + k_rd[2], kb + k_rd[3]};
+    bf16x8 kf[3][2];
+    k_frags<ROWB, 0>(kf[0], kbd);
+    k_frags<ROWB, 1>(kf[1], kbd);
 
     if (tile_partial(iter)) {
       asm volatile("");  // keep this a branch: full tiles skip it
@@ -532,10 +622,7 @@ void attn_fwd_bf16(KParams p) {
       }
       mx = max3f(max3f(t[0], t[1], t[2]), t[3], t[3]);
     }
-#pragma unroll
-    for (int dc = 0; dc < NDC / 2; ++dc)
-#pragma unroll
-      for (int kbk = 0; kbk < NKB; ++kbk) snxt[kbk] = mfma32(k_frag(kbuf_nxt, kbk, dc), qf[dc], snxt[kbk]);
+    s_steps<ROWB, NDC, NDB, 0, NDC / 2>(kf, kbd, qf, snxt);
     mx = pair_max(mx);
     const bool need_rescale = __builtin_amdgcn_ballot_w64(mx * c > m_run * c + kLazy) != 0;
 
@@ -571,23 +658,32 @@ void attn_fwd_bf16(KParams p) {
     };
 
     // -- block B: second half of S(j+1) beside the first half of P(j); O +=
-    //    V(j) P(j) beside the second half of P(j).
+    //    V(j) P(j) beside the second half of P(j).  The V^T operands of each
+    //    16-key step are read one step ahead of their MFMAs.
+    const unsigned vb = lds_addr(vbuf_cur);
+    const unsigned vb0 = vb + v_rd[0], vb1 = vb + v_rd[1];
+    bf16x8 fx[NDB], fy[NDB];
+    v_frags<ROWB, NDB, 0>(fx, vb0, vb1);
     make_p(0);
     make_p(1);
+    s_steps<ROWB, NDC, NDB, NDC / 2, NDC>(kf, kbd, qf, snxt);
+    v_frags<ROWB, NDB, 1>(fy, vb0, vb1);
+    lds_wait_frags<2 * NDB>(fx);
 #pragma unroll
-    for (int dc = NDC / 2; dc < NDC; ++dc)
+    for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fx[db], pb[0], oacc[db]);
+    v_frags<ROWB, NDB, 2>(fx, vb0, vb1);
+    lds_wait_frags<2 * NDB>(fy);
 #pragma unroll
-      for (int kbk = 0; kbk < NKB; ++kbk) snxt[kbk] = mfma32(k_frag(kbuf_nxt, kbk, dc), qf[dc], snxt[kbk]);
-#pragma unroll
-    for (int pc = 0; pc < 2; ++pc)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(v_frag(vbuf_cur, db, pc), pb[pc], oacc[db]);
+    for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fy[db], pb[1], oacc[db]);
     make_p(2);
     make_p(3);
+    v_frags<ROWB, NDB, 3>(fy, vb0, vb1);
+    lds_wait_frags<2 * NDB>(fx);
 #pragma unroll
-    for (int pc = 2; pc < NPC; ++pc)
+    for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fx[db], pb[2], oacc[db]);
+    lds_wait_frags<0>(fy);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(v_frag(vbuf_cur, db, pc), pb[pc], oacc[db]);
+    for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fy[db], pb[3], oacc[db]);
 #pragma unroll
     for (int kbk = 0; kbk < NKB; ++kbk) scur[kbk] = snxt[kbk];
   }
