@@ -113,16 +113,12 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(unsigned base) {
 }
 
 // The NDB V^T operands (dims 32*db + l32) of 16-key step PC of a V tile whose
-// per-lane read bases are vb0 (db even) and vb1 (db odd).
+// per-lane read bases are vbd[db].
 template <int ROWB, int NDB, int PC>
-__device__ __forceinline__ void v_frags(bf16x8 (&f)[NDB], unsigned vb0, unsigned vb1) {
+__device__ __forceinline__ void v_frags(bf16x8 (&f)[NDB], const unsigned (&vbd)[NDB]) {
   constexpr int STEP = 16 * PC * ROWB, HI = 8 * ROWB;
-  f[0] = lds_tr_pair<STEP, HI>(vb0);
-  f[1] = lds_tr_pair<STEP, HI>(vb1);
-  if constexpr (NDB > 2) {
-    f[2] = lds_tr_pair<STEP + 128, HI>(vb0);
-    f[3] = lds_tr_pair<STEP + 128, HI>(vb1);
-  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) f[db] = lds_tr_pair<STEP, HI>(vbd[db]);
 }
 
 // Wait until at most N LDS reads are outstanding; the operands are tied to the
@@ -184,6 +180,7 @@ struct Cfg {
   static constexpr int NDB = D / 32;            // 32-dim blocks of O^T
   static constexpr int ROWB = D * 2;            // bytes per K or V row
   static constexpr int REG = BN * ROWB;         // bytes of one K or V tile
+  static constexpr int VSH = D == 128 ? 2 : 1;  // V chunk swizzle shift
   static constexpr int BUF = 2 * REG;           // K tile then V tile
   static constexpr int NSTAGE = 3;              // LDS stages: K(j+1), K(j+2) / V(j), V(j+1) in flight
   static constexpr int NI = REG / 1024 / kBf16Waves;  // 1 KiB direct loads per wave per tile
@@ -196,7 +193,7 @@ __global__ __launch_bounds__(kBf16Threads) __attribute__((amdgpu_waves_per_eu(2,
 void attn_fwd_bf16(KParams p) {
   using C = Cfg<D>;
   constexpr int NDC = C::NDC, NDB = C::NDB, ROWB = C::ROWB, REG = C::REG, BUF = C::BUF,
-                NI = C::NI, NSTAGE = C::NSTAGE;
+                NI = C::NI, NSTAGE = C::NSTAGE, VSH = C::VSH;
   constexpr int WSTEP = kBf16Waves * 1024;  // bytes one direct load of every wave covers
 
   // the global-row path needs a K and a V tile of GK keys per wave
@@ -274,8 +271,9 @@ void attn_fwd_bf16(KParams p) {
   // chunks of row r permuted: physical chunk = logical chunk ^ swz(r).
   //   K: swz = r & 7         -> the K operand reads (8 consecutive rows, one
   //                              chunk) hit 8 distinct bank groups
-  //   V: swz = (r & 3) << 1  -> the transposed reads (4 consecutive rows, two
-  //                              chunks) hit distinct banks
+  //   V: swz = (r & 3) << VSH -> the transposed reads (4 consecutive rows, two
+  //                              chunks) spread over the banks; VSH = 2 where
+  //                              a row has 16 chunks (D = 128), else 1
   // A direct load writes 1 KiB: lane l of instruction n of wave w (of W
   // waves) fills slot s = (W*n + w)*64 + l, i.e. row s*16/ROWB and physical
   // chunk (s*16 % ROWB)/16; its source is that row's logical chunk.  Rows
@@ -284,7 +282,7 @@ void attn_fwd_bf16(KParams p) {
   const int slot_b = (wave * 64 + lane) * 16;
   const int srow = slot_b / ROWB, sphys = (slot_b % ROWB) / 16;
   const int k_src = srow * ROWB + (sphys ^ (srow & 7)) * 16;
-  const int v_src = srow * ROWB + (sphys ^ ((srow & 3) << 1)) * 16;
+  const int v_src = srow * ROWB + (sphys ^ ((srow & 3) << VSH)) * 16;
 
   auto rsrc = [&](const __bf16* base, int kt) {
     // descriptor over rows [kt*BN, S): whole tiles only (tail tiles clamp rows)
@@ -348,13 +346,17 @@ void attn_fwd_bf16(KParams p) {
   // 4 dims 32*db + 16*g + 4u of key 16*pc + 4*hf + t (g = lane bit 4), and the
   // transpose hands lane i element (i & 3) of lanes 4t + (i >> 2), t = 0..3,
   // i.e. dim 32*db + l32 of keys 4*hf + t.  Physical chunk of the 4 dims:
-  // (4*db + 2*g + (u >> 1)) ^ (2*t).
+  // (4*db + 2*g + (u >> 1)) ^ (t << VSH), which is 4*(db ^ t) + 2*g + (u >> 1)
+  // for VSH = 2 and 4*(db ^ (t >> 1)) + 2*(g ^ (t & 1)) + (u >> 1) for VSH = 1
+  // (NDB = 2).
   const int tt = (lane >> 2) & 3, uu = lane & 3, gg = (lane >> 4) & 1;
-  int v_rd[2];  // per-lane part for db & 1; the rest of the offset is an immediate
+  int v_rd[NDB];  // per-lane part for each db; the 16-key step is an immediate
 #pragma unroll
-  for (int d2 = 0; d2 < 2; ++d2)
-    v_rd[d2] = (4 * hf + tt) * ROWB + 8 * (uu & 1) + 16 * (2 * (gg ^ (tt & 1)) + (uu >> 1)) +
-               64 * (d2 ^ (tt >> 1));
+  for (int db = 0; db < NDB; ++db)
+    v_rd[db] = (VSH == 2)
+                   ? (4 * hf + tt) * ROWB + 64 * (db ^ tt) + 32 * gg + 16 * (uu >> 1) + 8 * (uu & 1)
+                   : (4 * hf + tt) * ROWB + 64 * (db ^ (tt >> 1)) + 32 * (gg ^ (tt & 1)) +
+                         16 * (uu >> 1) + 8 * (uu & 1);
 
   // Mask S^T of iteration iter in place.  Register r of block kbk holds key
   // 32*kbk + 8*(r/4) + 4*hf + r%4 of the tile for query q_row.
@@ -440,7 +442,7 @@ void attn_fwd_bf16(KParams p) {
       for (int n = 0; n < NIG; ++n) {
         const int row = n * RPI + lrow;
         const int key = imin(t * GK + row, s.S - 1);  // tail rows repeat a valid row (masked)
-        const int sw = is_v ? ((row & 3) << 1) : (row & 7);
+        const int sw = is_v ? ((row & 3) << VSH) : (row & 7);
         dma16_global((const char*)base + (size_t)key * ROWB + (lphys ^ sw) * 16, dst + n * 1024);
       }
     };
@@ -503,8 +505,11 @@ void attn_fwd_bf16(KParams p) {
       {
         const unsigned vb = lds_addr(vreg);
         bf16x8 fx[NDB], fy[NDB];
-        v_frags<ROWB, NDB, 0>(fx, vb + v_rd[0], vb + v_rd[1]);
-        v_frags<ROWB, NDB, 1>(fy, vb + v_rd[0], vb + v_rd[1]);
+        unsigned vbd[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) vbd[db] = vb + v_rd[db];
+        v_frags<ROWB, NDB, 0>(fx, vbd);
+        v_frags<ROWB, NDB, 1>(fy, vbd);
         lds_wait_frags<2 * NDB>(fx);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fx[db], pb[0], oacc[db]);
@@ -661,23 +666,25 @@ void attn_fwd_bf16(KParams p) {
     //    V(j) P(j) beside the second half of P(j).  The V^T operands of each
     //    16-key step are read one step ahead of their MFMAs.
     const unsigned vb = lds_addr(vbuf_cur);
-    const unsigned vb0 = vb + v_rd[0], vb1 = vb + v_rd[1];
+    unsigned vbd[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vbd[db] = vb + v_rd[db];
     bf16x8 fx[NDB], fy[NDB];
-    v_frags<ROWB, NDB, 0>(fx, vb0, vb1);
+    v_frags<ROWB, NDB, 0>(fx, vbd);
     make_p(0);
     make_p(1);
     s_steps<ROWB, NDC, NDB, NDC / 2, NDC>(kf, kbd, qf, snxt);
-    v_frags<ROWB, NDB, 1>(fy, vb0, vb1);
+    v_frags<ROWB, NDB, 1>(fy, vbd);
     lds_wait_frags<2 * NDB>(fx);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fx[db], pb[0], oacc[db]);
-    v_frags<ROWB, NDB, 2>(fx, vb0, vb1);
+    v_frags<ROWB, NDB, 2>(fx, vbd);
     lds_wait_frags<2 * NDB>(fy);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fy[db], pb[1], oacc[db]);
     make_p(2);
     make_p(3);
-    v_frags<ROWB, NDB, 3>(fy, vb0, vb1);
+    v_frags<ROWB, NDB, 3>(fy, vbd);
     lds_wait_frags<2 * NDB>(fx);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fx[db], pb[2], oacc[db]);
