@@ -19,15 +19,22 @@
 //     registers (converted to bf16, round to nearest even), A = V^T from a
 //     transposed LDS tile.  The accumulator lane again owns one query, so the
 //     rescale factor is a per-lane scalar.
-//   * Software pipeline over key tiles j: while the matrix cores compute
-//     S(j+1) = K(j+1) Q^T, the vector ALUs run the softmax of S(j); while they
-//     compute O += V(j) P(j), the vector ALUs finish P(j).  K and V go
-//     straight from HBM into LDS (buffer/global loads with the LDS flag: no
-//     staging registers) through a three-stage ring, issued two tiles ahead
-//     of use, with one barrier per tile.
-//     V^T operands come from row-major V tiles through ds_read_b64_tr_b16.
-//     MFMA accumulation chains are interleaved (a dependent MFMA waits ~44
-//     cycles, an independent one issues every 32).
+//   * Two wave groups per workgroup (waves 0-3 and 4-7, one of each per
+//     SIMD) in ping-pong: per key tile there are two barrier-separated steps,
+//     and in each one group runs its matrix block (O += V P for one tile and
+//     S = K Q^T for the next, 32 MFMAs) while the other runs its softmax, so
+//     the matrix cores and the vector ALUs of a SIMD work side by side.  The
+//     wave running its matrix block gets the higher issue priority.
+//   * K and V go straight from HBM into LDS (buffer/global loads with the LDS
+//     flag: no staging registers) through a three-stage ring; group 0 loads
+//     the K tiles and group 1 the V tiles, spread between their MFMAs.
+//   * LDS operands are read with inline-asm ds_read_b128 (K) and
+//     ds_read_b64_tr_b16 (V^T) up to eight MFMAs ahead, with exact lgkmcnt
+//     waits: the compiler would otherwise wait for every direct load in
+//     flight before each transposed read.  Steps are separated by a bare
+//     s_barrier for the same reason (__syncthreads adds a release fence that
+//     waits for direct loads); direct loads are covered by explicit vmcnt
+//     waits.
 //   * The output rescale runs only when a row maximum grows by more than a
 //     factor 2^8 (weights stay <= 2^8, far inside bf16/fp32 range); O / l is
 //     unchanged by the choice of reference maximum.
@@ -142,36 +149,106 @@ __device__ __forceinline__ bf16x8 lds_read16(unsigned base) {
   return r;
 }
 
-// The two K operands (keys 32*kbk + l32, kbk = 0, 1) of 16-dim step DC, from
-// per-lane bases kbd[DC & 3] (the swizzle repeats every four steps).
-template <int ROWB, int DC>
-__device__ __forceinline__ void k_frags(bf16x8 (&f)[2], const unsigned (&kbd)[4]) {
-  f[0] = lds_read16<128 * (DC >> 2)>(kbd[DC & 3]);
-  f[1] = lds_read16<32 * ROWB + 128 * (DC >> 2)>(kbd[DC & 3]);
+// Wait until at most N LDS reads are outstanding, tied to the operand f so
+// that no use of it is scheduled above the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait1(bf16x8& f) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f) : "i"(N));
 }
 
-// LDS reads issued after the K operands of step dc when the S(j+1) MFMAs of
-// step dc wait for them: the operands of steps dc+1 and dc+2 (read two steps
-// ahead), and the V^T operands of the first 16-key step of P.V, which are
-// issued between steps NDC/2 + 1 and NDC/2 + 2.
-constexpr int k_younger(int dc, int ndc, int ndb) {
-  return (dc + 1 < ndc ? 2 : 0) + (dc + 2 < ndc ? 2 : 0) +
-         (dc >= ndc / 2 && dc <= ndc / 2 + 1 ? 2 * ndb : 0);
+// Operand OP of the P.V part of a matrix block: V^T of dims 32*(OP % NDB) +
+// l32 for 16-key step OP / NDB (two transposed reads).
+template <int ROWB, int NDB, int OP>
+__device__ __forceinline__ bf16x8 v_op(const unsigned* vbd) {
+  return lds_tr_pair<16 * (OP / NDB) * ROWB, 8 * ROWB>(vbd[OP % NDB]);
+}
+// Operand OP of the S part: K rows 32*(OP % 2) + l32 for 16-dim step OP / 2
+// (one read from the per-lane base of that step).
+template <int ROWB, int OP>
+__device__ __forceinline__ bf16x8 k_op(const unsigned* kbd) {
+  constexpr int KBK = OP % 2, DC = OP / 2;
+  return lds_read16<KBK * 32 * ROWB>(kbd[DC]);
 }
 
-// Steps [DC, END) of S(j+1) = K(j+1) Q^T on a three-slot ring of K operands:
-// read step DC+2, wait for step DC, two MFMAs (one per 32-key block).
-template <int ROWB, int NDC, int NDB, int DC, int END>
-__device__ __forceinline__ void s_steps(bf16x8 (&kf)[3][2], const unsigned (&kbd)[4],
-                                        const bf16x8 (&qf)[NDC], f32x16 (&sn)[2]) {
-  if constexpr (DC < END) {
-    if constexpr (DC + 2 < NDC) k_frags<ROWB, DC + 2>(kf[(DC + 2) % 3], kbd);
-    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(kf[DC % 3][0]), "+v"(kf[DC % 3][1])
-                 : "i"(k_younger(DC, NDC, NDB)));
-    sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[DC % 3][0], qf[DC], sn[0], 0, 0, 0);
-    sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[DC % 3][1], qf[DC], sn[1], 0, 0, 0);
-    s_steps<ROWB, NDC, NDB, DC + 1, END>(kf, kbd, qf, sn);
+// Direct loads issued right after MFMA i of a part of l MFMAs that carries
+// ndma loads (spread evenly).
+constexpr int dma_after(int i, int l, int ndma) {
+  int c = 0;
+  for (int k = 0; k < ndma; ++k)
+    if (((k + 1) * l) / (ndma + 1) - 1 == i) ++c;
+  return c;
+}
+// The operand sequence of a matrix block.  MODE 0: P.V only (O^T += V^T P^T
+// over the NDB output blocks); MODE 1: S only (S^T = K Q^T over the two 32-key
+// blocks); MODE 2: P.V then S as one sequence, so the K operands of S are read
+// while the last P.V MFMAs run.
+template <int MODE, int NDB, int NDC>
+struct BlockSeq {
+  static constexpr int NPV = 4 * NDB, NSM = 2 * NDC;
+  static constexpr int L = MODE == 0 ? NPV : MODE == 1 ? NSM : NPV + NSM;
+  static constexpr bool is_pv(int i) { return MODE == 0 || (MODE == 2 && i < NPV); }
+  static constexpr int s_index(int i) { return MODE == 1 ? i : i - NPV; }
+  static constexpr int reads(int i) { return is_pv(i) ? 2 : 1; }
+  // LDS reads issued after operand i when MFMA i waits for it: the operands
+  // i+1 .. i+pf-1 of the ring
+  static constexpr int younger(int i, int pf) {
+    int n = 0;
+    for (int k = i + 1; k < i + pf && k < L; ++k) n += reads(k);
+    return n;
   }
+};
+
+template <int MODE, int ROWB, int NDB, int NDC, int OP>
+__device__ __forceinline__ bf16x8 block_op(const unsigned* vbd, const unsigned* kbd) {
+  using Q = BlockSeq<MODE, NDB, NDC>;
+  if constexpr (Q::is_pv(OP)) return v_op<ROWB, NDB, OP>(vbd);
+  else return k_op<ROWB, Q::s_index(OP)>(kbd);
+}
+
+// MFMAs [I, L) of a matrix block: wait for operand I, MFMA I, read operand
+// I + PF into the freed ring slot, then the direct loads scheduled after MFMA I.
+template <int MODE, int ROWB, int NDB, int NDC, int PF, int I, int NDMA, typename Dma>
+__device__ __forceinline__ void block_steps(bf16x8 (&ring)[PF], const unsigned* vbd,
+                                            const unsigned* kbd, const bf16x8* pb,
+                                            const bf16x8* qf, f32x16* oacc, f32x16* sc,
+                                            Dma& dma) {
+  using Q = BlockSeq<MODE, NDB, NDC>;
+  if constexpr (I < Q::L) {
+    static_assert(Q::younger(I, PF) <= 15, "lgkmcnt holds at most 15");
+    lds_wait1<Q::younger(I, PF)>(ring[I % PF]);
+    if constexpr (Q::is_pv(I)) {
+      oacc[I % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[I % PF], pb[I / NDB],
+                                                              oacc[I % NDB], 0, 0, 0);
+    } else {
+      constexpr int J = Q::s_index(I);
+      if constexpr (J / 2 == 0)
+        sc[J % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[I % PF], qf[0], f32x16{}, 0, 0, 0);
+      else
+        sc[J % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[I % PF], qf[J / 2], sc[J % 2],
+                                                            0, 0, 0);
+    }
+    if constexpr (I + PF < Q::L) ring[I % PF] = block_op<MODE, ROWB, NDB, NDC, I + PF>(vbd, kbd);
+    dma(dma_after(I, Q::L, NDMA));
+    block_steps<MODE, ROWB, NDB, NDC, PF, I + 1, NDMA>(ring, vbd, kbd, pb, qf, oacc, sc, dma);
+  }
+}
+template <int MODE, int ROWB, int NDB, int NDC, int PF, int I>
+__device__ __forceinline__ void block_prime(bf16x8 (&ring)[PF], const unsigned* vbd,
+                                            const unsigned* kbd) {
+  if constexpr (I < PF) {
+    ring[I] = block_op<MODE, ROWB, NDB, NDC, I>(vbd, kbd);
+    block_prime<MODE, ROWB, NDB, NDC, PF, I + 1>(ring, vbd, kbd);
+  }
+}
+template <int MODE, int ROWB, int NDB, int NDC, int NDMA, typename Dma>
+__device__ __forceinline__ void block_run(const unsigned* vbd, const unsigned* kbd,
+                                          const bf16x8* pb, const bf16x8* qf, f32x16* oacc,
+                                          f32x16* sc, Dma& dma) {
+  constexpr int L = BlockSeq<MODE, NDB, NDC>::L;
+  constexpr int PF = L < 8 ? L : 8;  // operands in flight: at most 7 * 2 reads outstanding
+  bf16x8 ring[PF];
+  block_prime<MODE, ROWB, NDB, NDC, PF, 0>(ring, vbd, kbd);
+  block_steps<MODE, ROWB, NDB, NDC, PF, 0, NDMA>(ring, vbd, kbd, pb, qf, oacc, sc, dma);
 }
 
 template <int D>
@@ -181,10 +258,16 @@ struct Cfg {
   static constexpr int ROWB = D * 2;            // bytes per K or V row
   static constexpr int REG = BN * ROWB;         // bytes of one K or V tile
   static constexpr int VSH = D == 128 ? 2 : 1;  // V chunk swizzle shift
+  // K chunk swizzle: the 16 rows that one 16-lane pass of a 16-byte operand
+  // read touches land on 16 distinct 16-byte bank groups of the 64 LDS banks
+  static __host__ __device__ constexpr int ksw(int row) {
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+  }
   static constexpr int BUF = 2 * REG;           // K tile then V tile
-  static constexpr int NSTAGE = 3;              // LDS stages: K(j+1), K(j+2) / V(j), V(j+1) in flight
-  static constexpr int NI = REG / 1024 / kBf16Waves;  // 1 KiB direct loads per wave per tile
-  static_assert(NI >= 1 && NI * kBf16Waves * 1024 == REG, "tile split into 1 KiB wave loads");
+  static constexpr int NSTAGE = 3;              // LDS stages of the K/V ring
+  static constexpr int NGL = REG / 1024 / 4;    // 1 KiB direct loads per wave per tile (4 waves)
+  static constexpr int RSTEP = 4096 / ROWB;     // rows between a lane's successive loads
+  static_assert(NGL * 4 * 1024 == REG && RSTEP % 8 == 0, "tile split into 1 KiB group loads");
   static_assert(NSTAGE * BUF <= 160 * 1024, "LDS budget of one CU");
 };
 
@@ -193,8 +276,7 @@ __global__ __launch_bounds__(kBf16Threads) __attribute__((amdgpu_waves_per_eu(2,
 void attn_fwd_bf16(KParams p) {
   using C = Cfg<D>;
   constexpr int NDC = C::NDC, NDB = C::NDB, ROWB = C::ROWB, REG = C::REG, BUF = C::BUF,
-                NI = C::NI, NSTAGE = C::NSTAGE, VSH = C::VSH;
-  constexpr int WSTEP = kBf16Waves * 1024;  // bytes one direct load of every wave covers
+                NGL = C::NGL, RSTEP = C::RSTEP, NSTAGE = C::NSTAGE, VSH = C::VSH;
 
   // the global-row path needs a K and a V tile of GK keys per wave
   constexpr int LDS_G = (MASK == MASK_LOCAL_GLOBAL) ? kBf16Waves * 2 * GK * ROWB : 0;
@@ -269,57 +351,47 @@ void attn_fwd_bf16(KParams p) {
   // ---- LDS layout and direct (global -> LDS) tile loads ---------------------
   // A tile region holds BN rows of ROWB bytes, row-major, with the 16-byte
   // chunks of row r permuted: physical chunk = logical chunk ^ swz(r).
-  //   K: swz = r & 7         -> the K operand reads (8 consecutive rows, one
-  //                              chunk) hit 8 distinct bank groups
+  //   K: swz = ksw(r)        -> the K operand reads (16 consecutive rows, one
+  //                              chunk) hit 16 distinct bank groups
   //   V: swz = (r & 3) << VSH -> the transposed reads (4 consecutive rows, two
   //                              chunks) spread over the banks; VSH = 2 where
   //                              a row has 16 chunks (D = 128), else 1
-  // A direct load writes 1 KiB: lane l of instruction n of wave w (of W
-  // waves) fills slot s = (W*n + w)*64 + l, i.e. row s*16/ROWB and physical
+  // K tiles are loaded by wave group 0 (waves 0-3) and V tiles by group 1.
+  // A direct load writes 1 KiB: lane l of load n of wave gw (0..3 in its
+  // group) fills slot s = (4n + gw)*64 + l, i.e. row s*16/ROWB and physical
   // chunk (s*16 % ROWB)/16; its source is that row's logical chunk.  Rows
-  // advance by W*1024/ROWB per n (a multiple of 8), so the source offset is a
-  // per-lane base plus n*W*1024.
-  const int slot_b = (wave * 64 + lane) * 16;
+  // advance by RSTEP (a multiple of 8) per n, so the source column is fixed
+  // per lane.
+  const int gw = wave & 3;
+  const int slot_b = (gw * 64 + lane) * 16;
   const int srow = slot_b / ROWB, sphys = (slot_b % ROWB) / 16;
-  const int k_src = srow * ROWB + (sphys ^ (srow & 7)) * 16;
-  const int v_src = srow * ROWB + (sphys ^ ((srow & 3) << VSH)) * 16;
-
-  auto rsrc = [&](const __bf16* base, int kt) {
-    // descriptor over rows [kt*BN, S): whole tiles only (tail tiles clamp rows)
-    const int row0 = kt * BN;
-    const int nbytes = imin(BN, s.S - row0) * ROWB;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)row0 * D), (short)0, nbytes,
-                                             0x00020000);
+  const int k_col = (sphys ^ C::ksw(srow)) * 16;
+  const int v_col = (sphys ^ ((srow & 3) << VSH)) * 16;
+  // Load n of this wave for tile iter of K (isk) or V into stage st.  Rows past
+  // S (tail tile) or past n_global (strip) repeat a valid row: their scores are
+  // masked, so they carry zero weight.  Tiles past the end of the range load
+  // clamped rows into a stage that is not read again.
+  auto dma = [&](bool isk, int iter, int st, int n) {
+    int row;
+    if (is_strip(iter)) row = gpos_s[imin(srow + n * RSTEP, s.n_global - 1)];
+    else row = imin(tile_kt(iter) * BN + srow + n * RSTEP, s.S - 1);
+    const char* src = (const char*)(isk ? kp : vp) + (size_t)row * ROWB + (isk ? k_col : v_col);
+    dma16_global(src, smem + (isk ? 0 : NSTAGE * REG) + st * REG + (n * 4 + gw) * 1024);
   };
-  // rows past S (tail tile) or past n_global (strip) repeat a valid row: their
-  // scores are masked, so they carry zero weight
-  auto load_region = [&](const __bf16* base, int src_lane, int iter, int dst) {
-    if (is_strip(iter)) {
-#pragma unroll
-      for (int n = 0; n < NI; ++n) {
-        const int row = gpos_s[imin(srow + n * (WSTEP / ROWB), s.n_global - 1)];
-        const int off = row * ROWB + (src_lane - srow * ROWB);
-        dma16_global((const char*)base + off, smem + dst + (n * kBf16Waves + wave) * 1024);
-      }
-      return;
-    }
-    const int kt = tile_kt(iter);
-    if (kt * BN + BN <= s.S) {
-      const __amdgpu_buffer_rsrc_t r = rsrc(base, kt);
-#pragma unroll
-      for (int n = 0; n < NI; ++n)
-        dma16_buffer(r, smem + dst + (n * kBf16Waves + wave) * 1024, src_lane, n * WSTEP);
-    } else {
-#pragma unroll
-      for (int n = 0; n < NI; ++n) {
-        const int row = imin(kt * BN + srow + n * (WSTEP / ROWB), s.S - 1);
-        const size_t off = (size_t)row * ROWB + (src_lane - srow * ROWB);
-        dma16_global((const char*)base + off, smem + dst + (n * kBf16Waves + wave) * 1024);
-      }
-    }
+  // in-loop form (iter >= 1, never the strip): a buffer descriptor over the
+  // tile's valid rows and a 32-bit lane offset clamped to the last valid row,
+  // so no lane is out of range.
+  const int k_off = srow * ROWB + k_col, v_off = srow * ROWB + v_col;
+  auto dma_band = [&](bool isk, int iter, int st, int n) {
+    // tiles past the last one of the sequence load the last tile instead
+    const int row0 = imin(tile_kt(iter), (s.S - 1) / BN) * BN;
+    const int nrows = imin(s.S - row0, BN);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((isk ? kp : vp) + (size_t)row0 * D), (short)0, nrows * ROWB, 0x00020000);
+    const int off = imin((isk ? k_off : v_off) + n * RSTEP * ROWB,
+                         (nrows - 1) * ROWB + (isk ? k_col : v_col));
+    dma16_buffer(r, smem + (isk ? 0 : NSTAGE * REG) + st * REG + (n * 4 + gw) * 1024, off, 0);
   };
-  auto load_k = [&](int iter, int buf) { load_region(kp, k_src, iter, buf * BUF); };
-  auto load_v = [&](int iter, int buf) { load_region(vp, v_src, iter, buf * BUF + REG); };
 
   // Per-wave tile class.  Tiles EMPTY for this wave (only at the ends of its
   // range, or when it holds no rows) are processed as fully masked.
@@ -329,17 +401,20 @@ void attn_fwd_bf16(KParams p) {
     if (it.is_global) return kt * BN + BN > s.S;
     return classify_tile(MASK, s.window, s.S, wqa, wqb, kt * BN, BN) != TILE_FULL;
   };
+  auto tile_empty = [&](int j) -> bool {
+    if (!wave_active) return true;
+    if (is_strip(j)) return false;
+    return classify_tile(MASK, s.window, s.S, wqa, wqb, tile_kt(j) * BN, BN) == TILE_EMPTY;
+  };
 
   // ---- operand reads -------------------------------------------------------
   // K operand (key 32*kbk + l32, dims 16*dc + 8*hf + [0,8)): logical chunk
-  // 2*dc + hf, physical (2*dc + hf) ^ (l32 & 7) = 2*((dc & 3) ^ (x >> 1)) +
-  // (hf ^ (x & 1)) + 8*(dc >> 2) with x = l32 & 7.
-  const int kx = l32 & 7;
-  int k_rd[4];  // per-lane part for dc & 3; the rest of the offset is an immediate
+  // 2*dc + hf, physical (2*dc + hf) ^ ksw(l32) (ksw(32*kbk + l32) = ksw(l32)).
+  int k_rd[NDC];  // per-lane part for each dc; the 32-key block is an immediate
 #pragma unroll
-  for (int d4 = 0; d4 < 4; ++d4) k_rd[d4] = l32 * ROWB + 16 * (hf ^ (kx & 1)) + 32 * (d4 ^ (kx >> 1));
+  for (int dc = 0; dc < NDC; ++dc) k_rd[dc] = l32 * ROWB + 16 * ((2 * dc + hf) ^ C::ksw(l32));
   auto k_frag = [&](const unsigned char* kbuf, int kbk, int dc) -> bf16x8 {
-    return *(const bf16x8*)(kbuf + k_rd[dc & 3] + kbk * 32 * ROWB + 128 * (dc >> 2));
+    return *(const bf16x8*)(kbuf + k_rd[dc] + kbk * 32 * ROWB);
   };
   // V^T operand (dim 32*db + l32, keys 16*pc + 4*hf + [0,4) then +8) from two
   // ds_read_b64_tr_b16 (v_frags): within each 16-lane group, lane 4t + u addresses the
@@ -405,22 +480,6 @@ void attn_fwd_bf16(KParams p) {
   const float c = p.c;
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
-  // ---- pipeline ---------------------------------------------------------
-  // Tile j lives in stage j % NSTAGE.  Iteration j issues the batch
-  // {K(j+3), V(j+2)} (those that exist) into the stages of K(j) and V(j-1),
-  // both consumed during iteration j-1.  At the top of iteration j the batch of
-  // iteration j-2 (K(j+1), V(j)) must have landed; the batch of iteration j-1
-  // may still be in flight, so vmcnt waits down to its size.
-  auto wait_batch = [&](int j) {
-    // in flight may remain: the batch issued just before iteration j
-    if (j + 2 < n_it) __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * NI));  // vmcnt(2*NI)
-    else if (j + 1 < n_it) __builtin_amdgcn_s_waitcnt(0x0f70 | NI);   // vmcnt(NI)
-    else __builtin_amdgcn_s_waitcnt(0x0f70);                           // vmcnt(0)
-  };
-  auto issue_batch = [&](int j) {
-    if (j + 3 < n_it) load_k(j + 3, (j + 3) % NSTAGE);
-    if (j + 2 < n_it) load_v(j + 2, (j + 2) % NSTAGE);
-  };
   if (MASK == MASK_LOCAL_GLOBAL && it.is_global) {
     // ---- global rows: keys split over the waves of a head -----------------
     // The wph waves of a query head hold the same 32 global rows and walk
@@ -442,7 +501,7 @@ void attn_fwd_bf16(KParams p) {
       for (int n = 0; n < NIG; ++n) {
         const int row = n * RPI + lrow;
         const int key = imin(t * GK + row, s.S - 1);  // tail rows repeat a valid row (masked)
-        const int sw = is_v ? ((row & 3) << VSH) : (row & 7);
+        const int sw = is_v ? ((row & 3) << VSH) : C::ksw(row);
         dma16_global((const char*)base + (size_t)key * ROWB + (lphys ^ sw) * 16, dst + n * 1024);
       }
     };
@@ -570,49 +629,59 @@ void attn_fwd_bf16(KParams p) {
       }
     }
   } else {
-  f32x16 scur[NKB], snxt[NKB];
-  load_k(0, 0);
-  load_v(0, 0);
-  if (n_it > 1) load_k(1, 1);
-  issue_batch(-1);  // K(2), V(1)
-  wait_batch(0);
-  __syncthreads();
+  f32x16 scur[NKB];  // S(j) of this wave's 32 queries
+  bf16x8 pb[NPC];    // P(j), the B operand of O += V(j) P(j); zero where no softmax ran
+  auto zero_p = [&]() {
 #pragma unroll
-  for (int kbk = 0; kbk < NKB; ++kbk)
+    for (int pc = 0; pc < NPC; ++pc)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) scur[kbk][r] = 0.f;
-#pragma unroll
-  for (int dc = 0; dc < NDC; ++dc)
-#pragma unroll
-    for (int kbk = 0; kbk < NKB; ++kbk) scur[kbk] = mfma32(k_frag(smem, kbk, dc), qf[dc], scur[kbk]);
+      for (int t = 0; t < 8; ++t) pb[pc][t] = (__bf16)0.f;
+  };
+  zero_p();
 
-  for (int iter = 0; iter < n_it; ++iter) {
-    // Every wave has left the previous tile (its LDS reads are done), and
-    // K(j+1), V(j) have landed.
-    wait_batch(iter);
-    __syncthreads();
-    const int cur = iter % NSTAGE, nxt = (iter + 1) % NSTAGE;
-    issue_batch(iter);
-    const unsigned char* kbuf_nxt = smem + nxt * BUF;      // K(j+1)
-    const unsigned char* vbuf_cur = smem + cur * BUF + REG;  // V(j)
-    // K(j+1) operands: read two 16-dim steps ahead of their MFMAs
-    const unsigned kb = lds_addr(kbuf_nxt);
-    const unsigned kbd[4] = {kb + k_rd[0], kb + k_rd[1], kb + k_rd[2], kb + k_rd[3]};
-    bf16x8 kf[3][2];
-    k_frags<ROWB, 0>(kf[0], kbd);
-    k_frags<ROWB, 1>(kf[1], kbd);
-
-    if (tile_partial(iter)) {
-      asm volatile("");  // keep this a branch: full tiles skip it
-      apply_mask(scur, iter);
+  // ---- the matrix block of one step --------------------------------------
+  // O^T += V(jv)^T P(jv)^T (if do_pv), then S(js) = K(js) Q^T (if do_s), as
+  // straight MFMA sequences whose LDS operands are read up to eight MFMAs
+  // ahead.  This wave's direct loads for tile dj (K if dk, else V; none if
+  // dj < 0) into stage dst are spread between the MFMAs, so the memory pipe
+  // never sees a burst; every step issues the same number of loads, which
+  // keeps the vmcnt waits exact.
+  auto mfma_block = [&](int jv, bool do_pv, int js, bool do_s, bool dk, int dj, int dst) {
+    int dn = 0;
+    auto do_dma = [&](int cnt) {
+      for (int k = 0; k < cnt; ++k) {
+        if (dj >= 0) dma_band(dk, dj, dst, dn);
+        ++dn;
+      }
+    };
+    if (!do_pv && !do_s) {
+      do_dma(NGL);
+      return;
     }
+    __builtin_amdgcn_s_setprio(1);
+    // One sequence for every block.  Where P.V is not needed, P is zero (the
+    // softmax of that tile was skipped) and its operands are read from the K
+    // tile of this block, which has landed (S needs it): a V stage may still
+    // be in flight or hold stale bits, and 0 * NaN would not add zero.  Where
+    // S is not needed, it is computed from a landed stage and never read.
+    const unsigned kb = lds_addr(smem + (js % NSTAGE) * REG);
+    const unsigned vb = do_pv ? lds_addr(smem + NSTAGE * REG + (jv % NSTAGE) * REG) : kb;
+    unsigned vbd[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vbd[db] = vb + v_rd[db];
+    unsigned kbd[NDC];
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) kbd[dc] = kb + k_rd[dc];
+    block_run<2, ROWB, NDB, NDC, NGL>(vbd, kbd, pb, qf, oacc, scur, do_dma);
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-    // -- block A: first half of S(j+1) = K(j+1) Q^T beside the row max of S(j).
-    //    S(j+1) is always computed; after the last tile it is unused.
-#pragma unroll
-    for (int kbk = 0; kbk < NKB; ++kbk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) snxt[kbk][r] = 0.f;
+  // ---- online softmax of S(j): mask, running maximum, weights P(j) and l -----
+  auto softmax = [&](int j) {
+    if (tile_partial(j)) {
+      asm volatile("");  // keep this a branch: full tiles skip it
+      apply_mask(scur, j);
+    }
     float mx;
     {
       // four independent v_max3 chains over the 32 scores of this lane, then join
@@ -627,12 +696,9 @@ void attn_fwd_bf16(KParams p) {
       }
       mx = max3f(max3f(t[0], t[1], t[2]), t[3], t[3]);
     }
-    s_steps<ROWB, NDC, NDB, 0, NDC / 2>(kf, kbd, qf, snxt);
     mx = pair_max(mx);
-    const bool need_rescale = __builtin_amdgcn_ballot_w64(mx * c > m_run * c + kLazy) != 0;
-
     // rare: a row maximum grew by more than 2^kLazy
-    if (need_rescale) {
+    if (__builtin_amdgcn_ballot_w64(mx * c > m_run * c + kLazy) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
       m_run = m_new;
@@ -644,10 +710,8 @@ void attn_fwd_bf16(KParams p) {
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
     const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-
-    // weights of the 8 registers of one P^T operand -> bf16, added to l
-    bf16x8 pb[NPC];
-    auto make_p = [&](int pc) {
+#pragma unroll
+    for (int pc = 0; pc < NPC; ++pc) {
       const int kbk = pc >> 1, rb = (pc & 1) * 8;
 #pragma unroll
       for (int t = 0; t < 8; t += 2) {
@@ -660,41 +724,61 @@ void attn_fwd_bf16(KParams p) {
         pb[pc][t] = pr[0];
         pb[pc][t + 1] = pr[1];
       }
-    };
+    }
+  };
 
-    // -- block B: second half of S(j+1) beside the first half of P(j); O +=
-    //    V(j) P(j) beside the second half of P(j).  The V^T operands of each
-    //    16-key step are read one step ahead of their MFMAs.
-    const unsigned vb = lds_addr(vbuf_cur);
-    unsigned vbd[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) vbd[db] = vb + v_rd[db];
-    bf16x8 fx[NDB], fy[NDB];
-    v_frags<ROWB, NDB, 0>(fx, vbd);
-    make_p(0);
-    make_p(1);
-    s_steps<ROWB, NDC, NDB, NDC / 2, NDC>(kf, kbd, qf, snxt);
-    v_frags<ROWB, NDB, 1>(fy, vbd);
-    lds_wait_frags<2 * NDB>(fx);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fx[db], pb[0], oacc[db]);
-    v_frags<ROWB, NDB, 2>(fx, vbd);
-    lds_wait_frags<2 * NDB>(fy);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fy[db], pb[1], oacc[db]);
-    make_p(2);
-    make_p(3);
-    v_frags<ROWB, NDB, 3>(fy, vbd);
-    lds_wait_frags<2 * NDB>(fx);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fx[db], pb[2], oacc[db]);
-    lds_wait_frags<0>(fy);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fy[db], pb[3], oacc[db]);
-#pragma unroll
-    for (int kbk = 0; kbk < NKB; ++kbk) scur[kbk] = snxt[kbk];
+  // ---- pipeline ---------------------------------------------------------
+  // Tile j lives in stage j % NSTAGE.  The waves form two groups, waves 0-3
+  // and 4-7, so that each SIMD runs one wave of each.  Per tile there are two
+  // barrier-separated steps; in each, one group runs its matrix block and the
+  // other its softmax, so the matrix cores and the vector ALUs of every SIMD
+  // work at the same time:
+  //   step 2j  : group 0 softmax(S(j)) -> P(j)   | group 1 O += V(j-1)P(j-1); S(j); loads V(j+1)
+  //   step 2j+1: group 0 O += V(j)P(j); S(j+1); loads K(j+3) | group 1 softmax(S(j))
+  // K(j) is last read in step 2j, so K(j+3) may overwrite its stage from step
+  // 2j+1 on; V(j-2) is last read in step 2j-2, so V(j+1) may overwrite its
+  // stage in step 2j.  At the end of step 2j each group waits for its own
+  // loads of K(j+1) and V(j) (read from step 2j+1 on): group 0 lets K(j+2)
+  // stay in flight, group 1 lets V(j+1), i.e. vmcnt(NGL).
+  // The steps are separated by bare s_barrier: __syncthreads() adds a
+  // workgroup release fence, which the compiler implements by waiting for
+  // every direct load in flight.  Direct loads are covered by the explicit
+  // vmcnt waits, and every LDS read of a step is waited for before its MFMA.
+  const int grp = wave >> 2;
+  if (grp == 0) {
+    for (int n = 0; n < NGL; ++n) dma(true, 0, 0, n);
+    for (int n = 0; n < NGL; ++n) dma(true, 1, 1, n);
+    for (int n = 0; n < NGL; ++n) dma(true, 2, 2, n);
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * NGL));  // K(0) landed
+  } else {
+    for (int n = 0; n < NGL; ++n) dma(false, 0, 0, n);
   }
-  }  // shared-ring path
+  __builtin_amdgcn_s_barrier();
+
+  if (grp == 0) {
+    if (!tile_empty(0)) mfma_block(0, false, 0, true, true, -1, 0);  // S(0), no loads
+    for (int j = 0; j <= n_it; ++j) {
+      if (j < n_it && !tile_empty(j)) softmax(j);  // step 2j
+      else zero_p();
+      __builtin_amdgcn_s_waitcnt(0x0f70 | NGL);    // K(j+1) landed
+      __builtin_amdgcn_s_barrier();
+      mfma_block(j, j < n_it && !tile_empty(j), j + 1, j + 1 < n_it && !tile_empty(j + 1),
+                 true, j + 3, (j + 3) % NSTAGE);  // step 2j+1
+      __builtin_amdgcn_s_barrier();
+    }
+  } else {
+    for (int j = 0; j <= n_it; ++j) {
+      mfma_block(j - 1, j >= 1 && !tile_empty(j - 1), j, j < n_it && !tile_empty(j),
+                 false, j + 1, (j + 1) % NSTAGE);  // step 2j
+      __builtin_amdgcn_s_waitcnt(0x0f70 | NGL);    // V(j) landed
+      __builtin_amdgcn_s_barrier();
+      if (j < n_it && !tile_empty(j)) softmax(j);  // step 2j+1
+      else zero_p();
+      __builtin_amdgcn_s_barrier();
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // no direct load may land after the workgroup ends
+  }  // ping-pong path
 
   // ---- epilogue: O = O^T / l, round to bf16, store --------------------------
   {
