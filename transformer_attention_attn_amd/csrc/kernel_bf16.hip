@@ -26,7 +26,7 @@
 //     the matrix cores and the vector ALUs of a SIMD work side by side.  The
 //     wave running its matrix block gets the higher issue priority.
 //   * K and V go straight from HBM into LDS (buffer/global loads with the LDS
-//     flag: no staging registers) through a three-stage ring; group 0 loads
+//     flag: no staging registers) through a four-stage ring; group 0 loads
 //     the K tiles and group 1 the V tiles, spread between their MFMAs.
 //   * LDS operands are read with inline-asm ds_read_b128 (K) and
 //     ds_read_b64_tr_b16 (V^T) up to eight MFMAs ahead, with exact lgkmcnt
@@ -264,7 +264,7 @@ struct Cfg {
     return D == 128 ? (row & 15) : ((row >> 1) & 7);
   }
   static constexpr int BUF = 2 * REG;           // K tile then V tile
-  static constexpr int NSTAGE = 3;              // LDS stages of the K/V ring
+  static constexpr int NSTAGE = 4;              // LDS stages of the K/V ring
   static constexpr int NGL = REG / 1024 / 4;    // 1 KiB direct loads per wave per tile (4 waves)
   static constexpr int RSTEP = 4096 / ROWB;     // rows between a lane's successive loads
   static_assert(NGL * 4 * 1024 == REG && RSTEP % 8 == 0, "tile split into 1 KiB group loads");
@@ -733,13 +733,15 @@ void attn_fwd_bf16(KParams p) {
   // barrier-separated steps; in each, one group runs its matrix block and the
   // other its softmax, so the matrix cores and the vector ALUs of every SIMD
   // work at the same time:
-  //   step 2j  : group 0 softmax(S(j)) -> P(j)   | group 1 O += V(j-1)P(j-1); S(j); loads V(j+1)
-  //   step 2j+1: group 0 O += V(j)P(j); S(j+1); loads K(j+3) | group 1 softmax(S(j))
-  // K(j) is last read in step 2j, so K(j+3) may overwrite its stage from step
-  // 2j+1 on; V(j-2) is last read in step 2j-2, so V(j+1) may overwrite its
-  // stage in step 2j.  At the end of step 2j each group waits for its own
-  // loads of K(j+1) and V(j) (read from step 2j+1 on): group 0 lets K(j+2)
-  // stay in flight, group 1 lets V(j+1), i.e. vmcnt(NGL).
+  //   step 2j  : group 0 softmax(S(j)) -> P(j)   | group 1 O += V(j-1)P(j-1); S(j); loads V(j+2)
+  //   step 2j+1: group 0 O += V(j)P(j); S(j+1); loads K(j+4) | group 1 softmax(S(j))
+  // Loads run two tiles ahead.  K(j) is last read in step 2j, so K(j+4) may
+  // overwrite its stage from step 2j+1 on; V(j-2) is last read in step 2j-2,
+  // so V(j+2) may overwrite its stage in step 2j.  At the end of step 2j each
+  // group waits for its own loads of K(j+1) and V(j) (read from step 2j+1
+  // on), letting the two later tiles' loads stay in flight: vmcnt(2*NGL).
+  // Every step issues the same number of loads (tiles past the end load a
+  // clamped tile), which keeps these counts exact.
   // The steps are separated by bare s_barrier: __syncthreads() adds a
   // workgroup release fence, which the compiler implements by waiting for
   // every direct load in flight.  Direct loads are covered by the explicit
@@ -749,9 +751,11 @@ void attn_fwd_bf16(KParams p) {
     for (int n = 0; n < NGL; ++n) dma(true, 0, 0, n);
     for (int n = 0; n < NGL; ++n) dma(true, 1, 1, n);
     for (int n = 0; n < NGL; ++n) dma(true, 2, 2, n);
-    __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * NGL));  // K(0) landed
+    for (int n = 0; n < NGL; ++n) dma(true, 3, 3, n);
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (3 * NGL));  // K(0) landed
   } else {
     for (int n = 0; n < NGL; ++n) dma(false, 0, 0, n);
+    for (int n = 0; n < NGL; ++n) dma(false, 1, 1, n);
   }
   __builtin_amdgcn_s_barrier();
 
@@ -760,17 +764,17 @@ void attn_fwd_bf16(KParams p) {
     for (int j = 0; j <= n_it; ++j) {
       if (j < n_it && !tile_empty(j)) softmax(j);  // step 2j
       else zero_p();
-      __builtin_amdgcn_s_waitcnt(0x0f70 | NGL);    // K(j+1) landed
+      __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * NGL));  // K(j+1) landed
       __builtin_amdgcn_s_barrier();
       mfma_block(j, j < n_it && !tile_empty(j), j + 1, j + 1 < n_it && !tile_empty(j + 1),
-                 true, j + 3, (j + 3) % NSTAGE);  // step 2j+1
+                 true, j + 4, (j + 4) % NSTAGE);  // step 2j+1
       __builtin_amdgcn_s_barrier();
     }
   } else {
     for (int j = 0; j <= n_it; ++j) {
       mfma_block(j - 1, j >= 1 && !tile_empty(j - 1), j, j < n_it && !tile_empty(j),
-                 false, j + 1, (j + 1) % NSTAGE);  // step 2j
-      __builtin_amdgcn_s_waitcnt(0x0f70 | NGL);    // V(j) landed
+                 false, j + 2, (j + 2) % NSTAGE);  // step 2j
+      __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * NGL));  // V(j) landed
       __builtin_amdgcn_s_barrier();
       if (j < n_it && !tile_empty(j)) softmax(j);  // step 2j+1
       else zero_p();
