@@ -716,11 +716,20 @@ void attn_fwd_bf16(KParams p) {
 #pragma unroll
       for (int t = 0; t < 8; t += 2) {
         bf16x2 pr;
-        pr[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(scur[kbk][rb + t], c, -mc));
-        pr[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(scur[kbk][rb + t + 1], c, -mc));
-        // the denominator sums exactly the rounded weights used in P.V
-        if (t & 2) l_run1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run1, false);
-        else l_run0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run0, false);
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kbk][rb + t], c, -mc));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kbk][rb + t + 1], c, -mc));
+        pr[0] = (__bf16)e0;
+        pr[1] = (__bf16)e1;
+        if constexpr (D == 128) {
+          // v_dot2 issues to the matrix pipe, which the other wave group keeps
+          // busy for a whole D = 128 block: sum the fp32 weights with adds
+          if (t & 2) l_run1 += e0 + e1;
+          else l_run0 += e0 + e1;
+        } else {
+          // the denominator sums exactly the rounded weights used in P.V
+          if (t & 2) l_run1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run1, false);
+          else l_run0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run0, false);
+        }
         pb[pc][t] = pr[0];
         pb[pc][t + 1] = pr[1];
       }
