@@ -20,7 +20,14 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["attn_api.cpp", "kernel_fp32.hip", "kernel_bf16.hip"]
+# (source, object name, extra flags): the bf16 kernel is compiled once per head
+# dimension, each object holding only the constants of its own tile shape
+SOURCES = [
+    ("attn_api.cpp", "attn_api", []),
+    ("kernel_fp32.hip", "kernel_fp32", []),
+    ("kernel_bf16.hip", "kernel_bf16_d64", ["-DATTN_HEAD_DIM=64"]),
+    ("kernel_bf16.hip", "kernel_bf16_d128", ["-DATTN_HEAD_DIM=128"]),
+]
 ARCH = "gfx950"
 
 
@@ -38,9 +45,10 @@ COMMON = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(unit, verbose: bool) -> str:
+    src, name, flags = unit
+    obj = os.path.join(BUILD_DIR, name + ".o")
+    cmd = [hipcc(), *COMMON, *flags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

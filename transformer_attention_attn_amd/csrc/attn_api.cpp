@@ -125,7 +125,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq
   std::copy(c.gpos, c.gpos + c.n_global, p.gpos);
 
   hipStream_t st = (hipStream_t)stream;
-  hipError_t err = dtype == ATTN_DTYPE_BF16 ? attn::launch_bf16(p, D, st) : attn::launch_fp32(p, D, st);
+  hipError_t err = dtype == ATTN_DTYPE_BF16 ? (D == 64 ? attn::launch_bf16_d64(p, st) : attn::launch_bf16_d128(p, st)) : attn::launch_fp32(p, D, st);
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

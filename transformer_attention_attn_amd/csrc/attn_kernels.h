@@ -30,9 +30,11 @@ constexpr int kF32Rows = 64;   // query rows per fp32 work item (one head)
 constexpr int kF32Keys = 32;   // keys per fp32 tile
 constexpr int kBf16Rows = 32 * kBf16Waves;  // query rows per bf16 work item (heads packed)
 constexpr int kBf16GlobalRows = 32;          // global rows per query head in a bf16 global item
-ATTN_HD int bf16_keys_per_tile(int) { return 64; }
+// keys per bf16 tile: 128 at D = 128 (a 64-MFMA block), 64 at D = 64 (32 MFMAs)
+ATTN_HD int bf16_keys_per_tile(int D) { return D == 128 ? 128 : 64; }
 
 hipError_t launch_fp32(const KParams& p, int D, hipStream_t stream);
-hipError_t launch_bf16(const KParams& p, int D, hipStream_t stream);
+hipError_t launch_bf16_d64(const KParams& p, hipStream_t stream);   // kernel_bf16.hip, D = 64 build
+hipError_t launch_bf16_d128(const KParams& p, hipStream_t stream);  // kernel_bf16.hip, D = 128 build
 
 }  // namespace attn

@@ -22,12 +22,18 @@
 //   * Two wave groups per workgroup (waves 0-3 and 4-7, one of each per
 //     SIMD) in ping-pong: per key tile there are two barrier-separated steps,
 //     and in each one group runs its matrix block (O += V P for one tile and
-//     S = K Q^T for the next, 32 MFMAs) while the other runs its softmax, so
-//     the matrix cores and the vector ALUs of a SIMD work side by side.  The
-//     wave running its matrix block gets the higher issue priority.
+//     S = K Q^T for the next) while the other runs its softmax, so the matrix
+//     cores and the vector ALUs of a SIMD work side by side.  The wave
+//     running its matrix block gets the higher issue priority.
+//   * Tile width per head dimension: 64 keys at D = 64 (a block is 32
+//     MFMAs), 128 keys at D = 128 (64 MFMAs), which halves the number of
+//     barrier-separated steps per key at D = 128.  The source is compiled
+//     once per head dimension (ATTN_HEAD_DIM), so each build holds only the
+//     constants of its own tile shape.
 //   * K and V go straight from HBM into LDS (buffer/global loads with the LDS
-//     flag: no staging registers) through a four-stage ring; group 0 loads
-//     the K tiles and group 1 the V tiles, spread between their MFMAs.
+//     flag: no staging registers).  D = 64: four-stage rings, group 0 loads
+//     the K tiles and group 1 the V tiles.  D = 128: 32 KB tiles, two-stage
+//     rings (128 KB), group 0 loads both.  Loads are spread between MFMAs.
 //   * LDS operands are read with inline-asm ds_read_b128 (K) and
 //     ds_read_b64_tr_b16 (V^T) up to eight MFMAs ahead, with exact lgkmcnt
 //     waits: the compiler would otherwise wait for every direct load in
@@ -54,10 +60,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BN = 64;           // keys per tile
+#ifndef ATTN_HEAD_DIM
+#error "compile this source once per head dimension: -DATTN_HEAD_DIM=64 or 128"
+#endif
+// Keys per tile of this build's head dimension.
+constexpr int HD = ATTN_HEAD_DIM;
+static_assert(HD == 64 || HD == 128, "head dimension 64 or 128");
+constexpr int BN = HD == 128 ? 128 : 64;
 constexpr int GK = 32;           // keys per private tile of the global-row path
 constexpr int NKB = BN / 32;     // 32-key blocks of S^T
-static_assert(NKB == 2, "the S^T steps hold two 32-key blocks");
 constexpr int NPC = BN / 16;     // 16-key reduction steps of O^T
 constexpr float kLazy = 8.f;     // rescale threshold, log2 units
 
@@ -162,13 +173,17 @@ template <int ROWB, int NDB, int OP>
 __device__ __forceinline__ bf16x8 v_op(const unsigned* vbd) {
   return lds_tr_pair<16 * (OP / NDB) * ROWB, 8 * ROWB>(vbd[OP % NDB]);
 }
-// Operand OP of the S part: K rows 32*(OP % 2) + l32 for 16-dim step OP / 2
-// (one read from the per-lane base of that step).
-template <int ROWB, int OP>
+// Operand OP of the S part: K rows 32*(OP % NKB) + l32 for 16-dim step
+// OP / NKB (one read from the per-lane base of that step).
+template <int ROWB, int NKB, int OP>
 __device__ __forceinline__ bf16x8 k_op(const unsigned* kbd) {
-  constexpr int KBK = OP % 2, DC = OP / 2;
+  constexpr int KBK = OP % NKB, DC = OP / NKB;
   return lds_read16<KBK * 32 * ROWB>(kbd[DC]);
 }
+
+// s_waitcnt immediate for vmcnt(n) (6-bit count split over two fields) with
+// the other counters left unconstrained.
+constexpr int vmcnt_enc(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 
 // Direct loads issued right after MFMA i of a part of l MFMAs that carries
 // ndma loads (spread evenly).
@@ -179,12 +194,12 @@ constexpr int dma_after(int i, int l, int ndma) {
   return c;
 }
 // The operand sequence of a matrix block.  MODE 0: P.V only (O^T += V^T P^T
-// over the NDB output blocks); MODE 1: S only (S^T = K Q^T over the two 32-key
-// blocks); MODE 2: P.V then S as one sequence, so the K operands of S are read
-// while the last P.V MFMAs run.
-template <int MODE, int NDB, int NDC>
+// over the NDB output blocks, 2*NKB 16-key steps); MODE 1: S only (S^T = K Q^T
+// over the NKB 32-key blocks); MODE 2: P.V then S as one sequence, so the K
+// operands of S are read while the last P.V MFMAs run.
+template <int MODE, int NDB, int NDC, int NKB>
 struct BlockSeq {
-  static constexpr int NPV = 4 * NDB, NSM = 2 * NDC;
+  static constexpr int NPV = 2 * NKB * NDB, NSM = NKB * NDC;
   static constexpr int L = MODE == 0 ? NPV : MODE == 1 ? NSM : NPV + NSM;
   static constexpr bool is_pv(int i) { return MODE == 0 || (MODE == 2 && i < NPV); }
   static constexpr int s_index(int i) { return MODE == 1 ? i : i - NPV; }
@@ -198,21 +213,21 @@ struct BlockSeq {
   }
 };
 
-template <int MODE, int ROWB, int NDB, int NDC, int OP>
+template <int MODE, int ROWB, int NDB, int NDC, int NKB, int OP>
 __device__ __forceinline__ bf16x8 block_op(const unsigned* vbd, const unsigned* kbd) {
-  using Q = BlockSeq<MODE, NDB, NDC>;
+  using Q = BlockSeq<MODE, NDB, NDC, NKB>;
   if constexpr (Q::is_pv(OP)) return v_op<ROWB, NDB, OP>(vbd);
-  else return k_op<ROWB, Q::s_index(OP)>(kbd);
+  else return k_op<ROWB, NKB, Q::s_index(OP)>(kbd);
 }
 
 // MFMAs [I, L) of a matrix block: wait for operand I, MFMA I, read operand
 // I + PF into the freed ring slot, then the direct loads scheduled after MFMA I.
-template <int MODE, int ROWB, int NDB, int NDC, int PF, int I, int NDMA, typename Dma>
+template <int MODE, int ROWB, int NDB, int NDC, int NKB, int PF, int I, int NDMA, typename Dma>
 __device__ __forceinline__ void block_steps(bf16x8 (&ring)[PF], const unsigned* vbd,
                                             const unsigned* kbd, const bf16x8* pb,
                                             const bf16x8* qf, f32x16* oacc, f32x16* sc,
                                             Dma& dma) {
-  using Q = BlockSeq<MODE, NDB, NDC>;
+  using Q = BlockSeq<MODE, NDB, NDC, NKB>;
   if constexpr (I < Q::L) {
     static_assert(Q::younger(I, PF) <= 15, "lgkmcnt holds at most 15");
     lds_wait1<Q::younger(I, PF)>(ring[I % PF]);
@@ -221,34 +236,34 @@ __device__ __forceinline__ void block_steps(bf16x8 (&ring)[PF], const unsigned* 
                                                               oacc[I % NDB], 0, 0, 0);
     } else {
       constexpr int J = Q::s_index(I);
-      if constexpr (J / 2 == 0)
-        sc[J % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[I % PF], qf[0], f32x16{}, 0, 0, 0);
+      if constexpr (J / NKB == 0)
+        sc[J % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[I % PF], qf[0], f32x16{}, 0, 0, 0);
       else
-        sc[J % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[I % PF], qf[J / 2], sc[J % 2],
-                                                            0, 0, 0);
+        sc[J % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[I % PF], qf[J / NKB],
+                                                              sc[J % NKB], 0, 0, 0);
     }
-    if constexpr (I + PF < Q::L) ring[I % PF] = block_op<MODE, ROWB, NDB, NDC, I + PF>(vbd, kbd);
+    if constexpr (I + PF < Q::L) ring[I % PF] = block_op<MODE, ROWB, NDB, NDC, NKB, I + PF>(vbd, kbd);
     dma(dma_after(I, Q::L, NDMA));
-    block_steps<MODE, ROWB, NDB, NDC, PF, I + 1, NDMA>(ring, vbd, kbd, pb, qf, oacc, sc, dma);
+    block_steps<MODE, ROWB, NDB, NDC, NKB, PF, I + 1, NDMA>(ring, vbd, kbd, pb, qf, oacc, sc, dma);
   }
 }
-template <int MODE, int ROWB, int NDB, int NDC, int PF, int I>
+template <int MODE, int ROWB, int NDB, int NDC, int NKB, int PF, int I>
 __device__ __forceinline__ void block_prime(bf16x8 (&ring)[PF], const unsigned* vbd,
                                             const unsigned* kbd) {
   if constexpr (I < PF) {
-    ring[I] = block_op<MODE, ROWB, NDB, NDC, I>(vbd, kbd);
-    block_prime<MODE, ROWB, NDB, NDC, PF, I + 1>(ring, vbd, kbd);
+    ring[I] = block_op<MODE, ROWB, NDB, NDC, NKB, I>(vbd, kbd);
+    block_prime<MODE, ROWB, NDB, NDC, NKB, PF, I + 1>(ring, vbd, kbd);
   }
 }
-template <int MODE, int ROWB, int NDB, int NDC, int NDMA, typename Dma>
+template <int MODE, int ROWB, int NDB, int NDC, int NKB, int NDMA, typename Dma>
 __device__ __forceinline__ void block_run(const unsigned* vbd, const unsigned* kbd,
                                           const bf16x8* pb, const bf16x8* qf, f32x16* oacc,
                                           f32x16* sc, Dma& dma) {
-  constexpr int L = BlockSeq<MODE, NDB, NDC>::L;
+  constexpr int L = BlockSeq<MODE, NDB, NDC, NKB>::L;
   constexpr int PF = L < 8 ? L : 8;  // operands in flight: at most 7 * 2 reads outstanding
   bf16x8 ring[PF];
-  block_prime<MODE, ROWB, NDB, NDC, PF, 0>(ring, vbd, kbd);
-  block_steps<MODE, ROWB, NDB, NDC, PF, 0, NDMA>(ring, vbd, kbd, pb, qf, oacc, sc, dma);
+  block_prime<MODE, ROWB, NDB, NDC, NKB, PF, 0>(ring, vbd, kbd);
+  block_steps<MODE, ROWB, NDB, NDC, NKB, PF, 0, NDMA>(ring, vbd, kbd, pb, qf, oacc, sc, dma);
 }
 
 template <int D>
@@ -264,7 +279,7 @@ struct Cfg {
     return D == 128 ? (row & 15) : ((row >> 1) & 7);
   }
   static constexpr int BUF = 2 * REG;           // K tile then V tile
-  static constexpr int NSTAGE = 4;              // LDS stages of the K/V ring
+  static constexpr int NSTAGE = BN == 128 ? 2 : 4;  // LDS stages of the K/V ring
   static constexpr int NGL = REG / 1024 / 4;    // 1 KiB direct loads per wave per tile (4 waves)
   static constexpr int RSTEP = 4096 / ROWB;     // rows between a lane's successive loads
   static_assert(NGL * 4 * 1024 == REG && RSTEP % 8 == 0, "tile split into 1 KiB group loads");
@@ -442,7 +457,7 @@ void attn_fwd_bf16(KParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kbk * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const int dist = q_row - gpos_s[key];
+          const int dist = q_row - gpos_s[key < kMaxGlobal ? key : 0];
           const bool vis = key < s.n_global && (dist > s.window || -dist > s.window);
           sc[kbk][r] = vis ? sc[kbk][r] : -INFINITY;
         }
@@ -646,16 +661,21 @@ void attn_fwd_bf16(KParams p) {
   // dj < 0) into stage dst are spread between the MFMAs, so the memory pipe
   // never sees a burst; every step issues the same number of loads, which
   // keeps the vmcnt waits exact.
+  // With two stages, group 0 loads both K(dj) and V(dj - 1).
+  constexpr int NDMA = NSTAGE == 2 ? 2 * NGL : NGL;
   auto mfma_block = [&](int jv, bool do_pv, int js, bool do_s, bool dk, int dj, int dst) {
     int dn = 0;
     auto do_dma = [&](int cnt) {
       for (int k = 0; k < cnt; ++k) {
-        if (dj >= 0) dma_band(dk, dj, dst, dn);
+        if (dj >= 0) {
+          if (NSTAGE == 2 && dn >= NGL) dma_band(false, dj - 1, (dj - 1) % NSTAGE, dn - NGL);
+          else dma_band(dk, dj, dst, dn);
+        }
         ++dn;
       }
     };
     if (!do_pv && !do_s) {
-      do_dma(NGL);
+      do_dma(NDMA);
       return;
     }
     __builtin_amdgcn_s_setprio(1);
@@ -672,7 +692,7 @@ void attn_fwd_bf16(KParams p) {
     unsigned kbd[NDC];
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) kbd[dc] = kb + k_rd[dc];
-    block_run<2, ROWB, NDB, NDC, NGL>(vbd, kbd, pb, qf, oacc, scur, do_dma);
+    block_run<2, ROWB, NDB, NDC, NKB, NDMA>(vbd, kbd, pb, qf, oacc, scur, do_dma);
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -685,9 +705,9 @@ void attn_fwd_bf16(KParams p) {
     float mx;
     {
       // four independent v_max3 chains over the 32 scores of this lane, then join
-      float t[4];
+      float t[2 * NKB];
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
+      for (int c4 = 0; c4 < 2 * NKB; ++c4) {
         const int kbk = c4 >> 1, rb = (c4 & 1) * 8;
         float x = max3f(scur[kbk][rb], scur[kbk][rb + 1], scur[kbk][rb + 2]);
         x = max3f(x, scur[kbk][rb + 3], scur[kbk][rb + 4]);
@@ -695,6 +715,8 @@ void attn_fwd_bf16(KParams p) {
         t[c4] = max3f(x, scur[kbk][rb + 7], scur[kbk][rb + 7]);
       }
       mx = max3f(max3f(t[0], t[1], t[2]), t[3], t[3]);
+#pragma unroll
+      for (int c4 = 4; c4 < 2 * NKB; c4 += 2) mx = max3f(mx, t[c4], t[c4 + 1]);
     }
     mx = pair_max(mx);
     // rare: a row maximum grew by more than 2^kLazy
@@ -756,6 +778,42 @@ void attn_fwd_bf16(KParams p) {
   // every direct load in flight.  Direct loads are covered by the explicit
   // vmcnt waits, and every LDS read of a step is waited for before its MFMA.
   const int grp = wave >> 2;
+  if constexpr (NSTAGE == 2) {
+    // Two stages of 128-key tiles (the four-stage schedule below with the
+    // loads moved): group 0 loads everything, K(j+2) and V(j+1) in step 2j+1
+    // (K(j) and V(j-1) were last read in step 2j: S(j) by group 1, P.V(j-1)
+    // by group 1), and waits for all of them at the end of step 2j+2, before
+    // the barrier into step 2j+3, the first that reads them.  Group 1 loads
+    // nothing, so its waits are implicit in group 0's.
+    if (grp == 0) {
+      for (int n = 0; n < NGL; ++n) dma(true, 0, 0, n);
+      for (int n = 0; n < NGL; ++n) dma(false, 0, 0, n);
+      for (int n = 0; n < NGL; ++n) dma(true, 1, 1, n);
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * NGL));  // K(0) landed
+    }
+    __builtin_amdgcn_s_barrier();
+    if (grp == 0) {
+      if (!tile_empty(0)) mfma_block(0, false, 0, true, true, -1, 0);  // S(0), no loads
+      for (int j = 0; j <= n_it; ++j) {
+        if (j < n_it && !tile_empty(j)) softmax(j);  // step 2j
+        else zero_p();
+        __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));  // K(j+1), V(j) landed
+        __builtin_amdgcn_s_barrier();
+        mfma_block(j, j < n_it && !tile_empty(j), j + 1, j + 1 < n_it && !tile_empty(j + 1),
+                   true, j + 2, j % NSTAGE);  // step 2j+1
+        __builtin_amdgcn_s_barrier();
+      }
+    } else {
+      for (int j = 0; j <= n_it; ++j) {
+        mfma_block(j - 1, j >= 1 && !tile_empty(j - 1), j, j < n_it && !tile_empty(j),
+                   false, -1, 0);  // step 2j
+        __builtin_amdgcn_s_barrier();
+        if (j < n_it && !tile_empty(j)) softmax(j);  // step 2j+1
+        else zero_p();
+        __builtin_amdgcn_s_barrier();
+      }
+    }
+  } else {
   if (grp == 0) {
     for (int n = 0; n < NGL; ++n) dma(true, 0, 0, n);
     for (int n = 0; n < NGL; ++n) dma(true, 1, 1, n);
@@ -789,6 +847,7 @@ void attn_fwd_bf16(KParams p) {
       else zero_p();
       __builtin_amdgcn_s_barrier();
     }
+  }
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // no direct load may land after the workgroup ends
   }  // ping-pong path
@@ -834,8 +893,10 @@ hipError_t launch_d(const KParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_bf16(const KParams& p, int D, hipStream_t stream) {
-  return D == 64 ? launch_d<64>(p, stream) : launch_d<128>(p, stream);
-}
+#if ATTN_HEAD_DIM == 64
+hipError_t launch_bf16_d64(const KParams& p, hipStream_t stream) { return launch_d<64>(p, stream); }
+#else
+hipError_t launch_bf16_d128(const KParams& p, hipStream_t stream) { return launch_d<128>(p, stream); }
+#endif
 
 }  // namespace attn
