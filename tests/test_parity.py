@@ -69,6 +69,24 @@ def test_scales(device, scale, dtype):
     assert err <= TOL[dtype], err
 
 
+# bf16 at D=128 walks 128-key tiles through a two-stage ring: sequence ends
+# and band edges on either side of a tile boundary, two and more ring turns
+TILE128 = []
+for S in (128, 255, 256, 257, 384, 641):
+    TILE128.append((S, "full", 0, ()))
+    TILE128.append((S, "causal", 0, ()))
+    for w in (127, 128, 129):
+        TILE128.append((S, "causal_window", w, ()))
+    TILE128.append((S, "local_global", 128, tuple(x for x in (0, 127, 128, 255) if x < S)))
+
+
+@pytest.mark.parametrize("case", TILE128, ids=lambda c: f"S{c[0]}-{c[1]}-w{c[2]}")
+def test_tile128_edges(device, case):
+    S, mask, window, g = case
+    err = run_case(device, 1, 8, 2, S, 128, "bf16", mask, window, g, seed=S + window)
+    assert err <= TOL["bf16"], err
+
+
 def test_many_globals(device):
     g = tuple(range(0, 1000, 16))  # 63 globals, several per tile
     err = run_case(device, 1, 4, 4, 1000, 128, "bf16", "local_global", 20, g, seed=5)

@@ -657,11 +657,11 @@ void attn_fwd_bf16(KParams p) {
   // ---- the matrix block of one step --------------------------------------
   // O^T += V(jv)^T P(jv)^T (if do_pv), then S(js) = K(js) Q^T (if do_s), as
   // straight MFMA sequences whose LDS operands are read up to eight MFMAs
-  // ahead.  This wave's direct loads for tile dj (K if dk, else V; none if
-  // dj < 0) into stage dst are spread between the MFMAs, so the memory pipe
-  // never sees a burst; every step issues the same number of loads, which
-  // keeps the vmcnt waits exact.
-  // With two stages, group 0 loads both K(dj) and V(dj - 1).
+  // ahead.  This wave's direct loads are spread between the MFMAs, so the
+  // memory pipe never sees a burst: with four stages, tile dj of K (if dk)
+  // or V into stage dst, the same number in every step of a group, which
+  // keeps its vmcnt waits exact; with two stages, K(dj) into stage dst and
+  // V(dj - 1) into its own stage.  No loads where dj < 0.
   constexpr int NDMA = NSTAGE == 2 ? 2 * NGL : NGL;
   auto mfma_block = [&](int jv, bool do_pv, int js, bool do_s, bool dk, int dj, int dst) {
     int dn = 0;
