@@ -19,3 +19,10 @@ from .reference import (  # noqa: F401
     visible_pair_count,
     weights,
 )
+from .decode import (  # noqa: F401
+    DECODE_MASK_KINDS,
+    decode_attention,
+    decode_cache_bytes,
+    decode_effective_flops,
+    decode_visible_count,
+)
