@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_FP32_TFLOPS = 157.3   # vector fp32
-KERNEL_SOURCES = ("kernel_bf16.hip", "attn_kernels.h", "attn_sched.h")
+KERNEL_SOURCES = ("kernel_bf16.hip", "gfx950_ops.h", "attn_kernels.h", "attn_sched.h")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_causal_gqa_s8192_hbm_traffic.md")
 
 

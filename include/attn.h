@@ -22,6 +22,8 @@
 #ifndef ATTN_H
 #define ATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -56,7 +58,9 @@ typedef enum {
   ATTN_ERR_ALIGN = 7,       /* a tensor pointer is not 16-byte aligned             */
   ATTN_ERR_HIP = 8,         /* the kernel launch failed (hipGetLastError)          */
   ATTN_ERR_ALIAS = 9,       /* o overlaps q, k or v                                */
-  ATTN_ERR_SCALE = 10       /* scale is NaN or infinite                            */
+  ATTN_ERR_SCALE = 10,      /* scale is NaN or infinite                            */
+  ATTN_ERR_WORKSPACE = 11   /* attn_decode: workspace missing, smaller than
+                               attn_decode_workspace reports, or not 16-byte aligned */
 } attn_status;
 
 #define ATTN_MAX_GLOBAL 64
@@ -111,6 +115,60 @@ typedef struct {
  * return for them (pointers are not needed and not checked). */
 int attn_plan(int B, int Hq, int Hkv, int S, int D, int mask_kind, int window,
               const int* global_idx, int n_global, int dtype, attn_plan_info* info);
+
+/*
+ * attn_decode -- enqueue decode attention of the Sq newest positions of every
+ * sequence against its key/value cache on `stream`.
+ *
+ * Operation ("Trasformer 浅析", section 推理：KV 缓存: the output at step t is
+ * the softmax of q_t against the cached keys of positions 1..t applied to the
+ * cached values; "Transformer 架构及其变体", section 预填充创建缓存，解码复用缓存:
+ * each step appends the new positions' keys and values to the cache, then the
+ * new queries read the stored history; sequences may hold caches of
+ * different lengths):
+ *
+ *   for every batch b, query head a, new position i < Sq:
+ *     h   = a / (Hq / Hkv),   L = cache_len[b],   p_i = L - Sq + i
+ *     visible positions j:  j <= p_i (ATTN_MASK_CAUSAL)  or  j < L (ATTN_MASK_FULL)
+ *     o[b][a][i][:] = softmax_j(scale * q[b][a][i] . k[b][h][j]) applied to v[b][h][j][:]
+ *
+ *   q           device [B][Hq][Sq][D] bf16: queries of the Sq newest positions
+ *   k_cache,    device [B][Hkv][Smax][D] bf16; sequence b's positions 0..L-1
+ *   v_cache       hold its keys / values, including the Sq new ones (already
+ *               appended); entries at or beyond L are never read into the result
+ *   o           device [B][Hq][Sq][D] bf16, written; must not overlap the inputs
+ *   cache_len   DEVICE pointer to B int32 lengths L in [0, Smax] (read by the
+ *               kernel, so the call can be captured once and replayed with new
+ *               lengths; values outside the range are clamped to it); NULL
+ *               means every sequence holds Smax positions
+ *   Sq          new positions per sequence, >= 1, with (Hq / Hkv) * Sq <= 32
+ *               (all query rows of one key/value head share one matrix-core tile)
+ *   Smax        cache capacity per sequence, >= 1
+ *   D           head width, 64 or 128
+ *   mask_kind   ATTN_MASK_CAUSAL or ATTN_MASK_FULL (identical when Sq == 1)
+ *   scale       multiplies q.k, used exactly as given
+ *   dtype       ATTN_DTYPE_BF16 (fp32 returns ATTN_ERR_UNSUPPORTED); arithmetic
+ *               as for attn_fwd's bf16 path
+ *   workspace   device scratch of at least the bytes attn_decode_workspace
+ *               reports for the same arguments (NULL allowed when that is 0);
+ *               16-byte aligned; owned by the caller, overwritten by the call;
+ *               calls that may run at the same time need separate workspaces
+ *
+ * A query that sees no position (p_i < 0, or L == 0) is written as zeros.
+ * Returns ATTN_OK after enqueuing one or two kernels (the second merges key
+ * splits); no synchronisation, no allocation.  Argument errors are detected on
+ * the host before any launch.  Deterministic for a given input and length.
+ */
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
+                const int* cache_len, int B, int Hq, int Hkv, int Sq, int Smax, int D,
+                int mask_kind, float scale, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_decode needs for these arguments (0 when it needs
+ * none); the same validation as attn_decode, no device access.  The size
+ * depends on B, Hq, Hkv, Sq, Smax and D, not on the lengths. */
+int attn_decode_workspace(int B, int Hq, int Hkv, int Sq, int Smax, int D, int mask_kind,
+                          int dtype, size_t* workspace_bytes);
 
 /* Static, NUL-terminated name of a status code. */
 const char* attn_status_string(int status);

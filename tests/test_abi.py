@@ -28,7 +28,7 @@ def test_library_loads_and_exports_header_symbols():
     assert names == sorted(attn.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert attn.version() == 100
+    assert attn.version() == 200
 
 
 def test_status_strings():

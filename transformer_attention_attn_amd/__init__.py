@@ -18,6 +18,10 @@ from ._binding import (  # noqa: F401
     MAX_GLOBAL,
     STATUS,
     AttnError,
+    decode,
+    decode_raw,
+    decode_workspace_bytes,
+    decode_workspace_status,
     fwd,
     fwd_raw,
     load,

@@ -28,9 +28,11 @@ STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_HEADS",
     4: "ATTN_ERR_UNSUPPORTED", 5: "ATTN_ERR_WINDOW", 6: "ATTN_ERR_GLOBAL",
     7: "ATTN_ERR_ALIGN", 8: "ATTN_ERR_HIP", 9: "ATTN_ERR_ALIAS", 10: "ATTN_ERR_SCALE",
+    11: "ATTN_ERR_WORKSPACE",
 }
 
-EXPORTS = ("attn_fwd", "attn_plan", "attn_status_string", "attn_version")
+EXPORTS = ("attn_fwd", "attn_plan", "attn_decode", "attn_decode_workspace",
+           "attn_status_string", "attn_version")
 
 
 class AttnError(RuntimeError):
@@ -75,6 +77,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int), i, i,
                               ctypes.POINTER(PlanInfo)]
     lib.attn_plan.restype = i
+    lib.attn_decode.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, f, i, p, ctypes.c_size_t, p]
+    lib.attn_decode.restype = i
+    lib.attn_decode_workspace.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
+    lib.attn_decode_workspace.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -166,6 +172,78 @@ def plan_status(B, Hq, Hkv, S, D, mask, window=0, global_idx=None, dtype=DTYPE_B
     info = PlanInfo()
     return lib.attn_plan(B, Hq, Hkv, S, D, _mask_id(mask), window, garr, ng, dtype,
                          ctypes.byref(info))
+
+
+def decode_workspace_status(B, Hq, Hkv, Sq, Smax, D, mask="causal", dtype=DTYPE_BF16):
+    """(status, bytes) of attn_decode_workspace for these arguments (host only)."""
+    lib = load()
+    n = ctypes.c_size_t(0)
+    st = lib.attn_decode_workspace(B, Hq, Hkv, Sq, Smax, D, _mask_id(mask), dtype, ctypes.byref(n))
+    return st, int(n.value)
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, Sq: int, Smax: int, D: int,
+                           mask="causal") -> int:
+    """Device workspace bytes attn_decode needs (0 when it needs none)."""
+    st, n = decode_workspace_status(B, Hq, Hkv, Sq, Smax, D, mask)
+    if st != 0:
+        raise AttnError(st)
+    return n
+
+
+def decode_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, len_ptr: int, B: int, Hq: int,
+               Hkv: int, Sq: int, Smax: int, D: int, mask, scale: float, dtype: int,
+               ws_ptr: int, ws_bytes: int, stream: int) -> int:
+    """Direct call of attn_decode with raw device addresses; returns the status."""
+    return load().attn_decode(q_ptr, k_ptr, v_ptr, o_ptr, len_ptr, B, Hq, Hkv, Sq, Smax, D,
+                              _mask_id(mask), float(scale), dtype, ws_ptr, ws_bytes, stream)
+
+
+def decode(q, k_cache, v_cache, cache_len=None, mask="causal", scale: Optional[float] = None,
+           out=None, workspace=None, stream=None):
+    """Decode attention of the Sq newest positions against key/value caches.
+
+    q: [B, Hq, Sq, D] bf16; k_cache, v_cache: [B, Hkv, Smax, D] bf16, contiguous,
+    on the GPU.  cache_len: int32 GPU tensor of B lengths (None: all Smax).
+    The workspace (a GPU tensor of at least decode_workspace_bytes bytes) is
+    allocated with torch when not given.  Returns o shaped like q.
+    """
+    import torch
+
+    if q.dtype != torch.bfloat16:
+        raise TypeError("decode takes bf16 tensors")
+    for t in (q, k_cache, v_cache):
+        if t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q and the caches must be contiguous 4-D bf16 GPU tensors")
+    B, Hq, Sq, D = q.shape
+    Hkv, Smax = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, Smax, D) or tuple(v_cache.shape) != (B, Hkv, Smax, D):
+        raise ValueError("caches must be [B, Hkv, Smax, D] matching q")
+    if cache_len is not None:
+        if cache_len.dtype != torch.int32 or not cache_len.is_cuda or cache_len.numel() != B:
+            raise ValueError("cache_len must be an int32 GPU tensor of B lengths")
+        cache_len = cache_len.contiguous()
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped like q")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    need = decode_workspace_bytes(B, Hq, Hkv, Sq, Smax, D, mask)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = decode_raw(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                        cache_len.data_ptr() if cache_len is not None else 0, B, Hq, Hkv, Sq,
+                        Smax, D, mask, scale, DTYPE_BF16, ws_ptr, ws_bytes, handle)
+    if st != 0:
+        raise AttnError(st)
+    return out
 
 
 def status_string(status: int) -> str:

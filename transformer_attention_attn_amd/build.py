@@ -27,6 +27,7 @@ SOURCES = [
     ("kernel_fp32.hip", "kernel_fp32", []),
     ("kernel_bf16.hip", "kernel_bf16_d64", ["-DATTN_HEAD_DIM=64"]),
     ("kernel_bf16.hip", "kernel_bf16_d128", ["-DATTN_HEAD_DIM=128"]),
+    ("kernel_decode.hip", "kernel_decode", []),
 ]
 ARCH = "gfx950"
 

@@ -15,7 +15,7 @@ namespace {
 using attn::KParams;
 using attn::Sched;
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 constexpr long long kMaxS = 1LL << 30;
 
 struct Checked {
@@ -97,6 +97,50 @@ long long visible_pairs(int S, int mask, int window, const int* g, int ng) {
   }
 }
 
+struct DecodePlan {
+  int status;
+  int n_split;
+  int chunk;
+  size_t ws_bytes;
+};
+
+// Validation and the key-split plan of a decode call.  Splits: enough
+// (b, kvh, split) workgroups to reach kDecodeWorkgroups, each split at least
+// kDecodeMinChunk keys of the cache capacity; the plan depends on the
+// capacity Smax only, so lengths may change from call to call (and live in
+// device memory) without changing the workspace.
+DecodePlan plan_decode(int B, int Hq, int Hkv, int Sq, int Smax, int D, int mask_kind, int dtype) {
+  DecodePlan d{};
+  d.status = ATTN_OK;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Smax < 1 || (long long)Smax > kMaxS) {
+    d.status = ATTN_ERR_SHAPE;
+    return d;
+  }
+  if (dtype != ATTN_DTYPE_BF16) { d.status = ATTN_ERR_UNSUPPORTED; return d; }
+  if (D != 64 && D != 128) { d.status = ATTN_ERR_UNSUPPORTED; return d; }
+  if (mask_kind != ATTN_MASK_FULL && mask_kind != ATTN_MASK_CAUSAL) {
+    d.status = ATTN_ERR_UNSUPPORTED;
+    return d;
+  }
+  if (Hq % Hkv != 0) { d.status = ATTN_ERR_HEADS; return d; }
+  if ((long long)(Hq / Hkv) * Sq > attn::kDecodeRows) { d.status = ATTN_ERR_UNSUPPORTED; return d; }
+  const long double elems = (long double)B * std::max(Hq, Hkv) * std::max(Sq, Smax) * D;
+  if (elems > 4.0e18L) { d.status = ATTN_ERR_SHAPE; return d; }
+  const long long pairs = (long long)B * Hkv;
+  const long long max_split = attn::cdiv(Smax, attn::kDecodeMinChunk);
+  long long ns = attn::cdiv((int)std::min<long long>(attn::kDecodeWorkgroups, 1LL << 30),
+                            (int)std::min<long long>(pairs, 1LL << 30));
+  ns = std::max<long long>(1, std::min(ns, max_split));
+  const int chunk = attn::cdiv(attn::cdiv(Smax, (int)ns), 32) * 32;
+  d.chunk = chunk;
+  d.n_split = attn::cdiv(Smax, chunk);
+  if (pairs * d.n_split > 0x7fffffffLL) { d.status = ATTN_ERR_SHAPE; return d; }
+  d.ws_bytes = d.n_split > 1
+                   ? (size_t)pairs * d.n_split * attn::kDecodeRows * (size_t)(D + 2) * sizeof(float)
+                   : 0;
+  return d;
+}
+
 }  // namespace
 
 extern "C" {
@@ -167,6 +211,52 @@ int attn_plan(int B, int Hq, int Hkv, int S, int D, int mask_kind, int window,
   return ATTN_OK;
 }
 
+int attn_decode_workspace(int B, int Hq, int Hkv, int Sq, int Smax, int D, int mask_kind,
+                          int dtype, size_t* workspace_bytes) {
+  if (!workspace_bytes) return ATTN_ERR_NULL;
+  const DecodePlan d = plan_decode(B, Hq, Hkv, Sq, Smax, D, mask_kind, dtype);
+  if (d.status != ATTN_OK) return d.status;
+  *workspace_bytes = d.ws_bytes;
+  return ATTN_OK;
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
+                const int* cache_len, int B, int Hq, int Hkv, int Sq, int Smax, int D,
+                int mask_kind, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULL;
+  const DecodePlan d = plan_decode(B, Hq, Hkv, Sq, Smax, D, mask_kind, dtype);
+  if (d.status != ATTN_OK) return d.status;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  for (const void* ptr : {q, k_cache, v_cache, (const void*)o})
+    if ((uintptr_t)ptr % 16 != 0) return ATTN_ERR_ALIGN;
+  if (cache_len && (uintptr_t)cache_len % 4 != 0) return ATTN_ERR_ALIGN;
+  const size_t nq = (size_t)B * Hq * Sq * D * 2, nkv = (size_t)B * Hkv * Smax * D * 2;
+  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k_cache, nkv) || overlaps(o, nq, v_cache, nkv))
+    return ATTN_ERR_ALIAS;
+  if (d.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < d.ws_bytes || (uintptr_t)workspace % 16 != 0)
+      return ATTN_ERR_WORKSPACE;
+    if (overlaps(workspace, d.ws_bytes, o, nq) || overlaps(workspace, d.ws_bytes, q, nq) ||
+        overlaps(workspace, d.ws_bytes, k_cache, nkv) || overlaps(workspace, d.ws_bytes, v_cache, nkv))
+      return ATTN_ERR_ALIAS;
+  }
+
+  attn::DParams p{};
+  p.q = q; p.k = k_cache; p.v = v_cache; p.o = o;
+  p.cache_len = cache_len;
+  p.ws = d.ws_bytes > 0 ? (float*)workspace : nullptr;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Smax = Smax; p.G = Hq / Hkv;
+  p.n_split = d.n_split;
+  p.chunk = d.chunk;
+  p.causal = mask_kind == ATTN_MASK_CAUSAL ? 1 : 0;
+  p.c = std::fabs(scale) * 1.4426950408889634f;
+  p.qmode = scale > 0.f ? 0 : (scale < 0.f ? 1 : 2);
+  if (p.qmode == 2) p.c = 1.f;  // all visible scores equal: weights are uniform
+  hipError_t err = attn::launch_decode(p, D, (hipStream_t)stream);
+  return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ATTN_OK";
@@ -180,6 +270,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
     case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS";
     case ATTN_ERR_SCALE: return "ATTN_ERR_SCALE";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
     default: return "ATTN_ERR_UNKNOWN";
   }
 }

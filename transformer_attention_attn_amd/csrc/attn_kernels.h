@@ -33,7 +33,28 @@ constexpr int kBf16GlobalRows = 32;          // global rows per query head in a 
 // keys per bf16 tile: 128 at D = 128 (a 64-MFMA block), 64 at D = 64 (32 MFMAs)
 ATTN_HD int bf16_keys_per_tile(int D) { return D == 128 ? 128 : 64; }
 
+// Decode attention against a key/value cache (kernel_decode.hip).  Passed by
+// value as the kernel argument block.
+struct DParams {
+  const void* q;          // [B][Hq][Sq][D] bf16
+  const void* k;          // [B][Hkv][Smax][D] bf16 cache
+  const void* v;          // [B][Hkv][Smax][D] bf16 cache
+  void* o;                // [B][Hq][Sq][D] bf16
+  const int* cache_len;   // device, B lengths, or null (all Smax)
+  float* ws;              // n_split > 1: partial (m, l, O) per (b, kvh, split), else null
+  int B, Hq, Hkv, Sq, Smax, G;
+  int n_split;            // key splits per (b, kvh)
+  int chunk;              // keys per split, a multiple of 32
+  int causal;             // 1: query i sees positions 0 .. L - Sq + i; 0: all L
+  float c;                // |scale| * log2(e), see qmode
+  int qmode;              // 0 use q, 1 use -q (negative scale), 2 use 0 (zero scale)
+};
+constexpr int kDecodeRows = 32;        // query rows (G * Sq) per key/value head, at most
+constexpr int kDecodeWorkgroups = 256; // workgroups the split plan aims for
+constexpr int kDecodeMinChunk = 256;   // keys per split, at least (eight waves x 32)
+
 hipError_t launch_fp32(const KParams& p, int D, hipStream_t stream);
+hipError_t launch_decode(const DParams& p, int D, hipStream_t stream);  // kernel_decode.hip
 hipError_t launch_bf16_d64(const KParams& p, hipStream_t stream);   // kernel_bf16.hip, D = 64 build
 hipError_t launch_bf16_d128(const KParams& p, hipStream_t stream);  // kernel_bf16.hip, D = 128 build
 

@@ -1,0 +1,354 @@
+// kernel_decode.hip -- bf16 decode attention against a key/value cache on gfx950.
+//
+// Method: the Sq newest positions of each sequence attend to the cached keys
+// and values of that sequence ("Trasformer 浅析", section 推理：KV 缓存: the
+// step-t output is the softmax of q_t against the cached keys of positions
+// 1..t, applied to the cached values; "Transformer 架构及其变体", section
+// 预填充创建缓存，解码复用缓存: decode reads the whole retained cache each
+// step, so it is bound by memory bandwidth, and the sequences of a batch hold
+// caches of different lengths).  Query i of the Sq new ones sits at cache
+// position L - Sq + i; the causal mask lets it see positions 0..L - Sq + i,
+// the full mask all L.
+//
+// gfx950 mapping:
+//   * One workgroup of eight wave64 per (sequence b, key/value head, key
+//     split).  The 32 query columns of v_mfma_f32_32x32x16_bf16 hold the
+//     G * Sq query rows of the group (G = Hq / Hkv heads x Sq positions, at
+//     most 32), so every cached key and value row is read from HBM once for
+//     all query heads that share it ("第 8 章 AI 算法Transformer大模型",
+//     section 8.2.1: shared key/value heads need one read instead of h).
+//   * The split's keys are cut into 32-key tiles; wave w walks its own
+//     contiguous share of them through a private LDS region (one K tile and
+//     one V tile, loaded straight into LDS), so the walk needs no workgroup
+//     barrier: K(t+1) loads while the softmax of tile t runs, V(t+1) while
+//     P.V of tile t runs.  Operands: K with ds_read_b128, V^T with
+//     ds_read_b64_tr_b16, both under the swizzles of the prefill kernel.
+//   * Online softmax per wave in log2 units with lazy rescaling, then the
+//     waves' partial (m, l, O) merge through LDS in a fixed pairing order.
+//   * One split: O / l is written as bf16.  Several splits: the partial
+//     (m, l, O) goes to the caller's workspace and the combine kernel merges
+//     the splits of each row with the same recurrence.
+#include "attn_kernels.h"
+#include "gfx950_ops.h"
+
+namespace attn {
+namespace {
+
+constexpr int DT = 32;              // keys per tile
+constexpr int DWAVES = 8;           // waves per workgroup
+constexpr float kDLazy = 8.f;       // rescale threshold, log2 units
+
+template <int D>
+struct DCfg {
+  static constexpr int NDC = D / 16;           // 16-dim reduction steps of S^T
+  static constexpr int NDB = D / 32;           // 32-dim blocks of O^T
+  static constexpr int ROWB = D * 2;           // bytes per K or V row
+  static constexpr int REG = DT * ROWB;        // one private K or V tile
+  static constexpr int NIG = REG / 1024;       // 1 KiB direct loads per tile
+  static constexpr int RPI = 1024 / ROWB;      // tile rows per 1 KiB load
+  static constexpr int VSH = D == 128 ? 2 : 1; // V chunk swizzle shift
+  static __device__ constexpr int ksw(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+  static constexpr int SLOT = 4 * NDB * 64 * 16 + 64 * 8;  // one wave's partial for the merge
+  static constexpr int LDS = DWAVES * 2 * REG;
+  static_assert(DWAVES / 2 * SLOT <= LDS, "merge slots fit in the walk regions");
+  static_assert(NIG < 16, "vmcnt immediates below 16");
+};
+
+template <int D>
+__global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
+  using C = DCfg<D>;
+  constexpr int NDC = C::NDC, NDB = C::NDB, ROWB = C::ROWB, REG = C::REG, NIG = C::NIG,
+                RPI = C::RPI, VSH = C::VSH, SLOT = C::SLOT;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+
+  // ---- work item: (b, kvh, split) ---------------------------------------------
+  const int split = (int)blockIdx.x % p.n_split;
+  const int pair = (int)blockIdx.x / p.n_split;
+  const int b = pair / p.Hkv, kvh = pair % p.Hkv;
+  int L = p.Smax;
+  if (p.cache_len) {
+    L = p.cache_len[b];
+    L = L < 0 ? 0 : (L > p.Smax ? p.Smax : L);  // lengths outside [0, Smax] are clamped
+  }
+  L = __builtin_amdgcn_readfirstlane(L);
+
+  // ---- this lane's query row: head kvh*G + r / Sq, new position r % Sq ----------
+  const int r = l32;
+  const int nrows = p.G * p.Sq;
+  const bool row_valid = r < nrows;
+  const int a = kvh * p.G + (row_valid ? r / p.Sq : 0);
+  const int qi = row_valid ? r % p.Sq : 0;
+  // last visible cache position of this row (inclusive); -1 when it sees none
+  const int lim = p.causal ? L - p.Sq + qi : L - 1;
+
+  const size_t Smax = (size_t)p.Smax;
+  const __bf16* kp = (const __bf16*)p.k + ((size_t)b * p.Hkv + kvh) * Smax * D;
+  const __bf16* vp = (const __bf16*)p.v + ((size_t)b * p.Hkv + kvh) * Smax * D;
+
+  // ---- Q^T operand: lane holds row r, dims 16*dc + 8*hf + [0, 8) ---------------
+  bf16x8 qf[NDC];
+  {
+    const __bf16* qrow = (const __bf16*)p.q + (((size_t)b * p.Hq + a) * p.Sq + qi) * D;
+    const u32x4 flip = (p.qmode == 1) ? u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}
+                                      : u32x4{0u, 0u, 0u, 0u};
+    const bool zero = (p.qmode == 2) || !row_valid;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (!zero) x = *(const u32x4*)(qrow + dc * 16 + hf * 8);
+      x ^= flip;
+      qf[dc] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  // ---- this wave's tiles: a contiguous share of the split's key range ----------
+  const int k0 = split * p.chunk;
+  const int k1 = (k0 + p.chunk < L) ? k0 + p.chunk : L;
+  const int ntile = k1 > k0 ? (k1 - k0 + DT - 1) / DT : 0;
+  const int t_lo = ntile * wave / DWAVES, t_hi = ntile * (wave + 1) / DWAVES;
+
+  unsigned char* kreg = smem + wave * 2 * REG;
+  unsigned char* vreg = kreg + REG;
+  // Direct load of tile t (keys k0 + 32 t ..): lane l fills 16 bytes of row
+  // n * RPI + l * 16 / ROWB.  Rows at or past L repeat the last valid row (their
+  // scores are masked, so they carry zero weight, and stay finite).
+  const int lrow = lane * 16 / ROWB, lphys = (lane * 16 % ROWB) / 16;
+  auto gload = [&](const __bf16* base, int t, unsigned char* dst, bool is_v) {
+#pragma unroll
+    for (int n = 0; n < NIG; ++n) {
+      const int row = n * RPI + lrow;
+      const int key = imin(k0 + t * DT + row, L - 1);
+      const int sw = is_v ? ((row & 3) << VSH) : C::ksw(row);
+      dma16_global((const char*)base + (size_t)key * ROWB + (lphys ^ sw) * 16, dst + n * 1024);
+    }
+  };
+
+  // operand read bases (same layouts as the prefill kernel)
+  int k_rd[NDC];
+#pragma unroll
+  for (int dc = 0; dc < NDC; ++dc) k_rd[dc] = l32 * ROWB + 16 * ((2 * dc + hf) ^ C::ksw(l32));
+  const int tt = (lane >> 2) & 3, uu = lane & 3, gg = (lane >> 4) & 1;
+  int v_rd[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+    v_rd[db] = (VSH == 2)
+                   ? (4 * hf + tt) * ROWB + 64 * (db ^ tt) + 32 * gg + 16 * (uu >> 1) + 8 * (uu & 1)
+                   : (4 * hf + tt) * ROWB + 64 * (db ^ (tt >> 1)) + 32 * (gg ^ (tt & 1)) +
+                         16 * (uu >> 1) + 8 * (uu & 1);
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) oacc[db][q] = 0.f;
+  float m_run = -INFINITY, l_run0 = 0.f, l_run1 = 0.f;
+  const float c = p.c;
+  // positions past which some row of the wave may be masked
+  const int lim_lo = p.causal ? L - p.Sq : L - 1;
+
+  if (t_lo < t_hi) {
+    gload(kp, t_lo, kreg, false);
+    gload(vp, t_lo, vreg, true);
+  }
+  for (int t = t_lo; t < t_hi; ++t) {
+    const bool more = t + 1 < t_hi;
+    __builtin_amdgcn_s_waitcnt(0x0f70 | NIG);  // K(t) landed; V(t) may be in flight
+    f32x16 sc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) sc[q] = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) sc = mfma32(*(const bf16x8*)(kreg + k_rd[dc]), qf[dc], sc);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // K operand reads done: the region may be refilled
+    if (more) gload(kp, t + 1, kreg, false);
+    const int tk = k0 + t * DT;
+    if (tk + DT - 1 > lim_lo) {
+      // register q of the accumulator holds key tk + 8*(q/4) + 4*hf + q%4
+      const int rel = lim - tk - 4 * hf;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) sc[q] = (8 * (q >> 2) + (q & 3) <= rel) ? sc[q] : -INFINITY;
+    }
+    float mx = max3f(sc[0], sc[1], sc[2]);
+    mx = max3f(mx, sc[3], sc[4]);
+    mx = max3f(mx, sc[5], sc[6]);
+    mx = max3f(mx, sc[7], sc[8]);
+    mx = max3f(mx, sc[9], sc[10]);
+    mx = max3f(mx, sc[11], sc[12]);
+    mx = max3f(mx, sc[13], sc[14]);
+    mx = max3f(mx, sc[15], sc[15]);
+    mx = pair_max(mx);
+    if (__builtin_amdgcn_ballot_w64(mx * c > m_run * c + kDLazy) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
+      m_run = m_new;
+      l_run0 *= alpha;
+      l_run1 *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) oacc[db][q] *= alpha;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+      for (int u = 0; u < 8; u += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * pc + u], c, -mc));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * pc + u + 1], c, -mc));
+        if (u & 2) l_run1 += e0 + e1;
+        else l_run0 += e0 + e1;
+        pb[pc][u] = (__bf16)e0;
+        pb[pc][u + 1] = (__bf16)e1;
+      }
+    if (more) __builtin_amdgcn_s_waitcnt(0x0f70 | NIG);  // V(t) landed; K(t+1) in flight
+    else __builtin_amdgcn_s_waitcnt(0x0f70);
+    {
+      const unsigned vb = lds_addr(vreg);
+      bf16x8 fx[NDB], fy[NDB];
+      unsigned vbd[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vbd[db] = vb + v_rd[db];
+      v_frags<ROWB, NDB, 0>(fx, vbd);
+      v_frags<ROWB, NDB, 1>(fy, vbd);
+      lds_wait_frags<2 * NDB>(fx);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fx[db], pb[0], oacc[db]);
+      lds_wait_frags<0>(fy);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fy[db], pb[1], oacc[db]);
+    }
+    if (more) gload(vp, t + 1, vreg, true);
+  }
+
+  // ---- merge the eight waves' partial (m, l, O): chunk w takes chunk w + half --
+  // In the O^T accumulator lane l of every wave owns the same (row, dims), so
+  // partials combine lane by lane:
+  //   m = max(m1, m2),  X = X1 * 2^((m1 - m) c) + X2 * 2^((m2 - m) c)  for X in {l, O}.
+  for (int half = DWAVES / 2; half >= 1; half >>= 1) {
+    __syncthreads();  // the walk regions (first pass) or slots (later passes) are free
+    if (wave >= half && wave < 2 * half) {
+      unsigned char* sl = smem + (wave - half) * SLOT;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 x = {oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2],
+                            oacc[db][4 * g4 + 3]};
+          *(float4*)(sl + ((4 * db + g4) * 64 + lane) * 16) = x;
+        }
+      *(float2*)(sl + 4 * NDB * 64 * 16 + lane * 8) = float2{m_run, l_run0 + l_run1};
+    }
+    __syncthreads();
+    if (wave < half) {
+      const unsigned char* sl = smem + wave * SLOT;
+      const float2 ml = *(const float2*)(sl + 4 * NDB * 64 * 16 + lane * 8);
+      const float m_new = fmaxf(m_run, ml.x);
+      if (m_new != -INFINITY) {
+        const float fa = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        const float fb = __builtin_amdgcn_exp2f((ml.x - m_new) * c);
+        l_run0 = (l_run0 + l_run1) * fa + ml.y * fb;
+        l_run1 = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 x = *(const float4*)(sl + ((4 * db + g4) * 64 + lane) * 16);
+            oacc[db][4 * g4] = oacc[db][4 * g4] * fa + x.x * fb;
+            oacc[db][4 * g4 + 1] = oacc[db][4 * g4 + 1] * fa + x.y * fb;
+            oacc[db][4 * g4 + 2] = oacc[db][4 * g4 + 2] * fa + x.z * fb;
+            oacc[db][4 * g4 + 3] = oacc[db][4 * g4 + 3] * fa + x.w * fb;
+          }
+        m_run = m_new;
+      }
+    }
+  }
+  if (wave != 0) return;
+
+  // ---- wave 0: the workgroup's (m, l, O) of the 32 rows ---------------------------
+  const float l_half = l_run0 + l_run1;
+  const float l_tot = l_half + __uint_as_float(__shfl_xor((int)__float_as_uint(l_half), 32));
+  if (p.n_split == 1) {
+    if (!row_valid) return;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;  // a row that sees nothing is zero
+    __bf16* op = (__bf16*)p.o + (((size_t)b * p.Hq + a) * p.Sq + qi) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = (__bf16)(oacc[db][g4 * 4 + q] * inv);
+        *(bf16x4*)(op + db * 32 + g4 * 8 + hf * 4) = w;
+      }
+    return;
+  }
+  // partial of this split: rows [32][D] fp32 (unnormalised O), then m (log2
+  // units, -inf when the row saw nothing here) and l per row
+  float* ws = p.ws + (size_t)blockIdx.x * (32 * (D + 2));
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const float4 x = {oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2],
+                        oacc[db][4 * g4 + 3]};
+      *(float4*)(ws + r * D + db * 32 + g4 * 8 + hf * 4) = x;
+    }
+  if (hf == 0) {
+    ws[32 * D + r] = m_run == -INFINITY ? -INFINITY : m_run * c;
+    ws[32 * D + 32 + r] = l_tot;
+  }
+}
+
+// Merge the splits of each (b, kvh): one workgroup per pair, one thread per
+// (row, dim) element in turn:  M = max_c m_c,
+//   O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c   (zero if M = -inf).
+template <int D>
+__global__ __launch_bounds__(256) void attn_decode_combine(DParams p) {
+  const int pair = (int)blockIdx.x;
+  const int b = pair / p.Hkv, kvh = pair % p.Hkv;
+  const int nrows = p.G * p.Sq;
+  const float* base = p.ws + (size_t)pair * p.n_split * (32 * (D + 2));
+  for (int e = threadIdx.x; e < nrows * D; e += 256) {
+    const int r = e / D, d = e % D;
+    float M = -INFINITY;
+    for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, base[(size_t)s * (32 * (D + 2)) + 32 * D + r]);
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < p.n_split; ++s) {
+        const float* w = base + (size_t)s * (32 * (D + 2));
+        const float ms = w[32 * D + r];
+        if (ms == -INFINITY) continue;
+        const float f = __builtin_amdgcn_exp2f(ms - M);
+        num += f * w[r * D + d];
+        den += f * w[32 * D + 32 + r];
+      }
+    }
+    const float out = den > 0.f ? num / den : 0.f;
+    const int a = kvh * p.G + r / p.Sq, qi = r % p.Sq;
+    ((__bf16*)p.o)[(((size_t)b * p.Hq + a) * p.Sq + qi) * D + d] = (__bf16)out;
+  }
+}
+
+template <int D>
+hipError_t launch_decode_d(const DParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((long long)p.B * p.Hkv * p.n_split));
+  hipLaunchKernelGGL(attn_decode_bf16<D>, grid, dim3(DWAVES * 64), 0, stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.n_split == 1) return err;
+  hipLaunchKernelGGL(attn_decode_combine<D>, dim3((unsigned)(p.B * p.Hkv)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DParams& p, int D, hipStream_t stream) {
+  return D == 64 ? launch_decode_d<64>(p, stream) : launch_decode_d<128>(p, stream);
+}
+
+}  // namespace attn

@@ -20,6 +20,18 @@ Workloads (shapes follow the examples on the pages):
   tokens {0, 1000, 3000, 6000}, 12 heads, B=1 S=8192 D=64: the document example
   of "Transformer 演进与变体", section 稀疏注意力 (Longformer paragraph).
 
+Decode workloads (the Sq newest positions of each sequence against its
+key/value cache, "Transformer 架构及其变体", section 预填充创建缓存，解码复用缓存):
+
+* ``decode_gqa_bf16_b16_l8192``  -- one new position per sequence, 16
+  sequences with full 8192-position caches, 32 query heads over 8 key/value
+  heads, D=128 (the head shapes of the grouped-query workload above).
+* ``decode_gqa_bf16_b8_sq4_l16384`` -- four new positions per sequence (a
+  chunk or draft tokens, causal among themselves), 8 sequences with ragged
+  cache lengths drawn uniformly from [Smax/4, Smax], Smax=16384.
+* ``decode_mqa_bf16_b4_l65536`` -- multi-query (one key/value head for 32
+  query heads), one new position, 4 sequences with full 65536-position caches.
+
 Values are iid N(0, 1) from ``numpy.random.default_rng(seed)``, drawn as
 float32 in the order Q, K, V, each shaped [B][H][S][D].  bf16 workloads round
 those draws to nearest-even bf16; the rounded values are what every consumer
@@ -79,6 +91,50 @@ WORKLOADS = {
 HEADLINE = "causal_gqa_bf16_s8192"
 
 
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Smax: int
+    D: int
+    mask: str      # "causal" or "full"
+    lengths: str   # "full": every cache holds Smax positions; "ragged": seeded in [Smax/4, Smax]
+    seed: int = 0
+    dtype: str = "bf16"
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+    def cache_len(self) -> np.ndarray:
+        if self.lengths == "full":
+            return np.full(self.B, self.Smax, dtype=np.int32)
+        rng = np.random.default_rng(self.seed + 1000)
+        return rng.integers(self.Smax // 4, self.Smax + 1, size=self.B).astype(np.int32)
+
+    def describe(self) -> dict:
+        d = dataclasses.asdict(self)
+        d["cache_len"] = [int(x) for x in self.cache_len()]
+        return d
+
+
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in (
+        DecodeWorkload("decode_gqa_bf16_b16_l8192", 16, 32, 8, 1, 8192, 128, MASK_CAUSAL, "full",
+                       seed=6),
+        DecodeWorkload("decode_gqa_bf16_b8_sq4_l16384", 8, 32, 8, 4, 16384, 128, MASK_CAUSAL,
+                       "ragged", seed=7),
+        DecodeWorkload("decode_mqa_bf16_b4_l65536", 4, 32, 1, 1, 65536, 128, MASK_CAUSAL, "full",
+                       seed=8),
+    )
+}
+DECODE_HEADLINE = "decode_gqa_bf16_b16_l8192"
+
+
 def bf16_round_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); return uint16 bit patterns.
 
@@ -121,6 +177,22 @@ def make_inputs(B, Hq, Hkv, S, D, dtype, seed):
 
 def workload_inputs(w: Workload):
     return make_inputs(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype, w.seed)
+
+
+def make_decode_inputs(B, Hq, Hkv, Sq, Smax, D, seed):
+    """bf16 decode inputs: q [B][Hq][Sq][D] and caches [B][Hkv][Smax][D], drawn in
+    the order Q, K, V; same dict layout as make_inputs."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, shape in (("q", (B, Hq, Sq, D)), ("k", (B, Hkv, Smax, D)), ("v", (B, Hkv, Smax, D))):
+        bits = bf16_round_bits(draw(shape, rng))
+        out[name + "_bits"] = bits
+        out[name] = bf16_bits_to_float(bits)
+    return out
+
+
+def decode_workload_inputs(w: DecodeWorkload):
+    return make_decode_inputs(w.B, w.Hq, w.Hkv, w.Sq, w.Smax, w.D, w.seed)
 
 
 def to_torch(inputs: dict, dtype: str, device):
