@@ -17,6 +17,11 @@ kernel is launched on.  Prints one JSON line:
             source changed since the counters were taken
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload,
             timed on the host's cores
+
+A decode workload (--workload decode_...) times one attn_decode call (its
+split-merge kernel included) and reports achieved HBM bandwidth instead:
+value = algorithmic bytes (the valid cache entries, q and o, each once) /
+time per step, against the 8 TB/s HBM peak.
 """
 from __future__ import annotations
 
@@ -34,6 +39,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_FP32_TFLOPS = 157.3   # vector fp32
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 KERNEL_SOURCES = ("kernel_bf16.hip", "gfx950_ops.h", "attn_kernels.h", "attn_sched.h")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_causal_gqa_s8192_hbm_traffic.md")
 
@@ -100,6 +106,125 @@ def cpu_baseline(w, inputs, n_heads: int):
     }
 
 
+def decode_cpu_baseline(w, inputs, lens, n_seq: int = 1):
+    """Time the decode oracle on the first n_seq sequences (all heads and rows)."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((x.get("num_threads", 1) for x in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    n = min(n_seq, w.B)
+    sub = [int(x) for x in lens[:n]]
+    t0 = time.perf_counter()
+    oracle.decode_attention(inputs["q"][:n], inputs["k"][:n], inputs["v"][:n], w.mask,
+                            cache_len=sub, scale=w.scale)
+    dt = time.perf_counter() - t0
+    nbytes = oracle.decode_cache_bytes(n, w.Hkv, w.D, sub, 2)
+    return {
+        "value": nbytes / dt / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"sequences 0..{n - 1} of {w.B}, all {w.Hq} heads and {w.Sq} new positions "
+                  f"({nbytes} cache bytes in {dt:.2f} s, fp64 NumPy)",
+        "seconds": dt,
+    }
+
+
+def bench_decode(args, name):
+    import numpy as np
+    import torch
+
+    import oracle
+    import transformer_attention_attn_amd as attn
+    import workloads
+
+    w = workloads.DECODE_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    print(f"bench: decode workload {name} {w.describe()}", file=sys.stderr, flush=True)
+    inputs = workloads.decode_workload_inputs(w)
+    q, k, v = (torch.from_numpy(inputs[n + "_bits"].view(np.int16)).view(torch.bfloat16)
+               .to(dev).contiguous() for n in ("q", "k", "v"))
+    lens = w.cache_len()
+    cl = torch.from_numpy(lens).to(dev)
+    out = torch.empty_like(q)
+    ws_n = attn.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Smax, w.D, w.mask)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        attn.decode(q, k, v, cache_len=cl, mask=w.mask, scale=w.scale, out=out, workspace=ws,
+                    stream=stream)
+
+    t_warm = time.perf_counter()
+    prewarm_steps = 0
+    while time.perf_counter() - t_warm < args.prewarm:
+        for _ in range(5):
+            step()
+        prewarm_steps += 5
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    cache_bytes = oracle.decode_cache_bytes(w.B, w.Hkv, w.D, lens, 2)
+    qo_bytes = 2 * w.B * w.Hq * w.Sq * w.D * 2
+    alg = cache_bytes + qo_bytes
+    gbs = alg / (ms * 1e-3) / 1e9
+    flops = oracle.decode_effective_flops(w.Hq, w.Sq, w.D, lens, w.mask)
+    print(f"bench: {ms * 1e3:.1f} us/step, {gbs:.1f} GB/s algorithmic", file=sys.stderr,
+          flush=True)
+    result = {
+        "metric": "decode attention achieved HBM GB/s (algorithmic bytes) + % of 8 TB/s, 1 GPU",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq,
+                   "Smax": w.Smax, "D": w.D, "mask": w.mask, "lengths": w.lengths,
+                   "algorithmic_bytes": alg, "effective_flops": flops,
+                   "workspace_bytes": ws_n, "parallelism": "none"},
+        "pct_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+        },
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+        "prewarm_steps": prewarm_steps,
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_parity:
+        got = out.float().cpu().numpy()
+        ref = oracle.decode_attention(inputs["q"][:1], inputs["k"][:1], inputs["v"][:1], w.mask,
+                                      cache_len=[int(lens[0])], scale=w.scale)
+        result["parity"] = {"batch": 0, "max_abs_err": float(np.max(np.abs(got[:1] - ref)))}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = decode_cpu_baseline(w, inputs, lens)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,13 +246,17 @@ def main(argv=None):
               "the kernel shards by key/value head, see DESIGN.md", file=sys.stderr)
         return 2
 
+    import workloads
+
+    name = args.workload or workloads.HEADLINE
+    if name in workloads.DECODE_WORKLOADS:
+        return bench_decode(args, name)
+
     import numpy as np
     import torch
 
     import transformer_attention_attn_amd as attn
-    import workloads
 
-    name = args.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
     dev = torch.device("cuda:0")
     print(f"bench: workload {name} {w.describe()}", file=sys.stderr, flush=True)

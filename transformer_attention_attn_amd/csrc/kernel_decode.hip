@@ -17,17 +17,22 @@
 //     most 32), so every cached key and value row is read from HBM once for
 //     all query heads that share it ("第 8 章 AI 算法Transformer大模型",
 //     section 8.2.1: shared key/value heads need one read instead of h).
-//   * The split's keys are cut into 32-key tiles; wave w walks its own
-//     contiguous share of them through a private LDS region (one K tile and
-//     one V tile, loaded straight into LDS), so the walk needs no workgroup
-//     barrier: K(t+1) loads while the softmax of tile t runs, V(t+1) while
-//     P.V of tile t runs.  Operands: K with ds_read_b128, V^T with
+//   * The split's keys are cut into 32-key tiles; wave w walks tiles w,
+//     w + 8, ... (so the eight waves stream neighbouring tiles of one
+//     contiguous range at any time) through a private LDS region (one K
+//     tile and one V tile, loaded straight into LDS), so the walk needs no
+//     workgroup barrier: the next K tile loads while the softmax of the
+//     current one runs, the next V tile while its P.V runs.  Operands: K with ds_read_b128, V^T with
 //     ds_read_b64_tr_b16, both under the swizzles of the prefill kernel.
 //   * Online softmax per wave in log2 units with lazy rescaling, then the
 //     waves' partial (m, l, O) merge through LDS in a fixed pairing order.
 //   * One split: O / l is written as bf16.  Several splits: the partial
 //     (m, l, O) goes to the caller's workspace and the combine kernel merges
-//     the splits of each row with the same recurrence.
+//     the splits of each row with the same recurrence (one workgroup per
+//     row, four thread groups over the splits).
+//   * A plain streaming read of 1 GiB reaches about 6.0-6.3 TB/s on MI355X
+//     (LDS-direct or vector loads); that, not the 8 TB/s peak, is the
+//     practical ceiling of this kernel.
 #include "attn_kernels.h"
 #include "gfx950_ops.h"
 
@@ -107,11 +112,10 @@ __global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
     }
   }
 
-  // ---- this wave's tiles: a contiguous share of the split's key range ----------
+  // ---- the split's key range [k0, k1) in 32-key tiles -------------------------
   const int k0 = split * p.chunk;
   const int k1 = (k0 + p.chunk < L) ? k0 + p.chunk : L;
   const int ntile = k1 > k0 ? (k1 - k0 + DT - 1) / DT : 0;
-  const int t_lo = ntile * wave / DWAVES, t_hi = ntile * (wave + 1) / DWAVES;
 
   unsigned char* kreg = smem + wave * 2 * REG;
   unsigned char* vreg = kreg + REG;
@@ -152,12 +156,14 @@ __global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
   // positions past which some row of the wave may be masked
   const int lim_lo = p.causal ? L - p.Sq : L - 1;
 
-  if (t_lo < t_hi) {
-    gload(kp, t_lo, kreg, false);
-    gload(vp, t_lo, vreg, true);
+  // wave w takes tiles w, w + 8, ...: at any time the eight waves stream
+  // neighbouring tiles of one contiguous range
+  if (wave < ntile) {
+    gload(kp, wave, kreg, false);
+    gload(vp, wave, vreg, true);
   }
-  for (int t = t_lo; t < t_hi; ++t) {
-    const bool more = t + 1 < t_hi;
+  for (int t = wave; t < ntile; t += DWAVES) {
+    const bool more = t + DWAVES < ntile;
     __builtin_amdgcn_s_waitcnt(0x0f70 | NIG);  // K(t) landed; V(t) may be in flight
     f32x16 sc;
 #pragma unroll
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) sc = mfma32(*(const bf16x8*)(kreg + k_rd[dc]), qf[dc], sc);
     __builtin_amdgcn_s_waitcnt(0xc07f);  // K operand reads done: the region may be refilled
-    if (more) gload(kp, t + 1, kreg, false);
+    if (more) gload(kp, t + DWAVES, kreg, false);
     const int tk = k0 + t * DT;
     if (tk + DT - 1 > lim_lo) {
       // register q of the accumulator holds key tk + 8*(q/4) + 4*hf + q%4
@@ -223,7 +229,7 @@ __global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(fy[db], pb[1], oacc[db]);
     }
-    if (more) gload(vp, t + 1, vreg, true);
+    if (more) gload(vp, t + DWAVES, vreg, true);
   }
 
   // ---- merge the eight waves' partial (m, l, O): chunk w takes chunk w + half --
@@ -305,34 +311,53 @@ __global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
   }
 }
 
-// Merge the splits of each (b, kvh): one workgroup per pair, one thread per
-// (row, dim) element in turn:  M = max_c m_c,
-//   O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c   (zero if M = -inf).
+// Merge the splits of one query row: one workgroup per (b, kvh, row) of
+// CG x D threads; thread (g, d) sums dimension d over the splits s = g mod CG,
+//   M = max_c m_c,  O[d] = sum_c 2^(m_c - M) O_c[d] / sum_c 2^(m_c - M) l_c
+// (zero if M = -inf), and the CG partial sums meet in LDS in a fixed order.
+constexpr int CG = 4;
 template <int D>
-__global__ __launch_bounds__(256) void attn_decode_combine(DParams p) {
-  const int pair = (int)blockIdx.x;
-  const int b = pair / p.Hkv, kvh = pair % p.Hkv;
+__global__ __launch_bounds__(CG * D) void attn_decode_combine(DParams p) {
+  constexpr int STRIDE = 32 * (D + 2);
+  __shared__ float red[CG * D];
+  __shared__ float part[2][CG][D];
   const int nrows = p.G * p.Sq;
-  const float* base = p.ws + (size_t)pair * p.n_split * (32 * (D + 2));
-  for (int e = threadIdx.x; e < nrows * D; e += 256) {
-    const int r = e / D, d = e % D;
-    float M = -INFINITY;
-    for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, base[(size_t)s * (32 * (D + 2)) + 32 * D + r]);
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < p.n_split; ++s) {
-        const float* w = base + (size_t)s * (32 * (D + 2));
-        const float ms = w[32 * D + r];
-        if (ms == -INFINITY) continue;
-        const float f = __builtin_amdgcn_exp2f(ms - M);
-        num += f * w[r * D + d];
-        den += f * w[32 * D + 32 + r];
-      }
-    }
-    const float out = den > 0.f ? num / den : 0.f;
-    const int a = kvh * p.G + r / p.Sq, qi = r % p.Sq;
-    ((__bf16*)p.o)[(((size_t)b * p.Hq + a) * p.Sq + qi) * D + d] = (__bf16)out;
+  const int pair = (int)blockIdx.x / nrows, r = (int)blockIdx.x % nrows;
+  const int b = pair / p.Hkv, kvh = pair % p.Hkv;
+  const int tid = threadIdx.x, d = tid % D, g = tid / D;
+  const float* base = p.ws + (size_t)pair * p.n_split * STRIDE;
+  float mloc = -INFINITY;
+  for (int s = tid; s < p.n_split; s += CG * D) mloc = fmaxf(mloc, base[(size_t)s * STRIDE + 32 * D + r]);
+  red[tid] = mloc;
+  __syncthreads();
+  for (int h = CG * D / 2; h > 0; h >>= 1) {
+    if (tid < h) red[tid] = fmaxf(red[tid], red[tid + h]);
+    __syncthreads();
   }
+  const float M = red[0];
+  float num = 0.f, den = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll 4
+    for (int s = g; s < p.n_split; s += CG) {
+      const float* w = base + (size_t)s * STRIDE;
+      const float ms = w[32 * D + r];
+      const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+      num += f * w[r * D + d];
+      den += f * w[32 * D + 32 + r];
+    }
+  }
+  part[0][g][d] = num;
+  part[1][g][d] = den;
+  __syncthreads();
+  if (g != 0) return;
+#pragma unroll
+  for (int k = 1; k < CG; ++k) {
+    num += part[0][k][d];
+    den += part[1][k][d];
+  }
+  const float out = den > 0.f ? num / den : 0.f;
+  const int a = kvh * p.G + r / p.Sq, qi = r % p.Sq;
+  ((__bf16*)p.o)[(((size_t)b * p.Hq + a) * p.Sq + qi) * D + d] = (__bf16)out;
 }
 
 template <int D>
@@ -341,7 +366,8 @@ hipError_t launch_decode_d(const DParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(attn_decode_bf16<D>, grid, dim3(DWAVES * 64), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.n_split == 1) return err;
-  hipLaunchKernelGGL(attn_decode_combine<D>, dim3((unsigned)(p.B * p.Hkv)), dim3(256), 0, stream, p);
+  const long long rows = (long long)p.B * p.Hkv * p.G * p.Sq;
+  hipLaunchKernelGGL(attn_decode_combine<D>, dim3((unsigned)rows), dim3(CG * D), 0, stream, p);
   return hipGetLastError();
 }
 
