@@ -106,6 +106,23 @@ def cpu_baseline(w, inputs, n_heads: int):
     }
 
 
+def calibration_copy(mib: int, dev):
+    """One plain elementwise copy of `mib` MiB (fp32 in, fp32 out) whose HBM counters
+    scale the attention kernels' (a fill kernel runs first to create the source)."""
+    if mib <= 0:
+        return
+    import torch
+
+    n = mib << 18  # fp32 elements
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)  # reads and writes exactly n * 4 bytes
+    torch.cuda.synchronize()
+    print(f"bench: calibration copy of {n * 4} bytes done", file=sys.stderr, flush=True)
+    del src, dst
+
+
 def decode_cpu_baseline(w, inputs, lens, n_seq: int = 1):
     """Time the decode oracle on the first n_seq sequences (all heads and rows)."""
     import oracle
@@ -154,6 +171,7 @@ def bench_decode(args, name):
     ws_n = attn.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Smax, w.D, w.mask)
     ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    calibration_copy(args.calibrate_copy_mib, dev)
 
     def step():
         attn.decode(q, k, v, cache_len=cl, mask=w.mask, scale=w.scale, out=out, workspace=ws,
@@ -269,15 +287,7 @@ def main(argv=None):
 
     stream = torch.cuda.current_stream(dev)
 
-    if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib << 18  # fp32 elements
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)  # reads and writes exactly n * 4 bytes
-        torch.cuda.synchronize()
-        print(f"bench: calibration copy of {n * 4} bytes done", file=sys.stderr, flush=True)
-        del src, dst
+    calibration_copy(args.calibrate_copy_mib, dev)
 
     def step():
         attn.fwd(q, k, v, mask=w.mask, window=w.window, global_idx=g, scale=w.scale, out=out,
