@@ -19,6 +19,8 @@
 //     registers (converted to bf16, round to nearest even), A = V^T from a
 //     transposed LDS tile.  The accumulator lane again owns one query, so the
 //     rescale factor is a per-lane scalar.
+//   * D = 64 runs two workgroups per CU (the kernel fits in 128 registers
+//     and 64 KB of LDS), D = 128 one.
 //   * Two wave groups per workgroup (waves 0-3 and 4-7, one of each per
 //     SIMD) in ping-pong: per key tile there are two barrier-separated steps,
 //     and in each one group runs its matrix block (O += V P for one tile and
@@ -159,7 +161,10 @@ __device__ __forceinline__ void block_run(const unsigned* vbd, const unsigned* k
                                           const bf16x8* pb, const bf16x8* qf, f32x16* oacc,
                                           f32x16* sc, Dma& dma) {
   constexpr int L = BlockSeq<MODE, NDB, NDC, NKB>::L;
-  constexpr int PF = L < 8 ? L : 8;  // operands in flight: at most 7 * 2 reads outstanding
+  // operands in flight (at most 7 * 2 reads outstanding); four at D = 64 to
+  // stay within 128 registers
+  constexpr int PFMAX = HD == 64 ? 4 : 8;
+  constexpr int PF = L < PFMAX ? L : PFMAX;
   bf16x8 ring[PF];
   block_prime<MODE, ROWB, NDB, NDC, NKB, PF, 0>(ring, vbd, kbd);
   block_steps<MODE, ROWB, NDB, NDC, NKB, PF, 0, NDMA>(ring, vbd, kbd, pb, qf, oacc, sc, dma);
@@ -185,8 +190,12 @@ struct Cfg {
   static_assert(NSTAGE * BUF <= 160 * 1024, "LDS budget of one CU");
 };
 
+// Waves per SIMD: one workgroup per CU at D = 128 (two waves per SIMD, up to
+// 256 registers each); two at D = 64, whose kernel fits in 128 registers and
+// 64 KB of LDS, so a second workgroup fills the gaps of the first.
+constexpr int kWavesPerEu = HD == 64 ? 4 : 2;
 template <int D, int MASK>
-__global__ __launch_bounds__(kBf16Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kBf16Threads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu, kWavesPerEu)))
 void attn_fwd_bf16(KParams p) {
   using C = Cfg<D>;
   constexpr int NDC = C::NDC, NDB = C::NDB, ROWB = C::ROWB, REG = C::REG, BUF = C::BUF,
