@@ -26,3 +26,9 @@ from .decode import (  # noqa: F401
     decode_effective_flops,
     decode_visible_count,
 )
+from .cross import (  # noqa: F401
+    CROSS_MASK_KINDS,
+    cross_attention,
+    cross_visible_pairs,
+    cross_visible_range,
+)
