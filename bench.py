@@ -18,10 +18,17 @@ kernel is launched on.  Prints one JSON line:
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload,
             timed on the host's cores
 
+  parity    max abs error of the GPU output against the oracle's on that
+            same sample (the oracle runs nowhere else in this script)
+
 A decode workload (--workload decode_...) times one attn_decode call (its
 split-merge kernel included) and reports achieved HBM bandwidth instead:
 value = algorithmic bytes (the valid cache entries, q and o, each once) /
 time per step, against the 8 TB/s HBM peak.
+
+A workload with separate query and key lengths (--workload chunk_prefill_...
+or cross_...) times one attn_fwd_ex call on its layout and reports effective
+TFLOP/s as the default does.
 """
 from __future__ import annotations
 
@@ -68,18 +75,28 @@ def committed_traffic(workload: str):
     return float(m_b.group(1))
 
 
-def cpu_baseline(w, inputs, n_heads: int):
-    """Time the oracle on the first n_heads query heads of batch 0 (all rows)."""
-    import numpy as np
-
-    import oracle
-
+def host_threads() -> int:
+    """Threads the host BLAS pool runs the oracle's NumPy products on."""
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max((x.get("num_threads", 1) for x in threadpool_info()), default=1)
+        return int(max((x.get("num_threads", 1) for x in threadpool_info()), default=1))
     except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def max_abs_err(got, ref) -> float:
+    import numpy as np
+
+    return float(np.max(np.abs(np.asarray(got, dtype=np.float64) - ref)))
+
+
+def cpu_baseline(w, inputs, n_heads: int):
+    """Time the oracle on the first n_heads query heads of batch 0 (all rows).
+    Returns (summary, oracle output [1, n_heads, S, D])."""
+    import oracle
+
+    threads = host_threads()
     G = w.Hq // w.Hkv
     n_heads = min(n_heads, w.Hq)
     n_kv = (n_heads + G - 1) // G
@@ -92,18 +109,18 @@ def cpu_baseline(w, inputs, n_heads: int):
         q = inputs["q"][:1, :Hs]
         n_heads = Hs
     t0 = time.perf_counter()
-    oracle.attention(q, k, v, w.mask, w.window, w.global_idx, scale=w.scale)
+    ref = oracle.attention(q, k, v, w.mask, w.window, w.global_idx, scale=w.scale)
     dt = time.perf_counter() - t0
     flops = oracle.effective_flops(1, n_heads, w.S, w.D, w.mask, w.window, w.global_idx)
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": threads,
         "kind": "oracle",
         "sample": f"batch 0, query heads 0..{n_heads - 1} of {w.Hq}, all {w.S} rows "
                   f"({flops:.3e} effective FLOPs in {dt:.2f} s, fp64 NumPy)",
         "seconds": dt,
-    }
+    }, ref
 
 
 def calibration_copy(mib: int, dev):
@@ -124,38 +141,121 @@ def calibration_copy(mib: int, dev):
 
 
 def decode_cpu_baseline(w, inputs, lens, n_seq: int = 1):
-    """Time the decode oracle on the first n_seq sequences (all heads and rows)."""
+    """Time the decode oracle on the first n_seq sequences (all heads and rows).
+    Returns (summary, oracle output [n_seq, Hq, Sq, D])."""
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max((x.get("num_threads", 1) for x in threadpool_info()), default=1)
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
+    threads = host_threads()
     n = min(n_seq, w.B)
     sub = [int(x) for x in lens[:n]]
     t0 = time.perf_counter()
-    oracle.decode_attention(inputs["q"][:n], inputs["k"][:n], inputs["v"][:n], w.mask,
-                            cache_len=sub, scale=w.scale)
+    ref = oracle.decode_attention(inputs["q"][:n], inputs["k"][:n], inputs["v"][:n], w.mask,
+                                  cache_len=sub, scale=w.scale)
     dt = time.perf_counter() - t0
-    nbytes = oracle.decode_cache_bytes(n, w.Hkv, w.D, sub, 2)
+    nbytes = decode_counts(w, sub)[0]
     return {
         "value": nbytes / dt / 1e9,
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": threads,
         "kind": "oracle",
         "sample": f"sequences 0..{n - 1} of {w.B}, all {w.Hq} heads and {w.Sq} new positions "
                   f"({nbytes} cache bytes in {dt:.2f} s, fp64 NumPy)",
         "seconds": dt,
-    }
+    }, ref
+
+
+def decode_counts(w, lens):
+    """(valid cache bytes, effective FLOPs) of one decode call over the given
+    sequence lengths: 2 * Hkv * D * 2 bytes per cached position; 4 * D FLOPs
+    per visible (query row, position) pair and query head."""
+    import numpy as np
+
+    L = np.asarray([int(x) for x in lens], dtype=np.int64)
+    cache_bytes = int(2 * w.Hkv * w.D * 2 * L.sum())
+    if w.mask == "full":
+        pairs = int(w.Sq * L.sum())
+    else:  # new position i of Sq sees positions 0 .. L - Sq + i
+        i = np.arange(w.Sq, dtype=np.int64)
+        pairs = int(np.clip(L[:, None] - w.Sq + i[None, :] + 1, 0, L[:, None]).sum())
+    return cache_bytes, 4 * w.D * pairs * w.Hq
+
+
+def ex_visible_pairs(w) -> int:
+    """Visible (query, key) pairs of one query head of an attn_fwd_ex call:
+    query i sits at key position p = i + Skv - Sq."""
+    import numpy as np
+
+    if w.mask == "full":
+        return w.Sq * w.Skv
+    p = np.arange(w.Sq, dtype=np.int64) + (w.Skv - w.Sq)
+    hi = np.clip(p + 1, 0, w.Skv)
+    lo = np.zeros_like(hi) if w.mask == "causal" else np.clip(p - w.window + 1, 0, w.Skv)
+    return int(np.maximum(hi - lo, 0).sum())
+
+
+def ex_cpu_baseline(w, inputs, seconds: float = 10.0):
+    """Time the oracle head by head on batch 0 (all rows of each head) until
+    `seconds` have passed.  Returns (summary, heads done, their oracle output)."""
+    import numpy as np
+
+    import oracle
+
+    threads = host_threads()
+    G = w.Hq // w.Hkv
+    refs = []
+    t0 = time.perf_counter()
+    while len(refs) < w.Hq and time.perf_counter() - t0 < seconds:
+        a = len(refs)
+        h = a // G
+        refs.append(oracle.cross_attention(inputs["q"][:1, a:a + 1], inputs["k"][:1, h:h + 1],
+                                           inputs["v"][:1, h:h + 1], w.mask, w.window,
+                                           scale=w.scale))
+    dt = time.perf_counter() - t0
+    n = len(refs)
+    flops = 4 * w.D * ex_visible_pairs(w) * n
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"batch 0, query heads 0..{n - 1} of {w.Hq} (as many as about {seconds:.0f} s "
+                  f"allows), all {w.Sq} rows ({flops:.3e} effective FLOPs in {dt:.2f} s, "
+                  f"fp64 NumPy)",
+        "seconds": dt,
+    }, n, np.concatenate(refs, axis=1)
+
+
+def time_steps(step, stream, args):
+    """Untimed warm-up (about `args.prewarm` seconds of steps, as the GPU clocks
+    ramp up over the first ~100 ms of load, then `args.warmup` steps), then
+    `args.steps` steps between two HIP events recorded on the launch stream.
+    Returns (ms per step, prewarm steps)."""
+    import torch
+
+    t_warm = time.perf_counter()
+    prewarm_steps = 0
+    while time.perf_counter() - t_warm < args.prewarm:
+        for _ in range(5):
+            step()
+        prewarm_steps += 5
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / args.steps, prewarm_steps
 
 
 def bench_decode(args, name):
     import numpy as np
     import torch
 
-    import oracle
     import transformer_attention_attn_amd as attn
     import workloads
 
@@ -177,29 +277,11 @@ def bench_decode(args, name):
         attn.decode(q, k, v, cache_len=cl, mask=w.mask, scale=w.scale, out=out, workspace=ws,
                     stream=stream)
 
-    t_warm = time.perf_counter()
-    prewarm_steps = 0
-    while time.perf_counter() - t_warm < args.prewarm:
-        for _ in range(5):
-            step()
-        prewarm_steps += 5
-        torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    cache_bytes = oracle.decode_cache_bytes(w.B, w.Hkv, w.D, lens, 2)
+    ms, prewarm_steps = time_steps(step, stream, args)
+    cache_bytes, flops = decode_counts(w, lens)
     qo_bytes = 2 * w.B * w.Hq * w.Sq * w.D * 2
     alg = cache_bytes + qo_bytes
     gbs = alg / (ms * 1e-3) / 1e9
-    flops = oracle.decode_effective_flops(w.Hq, w.Sq, w.D, lens, w.mask)
     print(f"bench: {ms * 1e3:.1f} us/step, {gbs:.1f} GB/s algorithmic", file=sys.stderr,
           flush=True)
     result = {
@@ -232,13 +314,87 @@ def bench_decode(args, name):
         "prewarm_steps": prewarm_steps,
         "gpu": torch.cuda.get_device_name(dev),
     }
-    if not args.no_parity:
-        got = out.float().cpu().numpy()
-        ref = oracle.decode_attention(inputs["q"][:1], inputs["k"][:1], inputs["v"][:1], w.mask,
-                                      cache_len=[int(lens[0])], scale=w.scale)
-        result["parity"] = {"batch": 0, "max_abs_err": float(np.max(np.abs(got[:1] - ref)))}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = decode_cpu_baseline(w, inputs, lens)
+        result["cpu_baseline"], ref = decode_cpu_baseline(w, inputs, lens)
+        if not args.no_parity:
+            got = out[:ref.shape[0]].float().cpu().numpy()
+            result["parity"] = {"sample": "the cpu_baseline sample",
+                                "max_abs_err": max_abs_err(got, ref)}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_ex(args, name):
+    import numpy as np
+    import torch
+
+    import transformer_attention_attn_amd as attn
+    import workloads
+
+    w = workloads.EX_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    print(f"bench: workload {name} {w.describe()}", file=sys.stderr, flush=True)
+    inputs = workloads.ex_workload_inputs(w)
+
+    def place(bits):
+        t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+        if w.layout == "bshd":  # [B][S][H][D] in memory, viewed as [B][H][S][D]
+            return t.transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+        return t.to(dev).contiguous()
+
+    q, k, v = (place(inputs[n + "_bits"]) for n in ("q", "k", "v"))
+    if w.layout == "bshd":
+        out = torch.empty((w.B, w.Sq, w.Hq, w.D), dtype=torch.bfloat16,
+                          device=dev).transpose(1, 2)
+    else:
+        out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.bfloat16, device=dev)
+    flops = 4 * w.D * ex_visible_pairs(w) * w.B * w.Hq
+    stream = torch.cuda.current_stream(dev)
+    calibration_copy(args.calibrate_copy_mib, dev)
+
+    def step():
+        attn.fwd_ex(q, k, v, mask=w.mask, window=w.window, scale=w.scale, out=out,
+                    stream=stream)
+
+    ms, prewarm_steps = time_steps(step, stream, args)
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(f"bench: {ms * 1e3:.1f} us/step, {tflops:.1f} effective TFLOP/s", file=sys.stderr,
+          flush=True)
+    peak = PEAK_BF16_TFLOPS
+    result = {
+        "metric": "effective attention TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, 1 GPU",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq,
+                   "Skv": w.Skv, "D": w.D, "mask": w.mask, "window": w.window,
+                   "layout": w.layout, "effective_flops": flops, "parallelism": "none"},
+        "pct_peak": round(100.0 * tflops / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4),
+            "traffic": None,
+        },
+        "prewarm_steps": prewarm_steps,
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"], n, ref = ex_cpu_baseline(w, inputs, args.cpu_seconds)
+        if not args.no_parity:
+            got = out[:1, :n].float().cpu().numpy()
+            result["parity"] = {"sample": "the cpu_baseline sample",
+                                "max_abs_err": max_abs_err(got, ref)}
     print(json.dumps(result), flush=True)
     return 0
 
@@ -250,6 +406,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle time budget of the cpu_baseline sample of a workload with "
+                         "separate query and key lengths")
     ap.add_argument("--prewarm", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -269,8 +428,9 @@ def main(argv=None):
     name = args.workload or workloads.HEADLINE
     if name in workloads.DECODE_WORKLOADS:
         return bench_decode(args, name)
+    if name in workloads.EX_WORKLOADS:
+        return bench_ex(args, name)
 
-    import numpy as np
     import torch
 
     import transformer_attention_attn_amd as attn
@@ -293,26 +453,7 @@ def main(argv=None):
         attn.fwd(q, k, v, mask=w.mask, window=w.window, global_idx=g, scale=w.scale, out=out,
                  stream=stream)
 
-    # Untimed warm-up: first about one second of steps (the GPU clocks ramp up
-    # over the first ~100 ms of load), then the requested W warmup steps.
-    t_warm = time.perf_counter()
-    prewarm_steps = 0
-    while time.perf_counter() - t_warm < args.prewarm:
-        for _ in range(5):
-            step()
-        prewarm_steps += 5
-        torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms, prewarm_steps = time_steps(step, stream, args)
     tflops = flops / (ms * 1e-3) / 1e12
     print(f"bench: {ms * 1e3:.1f} us/step, {tflops:.1f} effective TFLOP/s", file=sys.stderr,
           flush=True)
@@ -349,18 +490,12 @@ def main(argv=None):
         "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
     }
 
-    if not args.no_parity:
-        import oracle
-
-        rows = sorted({0, 1, 127, 128, w.S // 2, w.S - 1})
-        ref = oracle.attention(inputs["q"][:1], inputs["k"][:1], inputs["v"][:1], w.mask,
-                               w.window, w.global_idx, scale=w.scale, rows=rows)
-        got = out[:1].float().cpu().numpy()[:, :, rows]
-        result["parity"] = {"rows": rows, "batch": 0,
-                            "max_abs_err": float(np.max(np.abs(got - ref)))}
-
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_heads)
+        result["cpu_baseline"], ref = cpu_baseline(w, inputs, args.cpu_heads)
+        if not args.no_parity:
+            got = out[:1, :ref.shape[1]].float().cpu().numpy()
+            result["parity"] = {"sample": "the cpu_baseline sample",
+                                "max_abs_err": max_abs_err(got, ref)}
 
     print(json.dumps(result), flush=True)
     return 0

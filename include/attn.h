@@ -97,6 +97,54 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o,
              int mask_kind, int window, const int* global_idx, int n_global,
              float scale, int dtype, void* stream);
 
+/*
+ * attn_fwd_ex -- the forward pass with separate query and key lengths and
+ * strided layouts (bf16).
+ *
+ * Queries q[b][a][i] (i < Sq) attend to keys and values k, v[b][h][j]
+ * (j < Skv), h = a / (Hq / Hkv).  Cross attention ("Trasformer 浅析", section
+ * 交叉注意力: queries from one sequence, keys and values from another) is
+ * mask_kind FULL; a chunk of queries against a longer prefix ("Transformer
+ * 架构及其变体", section 预填充创建缓存，解码复用缓存: a long prefill may run in
+ * chunks) is CAUSAL or CAUSAL_WINDOW with the queries aligned to the END of
+ * the keys: query i sits at key position p_i = i + Skv - Sq and sees
+ *   CAUSAL          keys j <= p_i
+ *   CAUSAL_WINDOW   keys p_i - window < j <= p_i
+ *   FULL            every key
+ * A query that sees no key (p_i < 0, possible when Skv < Sq) is written as
+ * zeros.  With Sq == Skv and dense strides this is attn_fwd.
+ *
+ * Layouts: element (b, h, s, d) of each tensor is at
+ *   ptr + b * stride[0] + h * stride[1] + s * stride[2] + d
+ * (in elements; d contiguous).  [B][H][S][D] dense has strides
+ * {H*S*D, S*D, D}; [B][S][H][D] (sequence-major) has {S*H*D, D, H*D}.
+ * Strides must be non-negative multiples of 8 elements (16-byte rows), row
+ * strides at most 2^23 elements; o's rows must not overlap each other or the
+ * inputs.  LOCAL_GLOBAL and fp32 return ATTN_ERR_UNSUPPORTED here.
+ */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int B, Hq, Hkv;
+  int Sq;                 /* query rows per (batch, head)                 */
+  int Skv;                /* key / value rows per (batch, head)           */
+  int D;                  /* 64 or 128                                    */
+  long long q_stride[3];  /* element strides of q's batch, head, row dims */
+  long long k_stride[3];
+  long long v_stride[3];
+  long long o_stride[3];
+  int mask_kind;          /* ATTN_MASK_FULL, _CAUSAL or _CAUSAL_WINDOW     */
+  int window;             /* CAUSAL_WINDOW: >= 1                          */
+  float scale;
+  int dtype;              /* ATTN_DTYPE_BF16                              */
+} attn_fwd_args;
+
+/* Enqueue attn_fwd_ex on `stream`; same return and error conventions as
+ * attn_fwd (no allocation, no synchronisation, errors before any launch). */
+int attn_fwd_ex(const attn_fwd_args* args, void* stream);
+
 /* Host-only description of the work attn_fwd would launch for these arguments
  * (the same validation as attn_fwd, no device access).  Counts are per call. */
 typedef struct {

@@ -54,8 +54,9 @@ def cross_visible_range(Sq, Skv, i, kind, window=0):
     raise ValueError(f"unknown mask kind {kind!r}")
 
 
-def cross_attention(q, k, v, kind, window=0, scale=None):
-    """Attention output, float64, shape [B, Hq, Sq, D]."""
+def cross_attention(q, k, v, kind, window=0, scale=None, rows=None):
+    """Attention output, float64, shape [B, Hq, Sq, D]; with `rows` (query row
+    indices) only those rows, shape [B, Hq, len(rows), D]."""
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
@@ -68,11 +69,12 @@ def cross_attention(q, k, v, kind, window=0, scale=None):
     G = Hq // Hkv
     if scale is None:
         scale = 1.0 / np.sqrt(D)
-    out = np.zeros((B, Hq, Sq, D), dtype=np.float64)
+    rows = list(range(Sq)) if rows is None else [int(i) for i in rows]
+    out = np.zeros((B, Hq, len(rows), D), dtype=np.float64)
     for b in range(B):
         for a in range(Hq):
             h = a // G
-            for i in range(Sq):
+            for r, i in enumerate(rows):
                 lo, hi = cross_visible_range(Sq, Skv, i, kind, window)
                 if hi <= lo:
                     continue
@@ -80,7 +82,7 @@ def cross_attention(q, k, v, kind, window=0, scale=None):
                 vv = v[b, h, lo:hi].astype(np.float64)
                 s = float(scale) * (kk @ q[b, a, i].astype(np.float64))
                 e = np.exp(s - s.max())
-                out[b, a, i] = (e / e.sum()) @ vv
+                out[b, a, r] = (e / e.sum()) @ vv
     return out
 
 

@@ -1,0 +1,54 @@
+"""Host logic of the benchmark (CPU only): its FLOP and byte counts agree with
+the oracle's independent counts, and it refuses more than one GPU."""
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+import oracle
+import workloads
+from oracle import cross as cr
+
+
+@pytest.mark.parametrize("name", list(workloads.DECODE_WORKLOADS))
+def test_decode_counts_match_oracle(name):
+    w = workloads.DECODE_WORKLOADS[name]
+    lens = w.cache_len()
+    nbytes, flops = bench.decode_counts(w, lens)
+    assert nbytes == oracle.decode_cache_bytes(w.B, w.Hkv, w.D, lens, 2)
+    assert flops == oracle.decode_effective_flops(w.Hq, w.Sq, w.D, lens, w.mask)
+
+
+@pytest.mark.parametrize("mask", ["causal", "full"])
+def test_decode_counts_short_caches(mask):
+    """Lengths of zero and below the number of new positions."""
+    w = workloads.DecodeWorkload("t", 5, 8, 2, 4, 64, 64, mask, "full")
+    lens = [0, 1, 3, 4, 64]
+    assert bench.decode_counts(w, lens)[1] == oracle.decode_effective_flops(
+        w.Hq, w.Sq, w.D, lens, mask)
+
+
+@pytest.mark.parametrize("Sq,Skv", [(1, 1), (5, 3), (3, 5), (64, 1000), (300, 100)])
+@pytest.mark.parametrize("mask,window", [("full", 0), ("causal", 0), ("causal_window", 1),
+                                         ("causal_window", 37)])
+def test_ex_pairs_match_oracle(Sq, Skv, mask, window):
+    w = workloads.ExWorkload("t", 1, 4, 2, Sq, Skv, 64, mask, "bhsd", window=window)
+    assert bench.ex_visible_pairs(w) == cr.cross_visible_pairs(Sq, Skv, mask, window)
+
+
+@pytest.mark.parametrize("name", list(workloads.EX_WORKLOADS))
+def test_ex_workload_pairs(name):
+    w = workloads.EX_WORKLOADS[name]
+    assert bench.ex_visible_pairs(w) == cr.cross_visible_pairs(w.Sq, w.Skv, w.mask, w.window)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_max_abs_err():
+    assert bench.max_abs_err(np.array([1.0, 2.0]), np.array([1.5, 2.0])) == 0.5

@@ -1,0 +1,191 @@
+"""attn_fwd_ex (Sq != Skv, strided layouts) against the fp64 oracle.
+
+GPU cases compare every output element with oracle.cross_attention (queries
+aligned to the end of the keys) at the bf16 tolerance, over head-major,
+sequence-major and padded-row layouts for inputs and output; with Sq == Skv
+and dense layouts the result must equal attn_fwd's bit for bit.  Host-only
+cases check the validation.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.test_parity import TOL
+
+attn = pytest.importorskip("transformer_attention_attn_amd")
+
+
+def place(bits, layout, device):
+    """A [B, H, S, D] bf16 view of the bit array in the given memory layout."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    B, H, S, D = t.shape
+    if layout == "bhsd":
+        return t.to(device).contiguous()
+    if layout == "bshd":
+        return t.transpose(1, 2).contiguous().to(device).transpose(1, 2)
+    if layout == "padded":
+        buf = torch.zeros((B, H, S, D + 24), dtype=torch.bfloat16)
+        buf[..., :D] = t
+        return buf.to(device)[..., :D]
+    raise ValueError(layout)
+
+
+def empty_out(B, H, S, D, layout, device):
+    import torch
+
+    if layout == "bhsd":
+        return torch.empty((B, H, S, D), dtype=torch.bfloat16, device=device)
+    if layout == "bshd":
+        return torch.empty((B, S, H, D), dtype=torch.bfloat16, device=device).transpose(1, 2)
+    return torch.empty((B, H, S, D + 8), dtype=torch.bfloat16, device=device)[..., :D]
+
+
+def run_ex(device, B, Hq, Hkv, Sq, Skv, D, mask, window=0, layout="bhsd", out_layout="bhsd",
+           seed=0, scale=None):
+    import torch
+
+    print(f"fwd_ex case B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} {mask} w={window} "
+          f"{layout}->{out_layout} seed={seed}", flush=True)
+    rng = np.random.default_rng(seed)
+    bits = {}
+    vals = {}
+    for name, shape in (("q", (B, Hq, Sq, D)), ("k", (B, Hkv, Skv, D)), ("v", (B, Hkv, Skv, D))):
+        bits[name] = workloads.bf16_round_bits(workloads.draw(shape, rng))
+        vals[name] = workloads.bf16_bits_to_float(bits[name])
+    q, k, v = (place(bits[n], layout, device) for n in ("q", "k", "v"))
+    o = empty_out(B, Hq, Sq, D, out_layout, device)
+    attn.fwd_ex(q, k, v, mask=mask, window=window, scale=scale, out=o)
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy()
+    ref = oracle.cross_attention(vals["q"], vals["k"], vals["v"], mask, window, scale=scale)
+    assert np.all(np.isfinite(got))
+    return float(np.max(np.abs(got.astype(np.float64) - ref)))
+
+
+SWEEP = []
+_rng = np.random.default_rng(91)
+for D in (64, 128):
+    for (Sq, Skv) in ((100, 300), (300, 100), (257, 257), (1, 500), (64, 1000), (513, 2049),
+                      (129, 128)):
+        for mask in ("full", "causal", "causal_window"):
+            Hq, Hkv = [(8, 2), (4, 4), (8, 1)][int(_rng.integers(3))]
+            window = int(_rng.choice([1, 63, 200])) if mask == "causal_window" else 0
+            layout = ["bhsd", "bshd", "padded"][int(_rng.integers(3))]
+            out_layout = ["bhsd", "bshd", "padded"][int(_rng.integers(3))]
+            SWEEP.append((1 + int(_rng.integers(2)), Hq, Hkv, Sq, Skv, D, mask, window, layout,
+                          out_layout))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"D{c[5]}-Sq{c[3]}-Skv{c[4]}-{c[6]}-"
+                                                      f"{c[8]}-{c[9]}")
+def test_fwd_ex_sweep(device, case):
+    B, Hq, Hkv, Sq, Skv, D, mask, window, layout, out_layout = case
+    err = run_ex(device, B, Hq, Hkv, Sq, Skv, D, mask, window, layout, out_layout,
+                 seed=Sq * 3 + Skv + D)
+    assert err <= TOL["bf16"], err
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("D", [64, 128])
+def test_fwd_ex_square_dense_equals_fwd(device, D):
+    """Sq == Skv with dense layouts computes exactly what attn_fwd computes."""
+    import torch
+
+    inp = workloads.make_inputs(2, 8, 2, 700, D, "bf16", seed=21)
+    q, k, v = workloads.to_torch(inp, "bf16", device)
+    for mask, w in (("causal", 0), ("causal_window", 100), ("full", 0)):
+        a = attn.fwd(q, k, v, mask=mask, window=w)
+        b = attn.fwd_ex(q, k, v, mask=mask, window=w)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), mask
+
+
+@pytest.mark.gpu
+def test_fwd_ex_chunked_prefill_matches_full_prefill(device):
+    """Prefilling the last 512 positions as one chunk against the 1536-key
+    prefix gives the last 512 rows of the full causal prefill (same key order
+    and tiles, so the rows agree to the bf16 tolerance)."""
+    import torch
+
+    inp = workloads.make_inputs(1, 8, 2, 1536, 128, "bf16", seed=22)
+    q, k, v = workloads.to_torch(inp, "bf16", device)
+    full = attn.fwd(q, k, v, mask="causal")
+    chunk = attn.fwd_ex(q[:, :, 1024:], k, v, mask="causal")
+    torch.cuda.synchronize()
+    err = float((full[:, :, 1024:].float() - chunk.float()).abs().max())
+    assert err <= TOL["bf16"], err
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", list(workloads.EX_WORKLOADS))
+def test_fwd_ex_workload_full_size(device, name):
+    """The workloads with separate query and key lengths at full size, in the
+    layout and launch configuration the benchmark times; sampled (b, head)
+    pairs, sampled rows compared element-wise."""
+    import torch
+
+    w = workloads.EX_WORKLOADS[name]
+    print(f"fwd_ex workload {name}", flush=True)
+    inp = workloads.ex_workload_inputs(w)
+    q, k, v = (place(inp[n + "_bits"], w.layout, device) for n in ("q", "k", "v"))
+    o = empty_out(w.B, w.Hq, w.Sq, w.D, w.layout, device)
+    attn.fwd_ex(q, k, v, mask=w.mask, window=w.window, scale=w.scale, out=o)
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy()
+    rng = np.random.default_rng(w.seed + 5)
+    rows = sorted({0, 1, 127, 128, w.Sq // 2, w.Sq - 1}
+                  | {int(x) for x in rng.integers(w.Sq, size=10)})
+    G = w.Hq // w.Hkv
+    for b, a in {(0, 0), (w.B - 1, w.Hq - 1), (int(rng.integers(w.B)), int(rng.integers(w.Hq)))}:
+        h = a // G
+        ref = oracle.cross_attention(inp["q"][b:b + 1, a:a + 1], inp["k"][b:b + 1, h:h + 1],
+                                     inp["v"][b:b + 1, h:h + 1], w.mask, w.window, scale=w.scale,
+                                     rows=rows)
+        err = float(np.max(np.abs(got[b, a, rows].astype(np.float64) - ref[0, 0])))
+        print(f"{name} b={b} a={a}: max abs err {err:.3e}", flush=True)
+        assert err <= TOL["bf16"], (b, a, err)
+
+
+# ----------------------------------------------------------------------------
+# host-only validation (fake aligned addresses, never dereferenced)
+# ----------------------------------------------------------------------------
+
+def ex_status(**kw):
+    a = attn.FwdArgs()
+    base = 0x1000000
+    a.q, a.k, a.v, a.o = base, base * 3, base * 5, base * 7
+    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = 1, 8, 2, 100, 300, 128
+    dense = lambda H, S: [H * S * 128, S * 128, 128]  # noqa: E731
+    a.q_stride[:] = dense(8, 100)
+    a.k_stride[:] = dense(2, 300)
+    a.v_stride[:] = dense(2, 300)
+    a.o_stride[:] = dense(8, 100)
+    a.mask_kind, a.window, a.scale, a.dtype = 1, 0, 0.1, attn.DTYPE_BF16
+    for key, val in kw.items():
+        if key.endswith("_stride"):
+            getattr(a, key)[:] = val
+        else:
+            setattr(a, key, val)
+    return attn.status_string(attn.fwd_ex_raw(a, 0))
+
+
+def test_fwd_ex_rejects_bad_arguments():
+    assert ex_status(q=0) == "ATTN_ERR_NULL"
+    assert ex_status(Sq=0) == "ATTN_ERR_SHAPE"
+    assert ex_status(Skv=0) == "ATTN_ERR_SHAPE"
+    assert ex_status(Hq=6, Hkv=4) == "ATTN_ERR_HEADS"
+    assert ex_status(D=96) == "ATTN_ERR_UNSUPPORTED"
+    assert ex_status(dtype=attn.DTYPE_FP32) == "ATTN_ERR_UNSUPPORTED"
+    assert ex_status(mask_kind=3) == "ATTN_ERR_UNSUPPORTED"
+    assert ex_status(mask_kind=2, window=0) == "ATTN_ERR_WINDOW"
+    assert ex_status(scale=float("inf")) == "ATTN_ERR_SCALE"
+    assert ex_status(q=0x1000008) == "ATTN_ERR_ALIGN"
+    assert ex_status(k_stride=[2 * 300 * 128, 300 * 128, 132]) == "ATTN_ERR_ALIGN"
+    assert ex_status(k_stride=[2 * 300 * 128, 300 * 128, -128]) == "ATTN_ERR_ALIGN"
+    assert ex_status(v_stride=[0, 0, (1 << 23) + 8]) == "ATTN_ERR_SHAPE"
+    assert ex_status(o=0x1000000) == "ATTN_ERR_ALIAS"                  # o over q
+    assert ex_status(o_stride=[8 * 100 * 128, 100 * 128, 64]) == "ATTN_ERR_ALIAS"  # rows overlap

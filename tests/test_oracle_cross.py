@@ -91,6 +91,15 @@ def pin_brute_force_loop():
             assert abs(got[0, 0, i, d] - want) < 1e-13
 
 
+def pin_row_selection():
+    """Selected rows are the same rows of the whole output."""
+    rng = np.random.default_rng(16)
+    q, k, v = randn(rng, 1, 2, 9, 4), randn(rng, 1, 1, 13, 4), randn(rng, 1, 1, 13, 4)
+    whole = cr.cross_attention(q, k, v, "causal_window", 3)
+    part = cr.cross_attention(q, k, v, "causal_window", 3, rows=[8, 0, 4])
+    assert np.array_equal(part, whole[:, :, [8, 0, 4]])
+
+
 def pin_pair_counts():
     assert cr.cross_visible_pairs(4, 10, "full") == 40
     assert cr.cross_visible_pairs(4, 10, "causal") == 7 + 8 + 9 + 10
@@ -99,7 +108,7 @@ def pin_pair_counts():
 
 
 PINS = [pin_square_case, pin_chunk_is_last_rows, pin_matches_decode_oracle,
-        pin_fewer_keys_than_queries, pin_brute_force_loop, pin_pair_counts]
+        pin_fewer_keys_than_queries, pin_brute_force_loop, pin_row_selection, pin_pair_counts]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)

@@ -18,11 +18,14 @@ from ._binding import (  # noqa: F401
     MAX_GLOBAL,
     STATUS,
     AttnError,
+    FwdArgs,
     decode,
     decode_raw,
     decode_workspace_bytes,
     decode_workspace_status,
     fwd,
+    fwd_ex,
+    fwd_ex_raw,
     fwd_raw,
     load,
     plan,

@@ -31,7 +31,7 @@ STATUS = {
     11: "ATTN_ERR_WORKSPACE",
 }
 
-EXPORTS = ("attn_fwd", "attn_plan", "attn_decode", "attn_decode_workspace",
+EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_plan", "attn_decode", "attn_decode_workspace",
            "attn_status_string", "attn_version")
 
 
@@ -39,6 +39,20 @@ class AttnError(RuntimeError):
     def __init__(self, status: int):
         self.status = status
         super().__init__(f"attn call failed: {STATUS.get(status, status)}")
+
+
+class FwdArgs(ctypes.Structure):
+    """attn_fwd_args of include/attn.h."""
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+        ("B", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int),
+        ("Sq", ctypes.c_int), ("Skv", ctypes.c_int), ("D", ctypes.c_int),
+        ("q_stride", ctypes.c_longlong * 3), ("k_stride", ctypes.c_longlong * 3),
+        ("v_stride", ctypes.c_longlong * 3), ("o_stride", ctypes.c_longlong * 3),
+        ("mask_kind", ctypes.c_int), ("window", ctypes.c_int),
+        ("scale", ctypes.c_float), ("dtype", ctypes.c_int),
+    ]
 
 
 class PlanInfo(ctypes.Structure):
@@ -77,6 +91,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int), i, i,
                               ctypes.POINTER(PlanInfo)]
     lib.attn_plan.restype = i
+    lib.attn_fwd_ex.argtypes = [ctypes.POINTER(FwdArgs), p]
+    lib.attn_fwd_ex.restype = i
     lib.attn_decode.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, f, i, p, ctypes.c_size_t, p]
     lib.attn_decode.restype = i
     lib.attn_decode_workspace.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
@@ -147,6 +163,54 @@ def fwd(q, k, v, mask="causal", window: int = 0, global_idx=None, scale: Optiona
     with torch.cuda.device(q.device):
         st = fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, S, D,
                      mask, window, global_idx, scale, dt, handle)
+    if st != 0:
+        raise AttnError(st)
+    return out
+
+
+def fwd_ex_raw(args: FwdArgs, stream: int) -> int:
+    """Direct call of attn_fwd_ex; returns the status."""
+    return load().attn_fwd_ex(ctypes.byref(args), stream)
+
+
+def fwd_ex(q, k, v, mask="causal", window: int = 0, scale: Optional[float] = None, out=None,
+           stream=None):
+    """Forward pass with Sq != Skv and strided layouts (bf16).
+
+    q: [B, Hq, Sq, D], k, v: [B, Hkv, Skv, D] as torch views of any strides
+    whose last dimension is contiguous (e.g. a [B, S, H, D] tensor passed as
+    x.transpose(1, 2)).  Queries are aligned to the end of the keys (query i at
+    key position i + Skv - Sq).  Returns o shaped like q (a dense tensor unless
+    `out` is given, which may be strided too).
+    """
+    import torch
+
+    if q.dtype != torch.bfloat16:
+        raise TypeError("fwd_ex takes bf16 tensors")
+    for t in (q, k, v):
+        if t.dtype != q.dtype or not t.is_cuda or t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError("q, k, v must be 4-D bf16 GPU tensors with a contiguous last dim")
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Skv, D) or tuple(v.shape) != (B, Hkv, Skv, D):
+        raise ValueError("k, v must be [B, Hkv, Skv, D] matching q")
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (B, Hq, Sq, D) or out.dtype != q.dtype or out.stride(3) != 1:
+        raise ValueError("out must be shaped like q with a contiguous last dim")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    a = FwdArgs()
+    a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
+    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = B, Hq, Hkv, Sq, Skv, D
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
+        getattr(a, name)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    a.mask_kind, a.window, a.scale, a.dtype = _mask_id(mask), int(window), float(scale), DTYPE_BF16
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = fwd_ex_raw(a, handle)
     if st != 0:
         raise AttnError(st)
     return out

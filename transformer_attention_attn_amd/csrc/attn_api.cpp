@@ -134,7 +134,10 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int Sq, int Smax, int D, int mask
   const int chunk = attn::cdiv(attn::cdiv(Smax, (int)ns), 32) * 32;
   d.chunk = chunk;
   d.n_split = attn::cdiv(Smax, chunk);
-  if (pairs * d.n_split > 0x7fffffffLL) { d.status = ATTN_ERR_SHAPE; return d; }
+  if (pairs * std::max<long long>(d.n_split, attn::kDecodeRows) > 0x7fffffffLL) {
+    d.status = ATTN_ERR_SHAPE;  // grid sizes of the two kernels
+    return d;
+  }
   d.ws_bytes = d.n_split > 1
                    ? (size_t)pairs * d.n_split * attn::kDecodeRows * (size_t)(D + 2) * sizeof(float)
                    : 0;
@@ -170,6 +173,73 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq
 
   hipStream_t st = (hipStream_t)stream;
   hipError_t err = dtype == ATTN_DTYPE_BF16 ? (D == 64 ? attn::launch_bf16_d64(p, st) : attn::launch_bf16_d128(p, st)) : attn::launch_fp32(p, D, st);
+  return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
+  if (!a) return ATTN_ERR_NULL;
+  if (!a->q || !a->k || !a->v || !a->o) return ATTN_ERR_NULL;
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1 || a->Sq < 1 || a->Skv < 1 || (long long)a->Sq > kMaxS ||
+      (long long)a->Skv > kMaxS)
+    return ATTN_ERR_SHAPE;
+  if (a->dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (a->D != 64 && a->D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (a->mask_kind != ATTN_MASK_FULL && a->mask_kind != ATTN_MASK_CAUSAL &&
+      a->mask_kind != ATTN_MASK_CAUSAL_WINDOW)
+    return ATTN_ERR_UNSUPPORTED;
+  if (a->Hq % a->Hkv != 0) return ATTN_ERR_HEADS;
+  if (a->mask_kind == ATTN_MASK_CAUSAL_WINDOW && a->window < 1) return ATTN_ERR_WINDOW;
+  if (!std::isfinite(a->scale)) return ATTN_ERR_SCALE;
+  for (const void* ptr : {a->q, a->k, a->v, (const void*)a->o})
+    if ((uintptr_t)ptr % 16 != 0) return ATTN_ERR_ALIGN;
+  const long long* strides[4] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride};
+  for (const long long* st : strides) {
+    for (int d = 0; d < 3; ++d)
+      if (st[d] < 0 || st[d] % 8 != 0) return ATTN_ERR_ALIGN;
+    if (st[2] > (1LL << 23)) return ATTN_ERR_SHAPE;
+  }
+  // byte extents [ptr, ptr + span) of the four tensors
+  auto span = [&](const long long* st, int H, int S) {
+    return (size_t)(((long double)(a->B - 1) * st[0] + (long double)(H - 1) * st[1] +
+                     (long double)(S - 1) * st[2] + a->D) * 2);
+  };
+  const long double big = (long double)(a->B) * std::max(a->Hq, a->Hkv) *
+                          std::max(a->Sq, a->Skv) * a->D;
+  if (big > 4.0e18L) return ATTN_ERR_SHAPE;
+  const size_t nq = span(a->q_stride, a->Hq, a->Sq), nk = span(a->k_stride, a->Hkv, a->Skv);
+  const size_t nv = span(a->v_stride, a->Hkv, a->Skv), no = span(a->o_stride, a->Hq, a->Sq);
+  if (overlaps(a->o, no, a->q, nq) || overlaps(a->o, no, a->k, nk) || overlaps(a->o, no, a->v, nv))
+    return ATTN_ERR_ALIAS;
+  // o's own rows must be distinct: rows of one head D apart at least, heads and
+  // batches not folded onto each other
+  const long long* os = a->o_stride;
+  if (os[2] < a->D || (a->Hq > 1 && os[1] < (long long)a->Sq * os[2] && os[2] < (long long)a->Hq * os[1]) ||
+      (a->B > 1 && os[0] == 0) || (a->Hq > 1 && os[1] == 0))
+    return ATTN_ERR_ALIAS;
+
+  Sched s = attn::make_sched(a->B, a->Hq, a->Hkv, a->Sq, a->mask_kind, a->window, 0,
+                             attn::kBf16Rows, attn::bf16_keys_per_tile(a->D), 1,
+                             attn::kBf16GlobalRows);
+  if (s.n_items > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  s.Sk = a->Skv;
+  s.off = a->Skv - a->Sq;
+
+  KParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o;
+  p.s = s;
+  p.scale = a->scale;
+  p.c = std::fabs(a->scale) * 1.4426950408889634f;
+  p.qmode = a->scale > 0.f ? 0 : (a->scale < 0.f ? 1 : 2);
+  if (p.qmode == 2) p.c = 1.f;
+  p.general = 1;
+  for (int d = 0; d < 3; ++d) {
+    p.qs[d] = a->q_stride[d];
+    p.ks[d] = a->k_stride[d];
+    p.vs[d] = a->v_stride[d];
+    p.os[d] = a->o_stride[d];
+  }
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t err = a->D == 64 ? attn::launch_bf16_d64(p, st) : attn::launch_bf16_d128(p, st);
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -23,6 +23,10 @@ struct KParams {
   float c;       // bf16 kernel: |scale| * log2(e) (> 0), see qmode
   int qmode;     // bf16 kernel: 0 use q, 1 use -q (negative scale), 2 use 0 (zero scale)
   int gpos[kMaxGlobal];  // sorted distinct global-token positions (n_global of them)
+  // attn_fwd_ex only (general = 1): element strides of the batch, head and row
+  // dimensions of q, k, v and o (the head dimension is contiguous)
+  int general;
+  long long qs[3], ks[3], vs[3], os[3];
 };
 
 // Workgroup shapes used by the two kernels.

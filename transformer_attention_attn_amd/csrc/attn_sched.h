@@ -42,6 +42,9 @@ struct Sched {
   int n_gblocks;           // global-row blocks per pair: ceil(n_global / GR) (local+global only)
   long long n_global_items;  // P * n_gblocks, numbered first
   long long n_items;         // total workgroups
+  // attn_fwd_ex: Sk keys (S is then the number of query rows); query row i
+  // sits at key position i + off.  attn_fwd: Sk = S, off = 0.
+  int Sk, off;
 };
 
 struct Item {
@@ -79,6 +82,8 @@ ATTN_HD Sched make_sched(int B, int Hq, int Hkv, int S, int mask, int window, in
   s.n_gblocks = s.n_global > 0 ? cdiv(s.n_global, s.GR) : 0;
   s.n_global_items = (long long)s.P * s.n_gblocks;
   s.n_items = s.n_global_items + (long long)s.P * s.T;
+  s.Sk = S;
+  s.off = 0;
   return s;
 }
 

@@ -194,7 +194,11 @@ struct Cfg {
 // 256 registers each); two at D = 64, whose kernel fits in 128 registers and
 // 64 KB of LDS, so a second workgroup fills the gaps of the first.
 constexpr int kWavesPerEu = HD == 64 ? 4 : 2;
-template <int D, int MASK>
+// GEN = 1: the general form behind attn_fwd_ex -- Sq query rows (s.S) against
+// Sk keys (s.Sk), query i at key position i + s.off, element strides for the
+// batch, head and row dimensions of each tensor; the local+global mask is not
+// offered there.  GEN = 0 is attn_fwd's dense square layout.
+template <int D, int MASK, int GEN = 0>
 __global__ __launch_bounds__(kBf16Threads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu, kWavesPerEu)))
 void attn_fwd_bf16(KParams p) {
   using C = Cfg<D>;
@@ -241,11 +245,25 @@ void attn_fwd_bf16(KParams p) {
     q_row = row_valid ? gpos_s[slot] : 0;
   }
   const bool wave_active = wqa <= wqb;
+  // key count and the key positions of the wave's first and last rows
+  const int SK = GEN ? s.Sk : s.S;
+  const int wpa = GEN ? wqa + s.off : wqa, wpb = GEN ? wqb + s.off : wqb;
 
   const size_t S = (size_t)s.S;
-  const __bf16* qp = (const __bf16*)p.q + (size_t)(it.b * s.Hq + a) * S * D;
-  const __bf16* kp = (const __bf16*)p.k + (size_t)(it.b * s.Hkv + it.kvh) * S * D;
-  const __bf16* vp = (const __bf16*)p.v + (size_t)(it.b * s.Hkv + it.kvh) * S * D;
+  const __bf16* qp;
+  const __bf16* kp;
+  const __bf16* vp;
+  if constexpr (GEN) {
+    qp = (const __bf16*)p.q + it.b * p.qs[0] + a * p.qs[1];
+    kp = (const __bf16*)p.k + it.b * p.ks[0] + it.kvh * p.ks[1];
+    vp = (const __bf16*)p.v + it.b * p.vs[0] + it.kvh * p.vs[1];
+  } else {
+    qp = (const __bf16*)p.q + (size_t)(it.b * s.Hq + a) * S * D;
+    kp = (const __bf16*)p.k + (size_t)(it.b * s.Hkv + it.kvh) * S * D;
+    vp = (const __bf16*)p.v + (size_t)(it.b * s.Hkv + it.kvh) * S * D;
+  }
+  // bytes between consecutive K and V rows
+  const int KRB = GEN ? (int)p.ks[2] * 2 : ROWB, VRB = GEN ? (int)p.vs[2] * 2 : ROWB;
 
   // ---- Q^T operand: lane holds query q_row, dims 16*dc + 8*hf + [0, 8) -----
   bf16x8 qf[NDC];
@@ -256,7 +274,7 @@ void attn_fwd_bf16(KParams p) {
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (!zero) x = *(const u32x4*)(qp + (size_t)q_row * D + dc * 16 + hf * 8);
+      if (!zero) x = *(const u32x4*)(qp + (size_t)q_row * (GEN ? p.qs[2] : D) + dc * 16 + hf * 8);
       x ^= flip;
       qf[dc] = __builtin_bit_cast(bf16x8, x);
     }
@@ -264,10 +282,17 @@ void attn_fwd_bf16(KParams p) {
 
   // ---- key tiles to visit ------------------------------------------------
   int klo, khi;
-  key_range(s, it.is_global, r0, r1, &klo, &khi);
+  if constexpr (GEN) {
+    // keys seen by rows r0..r1 at key positions r0 + off .. r1 + off
+    const int pa = r0 + s.off, pb = r1 + s.off;
+    klo = MASK == MASK_CAUSAL_WINDOW ? imax(0, pa - s.window + 1) : 0;
+    khi = MASK == MASK_FULL ? SK - 1 : imin(pb, SK - 1);
+  } else {
+    key_range(s, it.is_global, r0, r1, &klo, &khi);
+  }
   const int kt_lo = klo / BN, kt_hi = khi / BN;
   const int has_strip = (MASK == MASK_LOCAL_GLOBAL && !it.is_global && s.n_global > 0) ? 1 : 0;
-  const int n_it = (kt_hi - kt_lo + 1) + has_strip;
+  const int n_it = (GEN && khi < klo) ? 0 : (kt_hi - kt_lo + 1) + has_strip;
   auto tile_kt = [&](int iter) { return kt_lo + iter - has_strip; };
   auto is_strip = [&](int iter) { return MASK == MASK_LOCAL_GLOBAL && has_strip && iter == 0; };
 
@@ -297,22 +322,24 @@ void attn_fwd_bf16(KParams p) {
   auto dma = [&](bool isk, int iter, int st, int n) {
     int row;
     if (is_strip(iter)) row = gpos_s[imin(srow + n * RSTEP, s.n_global - 1)];
-    else row = imin(tile_kt(iter) * BN + srow + n * RSTEP, s.S - 1);
-    const char* src = (const char*)(isk ? kp : vp) + (size_t)row * ROWB + (isk ? k_col : v_col);
+    else row = imin(tile_kt(iter) * BN + srow + n * RSTEP, SK - 1);
+    const char* src = (const char*)(isk ? kp : vp) + (size_t)row * (isk ? KRB : VRB) + (isk ? k_col : v_col);
     dma16_global(src, smem + (isk ? 0 : NSTAGE * REG) + st * REG + (n * 4 + gw) * 1024);
   };
   // in-loop form (iter >= 1, never the strip): a buffer descriptor over the
   // tile's valid rows and a 32-bit lane offset clamped to the last valid row,
   // so no lane is out of range.
-  const int k_off = srow * ROWB + k_col, v_off = srow * ROWB + v_col;
+  const int k_off = srow * KRB + k_col, v_off = srow * VRB + v_col;
   auto dma_band = [&](bool isk, int iter, int st, int n) {
     // tiles past the last one of the sequence load the last tile instead
-    const int row0 = imin(tile_kt(iter), (s.S - 1) / BN) * BN;
-    const int nrows = imin(s.S - row0, BN);
+    const int row0 = imin(tile_kt(iter), (SK - 1) / BN) * BN;
+    const int nrows = imin(SK - row0, BN);
+    const int RB = isk ? KRB : VRB;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((isk ? kp : vp) + (size_t)row0 * D), (short)0, nrows * ROWB, 0x00020000);
-    const int off = imin((isk ? k_off : v_off) + n * RSTEP * ROWB,
-                         (nrows - 1) * ROWB + (isk ? k_col : v_col));
+        (void*)((const char*)(isk ? kp : vp) + (size_t)row0 * RB), (short)0,
+        (nrows - 1) * RB + ROWB, 0x00020000);
+    const int off = imin((isk ? k_off : v_off) + n * RSTEP * RB,
+                         (nrows - 1) * RB + (isk ? k_col : v_col));
     dma16_buffer(r, smem + (isk ? 0 : NSTAGE * REG) + st * REG + (n * 4 + gw) * 1024, off, 0);
   };
 
@@ -322,12 +349,12 @@ void attn_fwd_bf16(KParams p) {
     if (!wave_active || is_strip(iter)) return true;
     const int kt = tile_kt(iter);
     if (it.is_global) return kt * BN + BN > s.S;
-    return classify_tile(MASK, s.window, s.S, wqa, wqb, kt * BN, BN) != TILE_FULL;
+    return classify_tile(MASK, s.window, SK, wpa, wpb, kt * BN, BN) != TILE_FULL;
   };
   auto tile_empty = [&](int j) -> bool {
     if (!wave_active) return true;
     if (is_strip(j)) return false;
-    return classify_tile(MASK, s.window, s.S, wqa, wqb, tile_kt(j) * BN, BN) == TILE_EMPTY;
+    return classify_tile(MASK, s.window, SK, wpa, wpb, tile_kt(j) * BN, BN) == TILE_EMPTY;
   };
 
   // ---- operand reads -------------------------------------------------------
@@ -376,10 +403,10 @@ void attn_fwd_bf16(KParams p) {
     // lo <= 32*kbk + 8*(r/4) + r%4 <= hi
     long long lo, hi;
     if (it.is_global) { lo = 0; hi = (long long)s.S - 1; }
-    else row_interval(MASK, s.window, s.S, q_row, &lo, &hi);
+    else row_interval(MASK, s.window, SK, GEN ? q_row + s.off : q_row, &lo, &hi);
     if (!wave_active) hi = lo - 1;
     const long long base = (long long)tile_kt(iter) * BN + 4 * hf;
-    const long long tail = (long long)s.S - 1;
+    const long long tail = (long long)SK - 1;
     const long long hi_a = hi < tail ? hi : tail;
     const int lo_r = (int)(lo - base < -1 ? -1 : (lo - base > BN ? BN : lo - base));
     const int hi_r = (int)(hi_a - base < -1 ? -1 : (hi_a - base > BN ? BN : hi_a - base));
@@ -772,8 +799,10 @@ void attn_fwd_bf16(KParams p) {
       for (int g = 0; g < s.n_global; ++g) store = store && (gpos_s[g] != q_row);
     }
     if (store) {
-      const float inv = 1.f / l_tot;
-      __bf16* op = (__bf16*)p.o + ((size_t)(it.b * s.Hq + a) * S + q_row) * D;
+      // (GEN: a query before the first key sees nothing and is written as zero)
+      const float inv = GEN ? (l_tot > 0.f ? 1.f / l_tot : 0.f) : 1.f / l_tot;
+      __bf16* op = GEN ? (__bf16*)p.o + it.b * p.os[0] + a * p.os[1] + q_row * p.os[2]
+                       : (__bf16*)p.o + ((size_t)(it.b * s.Hq + a) * S + q_row) * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -790,6 +819,14 @@ void attn_fwd_bf16(KParams p) {
 template <int D>
 hipError_t launch_d(const KParams& p, hipStream_t stream) {
   dim3 grid((unsigned)p.s.n_items), block(kBf16Threads);
+  if (p.general) {
+    switch (p.s.mask) {
+      case MASK_FULL: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_FULL, 1>), grid, block, 0, stream, p); break;
+      case MASK_CAUSAL: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL, 1>), grid, block, 0, stream, p); break;
+      default: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL_WINDOW, 1>), grid, block, 0, stream, p); break;
+    }
+    return hipGetLastError();
+  }
   switch (p.s.mask) {
     case MASK_FULL: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_FULL>), grid, block, 0, stream, p); break;
     case MASK_CAUSAL: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL>), grid, block, 0, stream, p); break;

@@ -32,6 +32,19 @@ key/value cache, "Transformer 架构及其变体", section 预填充创建缓存
 * ``decode_mqa_bf16_b4_l65536`` -- multi-query (one key/value head for 32
   query heads), one new position, 4 sequences with full 65536-position caches.
 
+Workloads with separate query and key lengths (queries aligned to the end of
+the keys):
+
+* ``chunk_prefill_gqa_bf16_q2048_kv8192`` -- the last 2048 positions of an
+  8192-token prompt prefilled as one chunk against the whole prefix, causal,
+  the grouped-query head shapes above ("Transformer 架构及其变体", section
+  预填充创建缓存，解码复用缓存).
+* ``cross_mha_bf16_q1024_kv4096_bshd`` -- cross attention, 1024 decoder
+  queries against 4096 encoder keys, every key visible, 16 heads of D=64, B=4,
+  all tensors sequence-major ([B][S][H][D]) ("Trasformer 浅析", section
+  交叉注意力; heads of 64 as in the original model's head width,
+  "Transformer 演进与变体", section MHA：多头注意力).
+
 Values are iid N(0, 1) from ``numpy.random.default_rng(seed)``, drawn as
 float32 in the order Q, K, V, each shaped [B][H][S][D].  bf16 workloads round
 those draws to nearest-even bf16; the rounded values are what every consumer
@@ -135,6 +148,44 @@ DECODE_WORKLOADS = {
 DECODE_HEADLINE = "decode_gqa_bf16_b16_l8192"
 
 
+@dataclasses.dataclass(frozen=True)
+class ExWorkload:
+    """A call of the entry point with separate query and key lengths and
+    strided layouts: Sq queries aligned to the end of Skv keys."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Skv: int
+    D: int
+    mask: str      # "full", "causal" or "causal_window"
+    layout: str    # "bhsd" (head-major) or "bshd" (sequence-major) for q, k, v and o
+    window: int = 0
+    seed: int = 0
+    dtype: str = "bf16"
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+    def describe(self) -> dict:
+        return dataclasses.asdict(self)
+
+
+EX_WORKLOADS = {
+    w.name: w
+    for w in (
+        # the last 2048 positions of an 8192-token prompt prefilled as one chunk
+        ExWorkload("chunk_prefill_gqa_bf16_q2048_kv8192", 1, 32, 8, 2048, 8192, 128, MASK_CAUSAL,
+                   "bhsd", seed=9),
+        # decoder queries against a longer encoder sequence, sequence-major tensors
+        ExWorkload("cross_mha_bf16_q1024_kv4096_bshd", 4, 16, 16, 1024, 4096, 64, MASK_FULL,
+                   "bshd", seed=10),
+    )
+}
+
+
 def bf16_round_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); return uint16 bit patterns.
 
@@ -193,6 +244,12 @@ def make_decode_inputs(B, Hq, Hkv, Sq, Smax, D, seed):
 
 def decode_workload_inputs(w: DecodeWorkload):
     return make_decode_inputs(w.B, w.Hq, w.Hkv, w.Sq, w.Smax, w.D, w.seed)
+
+
+def ex_workload_inputs(w: ExWorkload):
+    """q [B][Hq][Sq][D], k and v [B][Hkv][Skv][D]: the decode generator with the
+    cache capacity set to Skv (same draw order)."""
+    return make_decode_inputs(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.seed)
 
 
 def to_torch(inputs: dict, dtype: str, device):
