@@ -25,10 +25,30 @@ at key position p_i = i + Skv - Sq.  Visibility:
 A query that sees no key (p_i < 0, which needs Skv < Sq) has output zero.
 With Sq == Skv this is the square attention of reference.py.
 
+Optional parts of the same call:
+
+* ALiBi -- "Transformer 演进与变体", section 线性偏置注意力; "Trasformer 浅析",
+  section 加性偏置：ALiBi; "Transformer 架构及其变体", section
+  位置信息通过查询和键进入注意力: query head a adds minus its slope m_a times
+  the distance between query and key to each scaled score, before the
+  softmax.  Readings: the slope is indexed by the QUERY head a (the third
+  page's notation), the distance is |p_i - j| (the first page's absolute form;
+  it equals p_i - j on every key a causal or causal-window query sees), and
+  the bias is added after the 1/sqrt(d) scaling, not scaled itself.  Slopes
+  are inputs (the pages fix none; any real value is accepted).
+* Padded (ragged) batches -- "Trasformer 浅析", section 填充掩码与因果掩码:
+  short sequences of a batch are padded and the padded positions are masked
+  out.  Reading: sequence b holds q_len[b] valid query rows and kv_len[b]
+  valid keys, both at the START of its rows (right padding); the call on
+  sequence b is the call above with Sq = q_len[b] and Skv = kv_len[b], so
+  query i sits at p_i = i + kv_len[b] - q_len[b]; padded keys are never
+  visible and padded query rows are written as zero.  What the padded
+  positions hold never reaches a valid output.
+
 Layout: q [B][Hq][Sq][D], k and v [B][Hkv][Skv][D] (logical layout; strided
 device layouts are a matter of the tests).  float64 on the exact inputs.
 
-Pinned by tests/test_oracle_cross.py.
+Pinned by tests/test_oracle_cross.py (ALiBi and padded batches included).
 """
 from __future__ import annotations
 
@@ -54,9 +74,32 @@ def cross_visible_range(Sq, Skv, i, kind, window=0):
     raise ValueError(f"unknown mask kind {kind!r}")
 
 
-def cross_attention(q, k, v, kind, window=0, scale=None, rows=None):
+def alibi_penalty(slope, p, j):
+    """What ALiBi subtracts from the scaled score of query position p and key
+    positions j: the head's slope times their distance."""
+    return slope * np.abs(p - np.asarray(j, dtype=np.float64))
+
+
+def head_slope(slopes, a, G):
+    """ALiBi slope of query head a (G query heads per key/value head)."""
+    return slopes[a]
+
+
+def sequence_lengths(Sq, Skv, q_len, kv_len, b):
+    """Valid query rows and keys of sequence b."""
+    sq_b = Sq if q_len is None else int(q_len[b])
+    skv_b = Skv if kv_len is None else int(kv_len[b])
+    if not (0 <= sq_b <= Sq and 0 <= skv_b <= Skv):
+        raise ValueError("lengths must lie in [0, Sq] and [0, Skv]")
+    return sq_b, skv_b
+
+
+def cross_attention(q, k, v, kind, window=0, scale=None, rows=None, alibi_slopes=None,
+                    q_len=None, kv_len=None):
     """Attention output, float64, shape [B, Hq, Sq, D]; with `rows` (query row
-    indices) only those rows, shape [B, Hq, len(rows), D]."""
+    indices) only those rows, shape [B, Hq, len(rows), D].  `alibi_slopes`: Hq
+    slopes (None: no bias); `q_len`, `kv_len`: B valid lengths each (None: all
+    Sq / Skv rows valid)."""
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
@@ -70,17 +113,26 @@ def cross_attention(q, k, v, kind, window=0, scale=None, rows=None):
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     rows = list(range(Sq)) if rows is None else [int(i) for i in rows]
+    slopes = None if alibi_slopes is None else np.asarray(alibi_slopes, dtype=np.float64)
+    if slopes is not None and slopes.shape != (Hq,):
+        raise ValueError("alibi_slopes needs one slope per query head")
     out = np.zeros((B, Hq, len(rows), D), dtype=np.float64)
     for b in range(B):
+        sq_b, skv_b = sequence_lengths(Sq, Skv, q_len, kv_len, b)
         for a in range(Hq):
             h = a // G
             for r, i in enumerate(rows):
-                lo, hi = cross_visible_range(Sq, Skv, i, kind, window)
+                if i >= sq_b:
+                    continue  # padded query row
+                lo, hi = cross_visible_range(sq_b, skv_b, i, kind, window)
                 if hi <= lo:
                     continue
                 kk = k[b, h, lo:hi].astype(np.float64)
                 vv = v[b, h, lo:hi].astype(np.float64)
                 s = float(scale) * (kk @ q[b, a, i].astype(np.float64))
+                if slopes is not None:
+                    s = s - alibi_penalty(head_slope(slopes, a, G), i + skv_b - sq_b,
+                                          np.arange(lo, hi))
                 e = np.exp(s - s.max())
                 out[b, a, r] = (e / e.sum()) @ vv
     return out

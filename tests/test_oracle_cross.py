@@ -3,6 +3,9 @@
 oracle/cross.py is tied to independent routines: the square oracle
 (reference.py) when Sq == Skv or on the last rows of a longer sequence, the
 decode oracle (decode.py) for causal and full masks, and a pure-Python loop.
+ALiBi is tied to a closed form (geometric weights when all scores are zero)
+and to the square oracle with one extra dimension; padded batches to the
+decode oracle's cache lengths and the square oracle per sequence.
 ``test_planted_cross_mistakes_are_caught`` plants plausible mistakes and checks
 that a pin fails for each.
 """
@@ -100,6 +103,134 @@ def pin_row_selection():
     assert np.array_equal(part, whole[:, :, [8, 0, 4]])
 
 
+def geometric_weights(r, lo, hi, p, two_sided):
+    """Closed form of softmax(-m * dist) over keys lo..hi-1 with r = exp(-m):
+    weight of key j is r^|p - j| over the geometric sum of the same powers."""
+    def gsum(n):  # 1 + r + ... + r^(n-1)
+        return (1.0 - r ** n) / (1.0 - r) if n > 0 else 0.0
+    if two_sided:  # keys on both sides of p: distances 0..p-lo and 1..hi-1-p
+        total = gsum(p - lo + 1) + (gsum(hi - p) - 1.0)
+    else:          # keys lo..p only: distances 0..p-lo
+        total = gsum(p - lo + 1)
+    return {j: r ** abs(p - j) / total for j in range(lo, hi)}
+
+
+def pin_alibi_closed_form():
+    """With q = 0 every scaled score is 0, so the weights are the ALiBi bias
+    alone: geometric in the distance with ratio exp(-m_a) per query head.
+    v = identity reads the weights out.  Distinct slopes in each group of
+    heads, a scale that is not 1, and Sq < Skv (aligned queries)."""
+    B, Hq, Hkv, Sq, Skv = 1, 4, 2, 3, 7
+    slopes = np.array([0.3, 0.7, 1.1, 0.05])
+    q = np.zeros((B, Hq, Sq, Skv))
+    k = np.random.default_rng(17).standard_normal((B, Hkv, Skv, Skv))
+    v = np.broadcast_to(np.eye(Skv), (B, Hkv, Skv, Skv)).copy()
+    for kind, w in (("causal", 0), ("causal_window", 2), ("full", 0)):
+        got = cr.cross_attention(q, k, v, kind, w, scale=0.25, alibi_slopes=slopes)
+        for a in range(Hq):
+            r = math.exp(-slopes[a])
+            for i in range(Sq):
+                p = i + Skv - Sq
+                lo = max(0, p - w + 1) if kind == "causal_window" else 0
+                hi = Skv if kind == "full" else p + 1
+                want = geometric_weights(r, lo, hi, p, kind == "full")
+                for j in range(Skv):
+                    assert abs(got[0, a, i, j] - want.get(j, 0.0)) < 1e-14, (kind, a, i, j)
+
+
+def pin_alibi_as_extra_dimension():
+    """On causal and causal-window masks ALiBi equals plain attention with one
+    more dimension: query coordinate m_a / scale, key coordinate j (the bias
+    -m_a (p - j) is m_a j up to a per-row constant, which softmax ignores).
+    Checked against the square oracle on the whole sequence (chunk rows)."""
+    rng = np.random.default_rng(18)
+    B, Hq, Hkv, Sq, Skv, D, scale = 2, 4, 2, 6, 17, 8, 0.3
+    slopes = np.array([0.02, 0.5, 0.9, 0.13])
+    q = randn(rng, B, Hq, Sq, D)
+    k, v = randn(rng, B, Hkv, Skv, D), randn(rng, B, Hkv, Skv, D)
+    qf = np.concatenate([randn(rng, B, Hq, Skv - Sq, D), q], axis=2)
+    rows = list(range(Skv - Sq, Skv))
+    kx = np.concatenate([k, np.broadcast_to(np.arange(Skv, dtype=np.float64)[None, None, :, None],
+                                            (B, Hkv, Skv, 1))], axis=3)
+    for kind, w in (("causal", 0), ("causal_window", 5)):
+        got = cr.cross_attention(q, k, v, kind, w, scale=scale, alibi_slopes=slopes)
+        for a in range(Hq):
+            qx = np.concatenate([qf[:, a:a + 1], np.full((B, 1, Skv, 1), slopes[a] / scale)],
+                                axis=3)
+            h = a // (Hq // Hkv)
+            vx = np.concatenate([v[:, h:h + 1], np.zeros((B, 1, Skv, 1))], axis=3)
+            ref = oracle.attention(qx, kx[:, h:h + 1], vx, kind, w, scale=scale, rows=rows)
+            assert np.max(np.abs(got[:, a:a + 1] - ref[..., :D])) < 1e-12, (kind, a)
+
+
+def pin_ragged_matches_decode_oracle():
+    """Valid key counts per sequence (right padding): the decode oracle with
+    the same cache lengths; padded keys and values hold NaN."""
+    rng = np.random.default_rng(19)
+    B, Hq, Hkv, Sq, Skv, D = 4, 6, 2, 3, 21, 8
+    q = randn(rng, B, Hq, Sq, D)
+    k, v = randn(rng, B, Hkv, Skv, D), randn(rng, B, Hkv, Skv, D)
+    kv_len = [21, 0, 2, 13]
+    for b, L in enumerate(kv_len):
+        k[b, :, L:] = np.nan
+        v[b, :, L:] = np.nan
+    for kind in ("causal", "full"):
+        got = cr.cross_attention(q, k, v, kind, scale=0.4, kv_len=kv_len)
+        ref = dec.decode_attention(q, k, v, kind, cache_len=kv_len, scale=0.4)
+        assert np.all(np.isfinite(got))
+        assert np.max(np.abs(got - ref)) < 1e-13, kind
+
+
+def pin_ragged_queries_are_last_rows():
+    """Sequence b with q_len valid query rows and kv_len valid keys: its rows
+    are the last q_len rows of the square attention over its kv_len
+    positions; padded query rows are zero; padded content never leaks."""
+    rng = np.random.default_rng(20)
+    B, Hq, Hkv, Sq, Skv, D = 3, 4, 4, 5, 11, 8
+    q = randn(rng, B, Hq, Sq, D)
+    k, v = randn(rng, B, Hkv, Skv, D), randn(rng, B, Hkv, Skv, D)
+    q_len, kv_len = [5, 2, 0], [11, 6, 4]
+    for b in range(B):
+        q[b, :, q_len[b]:] = np.nan
+        k[b, :, kv_len[b]:] = np.nan
+        v[b, :, kv_len[b]:] = np.nan
+    for kind, w in (("causal", 0), ("causal_window", 3), ("full", 0)):
+        got = cr.cross_attention(q, k, v, kind, w, q_len=q_len, kv_len=kv_len)
+        assert np.all(np.isfinite(got))
+        for b in range(B):
+            nq, nk = q_len[b], kv_len[b]
+            assert np.all(got[b, :, nq:] == 0.0)
+            if nq == 0:
+                continue
+            qf = np.concatenate([randn(rng, 1, Hq, nk - nq, D), q[b:b + 1, :, :nq]], axis=2)
+            ref = oracle.attention(qf, k[b:b + 1, :, :nk], v[b:b + 1, :, :nk], kind, w,
+                                   rows=list(range(nk - nq, nk)))
+            assert np.max(np.abs(got[b:b + 1, :, :nq] - ref)) < 1e-12, (kind, b)
+
+
+def pin_alibi_ragged_brute_force():
+    """Pure-Python loops: ALiBi (full mask, two-sided distance) on a padded
+    batch with q_len < Sq and kv_len < Skv."""
+    rng = np.random.default_rng(21)
+    B, Hq, Sq, Skv, D, scale = 2, 2, 4, 6, 3, 0.7
+    slopes = [0.4, 1.3]
+    q, k, v = randn(rng, B, Hq, Sq, D), randn(rng, B, 1, Skv, D), randn(rng, B, 1, Skv, D)
+    q_len, kv_len = [3, 4], [5, 6]
+    got = cr.cross_attention(q, k, v, "full", scale=scale, alibi_slopes=slopes, q_len=q_len,
+                             kv_len=kv_len)
+    for b in range(B):
+        for a in range(Hq):
+            for i in range(q_len[b]):
+                p = i + kv_len[b] - q_len[b]
+                sc = [scale * math.fsum(q[b, a, i, d] * k[b, 0, j, d] for d in range(D))
+                      - slopes[a] * abs(p - j) for j in range(kv_len[b])]
+                m = max(sc)
+                e = [math.exp(x - m) for x in sc]
+                for d in range(D):
+                    want = math.fsum(e[j] * v[b, 0, j, d] for j in range(kv_len[b])) / math.fsum(e)
+                    assert abs(got[b, a, i, d] - want) < 1e-13
+
+
 def pin_pair_counts():
     assert cr.cross_visible_pairs(4, 10, "full") == 40
     assert cr.cross_visible_pairs(4, 10, "causal") == 7 + 8 + 9 + 10
@@ -108,7 +239,9 @@ def pin_pair_counts():
 
 
 PINS = [pin_square_case, pin_chunk_is_last_rows, pin_matches_decode_oracle,
-        pin_fewer_keys_than_queries, pin_brute_force_loop, pin_row_selection, pin_pair_counts]
+        pin_fewer_keys_than_queries, pin_brute_force_loop, pin_row_selection,
+        pin_alibi_closed_form, pin_alibi_as_extra_dimension, pin_ragged_matches_decode_oracle,
+        pin_ragged_queries_are_last_rows, pin_alibi_ragged_brute_force, pin_pair_counts]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -133,16 +266,36 @@ def _mut_full_is_causal(Sq, Skv, i, kind, window=0):
     return _ORIG(Sq, Skv, i, "causal" if kind == "full" else kind, window)
 
 
+_ORIG_PEN, _ORIG_SLOPE, _ORIG_LENS = cr.alibi_penalty, cr.head_slope, cr.sequence_lengths
+
 MUTATIONS = {
-    "top_left_alignment": _mut_top_left,
-    "window_one_too_wide": _mut_window_wide,
-    "full_mask_is_causal": _mut_full_is_causal,
+    "top_left_alignment": ("cross_visible_range", _mut_top_left),
+    "window_one_too_wide": ("cross_visible_range", _mut_window_wide),
+    "full_mask_is_causal": ("cross_visible_range", _mut_full_is_causal),
+    # ALiBi rewards distance instead of penalising it
+    "alibi_sign": ("alibi_penalty", lambda m, p, j: -_ORIG_PEN(m, p, j)),
+    # signed distance: wrong for keys after the query (full mask)
+    "alibi_signed_distance": ("alibi_penalty",
+                              lambda m, p, j: m * (p - np.asarray(j, dtype=np.float64))),
+    # the bias scaled like the scores
+    "alibi_scaled": ("alibi_penalty", lambda m, p, j: 0.5 * _ORIG_PEN(m, p, j)),
+    # slope of the key/value head instead of the query head
+    "alibi_slope_by_kv_head": ("head_slope", lambda sl, a, G: sl[(a // G) * G]),
+    # padding ignored: every key and query row valid
+    "padding_ignored": ("sequence_lengths", lambda Sq, Skv, ql, kl, b: (Sq, Skv)),
+    # valid query rows counted, but aligned as if all Sq rows were valid
+    "ragged_queries_misaligned": ("sequence_lengths",
+                                  lambda Sq, Skv, ql, kl, b: (
+                                      _ORIG_LENS(Sq, Skv, ql, kl, b)[0],
+                                      _ORIG_LENS(Sq, Skv, ql, kl, b)[1]
+                                      + Sq - _ORIG_LENS(Sq, Skv, ql, kl, b)[0])),
 }
 
 
 @pytest.mark.parametrize("mutation", sorted(MUTATIONS))
 def test_planted_cross_mistakes_are_caught(monkeypatch, mutation):
-    monkeypatch.setattr(cr, "cross_visible_range", MUTATIONS[mutation])
+    attr, fn = MUTATIONS[mutation]
+    monkeypatch.setattr(cr, attr, fn)
     failed = []
     for pin in PINS:
         try:
