@@ -180,17 +180,29 @@ def decode_counts(w, lens):
     return cache_bytes, 4 * w.D * pairs * w.Hq
 
 
-def ex_visible_pairs(w) -> int:
-    """Visible (query, key) pairs of one query head of an attn_fwd_ex call:
-    query i sits at key position p = i + Skv - Sq."""
+def ex_visible_pairs(Sq, Skv, mask, window=0) -> int:
+    """Visible (query, key) pairs of one query head of one sequence of an
+    attn_fwd_ex call: query i sits at key position p = i + Skv - Sq."""
     import numpy as np
 
-    if w.mask == "full":
-        return w.Sq * w.Skv
-    p = np.arange(w.Sq, dtype=np.int64) + (w.Skv - w.Sq)
-    hi = np.clip(p + 1, 0, w.Skv)
-    lo = np.zeros_like(hi) if w.mask == "causal" else np.clip(p - w.window + 1, 0, w.Skv)
+    if mask == "full":
+        return Sq * Skv
+    p = np.arange(Sq, dtype=np.int64) + (Skv - Sq)
+    hi = np.clip(p + 1, 0, Skv)
+    lo = np.zeros_like(hi) if mask == "causal" else np.clip(p - window + 1, 0, Skv)
     return int(np.maximum(hi - lo, 0).sum())
+
+
+def ex_effective_flops(w, batches=None) -> float:
+    """4 * D FLOPs per visible pair and query head, summed over the sequences
+    (each with its own valid lengths when the workload is padded)."""
+    q_len, kv_len = w.lengths_qkv()
+    total = 0
+    for b in (range(w.B) if batches is None else batches):
+        sq = w.Sq if q_len is None else int(q_len[b])
+        skv = w.Skv if kv_len is None else int(kv_len[b])
+        total += ex_visible_pairs(sq, skv, w.mask, w.window)
+    return 4.0 * w.D * total * w.Hq
 
 
 def ex_cpu_baseline(w, inputs, seconds: float = 10.0):
@@ -202,17 +214,22 @@ def ex_cpu_baseline(w, inputs, seconds: float = 10.0):
 
     threads = host_threads()
     G = w.Hq // w.Hkv
+    slopes = w.alibi_slopes()
+    q_len, kv_len = w.lengths_qkv()
     refs = []
     t0 = time.perf_counter()
     while len(refs) < w.Hq and time.perf_counter() - t0 < seconds:
         a = len(refs)
         h = a // G
-        refs.append(oracle.cross_attention(inputs["q"][:1, a:a + 1], inputs["k"][:1, h:h + 1],
-                                           inputs["v"][:1, h:h + 1], w.mask, w.window,
-                                           scale=w.scale))
+        refs.append(oracle.cross_attention(
+            inputs["q"][:1, a:a + 1], inputs["k"][:1, h:h + 1], inputs["v"][:1, h:h + 1],
+            w.mask, w.window, scale=w.scale,
+            alibi_slopes=None if slopes is None else slopes[a:a + 1].astype(np.float64),
+            q_len=None if q_len is None else q_len[:1],
+            kv_len=None if kv_len is None else kv_len[:1]))
     dt = time.perf_counter() - t0
     n = len(refs)
-    flops = 4 * w.D * ex_visible_pairs(w) * n
+    flops = ex_effective_flops(w, batches=[0]) / w.Hq * n
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -343,18 +360,22 @@ def bench_ex(args, name):
         return t.to(dev).contiguous()
 
     q, k, v = (place(inputs[n + "_bits"]) for n in ("q", "k", "v"))
+    slopes = w.alibi_slopes()
+    q_len, kv_len = w.lengths_qkv()
+    slopes_d, q_len_d, kv_len_d = (None if x is None else torch.from_numpy(x).to(dev)
+                                   for x in (slopes, q_len, kv_len))
     if w.layout == "bshd":
         out = torch.empty((w.B, w.Sq, w.Hq, w.D), dtype=torch.bfloat16,
                           device=dev).transpose(1, 2)
     else:
         out = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.bfloat16, device=dev)
-    flops = 4 * w.D * ex_visible_pairs(w) * w.B * w.Hq
+    flops = ex_effective_flops(w)
     stream = torch.cuda.current_stream(dev)
     calibration_copy(args.calibrate_copy_mib, dev)
 
     def step():
         attn.fwd_ex(q, k, v, mask=w.mask, window=w.window, scale=w.scale, out=out,
-                    stream=stream)
+                    stream=stream, alibi_slopes=slopes_d, q_len=q_len_d, kv_len=kv_len_d)
 
     ms, prewarm_steps = time_steps(step, stream, args)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -376,7 +397,8 @@ def bench_ex(args, name):
         "data": "synthetic",
         "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq,
                    "Skv": w.Skv, "D": w.D, "mask": w.mask, "window": w.window,
-                   "layout": w.layout, "effective_flops": flops, "parallelism": "none"},
+                   "layout": w.layout, "alibi": w.alibi, "lengths": w.lengths,
+                   "effective_flops": flops, "parallelism": "none"},
         "pct_peak": round(100.0 * tflops / peak, 2),
         "roofline": {
             "bound": "mfma",

@@ -121,6 +121,27 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o,
  * Strides must be non-negative multiples of 8 elements (16-byte rows), row
  * strides at most 2^23 elements; o's rows must not overlap each other or the
  * inputs.  LOCAL_GLOBAL and fp32 return ATTN_ERR_UNSUPPORTED here.
+ *
+ * Optional parts (NULL pointers leave them out):
+ *   alibi_slopes  device, Hq fp32 slopes m_a: query head a adds -m_a * |p_i - j|
+ *                 to each scaled score ("Transformer 演进与变体", section
+ *                 线性偏置注意力; "Trasformer 浅析", section 加性偏置：ALiBi;
+ *                 "Transformer 架构及其变体", section 位置信息通过查询和键进入注意力:
+ *                 a per-head penalty linear in the query-key distance, added
+ *                 after the 1/sqrt(d) scaling).  Slopes are read by the kernel;
+ *                 any finite value works while m_a / |scale| stays far below
+ *                 the fp32 range; a scale of magnitude below 2^-60 other than 0
+ *                 returns ATTN_ERR_SCALE.
+ *   q_len, kv_len device, B int32 each: sequence b holds q_len[b] valid query
+ *                 rows and kv_len[b] valid keys at the start of its rows (a
+ *                 right-padded batch, "Trasformer 浅析", section 填充掩码与因果
+ *                 掩码: padded positions are masked out).  It is computed as
+ *                 the call with Sq = q_len[b], Skv = kv_len[b] (so query i sits
+ *                 at key position i + kv_len[b] - q_len[b]); padded keys are
+ *                 never read into the result; padded query rows (i >= q_len[b])
+ *                 are written as zeros.  Values are clamped to [0, Sq] and
+ *                 [0, Skv]; read by the kernel, so a captured launch can be
+ *                 replayed with new lengths.
  */
 typedef struct {
   const void* q;
@@ -139,6 +160,9 @@ typedef struct {
   int window;             /* CAUSAL_WINDOW: >= 1                          */
   float scale;
   int dtype;              /* ATTN_DTYPE_BF16                              */
+  const float* alibi_slopes;  /* device [Hq] fp32, or NULL                */
+  const int* q_len;           /* device [B] int32, or NULL (all Sq valid)  */
+  const int* kv_len;          /* device [B] int32, or NULL (all Skv valid) */
 } attn_fwd_args;
 
 /* Enqueue attn_fwd_ex on `stream`; same return and error conventions as

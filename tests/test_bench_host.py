@@ -34,14 +34,20 @@ def test_decode_counts_short_caches(mask):
 @pytest.mark.parametrize("mask,window", [("full", 0), ("causal", 0), ("causal_window", 1),
                                          ("causal_window", 37)])
 def test_ex_pairs_match_oracle(Sq, Skv, mask, window):
-    w = workloads.ExWorkload("t", 1, 4, 2, Sq, Skv, 64, mask, "bhsd", window=window)
-    assert bench.ex_visible_pairs(w) == cr.cross_visible_pairs(Sq, Skv, mask, window)
+    assert bench.ex_visible_pairs(Sq, Skv, mask, window) == cr.cross_visible_pairs(
+        Sq, Skv, mask, window)
 
 
 @pytest.mark.parametrize("name", list(workloads.EX_WORKLOADS))
-def test_ex_workload_pairs(name):
+def test_ex_workload_flops(name):
     w = workloads.EX_WORKLOADS[name]
-    assert bench.ex_visible_pairs(w) == cr.cross_visible_pairs(w.Sq, w.Skv, w.mask, w.window)
+    q_len, kv_len = w.lengths_qkv()
+    pairs = 0
+    for b in range(w.B):
+        pairs += cr.cross_visible_pairs(w.Sq if q_len is None else int(q_len[b]),
+                                        w.Skv if kv_len is None else int(kv_len[b]),
+                                        w.mask, w.window)
+    assert bench.ex_effective_flops(w) == 4.0 * w.D * pairs * w.Hq
 
 
 def test_more_than_one_gpu_is_refused():

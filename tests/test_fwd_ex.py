@@ -1,10 +1,12 @@
-"""attn_fwd_ex (Sq != Skv, strided layouts) against the fp64 oracle.
+"""attn_fwd_ex (Sq != Skv, strided layouts, ALiBi, padded batches) against
+the fp64 oracle.
 
 GPU cases compare every output element with oracle.cross_attention (queries
 aligned to the end of the keys) at the bf16 tolerance, over head-major,
-sequence-major and padded-row layouts for inputs and output; with Sq == Skv
-and dense layouts the result must equal attn_fwd's bit for bit.  Host-only
-cases check the validation.
+sequence-major and padded-row layouts for inputs and output, with and
+without ALiBi slopes and per-sequence lengths (NaN in every padded position);
+with Sq == Skv and dense layouts the result must equal attn_fwd's bit for
+bit.  Host-only cases check the validation.
 """
 import numpy as np
 import pytest
@@ -44,23 +46,36 @@ def empty_out(B, H, S, D, layout, device):
 
 
 def run_ex(device, B, Hq, Hkv, Sq, Skv, D, mask, window=0, layout="bhsd", out_layout="bhsd",
-           seed=0, scale=None):
+           seed=0, scale=None, slopes=None, q_len=None, kv_len=None):
+    """Max abs error of attn_fwd_ex against the oracle.  With lengths, the
+    padded query rows, keys and values hold NaN (bf16 0x7FC0)."""
     import torch
 
     print(f"fwd_ex case B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} {mask} w={window} "
-          f"{layout}->{out_layout} seed={seed}", flush=True)
+          f"{layout}->{out_layout} seed={seed} scale={scale} alibi={slopes is not None} "
+          f"q_len={q_len} kv_len={kv_len}", flush=True)
     rng = np.random.default_rng(seed)
     bits = {}
     vals = {}
     for name, shape in (("q", (B, Hq, Sq, D)), ("k", (B, Hkv, Skv, D)), ("v", (B, Hkv, Skv, D))):
         bits[name] = workloads.bf16_round_bits(workloads.draw(shape, rng))
         vals[name] = workloads.bf16_bits_to_float(bits[name])
+    for b in range(B):
+        if q_len is not None:
+            bits["q"][b, :, q_len[b]:] = 0x7FC0
+        if kv_len is not None:
+            bits["k"][b, :, kv_len[b]:] = 0x7FC0
+            bits["v"][b, :, kv_len[b]:] = 0x7FC0
     q, k, v = (place(bits[n], layout, device) for n in ("q", "k", "v"))
     o = empty_out(B, Hq, Sq, D, out_layout, device)
-    attn.fwd_ex(q, k, v, mask=mask, window=window, scale=scale, out=o)
+    dev_arr = lambda x, dt: None if x is None else torch.tensor(list(x), dtype=dt, device=device)  # noqa: E731
+    attn.fwd_ex(q, k, v, mask=mask, window=window, scale=scale, out=o,
+                alibi_slopes=dev_arr(slopes, torch.float32), q_len=dev_arr(q_len, torch.int32),
+                kv_len=dev_arr(kv_len, torch.int32))
     torch.cuda.synchronize()
     got = o.float().cpu().numpy()
-    ref = oracle.cross_attention(vals["q"], vals["k"], vals["v"], mask, window, scale=scale)
+    ref = oracle.cross_attention(vals["q"], vals["k"], vals["v"], mask, window, scale=scale,
+                                 alibi_slopes=slopes, q_len=q_len, kv_len=kv_len)
     assert np.all(np.isfinite(got))
     return float(np.max(np.abs(got.astype(np.float64) - ref)))
 
@@ -87,6 +102,85 @@ def test_fwd_ex_sweep(device, case):
     err = run_ex(device, B, Hq, Hkv, Sq, Skv, D, mask, window, layout, out_layout,
                  seed=Sq * 3 + Skv + D)
     assert err <= TOL["bf16"], err
+
+
+ALIBI_SWEEP = []
+_rng = np.random.default_rng(92)
+for D in (64, 128):
+    for (Sq, Skv) in ((100, 300), (300, 100), (257, 257), (1, 500), (513, 2049)):
+        for mask in ("full", "causal", "causal_window"):
+            Hq, Hkv = [(8, 2), (4, 4), (8, 1)][int(_rng.integers(3))]
+            window = int(_rng.choice([1, 63, 200])) if mask == "causal_window" else 0
+            layout = ["bhsd", "bshd", "padded"][int(_rng.integers(3))]
+            ALIBI_SWEEP.append((1 + int(_rng.integers(2)), Hq, Hkv, Sq, Skv, D, mask, window,
+                                layout))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", ALIBI_SWEEP, ids=lambda c: f"D{c[5]}-Sq{c[3]}-Skv{c[4]}-{c[6]}-"
+                                                            f"{c[8]}")
+def test_fwd_ex_alibi_sweep(device, case):
+    """ALiBi with distinct slopes per query head (also inside one group)."""
+    B, Hq, Hkv, Sq, Skv, D, mask, window, layout = case
+    slopes = [float(x) for x in workloads.make_alibi_slopes(Hq)]
+    err = run_ex(device, B, Hq, Hkv, Sq, Skv, D, mask, window, layout, layout,
+                 seed=Sq + 7 * Skv + D, slopes=slopes)
+    assert err <= TOL["bf16"], err
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("scale", [0.0, -0.1, 0.5])
+@pytest.mark.parametrize("mask", ["full", "causal"])
+def test_fwd_ex_alibi_scales(device, scale, mask):
+    """Zero and negative scales, and steep slopes (weights decay within a
+    few keys), on both ALiBi forms."""
+    slopes = [0.02, 0.5, 2.0, 8.0]
+    err = run_ex(device, 1, 4, 2, 130, 700, 128, mask, seed=31, scale=scale, slopes=slopes)
+    assert err <= TOL["bf16"], err
+
+
+RAGGED = [
+    # (B, Hq, Hkv, Sq, Skv, D, mask, window, q_len, kv_len, alibi)
+    (4, 8, 2, 300, 300, 128, "causal", 0, (300, 1, 129, 0), (300, 1, 129, 0), False),
+    (3, 4, 4, 257, 257, 64, "full", 0, (257, 100, 64), (257, 100, 64), True),
+    (3, 8, 1, 200, 600, 128, "causal", 0, (200, 17, 0), (600, 300, 5), True),
+    (2, 8, 2, 130, 400, 64, "causal_window", 50, (130, 64), (130, 399), False),
+    (3, 4, 2, 400, 150, 128, "causal", 0, (400, 33, 150), (150, 150, 0), True),
+    (2, 4, 4, 64, 1000, 128, "full", 0, (64, 30), (1000, 999), False),
+    (4, 8, 8, 513, 513, 64, "causal_window", 128, (513, 256, 255, 129), (513, 256, 255, 129), True),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: f"D{c[5]}-Sq{c[3]}-Skv{c[4]}-{c[6]}-"
+                                                      f"{'alibi' if c[10] else 'plain'}")
+def test_fwd_ex_padded_batches(device, case):
+    """Per-sequence lengths (right padding, NaN in every padded position),
+    including empty sequences, single rows, q_len > kv_len and lengths on
+    and beside tile edges."""
+    B, Hq, Hkv, Sq, Skv, D, mask, window, q_len, kv_len, alibi = case
+    slopes = [float(x) for x in workloads.make_alibi_slopes(Hq)] if alibi else None
+    for layout in ("bhsd", "bshd"):
+        err = run_ex(device, B, Hq, Hkv, Sq, Skv, D, mask, window, layout, layout,
+                     seed=Sq + Skv + B, slopes=slopes, q_len=q_len, kv_len=kv_len)
+        assert err <= TOL["bf16"], (layout, err)
+
+
+@pytest.mark.gpu
+def test_fwd_ex_full_lengths_equal_no_lengths(device):
+    """Lengths equal to Sq and Skv give the same bits as no lengths."""
+    import torch
+
+    inp = workloads.make_decode_inputs(2, 8, 2, 300, 700, 128, seed=23)
+    q, k, v = (torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16)
+               .to(device).contiguous() for n in ("q", "k", "v"))
+    ql = torch.tensor([300, 300], dtype=torch.int32, device=device)
+    kl = torch.tensor([700, 700], dtype=torch.int32, device=device)
+    for mask in ("causal", "full"):
+        a = attn.fwd_ex(q, k, v, mask=mask)
+        b = attn.fwd_ex(q, k, v, mask=mask, q_len=ql, kv_len=kl)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), mask
 
 
 @pytest.mark.gpu
@@ -133,7 +227,11 @@ def test_fwd_ex_workload_full_size(device, name):
     inp = workloads.ex_workload_inputs(w)
     q, k, v = (place(inp[n + "_bits"], w.layout, device) for n in ("q", "k", "v"))
     o = empty_out(w.B, w.Hq, w.Sq, w.D, w.layout, device)
-    attn.fwd_ex(q, k, v, mask=w.mask, window=w.window, scale=w.scale, out=o)
+    slopes = w.alibi_slopes()
+    q_len, kv_len = w.lengths_qkv()
+    dev = lambda x: None if x is None else torch.from_numpy(x).to(device)  # noqa: E731
+    attn.fwd_ex(q, k, v, mask=w.mask, window=w.window, scale=w.scale, out=o,
+                alibi_slopes=dev(slopes), q_len=dev(q_len), kv_len=dev(kv_len))
     torch.cuda.synchronize()
     got = o.float().cpu().numpy()
     rng = np.random.default_rng(w.seed + 5)
@@ -142,9 +240,12 @@ def test_fwd_ex_workload_full_size(device, name):
     G = w.Hq // w.Hkv
     for b, a in {(0, 0), (w.B - 1, w.Hq - 1), (int(rng.integers(w.B)), int(rng.integers(w.Hq)))}:
         h = a // G
-        ref = oracle.cross_attention(inp["q"][b:b + 1, a:a + 1], inp["k"][b:b + 1, h:h + 1],
-                                     inp["v"][b:b + 1, h:h + 1], w.mask, w.window, scale=w.scale,
-                                     rows=rows)
+        ref = oracle.cross_attention(
+            inp["q"][b:b + 1, a:a + 1], inp["k"][b:b + 1, h:h + 1], inp["v"][b:b + 1, h:h + 1],
+            w.mask, w.window, scale=w.scale, rows=rows,
+            alibi_slopes=None if slopes is None else slopes[a:a + 1].astype(np.float64),
+            q_len=None if q_len is None else q_len[b:b + 1],
+            kv_len=None if kv_len is None else kv_len[b:b + 1])
         err = float(np.max(np.abs(got[b, a, rows].astype(np.float64) - ref[0, 0])))
         print(f"{name} b={b} a={a}: max abs err {err:.3e}", flush=True)
         assert err <= TOL["bf16"], (b, a, err)
@@ -156,6 +257,7 @@ def test_fwd_ex_workload_full_size(device, name):
 
 def ex_status(**kw):
     a = attn.FwdArgs()
+    a.alibi_slopes, a.q_len, a.kv_len = None, None, None
     base = 0x1000000
     a.q, a.k, a.v, a.o = base, base * 3, base * 5, base * 7
     a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = 1, 8, 2, 100, 300, 128
@@ -189,3 +291,9 @@ def test_fwd_ex_rejects_bad_arguments():
     assert ex_status(v_stride=[0, 0, (1 << 23) + 8]) == "ATTN_ERR_SHAPE"
     assert ex_status(o=0x1000000) == "ATTN_ERR_ALIAS"                  # o over q
     assert ex_status(o_stride=[8 * 100 * 128, 100 * 128, 64]) == "ATTN_ERR_ALIAS"  # rows overlap
+    assert ex_status(alibi_slopes=0x2000002) == "ATTN_ERR_ALIGN"
+    assert ex_status(q_len=0x2000001) == "ATTN_ERR_ALIGN"
+    assert ex_status(kv_len=0x2000003) == "ATTN_ERR_ALIGN"
+    assert ex_status(alibi_slopes=0x2000000, scale=1e-30) == "ATTN_ERR_SCALE"
+    assert ex_status(alibi_slopes=0x7000000 + 64) == "ATTN_ERR_ALIAS"  # slopes inside o
+    assert ex_status(kv_len=0x7000000) == "ATTN_ERR_ALIAS"             # lengths inside o

@@ -52,6 +52,8 @@ class FwdArgs(ctypes.Structure):
         ("v_stride", ctypes.c_longlong * 3), ("o_stride", ctypes.c_longlong * 3),
         ("mask_kind", ctypes.c_int), ("window", ctypes.c_int),
         ("scale", ctypes.c_float), ("dtype", ctypes.c_int),
+        ("alibi_slopes", ctypes.c_void_p), ("q_len", ctypes.c_void_p),
+        ("kv_len", ctypes.c_void_p),
     ]
 
 
@@ -174,14 +176,16 @@ def fwd_ex_raw(args: FwdArgs, stream: int) -> int:
 
 
 def fwd_ex(q, k, v, mask="causal", window: int = 0, scale: Optional[float] = None, out=None,
-           stream=None):
+           stream=None, alibi_slopes=None, q_len=None, kv_len=None):
     """Forward pass with Sq != Skv and strided layouts (bf16).
 
     q: [B, Hq, Sq, D], k, v: [B, Hkv, Skv, D] as torch views of any strides
     whose last dimension is contiguous (e.g. a [B, S, H, D] tensor passed as
     x.transpose(1, 2)).  Queries are aligned to the end of the keys (query i at
     key position i + Skv - Sq).  Returns o shaped like q (a dense tensor unless
-    `out` is given, which may be strided too).
+    `out` is given, which may be strided too).  Optional GPU tensors:
+    alibi_slopes float32 [Hq] (ALiBi), q_len and kv_len int32 [B] (valid rows
+    and keys per sequence of a right-padded batch; padded rows come out zero).
     """
     import torch
 
@@ -206,6 +210,14 @@ def fwd_ex(q, k, v, mask="causal", window: int = 0, scale: Optional[float] = Non
     for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
         getattr(a, name)[:] = [t.stride(0), t.stride(1), t.stride(2)]
     a.mask_kind, a.window, a.scale, a.dtype = _mask_id(mask), int(window), float(scale), DTYPE_BF16
+    for name, t, dt, n in (("alibi_slopes", alibi_slopes, torch.float32, Hq),
+                           ("q_len", q_len, torch.int32, B), ("kv_len", kv_len, torch.int32, B)):
+        if t is None:
+            setattr(a, name, None)
+            continue
+        if t.dtype != dt or t.device != q.device or tuple(t.shape) != (n,) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of {n} on q's device")
+        setattr(a, name, t.data_ptr())
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)

@@ -192,6 +192,11 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
   if (!std::isfinite(a->scale)) return ATTN_ERR_SCALE;
   for (const void* ptr : {a->q, a->k, a->v, (const void*)a->o})
     if ((uintptr_t)ptr % 16 != 0) return ATTN_ERR_ALIGN;
+  for (const void* ptr : {(const void*)a->alibi_slopes, (const void*)a->q_len,
+                          (const void*)a->kv_len})
+    if ((uintptr_t)ptr % 4 != 0) return ATTN_ERR_ALIGN;
+  // ALiBi slopes are turned into score units by 1 / |scale|
+  if (a->alibi_slopes && a->scale != 0.f && std::fabs(a->scale) < 0x1p-60f) return ATTN_ERR_SCALE;
   const long long* strides[4] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride};
   for (const long long* st : strides) {
     for (int d = 0; d < 3; ++d)
@@ -209,6 +214,10 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
   const size_t nq = span(a->q_stride, a->Hq, a->Sq), nk = span(a->k_stride, a->Hkv, a->Skv);
   const size_t nv = span(a->v_stride, a->Hkv, a->Skv), no = span(a->o_stride, a->Hq, a->Sq);
   if (overlaps(a->o, no, a->q, nq) || overlaps(a->o, no, a->k, nk) || overlaps(a->o, no, a->v, nv))
+    return ATTN_ERR_ALIAS;
+  if ((a->alibi_slopes && overlaps(a->o, no, a->alibi_slopes, (size_t)a->Hq * 4)) ||
+      (a->q_len && overlaps(a->o, no, a->q_len, (size_t)a->B * 4)) ||
+      (a->kv_len && overlaps(a->o, no, a->kv_len, (size_t)a->B * 4)))
     return ATTN_ERR_ALIAS;
   // o's own rows must be distinct: rows of one head D apart at least, heads and
   // batches not folded onto each other
@@ -232,6 +241,10 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
   p.qmode = a->scale > 0.f ? 0 : (a->scale < 0.f ? 1 : 2);
   if (p.qmode == 2) p.c = 1.f;
   p.general = 1;
+  p.qlen = a->q_len;
+  p.kvlen = a->kv_len;
+  p.slopes = a->alibi_slopes;
+  p.alibi_k = a->scale != 0.f ? 1.f / std::fabs(a->scale) : 1.4426950408889634f;
   for (int d = 0; d < 3; ++d) {
     p.qs[d] = a->q_stride[d];
     p.ks[d] = a->k_stride[d];

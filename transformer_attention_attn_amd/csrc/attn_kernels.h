@@ -27,6 +27,10 @@ struct KParams {
   // dimensions of q, k, v and o (the head dimension is contiguous)
   int general;
   long long qs[3], ks[3], vs[3], os[3];
+  const int* qlen;       // device, B valid query rows per sequence, or null (all Sq)
+  const int* kvlen;      // device, B valid keys per sequence, or null (all Skv)
+  const float* slopes;   // device, Hq ALiBi slopes, or null (no bias)
+  float alibi_k;         // slope -> score units: 1 / |scale|, or log2(e) for scale 0
 };
 
 // Workgroup shapes used by the two kernels.

@@ -194,14 +194,17 @@ struct Cfg {
 // 256 registers each); two at D = 64, whose kernel fits in 128 registers and
 // 64 KB of LDS, so a second workgroup fills the gaps of the first.
 constexpr int kWavesPerEu = HD == 64 ? 4 : 2;
-// GEN = 1: the general form behind attn_fwd_ex -- Sq query rows (s.S) against
-// Sk keys (s.Sk), query i at key position i + s.off, element strides for the
-// batch, head and row dimensions of each tensor; the local+global mask is not
-// offered there.  GEN = 0 is attn_fwd's dense square layout.
+// GEN = 0: attn_fwd's dense square layout.  GEN = 1: the general form behind
+// attn_fwd_ex -- Sq query rows (s.S) against Sk keys (s.Sk), query i at key
+// position i + s.off, element strides for the batch, head and row dimensions
+// of each tensor, optional per-sequence lengths (right padding); the
+// local+global mask is not offered there.  GEN = 2: GEN = 1 plus the ALiBi
+// bias.
 template <int D, int MASK, int GEN = 0>
 __global__ __launch_bounds__(kBf16Threads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu, kWavesPerEu)))
 void attn_fwd_bf16(KParams p) {
   using C = Cfg<D>;
+  constexpr bool ALIBI = GEN == 2;
   constexpr int NDC = C::NDC, NDB = C::NDB, ROWB = C::ROWB, REG = C::REG, BUF = C::BUF,
                 NGL = C::NGL, RSTEP = C::RSTEP, NSTAGE = C::NSTAGE, VSH = C::VSH;
 
@@ -217,6 +220,16 @@ void attn_fwd_bf16(KParams p) {
   const int l32 = lane & 31;
   const int hf = lane >> 5;  // lane half: selects the k sub-range of an MFMA operand
   const Item it = decode_item(s, blockIdx.x);
+  // valid query rows SQ and keys SK of this sequence, and the key position
+  // OFF of query row 0 (GEN: queries aligned to the end of the keys; with
+  // per-sequence lengths the rest of the rows and keys are padding)
+  int SQ = s.S, SK = GEN ? s.Sk : s.S, OFF = GEN ? s.off : 0;
+  if constexpr (GEN != 0) {
+    if (p.qlen) SQ = imin(imax(p.qlen[it.b], 0), s.S);
+    if (p.kvlen) SK = imin(imax(p.kvlen[it.b], 0), s.Sk);
+    OFF = SK - SQ;
+  }
+  const int SKA = GEN ? imax(SK, 1) : SK;  // rows addressed by the tile loads (row 0 always exists)
 
   if (MASK == MASK_LOCAL_GLOBAL) {
     if (tid < kMaxGlobal) gpos_s[tid] = tid < s.n_global ? p.gpos[tid] : 0;
@@ -231,12 +244,12 @@ void attn_fwd_bf16(KParams p) {
   bool row_valid;
   if (!it.is_global) {
     r0 = it.blk * s.BMh;
-    r1 = imin(r0 + s.BMh, s.S) - 1;
+    r1 = imin(r0 + s.BMh, SQ) - 1;
     const int q0 = r0 + rpart * 32;
     q_row = q0 + l32;
-    row_valid = q_row < s.S;
+    row_valid = q_row < SQ;
     wqa = q0;
-    wqb = imin(q0 + 31, s.S - 1);
+    wqb = imin(q0 + 31, SQ - 1);
   } else {
     // every wave of a head holds the head's (up to) 32 global rows; the waves
     // split the keys instead (see the global-row path below)
@@ -245,9 +258,15 @@ void attn_fwd_bf16(KParams p) {
     q_row = row_valid ? gpos_s[slot] : 0;
   }
   const bool wave_active = wqa <= wqb;
-  // key count and the key positions of the wave's first and last rows
-  const int SK = GEN ? s.Sk : s.S;
-  const int wpa = GEN ? wqa + s.off : wqa, wpb = GEN ? wqb + s.off : wqb;
+  // key positions of the wave's first and last valid rows
+  const int wpa = wqa + OFF, wpb = wqb + OFF;
+  // GEN: the wave also holds padded query rows (masked on every tile)
+  const bool wave_pad = GEN && wave_active && imin(wqa + 31, s.S - 1) >= SQ;
+  // ALiBi: the head's slope in units of the scores below (q.k, or log2 units
+  // when the scale is zero), and this lane's query position
+  float slope_u = 0.f;
+  if constexpr (ALIBI) slope_u = p.slopes[a] * p.alibi_k;
+  const int q_pos = q_row + OFF;
 
   const size_t S = (size_t)s.S;
   const __bf16* qp;
@@ -283,8 +302,8 @@ void attn_fwd_bf16(KParams p) {
   // ---- key tiles to visit ------------------------------------------------
   int klo, khi;
   if constexpr (GEN) {
-    // keys seen by rows r0..r1 at key positions r0 + off .. r1 + off
-    const int pa = r0 + s.off, pb = r1 + s.off;
+    // keys seen by the valid rows r0..r1 at key positions r0 + OFF .. r1 + OFF
+    const int pa = r0 + OFF, pb = r1 + OFF;
     klo = MASK == MASK_CAUSAL_WINDOW ? imax(0, pa - s.window + 1) : 0;
     khi = MASK == MASK_FULL ? SK - 1 : imin(pb, SK - 1);
   } else {
@@ -292,7 +311,7 @@ void attn_fwd_bf16(KParams p) {
   }
   const int kt_lo = klo / BN, kt_hi = khi / BN;
   const int has_strip = (MASK == MASK_LOCAL_GLOBAL && !it.is_global && s.n_global > 0) ? 1 : 0;
-  const int n_it = (GEN && khi < klo) ? 0 : (kt_hi - kt_lo + 1) + has_strip;
+  const int n_it = (GEN && (khi < klo || r1 < r0)) ? 0 : (kt_hi - kt_lo + 1) + has_strip;
   auto tile_kt = [&](int iter) { return kt_lo + iter - has_strip; };
   auto is_strip = [&](int iter) { return MASK == MASK_LOCAL_GLOBAL && has_strip && iter == 0; };
 
@@ -322,7 +341,7 @@ void attn_fwd_bf16(KParams p) {
   auto dma = [&](bool isk, int iter, int st, int n) {
     int row;
     if (is_strip(iter)) row = gpos_s[imin(srow + n * RSTEP, s.n_global - 1)];
-    else row = imin(tile_kt(iter) * BN + srow + n * RSTEP, SK - 1);
+    else row = imin(tile_kt(iter) * BN + srow + n * RSTEP, SKA - 1);
     const char* src = (const char*)(isk ? kp : vp) + (size_t)row * (isk ? KRB : VRB) + (isk ? k_col : v_col);
     dma16_global(src, smem + (isk ? 0 : NSTAGE * REG) + st * REG + (n * 4 + gw) * 1024);
   };
@@ -332,8 +351,8 @@ void attn_fwd_bf16(KParams p) {
   const int k_off = srow * KRB + k_col, v_off = srow * VRB + v_col;
   auto dma_band = [&](bool isk, int iter, int st, int n) {
     // tiles past the last one of the sequence load the last tile instead
-    const int row0 = imin(tile_kt(iter), (SK - 1) / BN) * BN;
-    const int nrows = imin(SK - row0, BN);
+    const int row0 = imin(tile_kt(iter), (SKA - 1) / BN) * BN;
+    const int nrows = imin(SKA - row0, BN);
     const int RB = isk ? KRB : VRB;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const char*)(isk ? kp : vp) + (size_t)row0 * RB), (short)0,
@@ -346,7 +365,7 @@ void attn_fwd_bf16(KParams p) {
   // Per-wave tile class.  Tiles EMPTY for this wave (only at the ends of its
   // range, or when it holds no rows) are processed as fully masked.
   auto tile_partial = [&](int iter) -> bool {
-    if (!wave_active || is_strip(iter)) return true;
+    if (!wave_active || is_strip(iter) || wave_pad) return true;
     const int kt = tile_kt(iter);
     if (it.is_global) return kt * BN + BN > s.S;
     return classify_tile(MASK, s.window, SK, wpa, wpb, kt * BN, BN) != TILE_FULL;
@@ -403,8 +422,8 @@ void attn_fwd_bf16(KParams p) {
     // lo <= 32*kbk + 8*(r/4) + r%4 <= hi
     long long lo, hi;
     if (it.is_global) { lo = 0; hi = (long long)s.S - 1; }
-    else row_interval(MASK, s.window, SK, GEN ? q_row + s.off : q_row, &lo, &hi);
-    if (!wave_active) hi = lo - 1;
+    else row_interval(MASK, s.window, SK, q_pos, &lo, &hi);
+    if (!wave_active || (GEN && !row_valid)) hi = lo - 1;
     const long long base = (long long)tile_kt(iter) * BN + 4 * hf;
     const long long tail = (long long)SK - 1;
     const long long hi_a = hi < tail ? hi : tail;
@@ -637,6 +656,34 @@ void attn_fwd_bf16(KParams p) {
       asm volatile("");  // keep this a branch: full tiles skip it
       apply_mask(scur, j);
     }
+    // ALiBi: minus slope times the distance between key and query positions.
+    // Register r of block kbk holds key d0 + 32*kbk + 8*(r/4) + r%4 relative
+    // to the query.  Causal masks: every visible key lies at or before the
+    // query, so the bias slope*(key - query) is linear in the key; its
+    // per-lane part b0 = slope*d0 is carried into the maximum and the
+    // exponent instead of into every score.
+    float b0 = 0.f;
+    if constexpr (ALIBI) {
+      const int d0 = tile_kt(j) * BN + 4 * hf - q_pos;
+      if constexpr (MASK == MASK_FULL) {
+        const float d0f = (float)d0;
+#pragma unroll
+        for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            scur[kbk][r] = __builtin_fmaf(
+                -slope_u, __builtin_fabsf(d0f + (float)(kbk * 32 + 8 * (r >> 2) + (r & 3))),
+                scur[kbk][r]);
+      } else {
+        b0 = slope_u * (float)d0;
+#pragma unroll
+        for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            scur[kbk][r] =
+                __builtin_fmaf((float)(kbk * 32 + 8 * (r >> 2) + (r & 3)), slope_u, scur[kbk][r]);
+      }
+    }
     float mx;
     {
       // four independent v_max3 chains over the 32 scores of this lane, then join
@@ -653,6 +700,7 @@ void attn_fwd_bf16(KParams p) {
 #pragma unroll
       for (int c4 = 4; c4 < 2 * NKB; c4 += 2) mx = max3f(mx, t[c4], t[c4 + 1]);
     }
+    if constexpr (ALIBI && MASK != MASK_FULL) mx += b0;
     mx = pair_max(mx);
     // rare: a row maximum grew by more than 2^kLazy
     if (__builtin_amdgcn_ballot_w64(mx * c > m_run * c + kLazy) != 0) {
@@ -666,7 +714,8 @@ void attn_fwd_bf16(KParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
-    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+    float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+    if constexpr (ALIBI && MASK != MASK_FULL) mc -= b0 * c;
 #pragma unroll
     for (int pc = 0; pc < NPC; ++pc) {
       const int kbk = pc >> 1, rb = (pc & 1) * 8;
@@ -794,12 +843,12 @@ void attn_fwd_bf16(KParams p) {
     const float l_other = __uint_as_float(__shfl_xor((int)lu, 32));
     const float l_tot = l_run + l_other;
     // global items: the first wave of each head holds the merged result
-    bool store = row_valid && (it.is_global ? rpart == 0 : wave_active);
+    // (GEN: padded query rows and rows that see no key are written as zero)
+    bool store = GEN ? q_row < s.S : row_valid && (it.is_global ? rpart == 0 : wave_active);
     if (MASK == MASK_LOCAL_GLOBAL && !it.is_global && store) {
       for (int g = 0; g < s.n_global; ++g) store = store && (gpos_s[g] != q_row);
     }
     if (store) {
-      // (GEN: a query before the first key sees nothing and is written as zero)
       const float inv = GEN ? (l_tot > 0.f ? 1.f / l_tot : 0.f) : 1.f / l_tot;
       __bf16* op = GEN ? (__bf16*)p.o + it.b * p.os[0] + a * p.os[1] + q_row * p.os[2]
                        : (__bf16*)p.o + ((size_t)(it.b * s.Hq + a) * S + q_row) * D;
@@ -819,6 +868,14 @@ void attn_fwd_bf16(KParams p) {
 template <int D>
 hipError_t launch_d(const KParams& p, hipStream_t stream) {
   dim3 grid((unsigned)p.s.n_items), block(kBf16Threads);
+  if (p.general && p.slopes) {
+    switch (p.s.mask) {
+      case MASK_FULL: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_FULL, 2>), grid, block, 0, stream, p); break;
+      case MASK_CAUSAL: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL, 2>), grid, block, 0, stream, p); break;
+      default: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL_WINDOW, 2>), grid, block, 0, stream, p); break;
+    }
+    return hipGetLastError();
+  }
   if (p.general) {
     switch (p.s.mask) {
       case MASK_FULL: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_FULL, 1>), grid, block, 0, stream, p); break;

@@ -44,6 +44,10 @@ the keys):
   all tensors sequence-major ([B][S][H][D]) ("Trasformer 浅析", section
   交叉注意力; heads of 64 as in the original model's head width,
   "Transformer 演进与变体", section MHA：多头注意力).
+* ``alibi_padded_mha_bf16_b8_s4096`` -- causal prefill of 8 right-padded
+  sequences (valid lengths uniform in [1024, 4096]) with the ALiBi distance
+  bias, 32 heads of D=128 ("Transformer 演进与变体", section 线性偏置注意力;
+  "Trasformer 浅析", section 填充掩码与因果掩码).  Slopes 2^(-8 (a+1) / 32).
 
 Values are iid N(0, 1) from ``numpy.random.default_rng(seed)``, drawn as
 float32 in the order Q, K, V, each shaped [B][H][S][D].  bf16 workloads round
@@ -164,13 +168,29 @@ class ExWorkload:
     window: int = 0
     seed: int = 0
     dtype: str = "bf16"
+    alibi: bool = False   # ALiBi with the slopes of alibi_slopes()
+    lengths: str = "full"  # "full", or "ragged": per-sequence lengths of lengths()
 
     @property
     def scale(self) -> float:
         return 1.0 / float(np.sqrt(self.D))
 
+    def alibi_slopes(self):
+        """Hq slopes (float32) when alibi is set, else None."""
+        return make_alibi_slopes(self.Hq) if self.alibi else None
+
+    def lengths_qkv(self):
+        """(q_len, kv_len) int32 arrays of B valid lengths, or (None, None)."""
+        if self.lengths == "full":
+            return None, None
+        return make_ragged_lengths(self.B, self.Sq, self.Skv, self.seed)
+
     def describe(self) -> dict:
-        return dataclasses.asdict(self)
+        d = dataclasses.asdict(self)
+        ql, kl = self.lengths_qkv()
+        if ql is not None:
+            d["q_len"], d["kv_len"] = [int(x) for x in ql], [int(x) for x in kl]
+        return d
 
 
 EX_WORKLOADS = {
@@ -182,8 +202,28 @@ EX_WORKLOADS = {
         # decoder queries against a longer encoder sequence, sequence-major tensors
         ExWorkload("cross_mha_bf16_q1024_kv4096_bshd", 4, 16, 16, 1024, 4096, 64, MASK_FULL,
                    "bshd", seed=10),
+        # causal prefill of a right-padded batch with ALiBi instead of positions in q/k
+        ExWorkload("alibi_padded_mha_bf16_b8_s4096", 8, 32, 32, 4096, 4096, 128, MASK_CAUSAL,
+                   "bhsd", seed=11, alibi=True, lengths="ragged"),
     )
 }
+
+
+def make_alibi_slopes(H: int) -> np.ndarray:
+    """Synthetic per-head ALiBi slopes: the geometric sequence 2^(-8 (a+1) / H),
+    a = 0..H-1 (the pages fix no slope values; this is an input recipe)."""
+    return np.exp2(-8.0 * (np.arange(H, dtype=np.float64) + 1.0) / H).astype(np.float32)
+
+
+def make_ragged_lengths(B: int, Sq: int, Skv: int, seed: int):
+    """Per-sequence valid lengths of a right-padded batch, drawn uniformly from
+    [Skv/4, Skv] for the keys with default_rng(seed + 2000); the query count is
+    the same number shifted by Sq - Skv (clamped to [0, Sq]), so a square batch
+    (Sq == Skv) has q_len == kv_len."""
+    rng = np.random.default_rng(seed + 2000)
+    kv = rng.integers(Skv // 4, Skv + 1, size=B)
+    q = np.clip(kv - (Skv - Sq), 0, Sq)
+    return q.astype(np.int32), kv.astype(np.int32)
 
 
 def bf16_round_bits(x: np.ndarray) -> np.ndarray:
