@@ -32,3 +32,10 @@ from .cross import (  # noqa: F401
     cross_visible_pairs,
     cross_visible_range,
 )
+from .sparse import (  # noqa: F401
+    bigbird_layout,
+    block_sparse_attention,
+    block_sparse_pairs,
+    fixed_layout,
+    strided_layout,
+)
