@@ -193,9 +193,48 @@ def ex_visible_pairs(Sq, Skv, mask, window=0) -> int:
     return int(np.maximum(hi - lo, 0).sum())
 
 
+def layout_pairs(words, S, causal, block=64) -> int:
+    """Visible (query, key) pairs of one head under a block-sparse layout
+    (uint32 bitmask rows over blocks of `block` positions)."""
+    import numpy as np
+
+    nb = -(-S // block)
+    bits = np.unpackbits(np.ascontiguousarray(words, dtype="<u4").view(np.uint8),
+                         bitorder="little").reshape(nb, -1)[:, :nb].astype(bool)
+    start = np.arange(nb) * block
+    width = np.minimum(start + block, S) - start       # keys of each block
+    total = 0
+    for I in range(nb):
+        rows = np.arange(start[I], start[I] + width[I])
+        J = np.nonzero(bits[I])[0]
+        if causal:  # keys j <= i of each visible block, for every row i of block I
+            total += int(np.clip(rows[:, None] - start[J][None, :] + 1, 0, width[J][None, :]).sum())
+        else:
+            total += int(width[J].sum()) * len(rows)
+    return total
+
+
+def ex_layout_words(w):
+    """The workload's block-sparse layout from the library's builders, or None."""
+    import transformer_attention_attn_amd as attn
+
+    nb = w.n_blocks()
+    if w.pattern == "strided":
+        return attn.layout_strided(nb, *w.pattern_args)
+    if w.pattern == "fixed":
+        return attn.layout_fixed(nb, *w.pattern_args)
+    if w.pattern == "bigbird":
+        radius, g, _ = w.pattern_args
+        return attn.layout_bigbird(nb, radius, g, w.rand_blocks())
+    return None
+
+
 def ex_effective_flops(w, batches=None) -> float:
     """4 * D FLOPs per visible pair and query head, summed over the sequences
     (each with its own valid lengths when the workload is padded)."""
+    if w.pattern:
+        nbat = w.B if batches is None else len(list(batches))
+        return 4.0 * w.D * layout_pairs(ex_layout_words(w), w.Sq, w.mask == "causal") * w.Hq * nbat
     q_len, kv_len = w.lengths_qkv()
     total = 0
     for b in (range(w.B) if batches is None else batches):
@@ -216,11 +255,22 @@ def ex_cpu_baseline(w, inputs, seconds: float = 10.0):
     G = w.Hq // w.Hkv
     slopes = w.alibi_slopes()
     q_len, kv_len = w.lengths_qkv()
+    lay = None
+    if w.pattern:  # the oracle's own layout of the pattern
+        nb = w.n_blocks()
+        lay = (oracle.strided_layout(nb, *w.pattern_args) if w.pattern == "strided" else
+               oracle.fixed_layout(nb, *w.pattern_args) if w.pattern == "fixed" else
+               oracle.bigbird_layout(nb, w.pattern_args[0], w.pattern_args[1], w.rand_blocks()))
     refs = []
     t0 = time.perf_counter()
     while len(refs) < w.Hq and time.perf_counter() - t0 < seconds:
         a = len(refs)
         h = a // G
+        if lay is not None:
+            refs.append(oracle.block_sparse_attention(
+                inputs["q"][:1, a:a + 1], inputs["k"][:1, h:h + 1], inputs["v"][:1, h:h + 1],
+                lay, 64, w.mask == "causal", scale=w.scale))
+            continue
         refs.append(oracle.cross_attention(
             inputs["q"][:1, a:a + 1], inputs["k"][:1, h:h + 1], inputs["v"][:1, h:h + 1],
             w.mask, w.window, scale=w.scale,
@@ -364,6 +414,8 @@ def bench_ex(args, name):
     q_len, kv_len = w.lengths_qkv()
     slopes_d, q_len_d, kv_len_d = (None if x is None else torch.from_numpy(x).to(dev)
                                    for x in (slopes, q_len, kv_len))
+    words = ex_layout_words(w)
+    layout_d = None if words is None else torch.from_numpy(words.view(np.int32)).to(dev)
     if w.layout == "bshd":
         out = torch.empty((w.B, w.Sq, w.Hq, w.D), dtype=torch.bfloat16,
                           device=dev).transpose(1, 2)
@@ -375,7 +427,8 @@ def bench_ex(args, name):
 
     def step():
         attn.fwd_ex(q, k, v, mask=w.mask, window=w.window, scale=w.scale, out=out,
-                    stream=stream, alibi_slopes=slopes_d, q_len=q_len_d, kv_len=kv_len_d)
+                    stream=stream, alibi_slopes=slopes_d, q_len=q_len_d, kv_len=kv_len_d,
+                    block_layout=layout_d)
 
     ms, prewarm_steps = time_steps(step, stream, args)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -398,6 +451,7 @@ def bench_ex(args, name):
         "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq,
                    "Skv": w.Skv, "D": w.D, "mask": w.mask, "window": w.window,
                    "layout": w.layout, "alibi": w.alibi, "lengths": w.lengths,
+                   "pattern": w.pattern, "pattern_args": list(w.pattern_args),
                    "effective_flops": flops, "parallelism": "none"},
         "pct_peak": round(100.0 * tflops / peak, 2),
         "roofline": {

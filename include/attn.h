@@ -23,6 +23,7 @@
 #define ATTN_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -64,6 +65,14 @@ typedef enum {
 } attn_status;
 
 #define ATTN_MAX_GLOBAL 64
+
+/* Block-sparse layouts (attn_fwd_ex's block_layout): blocks of 64 positions,
+ * at most 128 blocks (8192 positions); row I of a layout holds
+ * ATTN_LAYOUT_WORDS(nb) uint32 words, bit J % 32 of word J / 32 set when query
+ * block I may look at key block J. */
+#define ATTN_SPARSE_BLOCK 64
+#define ATTN_SPARSE_MAX_BLOCKS 128
+#define ATTN_LAYOUT_WORDS(nb) (((nb) + 31) / 32)
 
 /*
  * attn_fwd -- enqueue the attention forward pass on `stream`.
@@ -142,6 +151,15 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o,
  *                 are written as zeros.  Values are clamped to [0, Sq] and
  *                 [0, Skv]; read by the kernel, so a captured launch can be
  *                 replayed with new lengths.
+ *   block_layout  device, nb x ATTN_LAYOUT_WORDS(nb) uint32, nb = ceil(Sq / 64):
+ *                 block-sparse attention ("第 8 章 AI 算法Transformer大模型",
+ *                 section 8.3: sparse patterns, run as block-sparse products
+ *                 per 8.3.4).  Key j is visible from query i only when bit
+ *                 j / 64 of row i / 64 is set, in addition to the mask kind.
+ *                 Needs Sq == Skv <= 8192, mask FULL or CAUSAL, no ALiBi and
+ *                 no lengths (else ATTN_ERR_UNSUPPORTED).  The attn_layout_*
+ *                 builders below write the pages' patterns; any layout works.
+ *                 A query whose row sees no key is written as zeros.
  */
 typedef struct {
   const void* q;
@@ -163,11 +181,39 @@ typedef struct {
   const float* alibi_slopes;  /* device [Hq] fp32, or NULL                */
   const int* q_len;           /* device [B] int32, or NULL (all Sq valid)  */
   const int* kv_len;          /* device [B] int32, or NULL (all Skv valid) */
+  const uint32_t* block_layout; /* device block-sparse layout, or NULL       */
 } attn_fwd_args;
 
 /* Enqueue attn_fwd_ex on `stream`; same return and error conventions as
  * attn_fwd (no allocation, no synchronisation, errors before any launch). */
 int attn_fwd_ex(const attn_fwd_args* args, void* stream);
+
+/*
+ * Block-sparse layout builders (host memory, no device access): write the
+ * nb x ATTN_LAYOUT_WORDS(nb) words of a pattern of "第 8 章 AI 算法Transformer
+ * 大模型", section 8.3, over blocks of ATTN_SPARSE_BLOCK positions.  Return
+ * ATTN_ERR_NULL for a NULL output and ATTN_ERR_SHAPE for nb outside
+ * [1, ATTN_SPARSE_MAX_BLOCKS] or a parameter out of range; `layout` is
+ * caller-owned.
+ *
+ * attn_layout_strided  (8.3.1 strided: a local window plus every stride-th
+ *                      position) query block I sees J <= I with I - J <=
+ *                      local_blocks or I - J a multiple of stride_blocks (>= 1).
+ * attn_layout_fixed    (8.3.1 fixed: the own block plus the same column of the
+ *                      earlier blocks; the page's block is a chunk of
+ *                      chunk_blocks layout blocks, its column a block's place
+ *                      in the chunk) J <= I with J / chunk == I / chunk or
+ *                      J % chunk == I % chunk.
+ * attn_layout_bigbird  (8.3.3 Big Bird: window, random and global) |I - J| <=
+ *                      radius_blocks, or J < n_global_blocks, or I <
+ *                      n_global_blocks, or J one of the n_rand entries of row I
+ *                      of rand_blocks (nb x n_rand host ints in [0, nb): the
+ *                      random draw is the caller's).
+ */
+int attn_layout_strided(int nb, int local_blocks, int stride_blocks, uint32_t* layout);
+int attn_layout_fixed(int nb, int chunk_blocks, uint32_t* layout);
+int attn_layout_bigbird(int nb, int radius_blocks, int n_global_blocks, const int* rand_blocks,
+                        int n_rand, uint32_t* layout);
 
 /* Host-only description of the work attn_fwd would launch for these arguments
  * (the same validation as attn_fwd, no device access).  Counts are per call. */

@@ -41,6 +41,16 @@ def test_ex_pairs_match_oracle(Sq, Skv, mask, window):
 @pytest.mark.parametrize("name", list(workloads.EX_WORKLOADS))
 def test_ex_workload_flops(name):
     w = workloads.EX_WORKLOADS[name]
+    if w.pattern:
+        from oracle import sparse as sp
+
+        nb = w.n_blocks()
+        lay = (sp.strided_layout(nb, *w.pattern_args) if w.pattern == "strided" else
+               sp.fixed_layout(nb, *w.pattern_args) if w.pattern == "fixed" else
+               sp.bigbird_layout(nb, w.pattern_args[0], w.pattern_args[1], w.rand_blocks()))
+        pairs = sp.block_sparse_pairs(w.Sq, lay, 64, w.mask == "causal") * w.B
+        assert bench.ex_effective_flops(w) == 4.0 * w.D * pairs * w.Hq
+        return
     q_len, kv_len = w.lengths_qkv()
     pairs = 0
     for b in range(w.B):
@@ -58,3 +68,19 @@ def test_more_than_one_gpu_is_refused():
 
 def test_max_abs_err():
     assert bench.max_abs_err(np.array([1.0, 2.0]), np.array([1.5, 2.0])) == 0.5
+
+
+@pytest.mark.parametrize("S", [64, 100, 1000, 4096])
+@pytest.mark.parametrize("causal", [False, True])
+def test_layout_pairs_match_oracle(S, causal):
+    """The bench's pair count of a block-sparse layout equals the oracle's."""
+    from oracle import sparse as sp
+
+    nb = sp.n_blocks(S, 64)
+    rng = np.random.default_rng(S)
+    lay = rng.random((nb, nb)) < 0.3
+    words = np.zeros((nb, (nb + 31) // 32), dtype=np.uint32)
+    for I in range(nb):
+        for J in np.nonzero(lay[I])[0]:
+            words[I, J // 32] |= np.uint32(1) << np.uint32(J % 32)
+    assert bench.layout_pairs(words, S, causal) == sp.block_sparse_pairs(S, lay, 64, causal)

@@ -16,6 +16,8 @@ from ._binding import (  # noqa: F401
     MASK_LOCAL_GLOBAL,
     MASKS,
     MAX_GLOBAL,
+    SPARSE_BLOCK,
+    SPARSE_MAX_BLOCKS,
     STATUS,
     AttnError,
     FwdArgs,
@@ -27,6 +29,10 @@ from ._binding import (  # noqa: F401
     fwd_ex,
     fwd_ex_raw,
     fwd_raw,
+    layout_bigbird,
+    layout_fixed,
+    layout_strided,
+    layout_words,
     load,
     plan,
     plan_status,

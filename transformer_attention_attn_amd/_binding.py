@@ -32,7 +32,11 @@ STATUS = {
 }
 
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_plan", "attn_decode", "attn_decode_workspace",
+           "attn_layout_strided", "attn_layout_fixed", "attn_layout_bigbird",
            "attn_status_string", "attn_version")
+
+SPARSE_BLOCK = 64          # positions per block of a block-sparse layout
+SPARSE_MAX_BLOCKS = 128    # longest block-sparse sequence: 8192 positions
 
 
 class AttnError(RuntimeError):
@@ -53,7 +57,7 @@ class FwdArgs(ctypes.Structure):
         ("mask_kind", ctypes.c_int), ("window", ctypes.c_int),
         ("scale", ctypes.c_float), ("dtype", ctypes.c_int),
         ("alibi_slopes", ctypes.c_void_p), ("q_len", ctypes.c_void_p),
-        ("kv_len", ctypes.c_void_p),
+        ("kv_len", ctypes.c_void_p), ("block_layout", ctypes.c_void_p),
     ]
 
 
@@ -99,6 +103,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode.restype = i
     lib.attn_decode_workspace.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
     lib.attn_decode_workspace.restype = i
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    lib.attn_layout_strided.argtypes = [i, i, i, u32p]
+    lib.attn_layout_strided.restype = i
+    lib.attn_layout_fixed.argtypes = [i, i, u32p]
+    lib.attn_layout_fixed.restype = i
+    lib.attn_layout_bigbird.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_int), i, u32p]
+    lib.attn_layout_bigbird.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -175,8 +186,41 @@ def fwd_ex_raw(args: FwdArgs, stream: int) -> int:
     return load().attn_fwd_ex(ctypes.byref(args), stream)
 
 
+def layout_words(nb: int) -> int:
+    return (nb + 31) // 32
+
+
+def _layout_call(fn, nb, *args):
+    import numpy as np
+
+    out = np.zeros((max(nb, 0), layout_words(max(nb, 0))), dtype=np.uint32)
+    st = fn(nb, *args, out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)))
+    if st != 0:
+        raise AttnError(st)
+    return out
+
+
+def layout_strided(nb: int, local_blocks: int, stride_blocks: int):
+    """attn_layout_strided: [nb, words] uint32 bitmask of the strided pattern."""
+    return _layout_call(load().attn_layout_strided, nb, local_blocks, stride_blocks)
+
+
+def layout_fixed(nb: int, chunk_blocks: int):
+    """attn_layout_fixed: [nb, words] uint32 bitmask of the fixed pattern."""
+    return _layout_call(load().attn_layout_fixed, nb, chunk_blocks)
+
+
+def layout_bigbird(nb: int, radius_blocks: int, n_global_blocks: int, rand_blocks):
+    """attn_layout_bigbird: rand_blocks is an [nb, r] integer array (r may be 0)."""
+    import numpy as np
+
+    rb = np.ascontiguousarray(np.asarray(rand_blocks, dtype=np.int32).reshape(max(nb, 0), -1))
+    return _layout_call(load().attn_layout_bigbird, nb, radius_blocks, n_global_blocks,
+                        rb.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), rb.shape[1])
+
+
 def fwd_ex(q, k, v, mask="causal", window: int = 0, scale: Optional[float] = None, out=None,
-           stream=None, alibi_slopes=None, q_len=None, kv_len=None):
+           stream=None, alibi_slopes=None, q_len=None, kv_len=None, block_layout=None):
     """Forward pass with Sq != Skv and strided layouts (bf16).
 
     q: [B, Hq, Sq, D], k, v: [B, Hkv, Skv, D] as torch views of any strides
@@ -185,7 +229,9 @@ def fwd_ex(q, k, v, mask="causal", window: int = 0, scale: Optional[float] = Non
     key position i + Skv - Sq).  Returns o shaped like q (a dense tensor unless
     `out` is given, which may be strided too).  Optional GPU tensors:
     alibi_slopes float32 [Hq] (ALiBi), q_len and kv_len int32 [B] (valid rows
-    and keys per sequence of a right-padded batch; padded rows come out zero).
+    and keys per sequence of a right-padded batch; padded rows come out zero),
+    block_layout int32 [nb, words] (a layout_* bitmask on the GPU: block-sparse
+    attention over blocks of 64 positions).
     """
     import torch
 
@@ -210,13 +256,18 @@ def fwd_ex(q, k, v, mask="causal", window: int = 0, scale: Optional[float] = Non
     for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
         getattr(a, name)[:] = [t.stride(0), t.stride(1), t.stride(2)]
     a.mask_kind, a.window, a.scale, a.dtype = _mask_id(mask), int(window), float(scale), DTYPE_BF16
-    for name, t, dt, n in (("alibi_slopes", alibi_slopes, torch.float32, Hq),
-                           ("q_len", q_len, torch.int32, B), ("kv_len", kv_len, torch.int32, B)):
+    nb = (Sq + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    for name, t, dt, shape in (("alibi_slopes", alibi_slopes, torch.float32, (Hq,)),
+                               ("q_len", q_len, torch.int32, (B,)),
+                               ("kv_len", kv_len, torch.int32, (B,)),
+                               ("block_layout", block_layout, torch.int32,
+                                (nb, layout_words(nb)))):
         if t is None:
             setattr(a, name, None)
             continue
-        if t.dtype != dt or t.device != q.device or tuple(t.shape) != (n,) or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {dt} tensor of {n} on q's device")
+        if t.dtype != dt or t.device != q.device or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {shape} on "
+                             "q's device")
         setattr(a, name, t.data_ptr())
     if stream is None:
         stream = torch.cuda.current_stream(q.device)

@@ -24,6 +24,7 @@ LIB = os.path.join(PKG, "libattn.so")
 # dimension, each object holding only the constants of its own tile shape
 SOURCES = [
     ("attn_api.cpp", "attn_api", []),
+    ("attn_layout.cpp", "attn_layout", []),
     ("kernel_fp32.hip", "kernel_fp32", []),
     ("kernel_bf16.hip", "kernel_bf16_d64", ["-DATTN_HEAD_DIM=64"]),
     ("kernel_bf16.hip", "kernel_bf16_d128", ["-DATTN_HEAD_DIM=128"]),

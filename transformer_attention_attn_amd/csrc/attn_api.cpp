@@ -193,8 +193,14 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
   for (const void* ptr : {a->q, a->k, a->v, (const void*)a->o})
     if ((uintptr_t)ptr % 16 != 0) return ATTN_ERR_ALIGN;
   for (const void* ptr : {(const void*)a->alibi_slopes, (const void*)a->q_len,
-                          (const void*)a->kv_len})
+                          (const void*)a->kv_len, (const void*)a->block_layout})
     if ((uintptr_t)ptr % 4 != 0) return ATTN_ERR_ALIGN;
+  // block-sparse layouts: square, at most ATTN_SPARSE_MAX_BLOCKS blocks, full or
+  // causal mask, no bias or lengths
+  if (a->block_layout &&
+      (a->Sq != a->Skv || a->Sq > ATTN_SPARSE_MAX_BLOCKS * ATTN_SPARSE_BLOCK ||
+       a->mask_kind == ATTN_MASK_CAUSAL_WINDOW || a->alibi_slopes || a->q_len || a->kv_len))
+    return ATTN_ERR_UNSUPPORTED;
   // ALiBi slopes are turned into score units by 1 / |scale|
   if (a->alibi_slopes && a->scale != 0.f && std::fabs(a->scale) < 0x1p-60f) return ATTN_ERR_SCALE;
   const long long* strides[4] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride};
@@ -218,6 +224,10 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
   if ((a->alibi_slopes && overlaps(a->o, no, a->alibi_slopes, (size_t)a->Hq * 4)) ||
       (a->q_len && overlaps(a->o, no, a->q_len, (size_t)a->B * 4)) ||
       (a->kv_len && overlaps(a->o, no, a->kv_len, (size_t)a->B * 4)))
+    return ATTN_ERR_ALIAS;
+  const int lay_nb = (a->Sq + ATTN_SPARSE_BLOCK - 1) / ATTN_SPARSE_BLOCK;
+  const int lay_nw = ATTN_LAYOUT_WORDS(lay_nb);
+  if (a->block_layout && overlaps(a->o, no, a->block_layout, (size_t)lay_nb * lay_nw * 4))
     return ATTN_ERR_ALIAS;
   // o's own rows must be distinct: rows of one head D apart at least, heads and
   // batches not folded onto each other
@@ -245,6 +255,8 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
   p.kvlen = a->kv_len;
   p.slopes = a->alibi_slopes;
   p.alibi_k = a->scale != 0.f ? 1.f / std::fabs(a->scale) : 1.4426950408889634f;
+  p.layout = a->block_layout;
+  p.lay_nw = lay_nw;
   for (int d = 0; d < 3; ++d) {
     p.qs[d] = a->q_stride[d];
     p.ks[d] = a->k_stride[d];

@@ -31,7 +31,12 @@ struct KParams {
   const int* kvlen;      // device, B valid keys per sequence, or null (all Skv)
   const float* slopes;   // device, Hq ALiBi slopes, or null (no bias)
   float alibi_k;         // slope -> score units: 1 / |scale|, or log2(e) for scale 0
+  const unsigned* layout;  // device block-sparse layout (64-position blocks), or null
+  int lay_nw;              // words per layout row
 };
+
+// Longest sequence of a block-sparse call (its tile list lives in registers).
+constexpr int kSparseMaxKeys = 8192;
 
 // Workgroup shapes used by the two kernels.
 constexpr int kF32Rows = 64;   // query rows per fp32 work item (one head)

@@ -199,12 +199,13 @@ constexpr int kWavesPerEu = HD == 64 ? 4 : 2;
 // position i + s.off, element strides for the batch, head and row dimensions
 // of each tensor, optional per-sequence lengths (right padding); the
 // local+global mask is not offered there.  GEN = 2: GEN = 1 plus the ALiBi
-// bias.
+// bias.  GEN = 3: GEN = 1 with a block-sparse layout (square, no lengths).
 template <int D, int MASK, int GEN = 0>
 __global__ __launch_bounds__(kBf16Threads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu, kWavesPerEu)))
 void attn_fwd_bf16(KParams p) {
   using C = Cfg<D>;
   constexpr bool ALIBI = GEN == 2;
+  constexpr bool SPARSE = GEN == 3;
   constexpr int NDC = C::NDC, NDB = C::NDB, ROWB = C::ROWB, REG = C::REG, BUF = C::BUF,
                 NGL = C::NGL, RSTEP = C::RSTEP, NSTAGE = C::NSTAGE, VSH = C::VSH;
 
@@ -299,9 +300,59 @@ void attn_fwd_bf16(KParams p) {
     }
   }
 
+  // ---- block-sparse tile list (GEN = 3) ------------------------------------
+  // The item's key tiles in order, one per lane of lv[c] (64 per register):
+  // the tile index in bits 0-15 and, for each 64-row query block the item
+  // spans (slot = block - first block, at most four), which of the tile's
+  // 64-key halves that block may see, at bits 16 + 2*slot (both bits for a
+  // 64-key tile).  Tiles past the item's last row are left out under the
+  // causal mask.  Every wave builds the same list (no LDS, no barrier).
+  constexpr int NLV = SPARSE ? (kSparseMaxKeys / BN + 63) / 64 : 1;
+  unsigned lv[NLV];
+  int n_lv[NLV];
+  int n_list = 0;
+  const int wslot = (wqa >> 6) - (r0 >> 6);  // this wave's query block slot
+  if constexpr (SPARSE) {
+    const int qb0 = r0 >> 6, nqs = (r1 >> 6) - qb0 + 1;
+    const int nkt = cdiv(SK, BN);
+    const int kt_end = MASK == MASK_CAUSAL ? imin(nkt, r1 / BN + 1) : nkt;
+#pragma unroll
+    for (int c = 0; c < NLV; ++c) {
+      const int kt = c * 64 + lane;
+      unsigned e = 0;
+      if (kt < kt_end) {
+        unsigned codes = 0;
+        for (int sl = 0; sl < nqs; ++sl) {
+          const unsigned* row = p.layout + (size_t)(qb0 + sl) * p.lay_nw;
+          const unsigned cd = BN == 128 ? (row[kt >> 4] >> ((2 * kt) & 31)) & 3u
+                                        : ((row[kt >> 5] >> (kt & 31)) & 1u) * 3u;
+          codes |= cd << (2 * sl);
+        }
+        if (codes) e = (unsigned)kt | (codes << 16);
+      }
+      // lanes holding a tile move to the front in order, the others behind
+      const unsigned long long m = __builtin_amdgcn_ballot_w64(e != 0u);
+      const int below = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+      const int cnt = __builtin_popcountll(m);
+      const int dst = e ? below : cnt + (lane - below);
+      lv[c] = (unsigned)__builtin_amdgcn_ds_permute(dst * 4, (int)e);
+      n_lv[c] = cnt;
+      n_list += cnt;
+    }
+  }
+  // list entry of iteration iter (past the end: the last one; tile 0 if none)
+  auto entry = [&](int iter) -> unsigned {
+    const int t = imax(imin(iter, n_list - 1), 0);
+    if (NLV == 1 || t < n_lv[0]) return (unsigned)__builtin_amdgcn_readlane((int)lv[0], t);
+    return (unsigned)__builtin_amdgcn_readlane((int)lv[NLV - 1], t - n_lv[0]);
+  };
+  auto wave_code = [&](int iter) -> unsigned { return (entry(iter) >> (16 + 2 * wslot)) & 3u; };
+
   // ---- key tiles to visit ------------------------------------------------
-  int klo, khi;
-  if constexpr (GEN) {
+  int klo = 0, khi = -1;
+  if constexpr (SPARSE) {
+  } else if constexpr (GEN) {
     // keys seen by the valid rows r0..r1 at key positions r0 + OFF .. r1 + OFF
     const int pa = r0 + OFF, pb = r1 + OFF;
     klo = MASK == MASK_CAUSAL_WINDOW ? imax(0, pa - s.window + 1) : 0;
@@ -311,8 +362,12 @@ void attn_fwd_bf16(KParams p) {
   }
   const int kt_lo = klo / BN, kt_hi = khi / BN;
   const int has_strip = (MASK == MASK_LOCAL_GLOBAL && !it.is_global && s.n_global > 0) ? 1 : 0;
-  const int n_it = (GEN && (khi < klo || r1 < r0)) ? 0 : (kt_hi - kt_lo + 1) + has_strip;
-  auto tile_kt = [&](int iter) { return kt_lo + iter - has_strip; };
+  const int n_it = SPARSE ? n_list
+                          : (GEN && (khi < klo || r1 < r0)) ? 0 : (kt_hi - kt_lo + 1) + has_strip;
+  auto tile_kt = [&](int iter) -> int {
+    if constexpr (SPARSE) return (int)(entry(iter) & 0xffffu);
+    return kt_lo + iter - has_strip;
+  };
   auto is_strip = [&](int iter) { return MASK == MASK_LOCAL_GLOBAL && has_strip && iter == 0; };
 
   // ---- LDS layout and direct (global -> LDS) tile loads ---------------------
@@ -366,6 +421,7 @@ void attn_fwd_bf16(KParams p) {
   // range, or when it holds no rows) are processed as fully masked.
   auto tile_partial = [&](int iter) -> bool {
     if (!wave_active || is_strip(iter) || wave_pad) return true;
+    if (SPARSE && wave_code(iter) != 3u) return true;  // one 64-key half only
     const int kt = tile_kt(iter);
     if (it.is_global) return kt * BN + BN > s.S;
     return classify_tile(MASK, s.window, SK, wpa, wpb, kt * BN, BN) != TILE_FULL;
@@ -373,6 +429,7 @@ void attn_fwd_bf16(KParams p) {
   auto tile_empty = [&](int j) -> bool {
     if (!wave_active) return true;
     if (is_strip(j)) return false;
+    if (SPARSE && wave_code(j) == 0u) return true;
     return classify_tile(MASK, s.window, SK, wpa, wpb, tile_kt(j) * BN, BN) == TILE_EMPTY;
   };
 
@@ -427,8 +484,14 @@ void attn_fwd_bf16(KParams p) {
     const long long base = (long long)tile_kt(iter) * BN + 4 * hf;
     const long long tail = (long long)SK - 1;
     const long long hi_a = hi < tail ? hi : tail;
-    const int lo_r = (int)(lo - base < -1 ? -1 : (lo - base > BN ? BN : lo - base));
-    const int hi_r = (int)(hi_a - base < -1 ? -1 : (hi_a - base > BN ? BN : hi_a - base));
+    int lo_r = (int)(lo - base < -1 ? -1 : (lo - base > BN ? BN : lo - base));
+    int hi_r = (int)(hi_a - base < -1 ? -1 : (hi_a - base > BN ? BN : hi_a - base));
+    if constexpr (SPARSE && BN == 128) {
+      // the layout lets this wave see one 64-key half of the tile only
+      const unsigned cd = wave_code(iter);
+      if (cd == 1u) hi_r = imin(hi_r, 63 - 4 * hf);
+      else if (cd == 2u) lo_r = imax(lo_r, 64 - 4 * hf);
+    }
 #pragma unroll
     for (int kbk = 0; kbk < NKB; ++kbk)
 #pragma unroll
@@ -868,6 +931,11 @@ void attn_fwd_bf16(KParams p) {
 template <int D>
 hipError_t launch_d(const KParams& p, hipStream_t stream) {
   dim3 grid((unsigned)p.s.n_items), block(kBf16Threads);
+  if (p.general && p.layout) {
+    if (p.s.mask == MASK_FULL) hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_FULL, 3>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL, 3>), grid, block, 0, stream, p);
+    return hipGetLastError();
+  }
   if (p.general && p.slopes) {
     switch (p.s.mask) {
       case MASK_FULL: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_FULL, 2>), grid, block, 0, stream, p); break;

@@ -49,6 +49,14 @@ the keys):
   bias, 32 heads of D=128 ("Transformer 演进与变体", section 线性偏置注意力;
   "Trasformer 浅析", section 填充掩码与因果掩码).  Slopes 2^(-8 (a+1) / 32).
 
+* ``bigbird_bf16_b4_h12_s4096`` -- Big Bird over 64-position blocks: window
+  radius 1 block, 2 global blocks, 3 random blocks per query block, every
+  direction visible; B=4, 12 heads of D=64, S=4096 ("第 8 章 AI 算法
+  Transformer大模型", section 8.3.3 with the block-sparse form of 8.3.4).
+* ``strided_causal_gqa_bf16_s8192`` -- Sparse Transformer strided pattern
+  over 64-position blocks (the own block and 7 before it, plus every 8th
+  block back), causal, the grouped-query head shapes above (section 8.3.1).
+
 Values are iid N(0, 1) from ``numpy.random.default_rng(seed)``, drawn as
 float32 in the order Q, K, V, each shaped [B][H][S][D].  bf16 workloads round
 those draws to nearest-even bf16; the rounded values are what every consumer
@@ -170,6 +178,10 @@ class ExWorkload:
     dtype: str = "bf16"
     alibi: bool = False   # ALiBi with the slopes of alibi_slopes()
     lengths: str = "full"  # "full", or "ragged": per-sequence lengths of lengths()
+    # block-sparse pattern over 64-position blocks: "" (none), "strided" (args:
+    # local, stride), "fixed" (chunk) or "bigbird" (radius, n_global, n_random)
+    pattern: str = ""
+    pattern_args: Tuple[int, ...] = ()
 
     @property
     def scale(self) -> float:
@@ -179,6 +191,15 @@ class ExWorkload:
         """Hq slopes (float32) when alibi is set, else None."""
         return make_alibi_slopes(self.Hq) if self.alibi else None
 
+    def n_blocks(self) -> int:
+        return -(-self.Sq // SPARSE_BLOCK)
+
+    def rand_blocks(self) -> np.ndarray:
+        """Big Bird's random key blocks, [nb][n_random] (an input of the pattern)."""
+        if self.pattern != "bigbird":
+            raise ValueError("only the bigbird pattern draws random blocks")
+        return make_rand_blocks(self.n_blocks(), self.pattern_args[2], self.seed)
+
     def lengths_qkv(self):
         """(q_len, kv_len) int32 arrays of B valid lengths, or (None, None)."""
         if self.lengths == "full":
@@ -187,6 +208,7 @@ class ExWorkload:
 
     def describe(self) -> dict:
         d = dataclasses.asdict(self)
+        d["pattern_args"] = list(self.pattern_args)
         ql, kl = self.lengths_qkv()
         if ql is not None:
             d["q_len"], d["kv_len"] = [int(x) for x in ql], [int(x) for x in kl]
@@ -205,8 +227,24 @@ EX_WORKLOADS = {
         # causal prefill of a right-padded batch with ALiBi instead of positions in q/k
         ExWorkload("alibi_padded_mha_bf16_b8_s4096", 8, 32, 32, 4096, 4096, 128, MASK_CAUSAL,
                    "bhsd", seed=11, alibi=True, lengths="ragged"),
+        # Big Bird: window of 3 blocks, 2 global blocks, 3 random blocks per row
+        ExWorkload("bigbird_bf16_b4_h12_s4096", 4, 12, 12, 4096, 4096, 64, MASK_FULL, "bhsd",
+                   seed=12, pattern="bigbird", pattern_args=(1, 2, 3)),
+        # Sparse Transformer strided pattern on the grouped-query head shapes
+        ExWorkload("strided_causal_gqa_bf16_s8192", 1, 32, 8, 8192, 8192, 128, MASK_CAUSAL,
+                   "bhsd", seed=13, pattern="strided", pattern_args=(7, 8)),
     )
 }
+
+SPARSE_BLOCK = 64  # positions per block of the block-sparse patterns
+
+
+def make_rand_blocks(nb: int, r: int, seed: int) -> np.ndarray:
+    """r random key blocks per query block, uniform over [0, nb), drawn with
+    default_rng(seed + 3000) (Big Bird's random connections; the pages fix no
+    generator, so the draw is an input shared by both sides)."""
+    rng = np.random.default_rng(seed + 3000)
+    return rng.integers(0, nb, size=(nb, r)).astype(np.int32)
 
 
 def make_alibi_slopes(H: int) -> np.ndarray:
