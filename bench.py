@@ -295,8 +295,10 @@ def ex_cpu_baseline(w, inputs, seconds: float = 10.0):
 def time_steps(step, stream, args):
     """Untimed warm-up (about `args.prewarm` seconds of steps, as the GPU clocks
     ramp up over the first ~100 ms of load, then `args.warmup` steps), then
-    `args.steps` steps between two HIP events recorded on the launch stream.
-    Returns (ms per step, prewarm steps)."""
+    `args.steps` back-to-back steps with a HIP event recorded on the launch
+    stream before each step and after the last.  Returns (mean ms per step over
+    the whole timed region, prewarm steps, {"median_ms", "min_ms"} of the
+    single steps)."""
     import torch
 
     t_warm = time.perf_counter()
@@ -309,14 +311,38 @@ def time_steps(step, stream, args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
-    end.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / args.steps, prewarm_steps
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    spread = {"median_ms": round(per[len(per) // 2], 6), "min_ms": round(per[0], 6)}
+    return ev[0].elapsed_time(ev[-1]) / args.steps, prewarm_steps, spread
+
+
+def time_cold(step, stream, n: int, dev, mib: int = 512):
+    """Cold-cache timing: before each of n steps, write a `mib` MiB scratch
+    buffer on the same stream (evicting the caches), then time the step alone
+    between two HIP events.  Returns {"median_ms", "min_ms", "steps", "flush_mib"}."""
+    import torch
+
+    scratch = torch.empty(mib << 18, dtype=torch.float32, device=dev)
+    per = []
+    for i in range(n):
+        scratch.fill_(float(i))
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        b.synchronize()
+        per.append(a.elapsed_time(b))
+    del scratch
+    per.sort()
+    return {"median_ms": round(per[len(per) // 2], 6), "min_ms": round(per[0], 6), "steps": n,
+            "flush_mib": mib}
 
 
 def bench_decode(args, name):
@@ -344,7 +370,7 @@ def bench_decode(args, name):
         attn.decode(q, k, v, cache_len=cl, mask=w.mask, scale=w.scale, out=out, workspace=ws,
                     stream=stream)
 
-    ms, prewarm_steps = time_steps(step, stream, args)
+    ms, prewarm_steps, spread = time_steps(step, stream, args)
     cache_bytes, flops = decode_counts(w, lens)
     qo_bytes = 2 * w.B * w.Hq * w.Sq * w.D * 2
     alg = cache_bytes + qo_bytes
@@ -379,6 +405,7 @@ def bench_decode(args, name):
         },
         "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
         "prewarm_steps": prewarm_steps,
+        "step_spread": spread,
         "gpu": torch.cuda.get_device_name(dev),
     }
     if not args.no_cpu_baseline:
@@ -430,7 +457,7 @@ def bench_ex(args, name):
                     stream=stream, alibi_slopes=slopes_d, q_len=q_len_d, kv_len=kv_len_d,
                     block_layout=layout_d)
 
-    ms, prewarm_steps = time_steps(step, stream, args)
+    ms, prewarm_steps, spread = time_steps(step, stream, args)
     tflops = flops / (ms * 1e-3) / 1e12
     print(f"bench: {ms * 1e3:.1f} us/step, {tflops:.1f} effective TFLOP/s", file=sys.stderr,
           flush=True)
@@ -463,6 +490,7 @@ def bench_ex(args, name):
             "traffic": None,
         },
         "prewarm_steps": prewarm_steps,
+        "step_spread": spread,
         "gpu": torch.cuda.get_device_name(dev),
     }
     if not args.no_cpu_baseline:
@@ -489,6 +517,8 @@ def main(argv=None):
                     help="seconds of untimed steps before the warmup steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache line (steps timed after a 512 MiB cache flush)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one plain elementwise copy of this many MiB (fp32 in, fp32 "
                          "out), whose HBM counters scale the attention kernel's")
@@ -529,13 +559,17 @@ def main(argv=None):
         attn.fwd(q, k, v, mask=w.mask, window=w.window, global_idx=g, scale=w.scale, out=out,
                  stream=stream)
 
-    ms, prewarm_steps = time_steps(step, stream, args)
+    ms, prewarm_steps, spread = time_steps(step, stream, args)
     tflops = flops / (ms * 1e-3) / 1e12
     print(f"bench: {ms * 1e3:.1f} us/step, {tflops:.1f} effective TFLOP/s", file=sys.stderr,
           flush=True)
 
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     traffic = committed_traffic(name)
+    # Q, K, V and O once each (K and V once per key/value head)
+    esz = 2 if w.dtype == "bf16" else 4
+    alg_bytes = (2 * w.B * w.Hq + 2 * w.B * w.Hkv) * w.S * w.D * esz
+    cold = None if args.no_cold else time_cold(step, stream, 20, dev)
     result = {
         "metric": "effective attention TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, 1 GPU",
         "value": round(tflops, 3),
@@ -562,6 +596,11 @@ def main(argv=None):
             "traffic": traffic,
         },
         "prewarm_steps": prewarm_steps,
+        "step_spread": spread,
+        "algorithmic_bytes": alg_bytes,
+        "algorithmic_gbs": round(alg_bytes / (ms * 1e-3) / 1e9, 2),
+        "hbm_bytes_over_algorithmic": None if traffic is None else round(traffic / alg_bytes, 4),
+        "cold_cache": cold,
         "gpu": torch.cuda.get_device_name(dev),
         "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
     }
