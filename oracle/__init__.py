@@ -39,3 +39,8 @@ from .sparse import (  # noqa: F401
     fixed_layout,
     strided_layout,
 )
+from .fp8 import (  # noqa: F401
+    e4m3_decode,
+    fp8_attention,
+    fp8_error_bound,
+)

@@ -1,0 +1,92 @@
+"""fp64 CPU oracle for the FP8 forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or links
+this module; only the tests and the benchmark's CPU-baseline leg do.  It shares
+no code with the HIP path.
+
+What it computes: the FP8 variant of the fused attention that "Transformer 演进
+与变体", section Flash Attention (the FlashAttention-3 paragraph: FP8 for the
+matrix products, softmax and accumulation in BF16/FP32), and "第 8 章 AI 算法
+Transformer大模型", section 8.6.5 (low precision: kernels with an FP8 forward
+pass, per-tensor scale factors) describe: the two matrix products take FP8
+(E4M3) operands while the softmax and the accumulation stay in higher
+precision.  Reading: per-tensor scale factors are the caller's (folded into
+the score scale for q and k, applied to the output for v), so the codes are
+taken at face value.
+
+* The inputs q, k, v are E4M3 codes.  ``e4m3_decode`` is the plain definition
+  of that format (the OCP 8-bit float: 1 sign bit, 4 exponent bits with bias
+  7, 3 mantissa bits, subnormals below 2^-6, no infinities, 0x7F / 0xFF NaN),
+  written from the bit layout.
+* The reference output is exact masked attention (reference.py) on the decoded
+  values: the score product of E4M3 inputs is exact, so the only rounding of
+  the method that the oracle does not carry out is the E4M3 rounding of the
+  softmax weights P before the P.V product (the second product needs FP8
+  operands).
+
+Tolerance, derived from that rounding (reading: P is rounded to nearest,
+relative to whatever reference maximum the kernel holds at that moment):
+with p_j = exp(s_j - max_i s) of a row's visible keys and L = sum_j p_j,
+E4M3 rounding to nearest changes a weight by at most u = 2^-4 of itself in
+the normal range and by at most 2^-10 (half the smallest subnormal) below it;
+a kernel whose reference maximum is lower than the row's maximum holds the
+same weights multiplied by a power of two >= 1, so in units of p_j the error
+stays within e_j = u p_j + 2^-10.  With the denominator summed from the
+unrounded weights, O - O_exact = sum_j (p~_j - p_j) v_j / L, hence
+
+    |O - O_exact| <= b = sum_j e_j |v_j| / L,
+
+plus the bf16 rounding of the output (2^-9 |O|) and fp32 accumulation
+(far below both).  ``fp8_error_bound`` returns b per output element.
+
+Pinned by tests/test_oracle_fp8.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import reference
+
+U_E4M3 = 2.0 ** -4          # relative rounding bound in the normal range
+ABS_E4M3 = 2.0 ** -10       # absolute rounding bound below it
+
+
+def e4m3_decode(codes):
+    """Values (float64) of E4M3 codes (uint8 array)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    normal = sign * (1.0 + m / 8.0) * np.exp2(e - 7.0)
+    sub = sign * (m / 8.0) * 2.0 ** -6
+    val = np.where(e == 0, sub, normal)
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def fp8_attention(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=None):
+    """Exact masked attention (float64) on the decoded E4M3 inputs."""
+    return reference.attention(e4m3_decode(q_codes), e4m3_decode(k_codes), e4m3_decode(v_codes),
+                               kind, window, (), scale=scale, rows=rows)
+
+
+def fp8_error_bound(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=None):
+    """Per-element bound b (float64, shaped like the output) on the error the
+    E4M3 rounding of P can cause."""
+    q = e4m3_decode(q_codes)
+    k = e4m3_decode(k_codes)
+    v = e4m3_decode(v_codes)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((B, Hq, rows.size, D), dtype=np.float64)
+    for b in range(B):
+        for a in range(Hq):
+            h = reference.kv_head(a, Hq, Hkv)
+            w = reference.weights(q[b, a, rows], k[b, h], rows, kind, window, (), scale)
+            wmax = w.max(axis=1, keepdims=True)
+            # w = p / L with p_max = 1, so p = w / wmax and 1 / L = wmax
+            e = np.where(w > 0, U_E4M3 * w + ABS_E4M3 * wmax, 0.0)
+            out[b, a] = e @ np.abs(v[b, h])
+    return out
