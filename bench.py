@@ -46,6 +46,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_FP32_TFLOPS = 157.3   # vector fp32
+PEAK_FP8_TFLOPS = 5033.2   # 256 CU x 2.4 GHz x 8192 dense FP8 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 KERNEL_SOURCES = ("kernel_bf16.hip", "gfx950_ops.h", "attn_kernels.h", "attn_sched.h")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_causal_gqa_s8192_hbm_traffic.md")
@@ -546,7 +547,8 @@ def main(argv=None):
     print(f"bench: workload {name} {w.describe()}", file=sys.stderr, flush=True)
     inputs = workloads.workload_inputs(w)
     q, k, v = workloads.to_torch(inputs, w.dtype, dev)
-    out = torch.empty_like(q)
+    out = torch.empty(q.shape, dtype=torch.float32 if w.dtype == "fp32" else torch.bfloat16,
+                      device=dev)
     g = list(w.global_idx) or None
     plan = attn.plan(w.B, w.Hq, w.Hkv, w.S, w.D, w.mask, w.window, g, w.dtype)
     flops = plan["effective_flops"]
@@ -564,11 +566,12 @@ def main(argv=None):
     print(f"bench: {ms * 1e3:.1f} us/step, {tflops:.1f} effective TFLOP/s", file=sys.stderr,
           flush=True)
 
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    peak = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS}.get(w.dtype, PEAK_FP32_TFLOPS)
     traffic = committed_traffic(name)
     # Q, K, V and O once each (K and V once per key/value head)
-    esz = 2 if w.dtype == "bf16" else 4
-    alg_bytes = (2 * w.B * w.Hq + 2 * w.B * w.Hkv) * w.S * w.D * esz
+    esz = {"bf16": 2, "fp8": 1}.get(w.dtype, 4)
+    osz = 4 if w.dtype == "fp32" else 2
+    alg_bytes = (w.B * w.Hq * esz + 2 * w.B * w.Hkv * esz + w.B * w.Hq * osz) * w.S * w.D
     cold = None if args.no_cold else time_cold(step, stream, 20, dev)
     result = {
         "metric": "effective attention TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, 1 GPU",

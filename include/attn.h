@@ -45,7 +45,18 @@ typedef enum {
  * on the matrix cores; softmax statistics are fp32; the attention weights are
  * rounded to bf16 (nearest even) before the P.V product; o is rounded once to
  * bf16 at the end.  fp32 inputs are computed entirely in fp32. */
-typedef enum { ATTN_DTYPE_FP32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
+typedef enum {
+  ATTN_DTYPE_FP32 = 0,
+  ATTN_DTYPE_BF16 = 1,
+  /* q, k, v as OCP E4M3 bytes, o as bf16: attn_fwd only, D = 128, masks FULL,
+   * CAUSAL and CAUSAL_WINDOW ("Transformer 演进与变体", section Flash
+   * Attention, the FlashAttention-3 paragraph: FP8 operands for both matrix
+   * products, softmax and accumulation in higher precision).  Both products
+   * run on the FP8 matrix cores with fp32 accumulation; P is rounded to E4M3
+   * (nearest even) for the second.  Per-tensor scale factors stay with the
+   * caller: fold q's and k's into `scale`, multiply o by v's. */
+  ATTN_DTYPE_FP8_E4M3 = 2
+} attn_dtype;
 
 typedef enum {
   ATTN_OK = 0,
@@ -226,7 +237,8 @@ typedef struct {
   int rows_per_item;         /* query rows per head per work item                   */
   int heads_per_item;        /* query heads of one key/value head per work item     */
   int keys_per_tile;         /* keys per tile                                       */
-  int kernel;                /* 0 = fp32 kernel, 1 = bf16 matrix-core kernel         */
+  int kernel;                /* 0 = fp32 kernel, 1 = bf16 matrix-core kernel,
+                                2 = FP8 matrix-core kernel                           */
 } attn_plan_info;
 
 /* Fills *info for the given arguments; returns the same status attn_fwd would

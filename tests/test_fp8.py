@@ -1,0 +1,120 @@
+"""FP8 (E4M3) forward pass against the FP8 oracle.
+
+GPU cases compare every output element with oracle.fp8_attention (exact
+attention on the decoded E4M3 inputs, fp64) within the per-element bound
+oracle.fp8_error_bound derives for the method's rounding of P to E4M3, plus
+the bf16 rounding of the output: |O - O_exact| <= b + 2^-8 |O_exact| + 1e-3.
+With all queries zero every visible weight is exactly 1, so the output is the
+mean of the visible value rows and must match to the output's bf16 rounding:
+that case checks masks, tiles and the head mapping tightly.  Host-only cases
+check the validation.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+attn = pytest.importorskip("transformer_attention_attn_amd")
+
+
+def fp8_inputs(B, Hq, Hkv, S, seed, zero_q=False):
+    inp = workloads.make_inputs(B, Hq, Hkv, S, 128, "fp8", seed)
+    if zero_q:
+        inp["q_codes"][:] = 0
+        inp["q"][:] = 0.0
+    return inp
+
+
+def run_fp8(device, B, Hq, Hkv, S, mask, window=0, seed=0, scale=None, zero_q=False, rows=None):
+    import torch
+
+    print(f"fp8 case B={B} Hq={Hq} Hkv={Hkv} S={S} {mask} w={window} seed={seed} scale={scale} "
+          f"zero_q={zero_q}", flush=True)
+    inp = fp8_inputs(B, Hq, Hkv, S, seed, zero_q)
+    q, k, v = workloads.to_torch(inp, "fp8", device)
+    o = attn.fwd(q, k, v, mask=mask, window=window, scale=scale)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16
+    got = o.float().cpu().numpy().astype(np.float64)
+    codes = (inp["q_codes"], inp["k_codes"], inp["v_codes"])
+    ref = oracle.fp8_attention(*codes, mask, window, scale=scale, rows=rows)
+    if rows is not None:
+        got = got[:, :, rows]
+    assert np.all(np.isfinite(got))
+    if zero_q:
+        return got, ref, 2.0 ** -8 * np.abs(ref) + 1e-6
+    bound = oracle.fp8_error_bound(*codes, mask, window, scale=scale, rows=rows)
+    return got, ref, bound + 2.0 ** -8 * np.abs(ref) + 1e-3
+
+
+def check(got, ref, tol):
+    err = np.abs(got - ref)
+    worst = float(np.max(err / tol))
+    assert worst <= 1.0, (worst, float(err.max()))
+    return worst
+
+
+SWEEP = []
+_rng = np.random.default_rng(94)
+for S in (1, 64, 127, 128, 129, 300, 1000, 2049):
+    for mask in ("full", "causal", "causal_window"):
+        Hq, Hkv = [(8, 2), (4, 4), (8, 1), (16, 2)][int(_rng.integers(4))]
+        window = int(_rng.choice([1, 100, 300])) if mask == "causal_window" else 0
+        SWEEP.append((1 + int(_rng.integers(2)), Hq, Hkv, S, mask, window))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"S{c[3]}-{c[4]}-H{c[1]}x{c[2]}")
+def test_fp8_sweep(device, case):
+    B, Hq, Hkv, S, mask, window = case
+    worst = check(*run_fp8(device, B, Hq, Hkv, S, mask, window, seed=S + Hq))
+    print(f"worst error / tolerance {worst:.3f}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", SWEEP[::2], ids=lambda c: f"S{c[3]}-{c[4]}-H{c[1]}x{c[2]}")
+def test_fp8_zero_queries_exact_means(device, case):
+    B, Hq, Hkv, S, mask, window = case
+    check(*run_fp8(device, B, Hq, Hkv, S, mask, window, seed=S + 7, zero_q=True))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.3])
+def test_fp8_scales(device, scale):
+    check(*run_fp8(device, 1, 8, 2, 700, "causal", seed=5, scale=scale))
+
+
+@pytest.mark.gpu
+def test_fp8_workload_full_size(device):
+    """The FP8 workload at full size, sampled rows, in the benchmark's launch
+    configuration."""
+    w = workloads.WORKLOADS["causal_gqa_fp8_s8192"]
+    rows = [0, 1, 127, 128, 4095, 4096, 8190, 8191]
+    got, ref, tol = run_fp8(device, w.B, w.Hq, w.Hkv, w.S, w.mask, seed=w.seed, rows=rows)
+    print(f"fp8 full size: worst error / tolerance {check(got, ref, tol):.3f}", flush=True)
+
+
+# ----------------------------------------------------------------------------
+# host-only
+# ----------------------------------------------------------------------------
+
+FAKE = 0x100000
+
+
+def fp8_status(D=128, mask="causal", window=0, g=None, ptrs=(FAKE, FAKE * 3, FAKE * 5, FAKE * 7),
+               S=1000):
+    q, k, v, o = ptrs
+    return attn.status_string(attn.fwd_raw(q, k, v, o, 1, 8, 2, S, D, mask, window, g, 0.1,
+                                           attn.DTYPE_FP8, 0))
+
+
+def test_fp8_validation():
+    assert fp8_status(D=64) == "ATTN_ERR_UNSUPPORTED"
+    assert fp8_status(mask="local_global", window=10, g=[0]) == "ATTN_ERR_UNSUPPORTED"
+    assert fp8_status(ptrs=(FAKE + 8, FAKE * 3, FAKE * 5, FAKE * 7)) == "ATTN_ERR_ALIGN"
+    # o (bf16, 2 bytes per element) overlapping the end of q (1 byte per element)
+    nq = 8 * 1000 * 128
+    assert fp8_status(ptrs=(FAKE, FAKE * 3, FAKE * 5, FAKE + nq - 16)) == "ATTN_ERR_ALIAS"
+    info = attn.plan(1, 32, 8, 8192, 128, "causal", dtype="fp8")
+    assert info["kernel"] == 2 and info["keys_per_tile"] == 128

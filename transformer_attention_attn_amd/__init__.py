@@ -8,6 +8,7 @@ ctypes binding over it.  Build it with
 from ._binding import (  # noqa: F401
     DTYPE_BF16,
     DTYPE_FP32,
+    DTYPE_FP8,
     EXPORTS,
     LIB_PATH,
     MASK_CAUSAL,

@@ -14,7 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn.so")
 
 MASK_FULL, MASK_CAUSAL, MASK_CAUSAL_WINDOW, MASK_LOCAL_GLOBAL = 0, 1, 2, 3
-DTYPE_FP32, DTYPE_BF16 = 0, 1
+DTYPE_FP32, DTYPE_BF16, DTYPE_FP8 = 0, 1, 2
 MAX_GLOBAL = 64
 
 MASKS = {
@@ -145,16 +145,19 @@ def fwd(q, k, v, mask="causal", window: int = 0, global_idx=None, scale: Optiona
         out=None, stream=None):
     """Attention forward on torch device tensors.
 
-    q: [B, Hq, S, D], k, v: [B, Hkv, S, D], contiguous, bf16 or fp32, on the GPU.
+    q: [B, Hq, S, D], k, v: [B, Hkv, S, D], contiguous, bf16, fp32 or FP8
+    (torch.float8_e4m3fn: E4M3 codes; the output is then bf16), on the GPU.
     Returns o shaped like q (allocated with torch unless `out` is given).
     The kernel runs on `stream` (default: torch's current stream).
     """
     import torch
 
     if q.dtype == torch.bfloat16:
-        dt = DTYPE_BF16
+        dt, odt = DTYPE_BF16, torch.bfloat16
     elif q.dtype == torch.float32:
-        dt = DTYPE_FP32
+        dt, odt = DTYPE_FP32, torch.float32
+    elif q.dtype == torch.float8_e4m3fn:
+        dt, odt = DTYPE_FP8, torch.bfloat16
     else:
         raise TypeError(f"unsupported dtype {q.dtype}")
     for t in (q, k, v):
@@ -165,9 +168,9 @@ def fwd(q, k, v, mask="causal", window: int = 0, global_idx=None, scale: Optiona
     if tuple(k.shape) != (B, Hkv, S, D) or tuple(v.shape) != (B, Hkv, S, D):
         raise ValueError("k, v must be [B, Hkv, S, D] matching q")
     if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped like q")
+        out = torch.empty(q.shape, dtype=odt, device=q.device)
+    elif out.shape != q.shape or out.dtype != odt or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {odt} tensor shaped like q")
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
     if stream is None:
@@ -285,8 +288,8 @@ def plan(B: int, Hq: int, Hkv: int, S: int, D: int, mask="causal", window: int =
     lib = load()
     garr, ng = _globals(global_idx)
     info = PlanInfo()
-    st = lib.attn_plan(B, Hq, Hkv, S, D, _mask_id(mask), window, garr, ng,
-                       DTYPE_BF16 if dtype == "bf16" else DTYPE_FP32, ctypes.byref(info))
+    dt = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32, "fp8": DTYPE_FP8}[dtype]
+    st = lib.attn_plan(B, Hq, Hkv, S, D, _mask_id(mask), window, garr, ng, dt, ctypes.byref(info))
     if st != 0:
         raise AttnError(st)
     return info.as_dict()

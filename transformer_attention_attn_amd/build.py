@@ -29,6 +29,7 @@ SOURCES = [
     ("kernel_bf16.hip", "kernel_bf16_d64", ["-DATTN_HEAD_DIM=64"]),
     ("kernel_bf16.hip", "kernel_bf16_d128", ["-DATTN_HEAD_DIM=128"]),
     ("kernel_decode.hip", "kernel_decode", []),
+    ("kernel_fp8.hip", "kernel_fp8", []),
 ]
 ARCH = "gfx950"
 

@@ -30,8 +30,16 @@ Checked check_args(int B, int Hq, int Hkv, int S, int D, int mask_kind, int wind
   Checked c{};
   c.status = ATTN_OK;
   if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || (long long)S > kMaxS) { c.status = ATTN_ERR_SHAPE; return c; }
-  if (dtype != ATTN_DTYPE_FP32 && dtype != ATTN_DTYPE_BF16) { c.status = ATTN_ERR_UNSUPPORTED; return c; }
+  if (dtype != ATTN_DTYPE_FP32 && dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP8_E4M3) {
+    c.status = ATTN_ERR_UNSUPPORTED;
+    return c;
+  }
   if (D != 64 && D != 128) { c.status = ATTN_ERR_UNSUPPORTED; return c; }
+  // FP8: D = 128, masks without global tokens
+  if (dtype == ATTN_DTYPE_FP8_E4M3 && (D != 128 || mask_kind == ATTN_MASK_LOCAL_GLOBAL)) {
+    c.status = ATTN_ERR_UNSUPPORTED;
+    return c;
+  }
   if (mask_kind < ATTN_MASK_FULL || mask_kind > ATTN_MASK_LOCAL_GLOBAL) { c.status = ATTN_ERR_UNSUPPORTED; return c; }
   if (Hq % Hkv != 0) { c.status = ATTN_ERR_HEADS; return c; }
   // total elements and the flat index of the last element must fit in 63 bits
@@ -157,9 +165,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq
   if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
   for (const void* ptr : {q, k, v, (const void*)o})
     if ((uintptr_t)ptr % 16 != 0) return ATTN_ERR_ALIGN;
-  const size_t esz = dtype == ATTN_DTYPE_BF16 ? 2 : 4;
+  // element sizes of the inputs and of the output (FP8 writes bf16)
+  const size_t esz = dtype == ATTN_DTYPE_FP32 ? 4 : dtype == ATTN_DTYPE_BF16 ? 2 : 1;
+  const size_t osz = dtype == ATTN_DTYPE_FP32 ? 4 : 2;
   const size_t nq = (size_t)B * Hq * S * D * esz, nkv = (size_t)B * Hkv * S * D * esz;
-  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
+  const size_t no = (size_t)B * Hq * S * D * osz;
+  if (overlaps(o, no, q, nq) || overlaps(o, no, k, nkv) || overlaps(o, no, v, nkv))
     return ATTN_ERR_ALIAS;
 
   KParams p{};
@@ -172,7 +183,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq
   std::copy(c.gpos, c.gpos + c.n_global, p.gpos);
 
   hipStream_t st = (hipStream_t)stream;
-  hipError_t err = dtype == ATTN_DTYPE_BF16 ? (D == 64 ? attn::launch_bf16_d64(p, st) : attn::launch_bf16_d128(p, st)) : attn::launch_fp32(p, D, st);
+  hipError_t err = dtype == ATTN_DTYPE_BF16
+                       ? (D == 64 ? attn::launch_bf16_d64(p, st) : attn::launch_bf16_d128(p, st))
+                   : dtype == ATTN_DTYPE_FP8_E4M3 ? attn::launch_fp8_d128(p, st)
+                                                  : attn::launch_fp32(p, D, st);
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -279,7 +293,7 @@ int attn_plan(int B, int Hq, int Hkv, int S, int D, int mask_kind, int window,
   r.rows_per_item = s.BMh;
   r.heads_per_item = s.HP;
   r.keys_per_tile = s.BN;
-  r.kernel = dtype == ATTN_DTYPE_BF16 ? 1 : 0;
+  r.kernel = dtype == ATTN_DTYPE_BF16 ? 1 : dtype == ATTN_DTYPE_FP8_E4M3 ? 2 : 0;
   // Walk one pair's items (all pairs are alike) and scale by the pair count.
   long long visits = 0, partial = 0;
   for (long long id = 0; id < s.n_items; id += s.P) {

@@ -1,0 +1,369 @@
+// kernel_fp8.hip -- FP8 (E4M3) fused attention forward on gfx950 matrix cores.
+//
+// The FP8 variant of the tiled online-softmax attention ("Transformer 演进与变
+// 体", section Flash Attention, the FlashAttention-3 paragraph: FP8 operands for
+// the two matrix products, softmax and accumulation in higher precision):
+//   * S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit
+//     scales, fp32 accumulation): 64 dims per instruction.
+//   * Online softmax in fp32, as in the bf16 kernel (log2 units, lazy rescale,
+//     denominator summed from the fp32 weights).
+//   * P is rounded to E4M3 (v_cvt_pk_fp8_f32, round to nearest even; P <= 2^8
+//     stays far below the E4M3 maximum) and O^T += V^T P^T runs on the same
+//     instruction, 64 keys per instruction; O is accumulated in fp32 and
+//     written as bf16.
+//
+// gfx950 operand layouts used (checked on the hardware): for the 32x32x64
+// FP8 product, lane l holds row (A) or column (B) l % 32 and the 32
+// consecutive k indices 32 * (l / 32) + [0, 32), one byte each; the fp32
+// accumulator is that of every 32x32 product (lane l: column l % 32, rows
+// 8 * (r / 4) + 4 * (l / 32) + r % 4 of register r).  ds_read_b64_tr_b8: in
+// each 16-lane group, lane 8h + i receives byte i of the 8-byte rows read by
+// the group's lanes 2m + h, m = 0..7, in that order.
+//
+// Key order.  The A operand of S^T takes K row kappa(rho) for accumulator row
+// rho = 8q + 4h + t, with kappa(rho) = 16h + 4q + t, so register r of a 32-key
+// block holds key 16 * (l / 32) + r: each lane owns 16 consecutive keys.  For
+// O^T += V^T P^T over 64 keys (blocks 2s, 2s+1) the B operand is then the lane's
+// own 32 weights in register order, and the V^T operand reads, for each of its
+// four 8-byte transposed reads t, the eight keys 64s + 32(t/2) + 16(l/32) +
+// 8(t%2) + [0, 8) of its dimension.
+//
+// Workgroup: eight waves of 32 query rows (query heads of a key/value head
+// packed as in the bf16 kernel), 128-key tiles, K and V tiles loaded straight
+// into LDS (two stages), one tile ahead.  All waves run the same step (S,
+// softmax, P.V) between two barriers per tile.
+//
+// LDS swizzles (16-byte chunks of the 128-byte rows): K chunk c of row r sits
+// at c ^ g(r), g(r) = ((r >> 1) & 3) | (((r >> 4) & 1) << 2), so the 16 rows a
+// 16-lane pass of the K operand reads hit 16 distinct bank groups; V chunk c
+// at c ^ (2 * ((r >> 1) & 3)), so the 32 eight-byte pieces a pass of the
+// transposed reads touches are distinct.
+#include "attn_kernels.h"
+#include "gfx950_ops.h"
+
+namespace attn {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int F8_D = 128;                 // head dimension
+constexpr int F8_BN = 128;                // keys per tile
+constexpr int F8_ROWB = F8_D;             // bytes per K or V row
+constexpr int F8_REG = F8_BN * F8_ROWB;   // one K or V tile (16 KB)
+constexpr int F8_NSTAGE = 2;
+constexpr int F8_LOADS = F8_REG / 1024 / kBf16Waves;  // 1 KiB direct loads per wave per tile
+constexpr float kLazyF8 = 8.f;
+static_assert(F8_LOADS * kBf16Waves * 1024 == F8_REG, "tile split into 1 KiB loads");
+
+__device__ __forceinline__ int kswz(int row) { return ((row >> 1) & 3) | (((row >> 4) & 1) << 2); }
+__device__ __forceinline__ int vswz(int row) { return 2 * ((row >> 1) & 3); }
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Two 16-byte LDS reads at a0 + OFF and a1 + OFF (a 32-byte A operand), as
+// inline asm waited for explicitly (the compiler would otherwise wait for the
+// direct loads in flight before every LDS read).
+template <int OFF>
+__device__ __forceinline__ i32x8 lds_read32(unsigned a0, unsigned a1) {
+  u32x4 lo, hi;
+  asm volatile("ds_read_b128 %0, %2 offset:%4\n\tds_read_b128 %1, %3 offset:%4"
+               : "=&v"(lo), "=&v"(hi) : "v"(a0), "v"(a1), "i"(OFF));
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+// Four transposed 8-byte reads at base + O0..O3 (a 32-byte V^T operand).
+template <int O0, int O1, int O2, int O3>
+__device__ __forceinline__ i32x8 lds_tr8x4(unsigned base) {
+  u32x2 r0, r1, r2, r3;
+  asm volatile("ds_read_b64_tr_b8 %0, %4 offset:%5\n\tds_read_b64_tr_b8 %1, %4 offset:%6\n\t"
+               "ds_read_b64_tr_b8 %2, %4 offset:%7\n\tds_read_b64_tr_b8 %3, %4 offset:%8"
+               : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+               : "v"(base), "i"(O0), "i"(O1), "i"(O2), "i"(O3));
+  return i32x8{(int)r0[0], (int)r0[1], (int)r1[0], (int)r1[1], (int)r2[0], (int)r2[1], (int)r3[0], (int)r3[1]};
+}
+template <int N>
+__device__ __forceinline__ void lds_wait8(i32x8& f) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f) : "i"(N));
+}
+
+// S^T = K Q^T, 32-key blocks KBK..3 (two 64-dim MFMAs each).  On entry op[0]
+// holds the reads of (KBK, dim step 0) in flight; a_dc_c are the per-lane K
+// read addresses of dim step dc, chunk c (block 0).
+template <int KBK>
+__device__ __forceinline__ void s_blocks(i32x8 (&op)[2], unsigned a00, unsigned a01, unsigned a10,
+                                         unsigned a11, const i32x8 (&qf)[2], f32x16 (&sc)[4]) {
+  constexpr int OFF = KBK * 32 * F8_ROWB;
+  op[1] = lds_read32<OFF>(a10, a11);
+  lds_wait8<2>(op[0]);
+  sc[KBK] = mfma_fp8(op[0], qf[0], f32x16{});
+  if constexpr (KBK < 3) {
+    op[0] = lds_read32<OFF + 32 * F8_ROWB>(a00, a01);
+    lds_wait8<2>(op[1]);
+  } else {
+    lds_wait8<0>(op[1]);
+  }
+  sc[KBK] = mfma_fp8(op[1], qf[1], sc[KBK]);
+  if constexpr (KBK < 3) s_blocks<KBK + 1>(op, a00, a01, a10, a11, qf, sc);
+}
+
+// Row offset (bytes) of transposed read t of 64-key step SK.
+constexpr int vrow_off(int SK, int t) { return (64 * SK + 32 * (t >> 1) + 8 * (t & 1)) * F8_ROWB; }
+
+// O^T += V^T P^T, steps I..7 (I = 2 * dim block + key step).  On entry vo[I & 1]
+// holds the reads of step I in flight; vbase[db] is the per-lane V^T read base
+// of dim block db.
+template <int I>
+__device__ __forceinline__ void pv_steps(i32x8 (&vo)[2], const unsigned (&vbase)[4],
+                                         const i32x8 (&pf)[2], f32x16 (&oacc)[4]) {
+  constexpr int DB = I >> 1, SK = I & 1;
+  if constexpr (I < 7) {
+    constexpr int ND = (I + 1) >> 1, NS = (I + 1) & 1;
+    vo[(I + 1) & 1] = lds_tr8x4<vrow_off(NS, 0), vrow_off(NS, 1), vrow_off(NS, 2), vrow_off(NS, 3)>(vbase[ND]);
+    lds_wait8<4>(vo[I & 1]);
+  } else {
+    lds_wait8<0>(vo[I & 1]);
+  }
+  oacc[DB] = mfma_fp8(vo[I & 1], pf[SK], oacc[DB]);
+  if constexpr (I < 7) pv_steps<I + 1>(vo, vbase, pf, oacc);
+}
+
+template <int MASK>
+__global__ __launch_bounds__(kBf16Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_fp8(KParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[F8_NSTAGE * 2 * F8_REG];
+  const Sched& s = p.s;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+  const Item it = decode_item(s, blockIdx.x);
+
+  // ---- rows of this wave ------------------------------------------------
+  const int wph = kBf16Waves / s.HP;
+  const int a = it.kvh * s.G + it.hg * s.HP + wave / wph;
+  const int rpart = wave % wph;
+  const int r0 = it.blk * s.BMh;
+  const int r1 = imin(r0 + s.BMh, s.S) - 1;
+  const int q0 = r0 + rpart * 32;
+  const int q_row = q0 + l32;
+  const bool row_valid = q_row < s.S;
+  const int wqa = q0, wqb = imin(q0 + 31, s.S - 1);
+  const bool wave_active = wqa <= wqb;
+
+  const size_t S = (size_t)s.S;
+  const unsigned char* qp = (const unsigned char*)p.q + (size_t)(it.b * s.Hq + a) * S * F8_D;
+  const unsigned char* kp = (const unsigned char*)p.k + (size_t)(it.b * s.Hkv + it.kvh) * S * F8_D;
+  const unsigned char* vp = (const unsigned char*)p.v + (size_t)(it.b * s.Hkv + it.kvh) * S * F8_D;
+
+  // ---- Q^T operand: lane holds query q_row, dims 64*dc + 32*hf + [0, 32) ----
+  i32x8 qf[2];
+  {
+    const unsigned flip = p.qmode == 1 ? 0x80808080u : 0u;
+    const bool zero = p.qmode == 2 || !row_valid;
+#pragma unroll
+    for (int dc = 0; dc < 2; ++dc) {
+      u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+      if (!zero) {
+        const unsigned char* src = qp + (size_t)q_row * F8_D + dc * 64 + hf * 32;
+        x0 = *(const u32x4*)src;
+        x1 = *(const u32x4*)(src + 16);
+      }
+      x0 ^= flip;
+      x1 ^= flip;
+      qf[dc] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                     (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+    }
+  }
+
+  // ---- key tiles --------------------------------------------------------
+  int klo, khi;
+  key_range(s, 0, r0, r1, &klo, &khi);
+  const int kt_lo = klo / F8_BN, kt_hi = khi / F8_BN;
+  const int n_it = kt_hi - kt_lo + 1;
+
+  // Direct loads: load n of wave w fills 1 KiB slot sl = w * F8_LOADS + n of
+  // the tile, lane l the 16-byte chunk at row 8 * sl + l / 8, physical chunk
+  // l % 8 (its source: that row's logical chunk).  Rows past S repeat the
+  // last row (their scores are masked).
+  const int drow = lane >> 3, dphys = lane & 7;
+  auto dma_tile = [&](int iter, int st) {
+    const int kt = kt_lo + iter;
+#pragma unroll
+    for (int n = 0; n < F8_LOADS; ++n) {
+      const int trow = 8 * (wave * F8_LOADS + n) + drow;
+      const int row = imin(kt * F8_BN + trow, s.S - 1);
+      unsigned char* kd = smem + st * 2 * F8_REG + (wave * F8_LOADS + n) * 1024;
+      dma16_global(kp + (size_t)row * F8_ROWB + 16 * (dphys ^ kswz(trow)), kd);
+      dma16_global(vp + (size_t)row * F8_ROWB + 16 * (dphys ^ vswz(trow)), kd + F8_REG);
+    }
+  };
+
+  auto tile_class = [&](int iter) -> int {
+    if (!wave_active) return TILE_EMPTY;
+    return classify_tile(MASK, s.window, s.S, wqa, wqb, (kt_lo + iter) * F8_BN, F8_BN);
+  };
+
+  // ---- per-lane LDS read offsets ------------------------------------------
+  // K operand (key block kbk, dim step dc): row 32*kbk + kappa(l32), logical
+  // chunks 4*dc + 2*hf and + 1 (the block adds an immediate 32*kbk rows: the
+  // swizzle depends on row bits 1, 2 and 4 only).
+  const int krow = 16 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3);
+  int k_off[2][2];
+#pragma unroll
+  for (int dc = 0; dc < 2; ++dc)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) k_off[dc][c] = krow * F8_ROWB + 16 * ((4 * dc + 2 * hf + c) ^ kswz(krow));
+  // V^T operand (dim block db, key step sk, read t): this lane addresses row
+  // 64*sk + 32*(t/2) + 16*(grp/2) + 8*(t%2) + m, 8-byte piece 2*(grp%2) + h +
+  // 4*db, with grp = lane / 16, m = (lane % 16) / 2, h = lane % 2.  The row's
+  // bits 1-2 are m's, so the swizzle (pieces ^ 4*((row >> 1) & 3)) is per lane
+  // and the (sk, t) part is an immediate row offset.
+  const int grp = lane >> 4, vm = (lane & 15) >> 1, vh = lane & 1;
+  int v_off[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    v_off[db] = F8_REG + (16 * (grp >> 1) + vm) * F8_ROWB +
+                8 * (2 * (grp & 1) + vh + 4 * (db ^ ((vm >> 1) & 3)));
+
+  // ---- accumulators ------------------------------------------------------
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_run = -INFINITY;
+  float l_run0 = 0.f, l_run1 = 0.f;
+  const float c = p.c;
+
+  // ---- prologue -------------------------------------------------------
+  dma_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads landed
+  __syncthreads();
+
+  for (int j = 0; j < n_it; ++j) {
+    const int st = j & 1;
+    if (j + 1 < n_it) dma_tile(j + 1, st ^ 1);  // stage st^1 was last read in step j-1
+    const int cls = tile_class(j);
+    if (cls != TILE_EMPTY) {
+      const unsigned kb = lds_addr(smem + st * 2 * F8_REG);
+      // S^T = K Q^T: four 32-key blocks, two 64-dim steps each
+      f32x16 sc[4];
+      i32x8 op[2];
+      {
+        const unsigned a00 = kb + k_off[0][0], a01 = kb + k_off[0][1];
+        const unsigned a10 = kb + k_off[1][0], a11 = kb + k_off[1][1];
+        op[0] = lds_read32<0>(a00, a01);
+        s_blocks<0>(op, a00, a01, a10, a11, qf, sc);
+      }
+
+      // mask (partial tiles): register r of block kbk holds key
+      // 32*kbk + 16*hf + r of the tile
+      if (cls == TILE_PARTIAL) {
+        long long lo, hi;
+        row_interval(MASK, s.window, s.S, q_row, &lo, &hi);
+        if (!row_valid) hi = lo - 1;
+        const long long base = (long long)(kt_lo + j) * F8_BN + 16 * hf;
+        const long long hi_a = hi < (long long)s.S - 1 ? hi : (long long)s.S - 1;
+        const int lo_r = (int)(lo - base < -1 ? -1 : (lo - base > F8_BN ? F8_BN : lo - base));
+        const int hi_r = (int)(hi_a - base < -1 ? -1 : (hi_a - base > F8_BN ? F8_BN : hi_a - base));
+#pragma unroll
+        for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kbk * 32 + r;
+            sc[kbk][r] = (key >= lo_r && key <= hi_r) ? sc[kbk][r] : -INFINITY;
+          }
+      }
+      // online softmax
+      float mx;
+      {
+        float t[8];
+#pragma unroll
+        for (int c4 = 0; c4 < 8; ++c4) {
+          const int kbk = c4 >> 1, rb = (c4 & 1) * 8;
+          float x = max3f(sc[kbk][rb], sc[kbk][rb + 1], sc[kbk][rb + 2]);
+          x = max3f(x, sc[kbk][rb + 3], sc[kbk][rb + 4]);
+          x = max3f(x, sc[kbk][rb + 5], sc[kbk][rb + 6]);
+          t[c4] = max3f(x, sc[kbk][rb + 7], sc[kbk][rb + 7]);
+        }
+        mx = max3f(max3f(t[0], t[1], t[2]), max3f(t[3], t[4], t[5]), fmaxf(t[6], t[7]));
+      }
+      mx = pair_max(mx);
+      if (__builtin_amdgcn_ballot_w64(mx * c > m_run * c + kLazyF8) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
+        m_run = m_new;
+        l_run0 *= alpha;
+        l_run1 *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+      // weights of 64-key step sk: bytes 16*(kbk - 2*sk) + r, four per dword
+      i32x8 pf[2];
+#pragma unroll
+      for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r], c, -mc));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 1], c, -mc));
+          const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 2], c, -mc));
+          const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 3], c, -mc));
+          l_run0 += e0 + e1;
+          l_run1 += e2 + e3;
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
+          pf[kbk >> 1][4 * (kbk & 1) + r / 4] = w;
+        }
+
+      // O^T += V^T P^T: four 32-dim blocks, two 64-key steps each (the V
+      // tile follows the K tile; the offsets include F8_REG)
+      {
+        const unsigned vbase[4] = {kb + v_off[0], kb + v_off[1], kb + v_off[2], kb + v_off[3]};
+        i32x8 vo[2];
+        vo[0] = lds_tr8x4<vrow_off(0, 0), vrow_off(0, 1), vrow_off(0, 2), vrow_off(0, 3)>(vbase[0]);
+        pv_steps<0>(vo, vbase, pf, oacc);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // this wave's loads of tile j+1 landed
+    __syncthreads();                      // every wave is done with stage st
+  }
+
+  // ---- epilogue: O = O^T / l, round to bf16, store --------------------------
+  {
+    const float l_run = l_run0 + l_run1;
+    const float l_other = __uint_as_float(__shfl_xor((int)__float_as_uint(l_run), 32));
+    const float l_tot = l_run + l_other;
+    if (row_valid && wave_active) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      __bf16* op = (__bf16*)p.o + ((size_t)(it.b * s.Hq + a) * S + q_row) * F8_D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 w;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) w[t] = (__bf16)(oacc[db][g4 * 4 + t] * inv);
+          *(bf16x4*)(op + db * 32 + g4 * 8 + hf * 4) = w;
+        }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fp8_d128(const KParams& p, hipStream_t stream) {
+  dim3 grid((unsigned)p.s.n_items), block(kBf16Threads);
+  switch (p.s.mask) {
+    case MASK_FULL: hipLaunchKernelGGL((attn_fwd_fp8<MASK_FULL>), grid, block, 0, stream, p); break;
+    case MASK_CAUSAL: hipLaunchKernelGGL((attn_fwd_fp8<MASK_CAUSAL>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((attn_fwd_fp8<MASK_CAUSAL_WINDOW>), grid, block, 0, stream, p); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn

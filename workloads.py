@@ -19,6 +19,9 @@ Workloads (shapes follow the examples on the pages):
 * ``local_global_bf16_s8192`` -- bidirectional band |i-j| <= 512 plus global
   tokens {0, 1000, 3000, 6000}, 12 heads, B=1 S=8192 D=64: the document example
   of "Transformer 演进与变体", section 稀疏注意力 (Longformer paragraph).
+* ``causal_gqa_fp8_s8192`` -- the grouped-query workload with E4M3 inputs
+  (the FP8 forward of "Transformer 演进与变体", section Flash Attention), bf16
+  output.  The N(0, 1) draws are rounded to E4M3 (nearest even).
 
 Decode workloads (the Sq newest positions of each sequence against its
 key/value cache, "Transformer 架构及其变体", section 预填充创建缓存，解码复用缓存):
@@ -83,7 +86,7 @@ class Workload:
     Hkv: int
     S: int
     D: int
-    dtype: str  # "fp32" or "bf16"
+    dtype: str  # "fp32", "bf16" or "fp8" (E4M3 inputs, bf16 output)
     mask: str
     window: int = 0
     global_idx: Tuple[int, ...] = ()
@@ -109,6 +112,7 @@ WORKLOADS = {
                  window=4096, seed=4),
         Workload("local_global_bf16_s8192", 1, 12, 12, 8192, 64, "bf16", MASK_LOCAL_GLOBAL,
                  window=512, global_idx=(0, 1000, 3000, 6000), seed=5),
+        Workload("causal_gqa_fp8_s8192", 1, 32, 8, 8192, 128, "fp8", MASK_CAUSAL, seed=14),
     )
 }
 
@@ -284,9 +288,19 @@ def draw(shape, rng: np.random.Generator) -> np.ndarray:
     return rng.standard_normal(shape, dtype=np.float32)
 
 
+def e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest E4M3 value (ties to even, OCP
+    format) with torch's own conversion; return the uint8 codes."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
 def make_inputs(B, Hq, Hkv, S, D, dtype, seed):
     """Return dict with float32 arrays 'q','k','v' holding the values the kernel sees,
-    plus (for bf16) the uint16 bit patterns under 'q_bits','k_bits','v_bits'."""
+    plus (for bf16) the uint16 bit patterns under 'q_bits','k_bits','v_bits' or
+    (for fp8) the E4M3 codes under 'q_codes','k_codes','v_codes'."""
     rng = np.random.default_rng(seed)
     q = draw((B, Hq, S, D), rng)
     k = draw((B, Hkv, S, D), rng)
@@ -297,6 +311,10 @@ def make_inputs(B, Hq, Hkv, S, D, dtype, seed):
             bits = bf16_round_bits(x)
             out[name + "_bits"] = bits
             out[name] = bf16_bits_to_float(bits)
+        elif dtype == "fp8":
+            codes = e4m3_codes(x)
+            out[name + "_codes"] = codes
+            out[name] = codes_to_float(codes)
         elif dtype == "fp32":
             out[name] = x
         else:
@@ -330,6 +348,13 @@ def ex_workload_inputs(w: ExWorkload):
     return make_decode_inputs(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.seed)
 
 
+def codes_to_float(codes: np.ndarray) -> np.ndarray:
+    """E4M3 codes widened exactly to float32 (torch's decoding)."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).float().numpy()
+
+
 def to_torch(inputs: dict, dtype: str, device):
     """Move generated inputs into torch tensors of the kernel dtype (no arithmetic)."""
     import torch
@@ -338,6 +363,8 @@ def to_torch(inputs: dict, dtype: str, device):
     for name in ("q", "k", "v"):
         if dtype == "bf16":
             t = torch.from_numpy(inputs[name + "_bits"].view(np.int16)).view(torch.bfloat16)
+        elif dtype == "fp8":
+            t = torch.from_numpy(inputs[name + "_codes"]).view(torch.float8_e4m3fn)
         else:
             t = torch.from_numpy(inputs[name])
         res.append(t.to(device).contiguous())
