@@ -111,10 +111,11 @@ def sample_rows(w: workloads.Workload, n=48):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+@pytest.mark.parametrize("name", [n for n, w in workloads.WORKLOADS.items() if w.dtype != "fp8"])
 def test_workload_full_size(device, name):
     """The workloads at full size, in the launch configuration the benchmark
-    times; every element of the sampled query rows (all heads) is compared."""
+    times; every element of the sampled query rows (all heads) is compared
+    (the FP8 workload has its own bound, in test_fp8.py)."""
     w = workloads.WORKLOADS[name]
     rows = None if w.S <= 256 else sample_rows(w)
     err = run_case(device, w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype, w.mask, w.window, w.global_idx,
