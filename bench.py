@@ -49,29 +49,38 @@ PEAK_FP32_TFLOPS = 157.3   # vector fp32
 PEAK_FP8_TFLOPS = 5033.2   # 256 CU x 2.4 GHz x 8192 dense FP8 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 KERNEL_SOURCES = ("kernel_bf16.hip", "gfx950_ops.h", "attn_kernels.h", "attn_sched.h")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_causal_gqa_s8192_hbm_traffic.md")
+# committed HBM-traffic summaries per workload, with the sources their kernel is built from
+TRAFFIC_SUMMARIES = {
+    "causal_gqa_bf16_s8192": ("attn_fwd_bf16_causal_gqa_s8192_hbm_traffic.md", KERNEL_SOURCES),
+    "causal_gqa_fp8_s8192": ("attn_fwd_fp8_causal_gqa_s8192.md",
+                             ("kernel_fp8.hip", "gfx950_ops.h", "attn_kernels.h", "attn_sched.h")),
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "transformer_attention_attn_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
 def committed_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source for this workload."""
-    if not os.path.exists(TRAFFIC_SUMMARY):
+    """HBM bytes per launch from the committed counter summary of this
+    workload, if it was taken on the current kernel source."""
+    if workload not in TRAFFIC_SUMMARIES:
         return None
-    txt = open(TRAFFIC_SUMMARY, encoding="utf-8").read()
+    fname, sources = TRAFFIC_SUMMARIES[workload]
+    path = os.path.join(ROOT, "profiles", fname)
+    if not os.path.exists(path):
+        return None
+    txt = open(path, encoding="utf-8").read()
     m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", txt)
     m_wl = re.search(r"workload:\s*(\S+)", txt)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
     if not (m_hash and m_wl and m_b):
         return None
-    if m_hash.group(1) != kernel_source_hash() or m_wl.group(1) != workload:
+    if m_hash.group(1) != kernel_source_hash(sources) or m_wl.group(1) != workload:
         return None
     return float(m_b.group(1))
 
