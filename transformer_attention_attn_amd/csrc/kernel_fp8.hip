@@ -30,8 +30,10 @@
 //
 // Workgroup: eight waves of 32 query rows (query heads of a key/value head
 // packed as in the bf16 kernel), 128-key tiles, K and V tiles loaded straight
-// into LDS (two stages), one tile ahead.  All waves run the same step (S,
-// softmax, P.V) between two barriers per tile.
+// into LDS (two stages).  The schedule is the bf16 kernel's ping-pong: two
+// wave groups (one wave of each per SIMD) alternate, per barrier-separated
+// step, between the matrix block of one tile and the softmax of another, so
+// the matrix cores and the vector ALUs of a SIMD work side by side.
 //
 // LDS swizzles (16-byte chunks of the 128-byte rows): K chunk c of row r sits
 // at c ^ g(r), g(r) = ((r >> 1) & 3) | (((r >> 4) & 1) << 2), so the 16 rows a
@@ -51,9 +53,9 @@ constexpr int F8_BN = 128;                // keys per tile
 constexpr int F8_ROWB = F8_D;             // bytes per K or V row
 constexpr int F8_REG = F8_BN * F8_ROWB;   // one K or V tile (16 KB)
 constexpr int F8_NSTAGE = 2;
-constexpr int F8_LOADS = F8_REG / 1024 / kBf16Waves;  // 1 KiB direct loads per wave per tile
+constexpr int F8_LOADS = F8_REG / 1024 / 4;  // 1 KiB direct loads per loading wave per tile
 constexpr float kLazyF8 = 8.f;
-static_assert(F8_LOADS * kBf16Waves * 1024 == F8_REG, "tile split into 1 KiB loads");
+static_assert(F8_LOADS * 4 * 1024 == F8_REG, "tile split into 1 KiB loads of four waves");
 
 __device__ __forceinline__ int kswz(int row) { return ((row >> 1) & 3) | (((row >> 4) & 1) << 2); }
 __device__ __forceinline__ int vswz(int row) { return 2 * ((row >> 1) & 3); }
@@ -183,20 +185,32 @@ void attn_fwd_fp8(KParams p) {
   const int kt_lo = klo / F8_BN, kt_hi = khi / F8_BN;
   const int n_it = kt_hi - kt_lo + 1;
 
-  // Direct loads: load n of wave w fills 1 KiB slot sl = w * F8_LOADS + n of
-  // the tile, lane l the 16-byte chunk at row 8 * sl + l / 8, physical chunk
-  // l % 8 (its source: that row's logical chunk).  Rows past S repeat the
-  // last row (their scores are masked).
+  // Direct loads, issued by the four waves of group 0: load n of wave gw fills
+  // 1 KiB slot sl = gw * F8_LOADS + n of the tile, lane l the 16-byte chunk at
+  // row 8 * sl + l / 8, physical chunk l % 8 (its source: that row's logical
+  // chunk).  Rows past S repeat the last row (their scores are masked), so
+  // tiles past the end of the range load valid memory into a stage that is not
+  // read again.
+  const int gw = wave & 3;
   const int drow = lane >> 3, dphys = lane & 7;
-  auto dma_tile = [&](int iter, int st) {
+  auto dma_k = [&](int iter, int st) {
     const int kt = kt_lo + iter;
 #pragma unroll
     for (int n = 0; n < F8_LOADS; ++n) {
-      const int trow = 8 * (wave * F8_LOADS + n) + drow;
+      const int trow = 8 * (gw * F8_LOADS + n) + drow;
       const int row = imin(kt * F8_BN + trow, s.S - 1);
-      unsigned char* kd = smem + st * 2 * F8_REG + (wave * F8_LOADS + n) * 1024;
-      dma16_global(kp + (size_t)row * F8_ROWB + 16 * (dphys ^ kswz(trow)), kd);
-      dma16_global(vp + (size_t)row * F8_ROWB + 16 * (dphys ^ vswz(trow)), kd + F8_REG);
+      dma16_global(kp + (size_t)row * F8_ROWB + 16 * (dphys ^ kswz(trow)),
+                   smem + st * 2 * F8_REG + (gw * F8_LOADS + n) * 1024);
+    }
+  };
+  auto dma_v = [&](int iter, int st) {
+    const int kt = kt_lo + iter;
+#pragma unroll
+    for (int n = 0; n < F8_LOADS; ++n) {
+      const int trow = 8 * (gw * F8_LOADS + n) + drow;
+      const int row = imin(kt * F8_BN + trow, s.S - 1);
+      dma16_global(vp + (size_t)row * F8_ROWB + 16 * (dphys ^ vswz(trow)),
+                   smem + st * 2 * F8_REG + F8_REG + (gw * F8_LOADS + n) * 1024);
     }
   };
 
@@ -216,16 +230,16 @@ void attn_fwd_fp8(KParams p) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) k_off[dc][c] = krow * F8_ROWB + 16 * ((4 * dc + 2 * hf + c) ^ kswz(krow));
   // V^T operand (dim block db, key step sk, read t): this lane addresses row
-  // 64*sk + 32*(t/2) + 16*(grp/2) + 8*(t%2) + m, 8-byte piece 2*(grp%2) + h +
-  // 4*db, with grp = lane / 16, m = (lane % 16) / 2, h = lane % 2.  The row's
+  // 64*sk + 32*(t/2) + 16*(g/2) + 8*(t%2) + m, 8-byte piece 2*(g%2) + h +
+  // 4*db, with g = lane / 16, m = (lane % 16) / 2, h = lane % 2.  The row's
   // bits 1-2 are m's, so the swizzle (pieces ^ 4*((row >> 1) & 3)) is per lane
   // and the (sk, t) part is an immediate row offset.
-  const int grp = lane >> 4, vm = (lane & 15) >> 1, vh = lane & 1;
+  const int lg16 = lane >> 4, vm = (lane & 15) >> 1, vh = lane & 1;
   int v_off[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
-    v_off[db] = F8_REG + (16 * (grp >> 1) + vm) * F8_ROWB +
-                8 * (2 * (grp & 1) + vh + 4 * (db ^ ((vm >> 1) & 3)));
+    v_off[db] = F8_REG + (16 * (lg16 >> 1) + vm) * F8_ROWB +
+                8 * (2 * (lg16 & 1) + vh + 4 * (db ^ ((vm >> 1) & 3)));
 
   // ---- accumulators ------------------------------------------------------
   f32x16 oacc[4];
@@ -237,101 +251,139 @@ void attn_fwd_fp8(KParams p) {
   float l_run0 = 0.f, l_run1 = 0.f;
   const float c = p.c;
 
-  // ---- prologue -------------------------------------------------------
-  dma_tile(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads landed
-  __syncthreads();
-
-  for (int j = 0; j < n_it; ++j) {
-    const int st = j & 1;
-    if (j + 1 < n_it) dma_tile(j + 1, st ^ 1);  // stage st^1 was last read in step j-1
-    const int cls = tile_class(j);
-    if (cls != TILE_EMPTY) {
-      const unsigned kb = lds_addr(smem + st * 2 * F8_REG);
-      // S^T = K Q^T: four 32-key blocks, two 64-dim steps each
-      f32x16 sc[4];
+  // ---- the matrix block of one step: O^T += V(jv)^T P^T, then S(js) = K(js) Q^T
+  f32x16 sc[4];
+  i32x8 pf[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) pf[i] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  auto mfma_block = [&](int jv, bool do_pv, int js, bool do_s) {
+    __builtin_amdgcn_s_setprio(1);
+    if (do_pv) {
+      const unsigned vb = lds_addr(smem + (jv & 1) * 2 * F8_REG);
+      const unsigned vbase[4] = {vb + v_off[0], vb + v_off[1], vb + v_off[2], vb + v_off[3]};
+      i32x8 vo[2];
+      vo[0] = lds_tr8x4<vrow_off(0, 0), vrow_off(0, 1), vrow_off(0, 2), vrow_off(0, 3)>(vbase[0]);
+      pv_steps<0>(vo, vbase, pf, oacc);
+    }
+    if (do_s) {
+      const unsigned kb = lds_addr(smem + (js & 1) * 2 * F8_REG);
+      const unsigned a00 = kb + k_off[0][0], a01 = kb + k_off[0][1];
+      const unsigned a10 = kb + k_off[1][0], a11 = kb + k_off[1][1];
       i32x8 op[2];
-      {
-        const unsigned a00 = kb + k_off[0][0], a01 = kb + k_off[0][1];
-        const unsigned a10 = kb + k_off[1][0], a11 = kb + k_off[1][1];
-        op[0] = lds_read32<0>(a00, a01);
-        s_blocks<0>(op, a00, a01, a10, a11, qf, sc);
-      }
+      op[0] = lds_read32<0>(a00, a01);
+      s_blocks<0>(op, a00, a01, a10, a11, qf, sc);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-      // mask (partial tiles): register r of block kbk holds key
-      // 32*kbk + 16*hf + r of the tile
-      if (cls == TILE_PARTIAL) {
-        long long lo, hi;
-        row_interval(MASK, s.window, s.S, q_row, &lo, &hi);
-        if (!row_valid) hi = lo - 1;
-        const long long base = (long long)(kt_lo + j) * F8_BN + 16 * hf;
-        const long long hi_a = hi < (long long)s.S - 1 ? hi : (long long)s.S - 1;
-        const int lo_r = (int)(lo - base < -1 ? -1 : (lo - base > F8_BN ? F8_BN : lo - base));
-        const int hi_r = (int)(hi_a - base < -1 ? -1 : (hi_a - base > F8_BN ? F8_BN : hi_a - base));
-#pragma unroll
-        for (int kbk = 0; kbk < 4; ++kbk)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbk * 32 + r;
-            sc[kbk][r] = (key >= lo_r && key <= hi_r) ? sc[kbk][r] : -INFINITY;
-          }
-      }
-      // online softmax
-      float mx;
-      {
-        float t[8];
-#pragma unroll
-        for (int c4 = 0; c4 < 8; ++c4) {
-          const int kbk = c4 >> 1, rb = (c4 & 1) * 8;
-          float x = max3f(sc[kbk][rb], sc[kbk][rb + 1], sc[kbk][rb + 2]);
-          x = max3f(x, sc[kbk][rb + 3], sc[kbk][rb + 4]);
-          x = max3f(x, sc[kbk][rb + 5], sc[kbk][rb + 6]);
-          t[c4] = max3f(x, sc[kbk][rb + 7], sc[kbk][rb + 7]);
-        }
-        mx = max3f(max3f(t[0], t[1], t[2]), max3f(t[3], t[4], t[5]), fmaxf(t[6], t[7]));
-      }
-      mx = pair_max(mx);
-      if (__builtin_amdgcn_ballot_w64(mx * c > m_run * c + kLazyF8) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
-        m_run = m_new;
-        l_run0 *= alpha;
-        l_run1 *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-      const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-      // weights of 64-key step sk: bytes 16*(kbk - 2*sk) + r, four per dword
-      i32x8 pf[2];
+  // ---- online softmax of S(j) into the weights pf (E4M3) and l ---------------
+  auto softmax = [&](int j, int cls) {
+    if (cls == TILE_PARTIAL) {
+      // register r of block kbk holds key 32*kbk + 16*hf + r of the tile
+      long long lo, hi;
+      row_interval(MASK, s.window, s.S, q_row, &lo, &hi);
+      if (!row_valid) hi = lo - 1;
+      const long long base = (long long)(kt_lo + j) * F8_BN + 16 * hf;
+      const long long hi_a = hi < (long long)s.S - 1 ? hi : (long long)s.S - 1;
+      const int lo_r = (int)(lo - base < -1 ? -1 : (lo - base > F8_BN ? F8_BN : lo - base));
+      const int hi_r = (int)(hi_a - base < -1 ? -1 : (hi_a - base > F8_BN ? F8_BN : hi_a - base));
 #pragma unroll
       for (int kbk = 0; kbk < 4; ++kbk)
 #pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r], c, -mc));
-          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 1], c, -mc));
-          const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 2], c, -mc));
-          const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 3], c, -mc));
-          l_run0 += e0 + e1;
-          l_run1 += e2 + e3;
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-          w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
-          pf[kbk >> 1][4 * (kbk & 1) + r / 4] = w;
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbk * 32 + r;
+          sc[kbk][r] = (key >= lo_r && key <= hi_r) ? sc[kbk][r] : -INFINITY;
         }
-
-      // O^T += V^T P^T: four 32-dim blocks, two 64-key steps each (the V
-      // tile follows the K tile; the offsets include F8_REG)
-      {
-        const unsigned vbase[4] = {kb + v_off[0], kb + v_off[1], kb + v_off[2], kb + v_off[3]};
-        i32x8 vo[2];
-        vo[0] = lds_tr8x4<vrow_off(0, 0), vrow_off(0, 1), vrow_off(0, 2), vrow_off(0, 3)>(vbase[0]);
-        pv_steps<0>(vo, vbase, pf, oacc);
-      }
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // this wave's loads of tile j+1 landed
-    __syncthreads();                      // every wave is done with stage st
+    float mx;
+    {
+      float t[8];
+#pragma unroll
+      for (int c4 = 0; c4 < 8; ++c4) {
+        const int kbk = c4 >> 1, rb = (c4 & 1) * 8;
+        float x = max3f(sc[kbk][rb], sc[kbk][rb + 1], sc[kbk][rb + 2]);
+        x = max3f(x, sc[kbk][rb + 3], sc[kbk][rb + 4]);
+        x = max3f(x, sc[kbk][rb + 5], sc[kbk][rb + 6]);
+        t[c4] = max3f(x, sc[kbk][rb + 7], sc[kbk][rb + 7]);
+      }
+      mx = max3f(max3f(t[0], t[1], t[2]), max3f(t[3], t[4], t[5]), fmaxf(t[6], t[7]));
+    }
+    mx = pair_max(mx);
+    if (__builtin_amdgcn_ballot_w64(mx * c > m_run * c + kLazyF8) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
+      m_run = m_new;
+      l_run0 *= alpha;
+      l_run1 *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+    // weights of 64-key step sk: bytes 16*(kbk - 2*sk) + r, four per dword
+#pragma unroll
+    for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r], c, -mc));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 1], c, -mc));
+        const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 2], c, -mc));
+        const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 3], c, -mc));
+        l_run0 += e0 + e1;
+        l_run1 += e2 + e3;
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
+        pf[kbk >> 1][4 * (kbk & 1) + r / 4] = w;
+      }
+  };
+  auto zero_p = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pf[i] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  };
+
+  // ---- pipeline (the bf16 kernel's two-stage ping-pong) ----------------------
+  // Waves 0-3 (group 0) and 4-7 (group 1), one of each per SIMD.  Per tile two
+  // barrier-separated steps; in each, one group runs its matrix block and the
+  // other its softmax:
+  //   step 2j  : group 0 softmax(S(j))          | group 1 P.V(j-1), S(j)
+  //   step 2j+1: group 0 P.V(j), S(j+1); loads  | group 1 softmax(S(j))
+  // Tile j lives in stage j % 2.  Group 0 loads K(j+2) and V(j+1) in step
+  // 2j+1 (K(j) was last read in step 2j by group 1, V(j-1) in step 2j by group
+  // 1) and waits for them at the end of step 2j+2, before the barrier into step
+  // 2j+3, the first that reads them.  Group 1 loads nothing.
+  const int grp = wave >> 2;
+  if (grp == 0) {
+    dma_k(0, 0);
+    dma_v(0, 0);
+    dma_k(1, 1);
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * F8_LOADS));  // K(0) landed
   }
+  __builtin_amdgcn_s_barrier();
+  if (grp == 0) {
+    if (tile_class(0) != TILE_EMPTY) mfma_block(0, false, 0, true);  // S(0)
+    for (int j = 0; j <= n_it; ++j) {
+      const int cls = j < n_it ? tile_class(j) : TILE_EMPTY;
+      if (cls != TILE_EMPTY) softmax(j, cls);  // step 2j
+      else zero_p();
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // K(j+1), V(j) landed
+      __builtin_amdgcn_s_barrier();
+      dma_k(j + 2, j & 1);  // step 2j+1
+      dma_v(j + 1, (j + 1) & 1);
+      mfma_block(j, cls != TILE_EMPTY, j + 1, j + 1 < n_it && tile_class(j + 1) != TILE_EMPTY);
+      __builtin_amdgcn_s_barrier();
+    }
+  } else {
+    for (int j = 0; j <= n_it; ++j) {
+      const int cls = j < n_it ? tile_class(j) : TILE_EMPTY;
+      mfma_block(j - 1, j >= 1 && tile_class(j - 1) != TILE_EMPTY, j, cls != TILE_EMPTY);  // step 2j
+      __builtin_amdgcn_s_barrier();
+      if (cls != TILE_EMPTY) softmax(j, cls);  // step 2j+1
+      else zero_p();
+      __builtin_amdgcn_s_barrier();
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // no direct load may land after the workgroup ends
 
   // ---- epilogue: O = O^T / l, round to bf16, store --------------------------
   {
