@@ -103,7 +103,9 @@ typedef enum {
  *   scale       multiplies q.k; used exactly as given (0 gives uniform weights;
  *               the usual choice is 1/sqrt(D), "Trasformer 浅析", section
  *               缩放因子的必要性)
- *   dtype       attn_dtype of all four tensors
+ *   dtype       attn_dtype of all four tensors (ATTN_DTYPE_FP8_E4M3: q, k, v
+ *               one byte per element, o bf16; D = 128 and no global tokens,
+ *               else ATTN_ERR_UNSUPPORTED)
  *   stream      hipStream_t to launch on (NULL = the default stream)
  *
  * Returns ATTN_OK after enqueuing one kernel; the call does not synchronise.
