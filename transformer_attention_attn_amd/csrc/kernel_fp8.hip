@@ -55,6 +55,7 @@ constexpr int F8_REG = F8_BN * F8_ROWB;   // one K or V tile (16 KB)
 constexpr int F8_NSTAGE = 2;
 constexpr int F8_LOADS = F8_REG / 1024 / 4;  // 1 KiB direct loads per loading wave per tile
 constexpr float kLazyF8 = 8.f;
+constexpr float kLazyWF8 = 256.f;  // 2^kLazyF8
 static_assert(F8_LOADS * 4 * 1024 == F8_REG, "tile split into 1 KiB loads of four waves");
 
 __device__ __forceinline__ int kswz(int row) { return ((row >> 1) & 3) | (((row >> 4) & 1) << 2); }
@@ -295,47 +296,66 @@ void attn_fwd_fp8(KParams p) {
           sc[kbk][r] = (key >= lo_r && key <= hi_r) ? sc[kbk][r] : -INFINITY;
         }
     }
-    float mx;
-    {
-      float t[8];
+    // Weights first, against the current reference maximum, when every row of
+    // the wave has one; the per-lane sum of the tile's weights bounds each of
+    // them, so the row maximum (and the rescale) is only needed on a row's
+    // first tile and when that sum exceeds 2^kLazyF8, and the weights are then
+    // recomputed.  Weights stay <= 2^8, inside the E4M3 range.
+    bool with_max = __builtin_amdgcn_ballot_w64(row_valid && m_run == -INFINITY) != 0;
+    float t0, t1;
+#pragma nounroll
+    for (;;) {
+      if (with_max) {
+        float mx;
+        {
+          float t[8];
 #pragma unroll
-      for (int c4 = 0; c4 < 8; ++c4) {
-        const int kbk = c4 >> 1, rb = (c4 & 1) * 8;
-        float x = max3f(sc[kbk][rb], sc[kbk][rb + 1], sc[kbk][rb + 2]);
-        x = max3f(x, sc[kbk][rb + 3], sc[kbk][rb + 4]);
-        x = max3f(x, sc[kbk][rb + 5], sc[kbk][rb + 6]);
-        t[c4] = max3f(x, sc[kbk][rb + 7], sc[kbk][rb + 7]);
+          for (int c4 = 0; c4 < 8; ++c4) {
+            const int kbk = c4 >> 1, rb = (c4 & 1) * 8;
+            float x = max3f(sc[kbk][rb], sc[kbk][rb + 1], sc[kbk][rb + 2]);
+            x = max3f(x, sc[kbk][rb + 3], sc[kbk][rb + 4]);
+            x = max3f(x, sc[kbk][rb + 5], sc[kbk][rb + 6]);
+            t[c4] = max3f(x, sc[kbk][rb + 7], sc[kbk][rb + 7]);
+          }
+          mx = max3f(max3f(t[0], t[1], t[2]), max3f(t[3], t[4], t[5]), fmaxf(t[6], t[7]));
+        }
+        mx = pair_max(mx);
+        // a row maximum grew: move the reference to it
+        if (__builtin_amdgcn_ballot_w64(mx * c > m_run * c) != 0) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
+          m_run = m_new;
+          l_run0 *= alpha;
+          l_run1 *= alpha;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
       }
-      mx = max3f(max3f(t[0], t[1], t[2]), max3f(t[3], t[4], t[5]), fmaxf(t[6], t[7]));
+      const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+      t0 = 0.f;
+      t1 = 0.f;
+      // weights of 64-key step sk: bytes 16*(kbk - 2*sk) + r, four per dword
+#pragma unroll
+      for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r], c, -mc));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 1], c, -mc));
+          const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 2], c, -mc));
+          const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 3], c, -mc));
+          t0 += e0 + e1;
+          t1 += e2 + e3;
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
+          pf[kbk >> 1][4 * (kbk & 1) + r / 4] = w;
+        }
+      if (with_max || __builtin_amdgcn_ballot_w64(row_valid && !(t0 + t1 <= kLazyWF8)) == 0) break;
+      with_max = true;
     }
-    mx = pair_max(mx);
-    if (__builtin_amdgcn_ballot_w64(mx * c > m_run * c + kLazyF8) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
-      m_run = m_new;
-      l_run0 *= alpha;
-      l_run1 *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-    // weights of 64-key step sk: bytes 16*(kbk - 2*sk) + r, four per dword
-#pragma unroll
-    for (int kbk = 0; kbk < 4; ++kbk)
-#pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r], c, -mc));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 1], c, -mc));
-        const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 2], c, -mc));
-        const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 3], c, -mc));
-        l_run0 += e0 + e1;
-        l_run1 += e2 + e3;
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
-        pf[kbk >> 1][4 * (kbk & 1) + r / 4] = w;
-      }
+    l_run0 += t0;
+    l_run1 += t1;
   };
   auto zero_p = [&]() {
 #pragma unroll

@@ -322,6 +322,43 @@ def make_inputs(B, Hq, Hkv, S, D, dtype, seed):
     return out
 
 
+def make_trend_inputs(B, Hq, Hkv, S, D, dtype, seed, pattern, amp=16.0):
+    """make_inputs with a planted trend in the scores along the key index, for
+    the running-maximum paths of the kernels: every query gets +amp in
+    dimension 0, and dimension 0 of the keys is amp * t for t rising or
+    falling linearly over [-1, 1] ('rising', 'falling'), or amp * (1 + 4 r) at
+    the r-th of a few random positions ('spikes', each far above the last).
+    Quantised like make_inputs."""
+    rng = np.random.default_rng(seed)
+    q = draw((B, Hq, S, D), rng)
+    k = draw((B, Hkv, S, D), rng)
+    v = draw((B, Hkv, S, D), rng)
+    q[..., 0] += np.float32(amp)
+    t = np.linspace(-1.0, 1.0, S, dtype=np.float32)
+    if pattern == "rising":
+        k[..., 0] = np.float32(amp) * t
+    elif pattern == "falling":
+        k[..., 0] = -np.float32(amp) * t
+    elif pattern == "spikes":
+        pos = np.sort(rng.choice(S, size=max(1, S // 97), replace=False))
+        k[..., pos, 0] = np.float32(amp) * (1 + 4 * np.arange(len(pos), dtype=np.float32))
+    else:
+        raise ValueError(f"unknown pattern {pattern!r}")
+    out = {}
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if dtype == "bf16":
+            bits = bf16_round_bits(x)
+            out[name + "_bits"] = bits
+            out[name] = bf16_bits_to_float(bits)
+        elif dtype == "fp8":
+            codes = e4m3_codes(x)
+            out[name + "_codes"] = codes
+            out[name] = codes_to_float(codes)
+        else:
+            raise ValueError(f"unknown dtype {dtype!r}")
+    return out
+
+
 def workload_inputs(w: Workload):
     return make_inputs(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype, w.seed)
 
