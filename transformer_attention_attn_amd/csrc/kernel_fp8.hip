@@ -5,8 +5,10 @@
 // the two matrix products, softmax and accumulation in higher precision):
 //   * S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit
 //     scales, fp32 accumulation): 64 dims per instruction.
-//   * Online softmax in fp32, as in the bf16 kernel (log2 units, lazy rescale,
-//     denominator summed from the fp32 weights).
+//   * Online softmax in fp32, as in the bf16 kernel (log2 units, lazy
+//     reference maximum, denominator summed from the fp32 weights), except
+//     that the weights come first and the row maximum is computed only when
+//     their per-lane sum shows a weight above 2^8 (and on a row's first tile).
 //   * P is rounded to E4M3 (v_cvt_pk_fp8_f32, round to nearest even; P <= 2^8
 //     stays far below the E4M3 maximum) and O^T += V^T P^T runs on the same
 //     instruction, 64 keys per instruction; O is accumulated in fp32 and
