@@ -76,3 +76,28 @@ def test_trend_fp8(device, pattern, mask):
     tol = oracle.fp8_error_bound(*codes, mask) + 2.0 ** -8 * np.abs(ref) + 1e-3
     ratio = float(np.max(np.abs(o.float().cpu().numpy() - ref) / tol))
     assert ratio <= 1.0, ratio
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_trend_inputs_plant_the_trend(dtype):
+    """Host check of the generator: seeded, quantised like make_inputs, and the
+    oracle's row maximum really moves (rising: to the last visible key;
+    falling: stays at the first; spikes: to the latest spike)."""
+    B, Hq, Hkv, S, D = 1, 2, 1, 300, 128
+    a = workloads.make_trend_inputs(B, Hq, Hkv, S, D, dtype, seed=5, pattern="rising")
+    b = workloads.make_trend_inputs(B, Hq, Hkv, S, D, dtype, seed=5, pattern="rising")
+    for n in ("q", "k", "v"):
+        assert a[n].shape == ((B, Hq, S, D) if n == "q" else (B, Hkv, S, D))
+        assert np.array_equal(a[n], b[n])
+    scale = 1.0 / np.sqrt(D)
+    for pattern, where in (("rising", "last"), ("falling", "first"), ("spikes", "spike")):
+        x = workloads.make_trend_inputs(B, Hq, Hkv, S, D, dtype, seed=5, pattern=pattern)
+        s = (x["q"][0, 0].astype(np.float64) @ x["k"][0, 0].astype(np.float64).T) * scale
+        i = S - 1
+        arg = int(np.argmax(s[i, : i + 1]))
+        if where == "last":
+            assert arg > S - 20
+        elif where == "first":
+            assert arg < 20
+        else:
+            assert arg == int(np.argmax(x["k"][0, 0, :, 0]))
