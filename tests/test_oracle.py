@@ -197,6 +197,74 @@ def pin_workload_pair_totals():
         == 8192492
 
 
+def count_products_brute_force(S, D, kind, window=0, g=()):
+    """Pure-Python forward of one head on tiny inputs that counts the
+    floating-point multiplies and adds of its two products: every score is a
+    D-term dot product (D multiplies, D adds into a zero accumulator) and every
+    visible key adds its weighted value row to the output (D multiplies, D
+    adds).  The softmax's exp, max and sum are not counted.  Visibility is
+    written out here from the mask definitions, not taken from the oracle."""
+    rng = np.random.default_rng(S * 31 + D)
+    q = rng.standard_normal((S, D)).tolist()
+    k = rng.standard_normal((S, D)).tolist()
+    v = rng.standard_normal((S, D)).tolist()
+    ops = 0
+    for i in range(S):
+        vis = []
+        for j in range(S):
+            if kind == "full":
+                ok = True
+            elif kind == "causal":
+                ok = j <= i
+            elif kind == "causal_window":
+                ok = i - window < j <= i
+            else:
+                ok = abs(i - j) <= window or i in g or j in g
+            if ok:
+                vis.append(j)
+        scores = []
+        for j in vis:
+            acc = 0.0
+            for d in range(D):
+                acc = acc + q[i][d] * k[j][d]
+                ops += 2
+            scores.append(acc)
+        m = max(scores)
+        w = [math.exp(x - m) for x in scores]
+        tot = math.fsum(w)
+        out = [0.0] * D
+        for wj, j in zip(w, vis):
+            for d in range(D):
+                out[d] = out[d] + (wj / tot) * v[j][d]
+                ops += 2
+    return ops
+
+
+def pin_effective_flops():
+    # "Transformer 演进与变体", section 前馈网络效率: the score product and the
+    # output product of full attention are n^2 d multiply-adds each; two FLOPs
+    # per multiply-add, per query head and batch entry
+    for n, d in ((64, 16), (300, 128)):
+        assert oracle.effective_flops(1, 1, n, d, "full") == 2 * (n * n * d + n * n * d)
+        assert oracle.effective_flops(3, 5, n, d, "full") == 15 * 2 * (2 * n * n * d)
+    # operation counts of a pure-Python forward on tiny shapes, every mask kind
+    for kind, w, g in (("full", 0, ()), ("causal", 0, ()), ("causal_window", 3, ()),
+                       ("local_global", 2, (0, 9))):
+        S, D = 13, 5
+        assert oracle.effective_flops(1, 1, S, D, kind, w, g) == \
+            count_products_brute_force(S, D, kind, w, g), kind
+        assert oracle.effective_flops(2, 3, S, D, kind, w, g) == \
+            6 * count_products_brute_force(S, D, kind, w, g), kind
+    # the five workloads' totals (independently tabulated: 3.369e7, 1.375e11,
+    # 549,822,922,752, 9.621e11, 2.517e10)
+    assert oracle.effective_flops(1, 4, 256, 64, "causal") == 33685504
+    assert oracle.effective_flops(4, 32, 2048, 128, "causal") == 137506062336
+    assert oracle.effective_flops(1, 32, 8192, 128, "causal") == 549822922752
+    assert oracle.effective_flops(1, 32, 16384, 128, "causal_window", 4096) == 962106228736
+    assert oracle.effective_flops(1, 12, 8192, 64, "local_global", 512,
+                                  (0, 1000, 3000, 6000)) == 25167335424
+
+
 def pin_only_global_rows_see_everything():
     S, w, g = 8192, 512, (0, 1000, 3000, 6000)
     cnt = rows_closed_form(S, "local_global", w, g)
@@ -375,6 +443,7 @@ PINS = [
     pin_rows_sum_to_one,
     pin_visible_counts_closed_form,
     pin_workload_pair_totals,
+    pin_effective_flops,
     pin_only_global_rows_see_everything,
     pin_window_ge_S_equals_causal,
     pin_identical_keys_give_mean_of_visible_values,
@@ -496,6 +565,11 @@ def _mut_transposed_scores(q_rows, k, rows, kind, window=0, global_idx=(), scale
     return oracle_mod.softmax_rows(np.where(vis, s, -np.inf))
 
 
+def _mut_flops_two_d(B, Hq, S, D, kind, window=0, global_idx=()):
+    # one product counted, or multiply-adds counted as one FLOP
+    return 2 * D * oracle_mod.visible_pair_count(S, kind, window, global_idx) * B * Hq
+
+
 MUTATIONS = {
     "causal_drops_diagonal": ("visibility", _mut_causal_strict),
     "window_off_by_one": ("visibility", _mut_window_off_by_one),
@@ -506,6 +580,7 @@ MUTATIONS = {
     "softmax_wrong_sign": ("softmax_rows", _mut_softmax_wrong_sign),
     "scale_ignored": ("weights", _mut_scale_ignored),
     "scores_transposed": ("weights", _mut_transposed_scores),
+    "flops_two_d": ("effective_flops", _mut_flops_two_d),
 }
 
 
