@@ -43,4 +43,5 @@ from .fp8 import (  # noqa: F401
     e4m3_decode,
     fp8_attention,
     fp8_error_bound,
+    fp8_tolerance,
 )

@@ -34,10 +34,32 @@ same weights multiplied by a power of two >= 1, so in units of p_j the error
 stays within e_j = u p_j + 2^-10.  With the denominator summed from the
 unrounded weights, O - O_exact = sum_j (p~_j - p_j) v_j / L, hence
 
-    |O - O_exact| <= b = sum_j e_j |v_j| / L,
+    |O - O_exact| <= b = sum_j e_j |v_j| / L.
 
-plus the bf16 rounding of the output (2^-9 |O|) and fp32 accumulation
-(far below both).  ``fp8_error_bound`` returns b per output element.
+``fp8_error_bound`` returns b per output element.  ``fp8_tolerance`` adds the
+kernel's other roundings, each bounded from the arithmetic it does (first
+order in the fp32 unit u = 2^-24):
+
+* fp32 scores and exponent.  A score is an fp32 sum of D exact E4M3 products
+  (a product of two 4-bit significands fits fp32), error <= D u A_j with
+  A_j = sum_d |q_d k_jd|; the exponent argument x = s c - m c (c = |scale|
+  log2 e, rounded to fp32) adds at most 4 u c max(A) more, so
+  |dx| <= (D + 4) u c max_j A_j, and 2^x with v_exp_f32 (about one ulp) gives
+  each weight a relative error of at most ew = ln2 |dx| + 2 u.  Relative
+  weight errors of at most ew move a weighted mean by at most 2 ew (1 + 2 ew)
+  sum_j p_j |v_j| / L.
+* fp32 accumulation.  The numerator sum_j p~_j v_j runs as a chain of fp32
+  additions of partial sums of at most 16 keys (n_vis / 16 + 1 steps, plus
+  rescales and the final division), error <= (n_vis / 16 + 48) u
+  sum_j p_j |v_j| / L; the denominator is a chain of at most n_vis fp32
+  additions of positive weights, relative error <= (n_vis + 8) u, which moves
+  O by that fraction of |O|.
+* bf16 output.  O is rounded once to bf16 (8-bit significand, nearest even):
+  at most 2^-8 of the rounded value, i.e. 2^-8 (|O| + the bounds above).
+
+With all queries zero every weight is exactly 2^0 = 1 (the E4M3 rounding of 1
+is exact and the scores are exact zeros), so b and ew vanish and only the
+accumulation and output terms remain (``exact_weights=True``).
 
 Pinned by tests/test_oracle_fp8.py.
 """
@@ -49,6 +71,8 @@ from . import reference
 
 U_E4M3 = 2.0 ** -4          # relative rounding bound in the normal range
 ABS_E4M3 = 2.0 ** -10       # absolute rounding bound below it
+U_F32 = 2.0 ** -24          # fp32 unit roundoff (24-bit significand)
+U_BF16 = 2.0 ** -8          # bf16 unit roundoff (8-bit significand)
 
 
 def e4m3_decode(codes):
@@ -89,4 +113,45 @@ def fp8_error_bound(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=
             # w = p / L with p_max = 1, so p = w / wmax and 1 / L = wmax
             e = np.where(w > 0, U_E4M3 * w + ABS_E4M3 * wmax, 0.0)
             out[b, a] = e @ np.abs(v[b, h])
+    return out
+
+
+def fp8_tolerance(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=None,
+                  exact_weights=False, bf16_output=True):
+    """Per-element bound (float64, shaped like the output) on |O_kernel -
+    O_exact|: the E4M3 rounding of P (``fp8_error_bound``, left out when
+    ``exact_weights``), the fp32 score, exponent and accumulation errors and,
+    when ``bf16_output``, the bf16 rounding of the output (derivation in the
+    module docstring)."""
+    q = e4m3_decode(q_codes)
+    k = e4m3_decode(k_codes)
+    v = e4m3_decode(v_codes)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    c = abs(float(scale)) / np.log(2.0)
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    vis = reference.visibility(rows, S, kind, window)
+    n_vis = vis.sum(axis=1, keepdims=True).astype(np.float64)
+    exact = reference.attention(q, k, v, kind, window, (), scale=scale, rows=rows)
+    b = np.zeros_like(exact) if exact_weights else \
+        fp8_error_bound(q_codes, k_codes, v_codes, kind, window, scale, rows)
+    out = np.empty_like(exact)
+    for bb in range(B):
+        for a in range(Hq):
+            h = reference.kv_head(a, Hq, Hkv)
+            w = reference.weights(q[bb, a, rows], k[bb, h], rows, kind, window, (), scale)
+            mean_abs = w @ np.abs(v[bb, h])               # sum_j p_j |v_j| / L
+            if exact_weights:
+                ew = np.zeros((rows.size, 1))
+            else:
+                amag = np.where(vis, np.abs(q[bb, a, rows]) @ np.abs(k[bb, h]).T, 0.0)
+                ew = np.log(2.0) * (D + 4) * U_F32 * c * amag.max(axis=1, keepdims=True) \
+                    + 2 * U_F32
+            f = (2 * ew * (1 + 2 * ew) + (n_vis / 16 + 48) * U_F32) * mean_abs \
+                + (n_vis + 8) * U_F32 * np.abs(exact[bb, a])
+            out[bb, a] = b[bb, a] + f
+    if bf16_output:
+        out = out + U_BF16 * (np.abs(exact) + out)
     return out

@@ -7,6 +7,14 @@ torch's conversion, round to nearest even) at several reference maxima below
 the true one, the output formed with the unrounded denominator; the bound
 must hold everywhere and must not be vacuous.  Planted mistakes in the bound
 (a smaller relative unit, no subnormal term) make the simulation exceed it.
+
+fp8_tolerance (the bound plus the kernel's fp32 and bf16 roundings) is checked
+against a simulation of the kernel's whole arithmetic: fp32 scores and
+exponentials, weights rounded to E4M3, fp32 accumulation in 16-key chunks and a
+sequential fp32 denominator, an fp32 division and a bf16 output (nearest
+even).  With all queries zero the weights are exact, so the fp32 and bf16
+terms alone must cover the simulated error; planting a zero bf16 or fp32 unit
+makes the simulation exceed the tolerance.
 """
 import math
 
@@ -119,3 +127,93 @@ def test_planted_bound_mistakes_are_caught(monkeypatch, mutation):
             caught = True
     assert caught, mutation
     assert math.isfinite(f8.U_E4M3)
+
+
+def bf16_round(x):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(
+        torch.bfloat16).float().numpy().astype(np.float64)
+
+
+def simulate_kernel(q, k, v, kind, window, scale, shift, round_p=True, bf16_out=True):
+    """The FP8 forward's arithmetic in float32 on the decoded inputs: scores,
+    exponent argument and 2^x in float32, weights against a reference maximum
+    `shift` log2 units below the row maximum, P rounded to E4M3 (unless
+    round_p is False), the numerator accumulated in float32 16 keys at a time,
+    the denominator summed key by key in float32 from the unrounded weights,
+    one float32 division, the result rounded to bf16 when bf16_out."""
+    qd, kd, vd = (f8.e4m3_decode(x).astype(np.float32) for x in (q, k, v))
+    B, Hq, S, D = qd.shape
+    Hkv = kd.shape[1]
+    c = np.float32(abs(scale) / math.log(2.0))
+    sign = np.float32(1.0 if scale >= 0 else -1.0)
+    out = np.empty((B, Hq, S, D))
+    vis = ref.visibility(np.arange(S), S, kind, window)
+    for b in range(B):
+        for a in range(Hq):
+            h = ref.kv_head(a, Hq, Hkv)
+            s = (qd[b, a] @ kd[b, h].T) * sign                    # float32
+            x = np.where(vis, s * c, np.float32(-np.inf)).astype(np.float32)
+            m = x.max(axis=1, keepdims=True) - np.float32(shift)
+            p = np.exp2((x - m).astype(np.float32)).astype(np.float32)
+            pr = e4m3_round(p).astype(np.float32) if round_p else p
+            num = np.zeros((S, D), dtype=np.float32)
+            for j0 in range(0, S, 16):
+                num = (num + (pr[:, j0:j0 + 16].astype(np.float64)
+                              @ vd[b, h, j0:j0 + 16].astype(np.float64)).astype(np.float32))
+            den = np.zeros((S, 1), dtype=np.float32)
+            for j in range(S):
+                den = (den + p[:, j:j + 1]).astype(np.float32)
+            o = (num / den).astype(np.float32)
+            out[b, a] = bf16_round(o) if bf16_out else o
+    return out
+
+
+def check_tolerance(spread, exact_weights=False, bf16_out=True, scale=0.5):
+    rng = np.random.default_rng(62)
+    B, Hq, Hkv, S, D = 1, 2, 1, 80, 32
+    q = np.zeros((B, Hq, S, D), dtype=np.uint8) if exact_weights else \
+        random_codes(rng, (B, Hq, S, D), spread)
+    k = random_codes(rng, (B, Hkv, S, D), spread)
+    v = random_codes(rng, (B, Hkv, S, D), 1.0)
+    worst = 0.0
+    for kind, w in (("causal", 0), ("full", 0), ("causal_window", 9)):
+        exact = f8.fp8_attention(q, k, v, kind, w, scale=scale)
+        tol = f8.fp8_tolerance(q, k, v, kind, w, scale=scale, exact_weights=exact_weights,
+                               bf16_output=bf16_out)
+        for shift in ((0.0,) if exact_weights else (0.0, 0.37, 3.0, 7.9)):
+            got = simulate_kernel(q, k, v, kind, w, scale, shift, round_p=not exact_weights,
+                                  bf16_out=bf16_out)
+            err = np.abs(got - exact)
+            assert np.all(err <= tol), (kind, shift, float((err - tol).max()))
+            worst = max(worst, float((err / tol).max()))
+    return worst
+
+
+def test_tolerance_covers_the_kernel_arithmetic():
+    pytest.importorskip("torch")
+    assert check_tolerance(1.0) > 0.05
+    check_tolerance(3.0)
+    check_tolerance(1.0, scale=-0.3)
+
+
+def test_tolerance_with_exact_weights():
+    pytest.importorskip("torch")
+    # the bf16 output rounding is the dominant part: a real error reaches it
+    assert check_tolerance(1.0, exact_weights=True) > 0.2
+    # without the output rounding only the fp32 terms remain, and they hold
+    check_tolerance(1.0, exact_weights=True, bf16_out=False)
+
+
+@pytest.mark.parametrize("mutation", ["no_bf16_term", "no_fp32_term"])
+def test_planted_tolerance_mistakes_are_caught(monkeypatch, mutation):
+    pytest.importorskip("torch")
+    if mutation == "no_bf16_term":
+        monkeypatch.setattr(f8, "U_BF16", 0.0)
+        with pytest.raises(AssertionError):
+            check_tolerance(1.0, exact_weights=True)
+    else:
+        monkeypatch.setattr(f8, "U_F32", 0.0)
+        with pytest.raises(AssertionError):
+            check_tolerance(1.0, exact_weights=True, bf16_out=False)
