@@ -11,12 +11,20 @@ kernel is launched on.  Prints one JSON line:
   value     effective TFLOP/s = unmasked FLOPs (4*D per visible (query, key)
             pair per query head) / time per step
   roofline  matrix-core bound: achieved TFLOP/s of the attention kernel (its
-            algorithmic FLOPs per launch / its average launch duration) vs the
-            MI355X dense bf16 peak; traffic = HBM bytes per launch from the
-            committed rocprofv3 counter summary, or null when the kernel
-            source changed since the counters were taken
+            algorithmic FLOPs per launch / its average launch duration, which
+            is the event-timed time per step: a step is exactly one launch of
+            that kernel; the committed rocprofv3 kernel trace of the same
+            command gives the same average) vs the MI355X dense bf16 peak;
+            traffic = HBM bytes per launch from the committed rocprofv3 counter
+            summary, or null when the kernel source changed since the counters
+            were taken
+  clock     the graphics clock sampled with amd-smi while the untimed steps
+            run, and the same throughput as a percentage of CUs x 4096 FLOP
+            x that clock (the dense peak at the clock the chip actually holds)
+  inputs_sha256  SHA-256 of the bytes of q, k and v as uploaded
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload,
-            timed on the host's cores
+            timed on the host's cores (cores = the BLAS threads it ran on,
+            host_cpu_count = os.cpu_count())
 
   parity    max abs error of the GPU output against the oracle's on that
             same sample (the oracle runs nowhere else in this script)
@@ -101,36 +109,97 @@ def max_abs_err(got, ref) -> float:
     return float(np.max(np.abs(np.asarray(got, dtype=np.float64) - ref)))
 
 
-def cpu_baseline(w, inputs, n_heads: int):
-    """Time the oracle on the first n_heads query heads of batch 0 (all rows).
-    Returns (summary, oracle output [1, n_heads, S, D])."""
+def cpu_baseline(w, inputs, n_heads: int, seconds: float):
+    """Time the oracle on batch 0 (all rows), one key/value head's query heads
+    at a time, up to n_heads query heads or until `seconds` have passed.
+    Returns (summary, oracle output [1, heads done, S, D])."""
+    import numpy as np
+
     import oracle
 
     threads = host_threads()
     G = w.Hq // w.Hkv
     n_heads = min(n_heads, w.Hq)
-    n_kv = (n_heads + G - 1) // G
-    q = inputs["q"][:1, :n_heads]
-    k = inputs["k"][:1, :n_kv]
-    v = inputs["v"][:1, :n_kv]
-    # keep the head map: query head a of the sample still reads kv head a // G
-    Hs = n_kv * G
-    if Hs != n_heads:
-        q = inputs["q"][:1, :Hs]
-        n_heads = Hs
+    refs = []
     t0 = time.perf_counter()
-    ref = oracle.attention(q, k, v, w.mask, w.window, w.global_idx, scale=w.scale)
+    while sum(r.shape[1] for r in refs) < n_heads and time.perf_counter() - t0 < seconds:
+        h = len(refs)  # key/value head; its query heads h*G .. h*G + G - 1 keep the head map
+        refs.append(oracle.attention(inputs["q"][:1, h * G:(h + 1) * G], inputs["k"][:1, h:h + 1],
+                                     inputs["v"][:1, h:h + 1], w.mask, w.window, w.global_idx,
+                                     scale=w.scale))
     dt = time.perf_counter() - t0
-    flops = oracle.effective_flops(1, n_heads, w.S, w.D, w.mask, w.window, w.global_idx)
+    ref = np.concatenate(refs, axis=1)
+    done = ref.shape[1]
+    flops = oracle.effective_flops(1, done, w.S, w.D, w.mask, w.window, w.global_idx)
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "host_cpu_count": os.cpu_count(),
         "kind": "oracle",
-        "sample": f"batch 0, query heads 0..{n_heads - 1} of {w.Hq}, all {w.S} rows "
+        "sample": f"batch 0, query heads 0..{done - 1} of {w.Hq}, all {w.S} rows "
                   f"({flops:.3e} effective FLOPs in {dt:.2f} s, fp64 NumPy)",
         "seconds": dt,
     }, ref
+
+
+def inputs_sha256(*tensors) -> dict:
+    """SHA-256 of each tensor's bytes (q, k, v as uploaded)."""
+    import torch
+
+    out = {}
+    for name, t in zip(("q", "k", "v"), tensors):
+        b = t.detach().contiguous().cpu().view(torch.uint8).numpy().tobytes()
+        out[name] = hashlib.sha256(b).hexdigest()
+    return out
+
+
+class ClockSampler:
+    """Samples the graphics clock with amd-smi in a background thread while
+    the GPU is busy (None where the tool or its output is unavailable)."""
+
+    def __init__(self):
+        import threading
+
+        self.mhz = []
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _gfx_clocks(node, found):
+        if isinstance(node, dict):
+            for key, val in node.items():
+                if isinstance(key, str) and key.lower().startswith("gfx") and isinstance(val, dict):
+                    clk = val.get("clk")
+                    if isinstance(clk, dict) and isinstance(clk.get("value"), (int, float)):
+                        found.append(float(clk["value"]))
+                ClockSampler._gfx_clocks(val, found)
+        elif isinstance(node, list):
+            for x in node:
+                ClockSampler._gfx_clocks(x, found)
+
+    def _run(self):
+        import subprocess
+
+        try:
+            res = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"],
+                                 capture_output=True, text=True, timeout=10)
+            found = []
+            self._gfx_clocks(json.loads(res.stdout), found)
+            found = [x for x in found if x > 0]
+            if found:
+                self.mhz.append(sum(found) / len(found))
+        except Exception:  # noqa: BLE001 - the clock is an optional extra
+            pass
+
+    def start(self):
+        self._thread.start()
+
+    def alive(self):
+        return self._thread.is_alive()
+
+    def result(self):
+        self._thread.join(timeout=15)
+        return self.mhz[0] if self.mhz else None
 
 
 def calibration_copy(mib: int, dev):
@@ -167,6 +236,7 @@ def decode_cpu_baseline(w, inputs, lens, n_seq: int = 1):
         "value": nbytes / dt / 1e9,
         "unit": "GB/s",
         "cores": threads,
+        "host_cpu_count": os.cpu_count(),
         "kind": "oracle",
         "sample": f"sequences 0..{n - 1} of {w.B}, all {w.Hq} heads and {w.Sq} new positions "
                   f"({nbytes} cache bytes in {dt:.2f} s, fp64 NumPy)",
@@ -294,6 +364,7 @@ def ex_cpu_baseline(w, inputs, seconds: float = 10.0):
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "host_cpu_count": os.cpu_count(),
         "kind": "oracle",
         "sample": f"batch 0, query heads 0..{n - 1} of {w.Hq} (as many as about {seconds:.0f} s "
                   f"allows), all {w.Sq} rows ({flops:.3e} effective FLOPs in {dt:.2f} s, "
@@ -313,11 +384,22 @@ def time_steps(step, stream, args):
 
     t_warm = time.perf_counter()
     prewarm_steps = 0
-    while time.perf_counter() - t_warm < args.prewarm:
+    # the clock sample runs while the steps keep the GPU busy (the untimed
+    # phase is extended until it has finished, by at most 15 s)
+    sampler = ClockSampler() if getattr(args, "clock", False) else None
+    started = False
+    while True:
+        el = time.perf_counter() - t_warm
+        waiting = started and sampler.alive()
+        if (el >= args.prewarm and not waiting) or el > args.prewarm + 15:
+            break
         for _ in range(5):
             step()
         prewarm_steps += 5
         torch.cuda.synchronize()
+        if sampler is not None and not started and el > 0.3:
+            sampler.start()
+            started = True
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -329,6 +411,8 @@ def time_steps(step, stream, args):
     torch.cuda.synchronize()
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     spread = {"median_ms": round(per[len(per) // 2], 6), "min_ms": round(per[0], 6)}
+    if started:
+        args.clock_mhz = sampler.result()
     return ev[0].elapsed_time(ev[-1]) / args.steps, prewarm_steps, spread
 
 
@@ -513,6 +597,17 @@ def bench_ex(args, name):
     return 0
 
 
+def clock_line(tflops, dtype, cus, mhz):
+    """The sampled graphics clock and the throughput as a percentage of the
+    dense matrix-core peak at that clock (CUs x FLOP/clk/CU x clock)."""
+    per_clk = {"bf16": 4096, "fp8": 8192}.get(dtype)
+    if mhz is None or per_clk is None:
+        return {"sclk_mhz": mhz, "pct_of_peak_at_sclk": None}
+    peak = cus * per_clk * mhz * 1e6 / 1e12
+    return {"sclk_mhz": round(mhz, 1), "peak_at_sclk_tflops": round(peak, 1),
+            "pct_of_peak_at_sclk": round(100.0 * tflops / peak, 2)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -520,9 +615,11 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-heads", type=int, default=32)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="oracle time budget of the cpu_baseline sample of a workload with "
-                         "separate query and key lengths")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="oracle time budget of the cpu_baseline sample (whole key/value "
+                         "groups of batch 0 until it is spent)")
+    ap.add_argument("--no-clock", dest="clock", action="store_false",
+                    help="do not sample the graphics clock with amd-smi")
     ap.add_argument("--prewarm", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -615,10 +712,13 @@ def main(argv=None):
         "cold_cache": cold,
         "gpu": torch.cuda.get_device_name(dev),
         "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
+        "clock": clock_line(tflops, w.dtype, torch.cuda.get_device_properties(dev)
+                            .multi_processor_count, getattr(args, "clock_mhz", None)),
+        "inputs_sha256": inputs_sha256(q, k, v),
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"], ref = cpu_baseline(w, inputs, args.cpu_heads)
+        result["cpu_baseline"], ref = cpu_baseline(w, inputs, args.cpu_heads, args.cpu_seconds)
         if not args.no_parity:
             got = out[:1, :ref.shape[1]].float().cpu().numpy()
             result["parity"] = {"sample": "the cpu_baseline sample",

@@ -148,6 +148,10 @@ RAGGED = [
     (3, 4, 2, 400, 150, 128, "causal", 0, (400, 33, 150), (150, 150, 0), True),
     (2, 4, 4, 64, 1000, 128, "full", 0, (64, 30), (1000, 999), False),
     (4, 8, 8, 513, 513, 64, "causal_window", 128, (513, 256, 255, 129), (513, 256, 255, 129), True),
+    # windows near INT_MAX with queries ahead of their keys (position - window
+    # must not wrap in 32 bits)
+    (3, 8, 2, 300, 200, 128, "causal_window", 2**31 - 1, (300, 100, 50), (200, 40, 50), False),
+    (2, 4, 4, 257, 129, 64, "causal_window", 2**31 - 2, (257, 200), (129, 1), True),
 ]
 
 
@@ -164,6 +168,16 @@ def test_fwd_ex_padded_batches(device, case):
         err = run_ex(device, B, Hq, Hkv, Sq, Skv, D, mask, window, layout, layout,
                      seed=Sq + Skv + B, slopes=slopes, q_len=q_len, kv_len=kv_len)
         assert err <= TOL["bf16"], (layout, err)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("D", [64, 128])
+def test_fwd_ex_huge_window_sq_gt_skv(device, D):
+    """Sq > Skv (the first queries see no key) with windows near INT_MAX: the
+    same result as the causal mask."""
+    for w in (2**31 - 1, 2**30 + 5):
+        err = run_ex(device, 1, 8, 2, 333, 130, D, "causal_window", w, seed=D + 3)
+        assert err <= TOL["bf16"], (w, err)
 
 
 @pytest.mark.gpu

@@ -122,3 +122,64 @@ def test_workload_full_size(device, name):
                    seed=w.seed, scale=w.scale, rows=rows)
     print(f"{name}: max abs err {err:.3e}", flush=True)
     assert err <= TOL[w.dtype], err
+
+
+# Eight and more query heads per key/value head: a work item packs eight query
+# heads (one 32-row wave per head), and the global rows of the local+global
+# mask run with one wave per head (no key split to merge).  Hkv = 1 is
+# multi-query attention ("Transformer 演进与变体", section GQA：分组查询注意力:
+# a group size equal to the head count is MQA; the 64-head, 8-group layout).
+WIDE_GROUPS = []
+_heads = [(8, 1), (16, 2), (32, 1), (32, 4), (16, 1), (64, 8)]
+for D in (64, 128):
+    for mi, mask in enumerate(("full", "causal", "causal_window", "local_global")):
+        for si, S in enumerate((1, 65, 129, 1000)):
+            Hq, Hkv = _heads[(mi * 4 + si + D // 64) % len(_heads)]
+            window = {"causal_window": (1, 64, 100, 333)[si], "local_global": (0, 3, 64, 150)[si]}
+            g = tuple(x for x in (0, 64, 500, 999) if x < S) if mask == "local_global" else ()
+            WIDE_GROUPS.append((1 + (si % 2), Hq, Hkv, S, D, mask, window.get(mask, 0), g))
+
+
+@pytest.mark.parametrize("case", WIDE_GROUPS,
+                         ids=lambda c: f"D{c[4]}-S{c[3]}-{c[5]}-H{c[1]}x{c[2]}")
+def test_wide_groups(device, case):
+    B, Hq, Hkv, S, D, mask, window, g = case
+    err = run_case(device, B, Hq, Hkv, S, D, "bf16", mask, window, g, seed=S + Hq + D)
+    assert err <= TOL["bf16"], err
+
+
+def _all_rows(device, w, head_lo, head_hi):
+    """Every output row of query heads [head_lo, head_hi) of a workload
+    against the oracle (the heads' key/value heads are sliced with them)."""
+    import torch
+    import transformer_attention_attn_amd as attn
+
+    G = w.Hq // w.Hkv
+    inp = workloads.make_inputs(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype, w.seed)
+    q, k, v = workloads.to_torch(inp, w.dtype, device)
+    o = attn.fwd(q, k, v, mask=w.mask, window=w.window,
+                 global_idx=list(w.global_idx) or None, scale=w.scale)
+    torch.cuda.synchronize()
+    got = o[:, head_lo:head_hi].float().cpu().numpy().astype(np.float64)
+    ref = oracle.attention(inp["q"][:, head_lo:head_hi], inp["k"][:, head_lo // G:head_hi // G],
+                           inp["v"][:, head_lo // G:head_hi // G], w.mask, w.window, w.global_idx,
+                           scale=w.scale)
+    return float(np.max(np.abs(got - ref)))
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_window_workload_all_rows(device, part):
+    """The 16384-position sliding-window workload: every row of eight query
+    heads (two key/value heads) per case, all 32 heads over the four cases."""
+    w = workloads.WORKLOADS["window_gqa_bf16_s16384"]
+    err = _all_rows(device, w, 8 * part, 8 * part + 8)
+    print(f"window workload heads {8 * part}..{8 * part + 7}: max abs err {err:.3e}", flush=True)
+    assert err <= TOL["bf16"], err
+
+
+def test_local_global_workload_all_rows(device):
+    """The local+global workload: every row of all 12 heads."""
+    w = workloads.WORKLOADS["local_global_bf16_s8192"]
+    err = _all_rows(device, w, 0, w.Hq)
+    print(f"local+global workload: max abs err {err:.3e}", flush=True)
+    assert err <= TOL["bf16"], err

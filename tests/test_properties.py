@@ -96,17 +96,18 @@ def test_bitwise_reproducible_and_no_allocation(device):
 
     w = workloads.WORKLOADS["causal_gqa_bf16_s8192"]
     _, (q, k, v) = _inputs(device, w.B, w.Hq, w.Hkv, w.S, w.D, seed=w.seed)
-    out = torch.empty_like(q)
+    outs = [torch.empty_like(q) for _ in range(4)]
+    attn.fwd(q, k, v, mask="causal", out=outs[0])  # first launch loads the code object
     torch.cuda.synchronize()
     free0 = torch.cuda.mem_get_info(device)[0]
-    ref = attn.fwd(q, k, v, mask="causal", out=out).clone()
-    for _ in range(3):
-        attn.fwd(q, k, v, mask="causal", out=out)
-        torch.cuda.synchronize()
-        assert torch.equal(out, ref)
+    for o in outs:
+        attn.fwd(q, k, v, mask="causal", out=o)
+    torch.cuda.synchronize()
     free1 = torch.cuda.mem_get_info(device)[0]
-    # ref's clone is the only new allocation (64 MiB, through torch's caching allocator)
-    assert free0 - free1 <= ref.numel() * 2 + (64 << 20)
+    # every buffer existed before the first reading: the calls allocate nothing
+    assert free0 == free1, free0 - free1
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
 
 
 def test_non_default_stream(device):

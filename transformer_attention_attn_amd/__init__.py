@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     STATUS,
     AttnError,
     FwdArgs,
+    check_devices,
     decode,
     decode_raw,
     decode_workspace_bytes,

@@ -118,6 +118,19 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
+def check_devices(q, **tensors) -> None:
+    """Raise ValueError unless q and every given tensor (None entries are
+    skipped) is a GPU tensor on q's device.  Runs before every launch: a host
+    pointer, or one on another GPU, must never reach a kernel."""
+    if not getattr(q, "is_cuda", False):
+        raise ValueError("q must be a GPU tensor")
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not getattr(t, "is_cuda", False) or t.device != q.device:
+            raise ValueError(f"{name} must be a GPU tensor on q's device ({q.device})")
+
+
 def _mask_id(mask) -> int:
     if isinstance(mask, str):
         return MASKS[mask]
@@ -171,6 +184,7 @@ def fwd(q, k, v, mask="causal", window: int = 0, global_idx=None, scale: Optiona
         out = torch.empty(q.shape, dtype=odt, device=q.device)
     elif out.shape != q.shape or out.dtype != odt or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous {odt} tensor shaped like q")
+    check_devices(q, k=k, v=v, out=out)
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
     if stream is None:
@@ -251,6 +265,8 @@ def fwd_ex(q, k, v, mask="causal", window: int = 0, scale: Optional[float] = Non
         out = torch.empty((B, Hq, Sq, D), dtype=q.dtype, device=q.device)
     elif tuple(out.shape) != (B, Hq, Sq, D) or out.dtype != q.dtype or out.stride(3) != 1:
         raise ValueError("out must be shaped like q with a contiguous last dim")
+    check_devices(q, k=k, v=v, out=out, alibi_slopes=alibi_slopes, q_len=q_len,
+                  kv_len=kv_len, block_layout=block_layout)
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
     a = FwdArgs()
@@ -362,6 +378,8 @@ def decode(q, k_cache, v_cache, cache_len=None, mask="causal", scale: Optional[f
     need = decode_workspace_bytes(B, Hq, Hkv, Sq, Smax, D, mask)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    check_devices(q, k_cache=k_cache, v_cache=v_cache, out=out, cache_len=cache_len,
+                  workspace=workspace)
     ws_ptr = workspace.data_ptr() if workspace is not None else 0
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:

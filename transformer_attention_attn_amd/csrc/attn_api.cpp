@@ -250,7 +250,12 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
       (a->B > 1 && os[0] == 0) || (a->Hq > 1 && os[1] == 0))
     return ATTN_ERR_ALIAS;
 
-  Sched s = attn::make_sched(a->B, a->Hq, a->Hkv, a->Sq, a->mask_kind, a->window, 0,
+  // A window of Skv keys or more admits every key at or before the query (a
+  // query's key position is at most Skv - 1), so larger windows are clamped to
+  // Skv: the kernels then form position - window (positions down to -Sq) in
+  // 32-bit arithmetic without overflow.
+  const int window = a->mask_kind == ATTN_MASK_CAUSAL_WINDOW ? std::min(a->window, a->Skv) : 0;
+  Sched s = attn::make_sched(a->B, a->Hq, a->Hkv, a->Sq, a->mask_kind, window, 0,
                              attn::kBf16Rows, attn::bf16_keys_per_tile(a->D), 1,
                              attn::kBf16GlobalRows);
   if (s.n_items > 0x7fffffffLL) return ATTN_ERR_SHAPE;
