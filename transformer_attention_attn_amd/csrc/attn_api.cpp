@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -70,6 +71,23 @@ Checked check_args(int B, int Hq, int Hkv, int S, int D, int mask_kind, int wind
                            attn::bf16_keys_per_tile(D), 1, attn::kBf16GlobalRows);
   if (c.s.n_items > 0x7fffffffLL) { c.status = ATTN_ERR_SHAPE; return c; }
   return c;
+}
+
+// Compute units of the device a stream launches on (cached per device; 0 when
+// the runtime cannot tell, which keeps the one-workgroup-per-item launch).
+int device_cus(hipStream_t stream) {
+  static std::atomic<int> cache[64];
+  int dev = -1;
+  if (stream ? hipStreamGetDevice(stream, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+    return 0;
+  if (dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -183,10 +201,21 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq
   std::copy(c.gpos, c.gpos + c.n_global, p.gpos);
 
   hipStream_t st = (hipStream_t)stream;
-  hipError_t err = dtype == ATTN_DTYPE_BF16
-                       ? (D == 64 ? attn::launch_bf16_d64(p, st) : attn::launch_bf16_d128(p, st))
-                   : dtype == ATTN_DTYPE_FP8_E4M3 ? attn::launch_fp8_d128(p, st)
-                                                  : attn::launch_fp32(p, D, st);
+  hipError_t err;
+  if (dtype == ATTN_DTYPE_BF16 && D == 128 && mask_kind != ATTN_MASK_LOCAL_GLOBAL &&
+      p.qmode == 0) {
+    // more items than CUs: one persistent workgroup per CU walks them (the
+    // persistent kernel takes q as given, so negative and zero scales, which
+    // flip or zero q, keep the one-workgroup-per-item launch)
+    const int cus = device_cus(st);
+    err = (cus > 0 && c.s.n_items > cus) ? attn::launch_bf16_pers_d128(p, cus, st)
+                                         : attn::launch_bf16_d128(p, st);
+  } else {
+    err = dtype == ATTN_DTYPE_BF16
+              ? (D == 64 ? attn::launch_bf16_d64(p, st) : attn::launch_bf16_d128(p, st))
+          : dtype == ATTN_DTYPE_FP8_E4M3 ? attn::launch_fp8_d128(p, st)
+                                         : attn::launch_fp32(p, D, st);
+  }
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -70,6 +70,9 @@ hipError_t launch_fp32(const KParams& p, int D, hipStream_t stream);
 hipError_t launch_decode(const DParams& p, int D, hipStream_t stream);  // kernel_decode.hip
 hipError_t launch_bf16_d64(const KParams& p, hipStream_t stream);   // kernel_bf16.hip, D = 64 build
 hipError_t launch_bf16_d128(const KParams& p, hipStream_t stream);  // kernel_bf16.hip, D = 128 build
+// persistent form of the D = 128 dense square kernel (masks FULL, CAUSAL,
+// CAUSAL_WINDOW): `grid` workgroups walk the s.n_items work items
+hipError_t launch_bf16_pers_d128(const KParams& p, int grid, hipStream_t stream);
 // FP8 (E4M3) inputs, bf16 output, D = 128, masks without global tokens
 hipError_t launch_fp8_d128(const KParams& p, hipStream_t stream);  // kernel_fp8.hip
 

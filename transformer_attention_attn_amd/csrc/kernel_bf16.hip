@@ -94,6 +94,10 @@ constexpr int dma_after(int i, int l, int ndma) {
     if (((k + 1) * l) / (ndma + 1) - 1 == i) ++c;
   return c;
 }
+template <int M>
+struct ModeC {
+  static constexpr int value = M;
+};
 // The operand sequence of a matrix block.  MODE 0: P.V only (O^T += V^T P^T
 // over the NDB output blocks, 2*NKB 16-key steps); MODE 1: S only (S^T = K Q^T
 // over the NKB 32-key blocks); MODE 2: P.V then S as one sequence, so the K
@@ -170,6 +174,40 @@ __device__ __forceinline__ void block_run(const unsigned* vbd, const unsigned* k
   block_steps<MODE, ROWB, NDB, NDC, NKB, PF, 0, NDMA>(ring, vbd, kbd, pb, qf, oacc, sc, dma);
 }
 
+// The lane id, read afresh: values derived from it are recomputed where used
+// instead of being held (and spilled) across the persistent kernel's items.
+__device__ __forceinline__ unsigned fresh_lane() {
+  unsigned l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// A buffer descriptor over [base, base + bytes) built from wave-uniform
+// values: the fields are read from the first lane, so the descriptor sits in
+// scalar registers even where the compiler cannot prove them uniform (a
+// descriptor in vector registers turns every access into a loop over lanes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((unsigned long long)hi << 32) | lo), (short)0,
+                                           n, 0x00020000);
+}
+
+// Persistent launches (one workgroup per CU): round k of workgroup w takes
+// item k*W + w on even rounds and the mirrored slot on odd rounds, mirrored
+// in groups of eight so that the item's id modulo 8 (its key/value head when
+// there are eight pairs) stays w % 8, the XCD the workgroup runs on.  With the
+// causal heaviest-first order the mirrored rounds pair long items with short
+// ones, so the workgroups' tile counts come out nearly equal.  -1: no item.
+__device__ __forceinline__ int pers_item_id(int k, int w, int W, int n_items) {
+  int slot = w;
+  if (k & 1) slot = (W % 8 == 0) ? (W - 8 - (w & ~7)) + (w & 7) : W - 1 - w;
+  const long long id = (long long)k * W + slot;
+  return id < n_items ? (int)id : -1;
+}
+
 template <int D>
 struct Cfg {
   static constexpr int NDC = D / 16;            // 16-dim reduction steps of S^T
@@ -200,9 +238,21 @@ constexpr int kWavesPerEu = HD == 64 ? 4 : 2;
 // of each tensor, optional per-sequence lengths (right padding); the
 // local+global mask is not offered there.  GEN = 2: GEN = 1 plus the ALiBi
 // bias.  GEN = 3: GEN = 1 with a block-sparse layout (square, no lengths).
-template <int D, int MASK, int GEN = 0>
+// LDS for the global token positions, only in kernels of the local+global
+// mask (the persistent kernels use all 160 KB otherwise)
+template <bool LG>
+__device__ __forceinline__ int* gpos_storage() {
+  if constexpr (LG) {
+    __shared__ int gpos[kMaxGlobal];
+    return gpos;
+  } else {
+    return nullptr;
+  }
+}
+
+template <int D, int MASK, int GEN = 0, int PERS = 0>
 __global__ __launch_bounds__(kBf16Threads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu, kWavesPerEu)))
-void attn_fwd_bf16(KParams p) {
+void attn_fwd_bf16(KParams p_arg) {
   using C = Cfg<D>;
   constexpr bool ALIBI = GEN == 2;
   constexpr bool SPARSE = GEN == 3;
@@ -211,16 +261,66 @@ void attn_fwd_bf16(KParams p) {
 
   // the global-row path needs a K and a V tile of GK keys per wave
   constexpr int LDS_G = (MASK == MASK_LOCAL_GLOBAL) ? kBf16Waves * 2 * GK * ROWB : 0;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * BUF > LDS_G ? NSTAGE * BUF : LDS_G];
-  __shared__ int gpos_s[kMaxGlobal];
+  constexpr int LDS_MAIN = NSTAGE * BUF > LDS_G ? NSTAGE * BUF : LDS_G;
+  // PERS: the next item's Q of wave group 0 (32 rows per wave, laid out like
+  // the first 32 rows of a K tile)
+  constexpr int LDS_Q = PERS ? 4 * 32 * ROWB : 0;
+  static_assert(LDS_MAIN + LDS_Q + (MASK == MASK_LOCAL_GLOBAL ? kMaxGlobal * 4 : 0) <= 160 * 1024,
+                "LDS budget of one CU");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_MAIN + LDS_Q];
+  int* const gpos_s = gpos_storage<MASK == MASK_LOCAL_GLOBAL>();
 
-  const Sched& s = p.s;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int grp = wave >> 2;  // wave group of the ping-pong schedule
   const int l32 = lane & 31;
   const int hf = lane >> 5;  // lane half: selects the k sub-range of an MFMA operand
-  const Item it = decode_item(s, blockIdx.x);
+  if (MASK == MASK_LOCAL_GLOBAL) {
+    if (tid < kMaxGlobal) gpos_s[tid] = tid < p_arg.s.n_global ? p_arg.gpos[tid] : 0;
+    __syncthreads();
+  }
+  // PERS: the workgroup walks its list of items (see pers_item_id); else it
+  // runs the one item blockIdx.x.  The key/value tiles of consecutive items
+  // form one stream (gofs: the place of this item's first tile in it; stream
+  // tile t lives in stage t % NSTAGE).
+  int gofs = 0;
+  // PERS: the items of this and the next two rounds, decoded once each and
+  // carried from round to round (id < 0: none)
+  int id_n1 = -1, id_n2 = -1;
+  Item it_n1{}, it_n2{};
+  bf16x8 qf[NDC];  // Q^T operand of the current item
+  for (int round = 0; PERS || round == 0; ++round) {
+  // PERS: the arguments are read again for every item from the kernel
+  // argument segment, through a pointer the compiler cannot see through, so
+  // nothing derived from them is held in registers across items (the item's
+  // code runs at the register limit of two waves per SIMD)
+  typedef const __attribute__((address_space(4))) KParams* KArgPtr;
+  KArgPtr kap = (KArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  if constexpr (PERS) asm volatile("" : "+s"(kap));
+  KParams p_item;
+  __builtin_memcpy(&p_item, (const KParams*)kap, sizeof(KParams));
+  const KParams& p = PERS ? p_item : p_arg;
+  const Sched& s = p.s;
+  Item it;
+  if constexpr (PERS) {
+    if (round == 0) {
+      const int id0 = pers_item_id(0, blockIdx.x, gridDim.x, (int)s.n_items);
+      if (id0 < 0) break;
+      it = decode_item(s, id0);
+      id_n1 = pers_item_id(1, blockIdx.x, gridDim.x, (int)s.n_items);
+      if (id_n1 >= 0) it_n1 = decode_item(s, id_n1);
+    } else {
+      if (id_n1 < 0) break;
+      it = it_n1;
+      id_n1 = id_n2;
+      it_n1 = it_n2;
+    }
+    id_n2 = id_n1 >= 0 ? pers_item_id(round + 2, blockIdx.x, gridDim.x, (int)s.n_items) : -1;
+    if (id_n2 >= 0) it_n2 = decode_item(s, id_n2);
+  } else {
+    it = decode_item(s, blockIdx.x);
+  }
   // valid query rows SQ and keys SK of this sequence, and the key position
   // OFF of query row 0 (GEN: queries aligned to the end of the keys; with
   // per-sequence lengths the rest of the rows and keys are padding)
@@ -232,11 +332,6 @@ void attn_fwd_bf16(KParams p) {
   }
   const int SKA = GEN ? imax(SK, 1) : SK;  // rows addressed by the tile loads (row 0 always exists)
 
-  if (MASK == MASK_LOCAL_GLOBAL) {
-    if (tid < kMaxGlobal) gpos_s[tid] = tid < s.n_global ? p.gpos[tid] : 0;
-    __syncthreads();
-  }
-
   // ---- rows of this wave -------------------------------------------------
   const int wph = kBf16Waves / s.HP;              // waves per query head
   const int a = it.kvh * s.G + it.hg * s.HP + wave / wph;
@@ -247,7 +342,7 @@ void attn_fwd_bf16(KParams p) {
     r0 = it.blk * s.BMh;
     r1 = imin(r0 + s.BMh, SQ) - 1;
     const int q0 = r0 + rpart * 32;
-    q_row = q0 + l32;
+    q_row = q0 + (PERS ? (int)(fresh_lane() & 31) : l32);
     row_valid = q_row < SQ;
     wqa = q0;
     wqb = imin(q0 + 31, SQ - 1);
@@ -286,11 +381,13 @@ void attn_fwd_bf16(KParams p) {
   const int KRB = GEN ? (int)p.ks[2] * 2 : ROWB, VRB = GEN ? (int)p.vs[2] * 2 : ROWB;
 
   // ---- Q^T operand: lane holds query q_row, dims 16*dc + 8*hf + [0, 8) -----
-  bf16x8 qf[NDC];
-  {
-    const u32x4 flip = (p.qmode == 1) ? u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}
-                                      : u32x4{0u, 0u, 0u, 0u};
-    const bool zero = (p.qmode == 2) || !row_valid;
+  // PERS: loaded inside each wave group's part of the schedule (see below)
+  auto load_q_global = [&]() {
+    // (the persistent kernel runs with plain Q only)
+    const u32x4 flip = (!PERS && p.qmode == 1)
+                           ? u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}
+                           : u32x4{0u, 0u, 0u, 0u};
+    const bool zero = (!PERS && p.qmode == 2) || !row_valid;
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
       u32x4 x = {0u, 0u, 0u, 0u};
@@ -298,7 +395,8 @@ void attn_fwd_bf16(KParams p) {
       x ^= flip;
       qf[dc] = __builtin_bit_cast(bf16x8, x);
     }
-  }
+  };
+  if constexpr (!PERS) load_q_global();
 
   // ---- block-sparse tile list (GEN = 3) ------------------------------------
   // The item's key tiles in order, one per lane of lv[c] (64 per register):
@@ -361,6 +459,27 @@ void attn_fwd_bf16(KParams p) {
     key_range(s, it.is_global, r0, r1, &klo, &khi);
   }
   const int kt_lo = klo / BN, kt_hi = khi / BN;
+  // PERS: the first tiles of the next two items (the loads run two tiles
+  // ahead, across item boundaries): key/value head index b * Hkv + kvh (-1:
+  // none), first tile, tile count
+  int nx_kv = -1, nx_lo = 0, nx_n = 0, nx2_kv = -1, nx2_lo = 0;
+  if constexpr (PERS) {
+    if (id_n1 >= 0) {
+      const int a0 = it_n1.blk * s.BMh, a1 = imin(a0 + s.BMh, s.S) - 1;
+      int lo1, hi1;
+      key_range(s, 0, a0, a1, &lo1, &hi1);
+      nx_kv = it_n1.b * s.Hkv + it_n1.kvh;
+      nx_lo = lo1 / BN;
+      nx_n = hi1 / BN - nx_lo + 1;
+      if (id_n2 >= 0) {
+        const int b0 = it_n2.blk * s.BMh, b1 = imin(b0 + s.BMh, s.S) - 1;
+        int lo2, hi2;
+        key_range(s, 0, b0, b1, &lo2, &hi2);
+        nx2_kv = it_n2.b * s.Hkv + it_n2.kvh;
+        nx2_lo = lo2 / BN;
+      }
+    }
+  }
   const int has_strip = (MASK == MASK_LOCAL_GLOBAL && !it.is_global && s.n_global > 0) ? 1 : 0;
   const int n_it = SPARSE ? n_list
                           : (GEN && (khi < klo || r1 < r0)) ? 0 : (kt_hi - kt_lo + 1) + has_strip;
@@ -404,18 +523,69 @@ void attn_fwd_bf16(KParams p) {
   // tile's valid rows and a 32-bit lane offset clamped to the last valid row,
   // so no lane is out of range.
   const int k_off = srow * KRB + k_col, v_off = srow * VRB + v_col;
-  auto dma_band = [&](bool isk, int iter, int st, int n) {
+  // PERS: byte bases of the next two items' key and value rows
+  const char* nx_k = nullptr;
+  const char* nx_v = nullptr;
+  const char* nx2_k = nullptr;
+  const char* nx2_v = nullptr;
+  if constexpr (PERS) {
+    if (nx_kv >= 0) {
+      nx_k = (const char*)p.k + (size_t)nx_kv * S * ROWB;
+      nx_v = (const char*)p.v + (size_t)nx_kv * S * ROWB;
+    }
+    if (nx2_kv >= 0) {
+      nx2_k = (const char*)p.k + (size_t)nx2_kv * S * ROWB;
+      nx2_v = (const char*)p.v + (size_t)nx2_kv * S * ROWB;
+    }
+  }
+  // The buffer descriptor of one K or V tile (iter: the item's tile index;
+  // PERS: tiles past the item's last are the next items' first tiles) over
+  // its valid rows, with the offset clamp of its last valid row.  Built once
+  // per block, shared by the block's direct loads of that tile.
+  struct TileRsrc {
+    __amdgpu_buffer_rsrc_t r;
+    int lclamp;
+  };
+  auto tile_rsrc = [&](bool isk, int iter) -> TileRsrc {
+    const char* base = (const char*)(isk ? kp : vp);
+    int kt = tile_kt(iter);
+    TileRsrc t;
+    if constexpr (PERS) {
+      if (iter >= n_it) {
+        if (iter - n_it < nx_n) {
+          base = isk ? nx_k : nx_v;
+          kt = nx_lo + iter - n_it;
+        } else {
+          base = isk ? nx2_k : nx2_v;
+          kt = nx2_lo;
+        }
+        if (base == nullptr) {
+          // past the end of the stream: a descriptor of no bytes (its loads
+          // are out of range and read nothing) into a stage read no more
+          t.r = __builtin_amdgcn_make_buffer_rsrc((void*)p.k, (short)0, 0, 0x00020000);
+          t.lclamp = 0;
+          return t;
+        }
+      }
+    }
     // tiles past the last one of the sequence load the last tile instead
-    const int row0 = imin(tile_kt(iter), (SKA - 1) / BN) * BN;
+    const int row0 = imin(kt, (SKA - 1) / BN) * BN;
     const int nrows = imin(SKA - row0, BN);
     const int RB = isk ? KRB : VRB;
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const char*)(isk ? kp : vp) + (size_t)row0 * RB), (short)0,
-        (nrows - 1) * RB + ROWB, 0x00020000);
-    const int off = imin((isk ? k_off : v_off) + n * RSTEP * RB,
-                         (nrows - 1) * RB + (isk ? k_col : v_col));
-    dma16_buffer(r, smem + (isk ? 0 : NSTAGE * REG) + st * REG + (n * 4 + gw) * 1024, off, 0);
+    t.r = __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)row0 * RB), (short)0,
+                                            (nrows - 1) * RB + ROWB, 0x00020000);
+    t.lclamp = (nrows - 1) * RB + (isk ? k_col : v_col);
+    return t;
   };
+  auto dma_tile_at = [&](bool isk, const TileRsrc& t, int st, int n, int lb) {
+    const int RB = isk ? KRB : VRB;
+    const int off = imin(lb + n * RSTEP * RB, t.lclamp);
+    dma16_buffer(t.r, smem + (isk ? 0 : NSTAGE * REG) + st * REG + (n * 4 + gw) * 1024, off, 0);
+  };
+  auto dma_tile = [&](bool isk, const TileRsrc& t, int st, int n) {
+    dma_tile_at(isk, t, st, n, isk ? k_off : v_off);
+  };
+  auto dma_band = [&](bool isk, int iter, int st, int n) { dma_tile(isk, tile_rsrc(isk, iter), st, n); };
 
   // Per-wave tile class.  Tiles EMPTY for this wave (only at the ends of its
   // range, or when it holds no rows) are processed as fully masked.
@@ -436,11 +606,33 @@ void attn_fwd_bf16(KParams p) {
   // ---- operand reads -------------------------------------------------------
   // K operand (key 32*kbk + l32, dims 16*dc + 8*hf + [0,8)): logical chunk
   // 2*dc + hf, physical (2*dc + hf) ^ ksw(l32) (ksw(32*kbk + l32) = ksw(l32)).
-  int k_rd[NDC];  // per-lane part for each dc; the 32-key block is an immediate
+  // The read address of step dc is one lane base XOR (dc << 5): (2*dc + hf)
+  // ^ x = 2*(dc ^ (x >> 1)) + (hf ^ (x & 1)) with x = ksw(l32), and 32*(dc ^
+  // xh) = 32*dc ^ 32*xh touches bits 5-7 only, which no other term of the
+  // address (row, chunk bit 4, a tile base aligned to 1 KiB) does.
+  const int k_lane = l32 * ROWB + 16 * (hf ^ (C::ksw(l32) & 1)) + 32 * (C::ksw(l32) >> 1);
+  // PERS, wave group 0 from the second item on: Q from the rows its waves
+  // staged in LDS during the previous item (same layout and read pattern as
+  // the first 32 rows of a K tile).  The direct loads were followed by the
+  // previous item's last 16 tile loads and its 16 stores.
+  auto load_q_staged = [&]() {
+    if constexpr (PERS) {
+      static_assert(NDC == 8, "the staged Q read covers eight operands");
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * 4 * NDB));
+      const unsigned fl = fresh_lane(), fl32 = fl & 31, fhf = fl >> 5;
+      const unsigned qb = lds_addr(smem + LDS_MAIN + wave * 32 * ROWB) + fl32 * ROWB +
+                          16 * (fhf ^ (C::ksw(fl32) & 1)) + 32 * (C::ksw(fl32) >> 1);
 #pragma unroll
-  for (int dc = 0; dc < NDC; ++dc) k_rd[dc] = l32 * ROWB + 16 * ((2 * dc + hf) ^ C::ksw(l32));
+      for (int dc = 0; dc < NDC; ++dc) qf[dc] = lds_read16<0>(qb ^ (unsigned)(dc << 5));
+      // (the operands are tied to the wait, so no use is scheduled above it)
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]), "+v"(qf[5]),
+                     "+v"(qf[6]), "+v"(qf[7]));
+    }
+  };
   auto k_frag = [&](const unsigned char* kbuf, int kbk, int dc) -> bf16x8 {
-    return *(const bf16x8*)(kbuf + k_rd[dc] + kbk * 32 * ROWB);
+    const unsigned a = ((lds_addr(kbuf) + k_lane) ^ (unsigned)(dc << 5)) + kbk * 32 * ROWB;
+    return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)a;
   };
   // V^T operand (dim 32*db + l32, keys 16*pc + 4*hf + [0,4) then +8) from two
   // ds_read_b64_tr_b16 (v_frags): within each 16-lane group, lane 4t + u addresses the
@@ -449,15 +641,13 @@ void attn_fwd_bf16(KParams p) {
   // i.e. dim 32*db + l32 of keys 4*hf + t.  Physical chunk of the 4 dims:
   // (4*db + 2*g + (u >> 1)) ^ (t << VSH), which is 4*(db ^ t) + 2*g + (u >> 1)
   // for VSH = 2 and 4*(db ^ (t >> 1)) + 2*(g ^ (t & 1)) + (u >> 1) for VSH = 1
-  // (NDB = 2).
+  // (NDB = 2).  Again the db part is 64*db XORed into bits 6-7 of one lane
+  // base, so the read address of block db is (base + v_lane) ^ (db << 6).
   const int tt = (lane >> 2) & 3, uu = lane & 3, gg = (lane >> 4) & 1;
-  int v_rd[NDB];  // per-lane part for each db; the 16-key step is an immediate
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-    v_rd[db] = (VSH == 2)
-                   ? (4 * hf + tt) * ROWB + 64 * (db ^ tt) + 32 * gg + 16 * (uu >> 1) + 8 * (uu & 1)
-                   : (4 * hf + tt) * ROWB + 64 * (db ^ (tt >> 1)) + 32 * (gg ^ (tt & 1)) +
-                         16 * (uu >> 1) + 8 * (uu & 1);
+  const int v_lane = (VSH == 2)
+                         ? (4 * hf + tt) * ROWB + 64 * tt + 32 * gg + 16 * (uu >> 1) + 8 * (uu & 1)
+                         : (4 * hf + tt) * ROWB + 64 * (tt >> 1) + 32 * (gg ^ (tt & 1)) +
+                               16 * (uu >> 1) + 8 * (uu & 1);
 
   // Mask S^T of iteration iter in place.  Register r of block kbk holds key
   // 32*kbk + 8*(r/4) + 4*hf + r%4 of the tile for query q_row.
@@ -481,7 +671,7 @@ void attn_fwd_bf16(KParams p) {
     if (it.is_global) { lo = 0; hi = (long long)s.S - 1; }
     else row_interval(MASK, s.window, SK, q_pos, &lo, &hi);
     if (!wave_active || (GEN && !row_valid)) hi = lo - 1;
-    const long long base = (long long)tile_kt(iter) * BN + 4 * hf;
+    const long long base = (long long)tile_kt(iter) * BN + 4 * (PERS ? (int)(fresh_lane() >> 5) : hf);
     const long long tail = (long long)SK - 1;
     const long long hi_a = hi < tail ? hi : tail;
     int lo_r = (int)(lo - base < -1 ? -1 : (lo - base > BN ? BN : lo - base));
@@ -598,7 +788,7 @@ void attn_fwd_bf16(KParams p) {
         bf16x8 fx[NDB], fy[NDB];
         unsigned vbd[NDB];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) vbd[db] = vb + v_rd[db];
+        for (int db = 0; db < NDB; ++db) vbd[db] = (vb + v_lane) ^ (unsigned)(db << 6);
         v_frags<ROWB, NDB, 0>(fx, vbd);
         v_frags<ROWB, NDB, 1>(fy, vbd);
         lds_wait_frags<2 * NDB>(fx);
@@ -662,6 +852,14 @@ void attn_fwd_bf16(KParams p) {
     }
   } else {
   f32x16 scur[NKB];  // S(j) of this wave's 32 queries
+  if constexpr (PERS) {
+    // defined on entry to each item: an undefined value carried around the
+    // item loop would keep its registers reserved through the whole loop
+#pragma unroll
+    for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) scur[kbk][r] = 0.f;
+  }
   bf16x8 pb[NPC];    // P(j), the B operand of O += V(j) P(j); zero where no softmax ran
   auto zero_p = [&]() {
 #pragma unroll
@@ -680,13 +878,25 @@ void attn_fwd_bf16(KParams p) {
   // keeps its vmcnt waits exact; with two stages, K(dj) into stage dst and
   // V(dj - 1) into its own stage.  No loads where dj < 0.
   constexpr int NDMA = NSTAGE == 2 ? 2 * NGL : NGL;
-  auto mfma_block = [&](int jv, bool do_pv, int js, bool do_s, bool dk, int dj, int dst) {
+  // mode: ModeC<2> (P.V then S), ModeC<0> (P.V only) or ModeC<1> (S only)
+  auto mfma_block_m = [&](auto mode, int jv, bool do_pv, int js, bool do_s, bool dk, int dj, int dst) {
+    constexpr int MODE = decltype(mode)::value;
+    if constexpr (MODE == 0) do_s = false;
+    if constexpr (MODE == 1) do_pv = false;
     int dn = 0;
+    // the block's two tiles to load: K(dj) (or V(dj) with four stages) and,
+    // with two stages, V(dj - 1)
+    const TileRsrc t0 = tile_rsrc(dk, dj >= 0 ? dj : 0);
+    const TileRsrc t1 = tile_rsrc(false, dj >= 1 ? dj - 1 : 0);
+    // the lane bases, opaque per block: the compiler adds each load's row
+    // step at the load instead of keeping one offset per load live
+    int kl = k_off, vl = v_off;
+    asm volatile("" : "+v"(kl), "+v"(vl));
     auto do_dma = [&](int cnt) {
       for (int k = 0; k < cnt; ++k) {
         if (dj >= 0) {
-          if (NSTAGE == 2 && dn >= NGL) dma_band(false, dj - 1, (dj - 1) % NSTAGE, dn - NGL);
-          else dma_band(dk, dj, dst, dn);
+          if (NSTAGE == 2 && dn >= NGL) dma_tile_at(false, t1, (gofs + dj - 1) % NSTAGE, dn - NGL, vl);
+          else dma_tile_at(dk, t0, dst, dn, dk ? kl : vl);
         }
         ++dn;
       }
@@ -696,21 +906,29 @@ void attn_fwd_bf16(KParams p) {
       return;
     }
     __builtin_amdgcn_s_setprio(1);
-    // One sequence for every block.  Where P.V is not needed, P is zero (the
-    // softmax of that tile was skipped) and its operands are read from the K
-    // tile of this block, which has landed (S needs it): a V stage may still
-    // be in flight or hold stale bits, and 0 * NaN would not add zero.  Where
-    // S is not needed, it is computed from a landed stage and never read.
-    const unsigned kb = lds_addr(smem + (js % NSTAGE) * REG);
-    const unsigned vb = do_pv ? lds_addr(smem + NSTAGE * REG + (jv % NSTAGE) * REG) : kb;
+    // One sequence for every block of a mode.  Where P.V is not needed, P is
+    // zero (the softmax of that tile was skipped) and its operands are read
+    // from the K tile of this block, which has landed (S needs it): a V stage
+    // may still be in flight or hold stale bits, and 0 * NaN would not add
+    // zero.  Where S is not needed, it is computed from a landed stage and
+    // never read.
+    const unsigned kb = lds_addr(smem + ((gofs + js) % NSTAGE) * REG);
+    const unsigned vb = (MODE == 0 || do_pv) ? lds_addr(smem + NSTAGE * REG + ((gofs + jv) % NSTAGE) * REG) : kb;
+    // (the bases are opaque to the compiler, which would otherwise fold the
+    // XOR constants into NDB + NDC loop-invariant registers again)
+    unsigned v0 = vb + v_lane, k0 = kb + k_lane;
+    asm volatile("" : "+v"(v0), "+v"(k0));
     unsigned vbd[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) vbd[db] = vb + v_rd[db];
+    for (int db = 0; db < NDB; ++db) vbd[db] = v0 ^ (unsigned)(db << 6);
     unsigned kbd[NDC];
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) kbd[dc] = kb + k_rd[dc];
-    block_run<2, ROWB, NDB, NDC, NKB, NDMA>(vbd, kbd, pb, qf, oacc, scur, do_dma);
+    for (int dc = 0; dc < NDC; ++dc) kbd[dc] = k0 ^ (unsigned)(dc << 5);
+    block_run<MODE, ROWB, NDB, NDC, NKB, NDMA>(vbd, kbd, pb, qf, oacc, scur, do_dma);
     __builtin_amdgcn_s_setprio(0);
+  };
+  auto mfma_block = [&](int jv, bool do_pv, int js, bool do_s, bool dk, int dj, int dst) {
+    mfma_block_m(ModeC<2>{}, jv, do_pv, js, do_s, dk, dj, dst);
   };
 
   // ---- online softmax of S(j): mask, running maximum, weights P(j) and l -----
@@ -824,8 +1042,115 @@ void attn_fwd_bf16(KParams p) {
   // workgroup release fence, which the compiler implements by waiting for
   // every direct load in flight.  Direct loads are covered by the explicit
   // vmcnt waits, and every LDS read of a step is waited for before its MFMA.
-  const int grp = wave >> 2;
-  if constexpr (NSTAGE == 2) {
+  // PERS, wave group 0: the Q rows of this wave in item iq into its LDS
+  // staging rows by direct loads.  Load n fills
+  // rows 4n..4n+3; lane l writes physical chunk l % 16 of row 4n + l / 16,
+  // which holds logical chunk (l % 16) ^ ksw(row), the K tile swizzle.  The
+  // descriptor covers the item's rows of this wave (rows past the sequence
+  // are out of range; their outputs are never stored).
+  constexpr int NQL = 32 * ROWB / 1024;  // direct loads per wave
+  auto stage_q = [&](const Item& iq) {
+    if constexpr (PERS) {
+      const unsigned lid = fresh_lane();
+      const int qa = iq.blk * s.BMh + rpart * 32;
+      const int qb = imin(qa + 31, imin(iq.blk * s.BMh + s.BMh, s.S) - 1);
+      const int na = iq.kvh * s.G + iq.hg * s.HP + wave / wph;
+      const __amdgpu_buffer_rsrc_t r = uniform_rsrc(
+          (const char*)p.q + ((size_t)(iq.b * s.Hq + na) * S + qa) * ROWB,
+          qb >= qa ? (qb - qa + 1) * ROWB : 0);
+      unsigned char* dst = smem + LDS_MAIN + wave * 32 * ROWB;
+#pragma unroll
+      for (int n = 0; n < NQL; ++n) {
+        const int row = 4 * n + (int)(lid >> 4);
+        const int off = row * ROWB + (int)(((lid & 15) ^ (unsigned)C::ksw(row)) * 16);
+        dma16_buffer(r, dst + n * 1024, off, 0);
+      }
+    }
+  };
+  if constexpr (PERS) {
+    static_assert(NSTAGE == 2, "the persistent form runs the two-stage schedule");
+    // The schedule below per item, with the loads running on through the
+    // stream, the first and last blocks of each group cut to the MFMAs they
+    // need (S only, P.V only) and the dead last step dropped: in step 2n
+    // group 1 adds its last P.V while group 0 stores its rows; the next item
+    // starts with the barrier that ends step 2n, its first K and V tiles
+    // already in LDS.  Group 0 loads all tiles (on the first item also the
+    // first three) and stages the next item's Q in LDS right after its last
+    // S block, three steps ahead of its use; group 1 loads its Q at the
+    // item's start and first needs it in step 0, while group 0 runs S(0) and
+    // its softmax.  The vector memory counter retires in order, so
+    // group 0's waits for its tile loads leave the Q loads and stores issued
+    // after them in flight: nq_out counts those (8 per Q, 16 per set of
+    // stores).
+    constexpr int NST = 4 * NDB;
+    // (each group defines its Q in its own part, so that no path shows the
+    // compiler a load into those registers still in flight on the other)
+    if (grp == 0) {
+      int nq_out = 0;
+      if (round == 0) {
+        stage_q(it);  // this item's Q, waited for with the first tiles
+        int kl = k_off, vl = v_off;
+        asm volatile("" : "+v"(kl), "+v"(vl));
+        const TileRsrc k0 = tile_rsrc(true, 0), v0 = tile_rsrc(false, 0), k1 = tile_rsrc(true, 1);
+        for (int n = 0; n < NGL; ++n) dma_tile_at(true, k0, gofs % NSTAGE, n, kl);
+        for (int n = 0; n < NGL; ++n) dma_tile_at(false, v0, gofs % NSTAGE, n, vl);
+        for (int n = 0; n < NGL; ++n) dma_tile_at(true, k1, (gofs + 1) % NSTAGE, n, kl);
+        __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));  // Q and K(0) landed
+      } else {
+        nq_out = NST;  // the previous item's stores
+      }
+      load_q_staged();
+      // (later items: K(0) landed before the wait that ended step 2n-2 of
+      // the previous item)
+      __builtin_amdgcn_s_barrier();
+      if (!tile_empty(0)) mfma_block_m(ModeC<1>{}, 0, false, 0, true, true, -1, 0);  // S(0), no loads
+      // the wait at the end of step 2j: K(j+1), V(j) landed, the nq_out
+      // loads and stores issued after them may still be in flight
+      auto wait_tiles = [&]() {
+        if (nq_out == 0) __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+        else if (nq_out == NQL) __builtin_amdgcn_s_waitcnt(vmcnt_enc(NQL));
+        else if (nq_out == NST) __builtin_amdgcn_s_waitcnt(vmcnt_enc(NST));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_enc(NST + NQL));
+      };
+      for (int j = 0; j < n_it - 1; ++j) {
+        if (!tile_empty(j)) softmax(j);  // step 2j
+        else zero_p();
+        wait_tiles();
+        __builtin_amdgcn_s_barrier();
+        mfma_block(j, !tile_empty(j), j + 1, !tile_empty(j + 1), true, j + 2, (gofs + j) % NSTAGE);  // step 2j+1
+        nq_out = 0;
+        __builtin_amdgcn_s_barrier();
+      }
+      // the last S block is done: stage the next item's Q
+      if (id_n1 >= 0) {
+        stage_q(it_n1);
+        nq_out += NQL;
+      }
+      {
+        const int j = n_it - 1;
+        if (!tile_empty(j)) softmax(j);  // step 2n-2
+        else zero_p();
+        wait_tiles();
+        __builtin_amdgcn_s_barrier();
+        mfma_block_m(ModeC<0>{}, j, !tile_empty(j), j, false, true, j + 2, (gofs + j) % NSTAGE);  // step 2n-1
+        __builtin_amdgcn_s_barrier();
+      }
+    } else {
+      load_q_global();
+      __builtin_amdgcn_s_barrier();
+      for (int j = 0; j < n_it; ++j) {
+        mfma_block(j - 1, j >= 1 && !tile_empty(j - 1), j, !tile_empty(j), false, -1, 0);  // step 2j
+        __builtin_amdgcn_s_barrier();
+        if (!tile_empty(j)) softmax(j);  // step 2j+1
+        else zero_p();
+        __builtin_amdgcn_s_barrier();
+      }
+      mfma_block_m(ModeC<0>{}, n_it - 1, !tile_empty(n_it - 1), n_it - 1, false, false, -1, 0);  // step 2n
+      // (nothing of this group is in flight here; the wait tells the compiler
+      // so on every path, also where a skipped S(0) never waited for the Q)
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+    }
+  } else if constexpr (NSTAGE == 2) {
     // Two stages of 128-key tiles (the four-stage schedule below with the
     // loads moved): group 0 loads everything, K(j+2) and V(j+1) in step 2j+1
     // (K(j) and V(j-1) were last read in step 2j: S(j) by group 1, P.V(j-1)
@@ -896,9 +1221,35 @@ void attn_fwd_bf16(KParams p) {
     }
   }
   }
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // no direct load may land after the workgroup ends
+  // no direct load may land after the workgroup ends (PERS: after its last
+  // item; the loads in flight between items belong to the next one)
+  if constexpr (!PERS) __builtin_amdgcn_s_waitcnt(0x0f70);
   }  // ping-pong path
 
+  // ---- PERS: this item's O --------------------------------------------------
+  // Stores through a scalar descriptor over the wave's rows and a lane offset
+  // from a freshly read lane id, so nothing long-lived is needed here.
+  if constexpr (PERS) {
+    const unsigned lid = fresh_lane();
+    const int row_off = (int)(lid & 31) * ROWB;
+    const unsigned lu = __float_as_uint(l_run0 + l_run1);
+    const auto sw = __builtin_amdgcn_permlane32_swap(lu, lu, false, false);
+    const float inv = 1.f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+    const int qa = r0 + rpart * 32;
+    const __amdgpu_buffer_rsrc_t r = uniform_rsrc(
+        (char*)p.o + ((size_t)(it.b * s.Hq + a) * S + qa) * ROWB,
+        wave_active ? (wqb - qa + 1) * ROWB : 0);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[t] = (__bf16)(oacc[db][g4 * 4 + t] * inv);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, w), r,
+                                              row_off + (db * 32 + g4 * 8) * 2 + (int)(lid >> 5) * 8, 0, 0);
+      }
+  } else
   // ---- epilogue: O = O^T / l, round to bf16, store --------------------------
   {
     const float l_run = l_run0 + l_run1;
@@ -926,6 +1277,9 @@ void attn_fwd_bf16(KParams p) {
         }
     }
   }
+  gofs += n_it;
+  }  // items
+  if constexpr (PERS) __builtin_amdgcn_s_waitcnt(0x0f70);
 }
 
 template <int D>
@@ -962,6 +1316,18 @@ hipError_t launch_d(const KParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+#if ATTN_HEAD_DIM == 128
+hipError_t launch_bf16_pers_d128(const KParams& p, int grid, hipStream_t stream) {
+  dim3 g((unsigned)grid), block(kBf16Threads);
+  switch (p.s.mask) {
+    case MASK_FULL: hipLaunchKernelGGL((attn_fwd_bf16<128, MASK_FULL, 0, 1>), g, block, 0, stream, p); break;
+    case MASK_CAUSAL: hipLaunchKernelGGL((attn_fwd_bf16<128, MASK_CAUSAL, 0, 1>), g, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((attn_fwd_bf16<128, MASK_CAUSAL_WINDOW, 0, 1>), g, block, 0, stream, p); break;
+  }
+  return hipGetLastError();
+}
+#endif
 
 #if ATTN_HEAD_DIM == 64
 hipError_t launch_bf16_d64(const KParams& p, hipStream_t stream) { return launch_d<64>(p, stream); }
