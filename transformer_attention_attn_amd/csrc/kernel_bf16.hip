@@ -574,7 +574,11 @@ void attn_fwd_bf16(KParams p_arg) {
     const int RB = isk ? KRB : VRB;
     t.r = __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)row0 * RB), (short)0,
                                             (nrows - 1) * RB + ROWB, 0x00020000);
-    t.lclamp = (nrows - 1) * RB + (isk ? k_col : v_col);
+    // (the lane's column is opaque here: the sum is formed per tile instead
+    // of the compiler keeping a column-minus-row constant live)
+    int col = isk ? k_col : v_col;
+    asm volatile("" : "+v"(col));
+    t.lclamp = (nrows - 1) * RB + col;
     return t;
   };
   auto dma_tile_at = [&](bool isk, const TileRsrc& t, int st, int n, int lb) {
@@ -613,12 +617,12 @@ void attn_fwd_bf16(KParams p_arg) {
   const int k_lane = l32 * ROWB + 16 * (hf ^ (C::ksw(l32) & 1)) + 32 * (C::ksw(l32) >> 1);
   // PERS, wave group 0 from the second item on: Q from the rows its waves
   // staged in LDS during the previous item (same layout and read pattern as
-  // the first 32 rows of a K tile).  The direct loads were followed by the
-  // previous item's last 16 tile loads and its 16 stores.
+  // the first 32 rows of a K tile).  Only the previous item's 8 stores
+  // may have been issued after those direct loads and still be in flight.
   auto load_q_staged = [&]() {
     if constexpr (PERS) {
       static_assert(NDC == 8, "the staged Q read covers eight operands");
-      __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * 4 * NDB));
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * NDB));
       const unsigned fl = fresh_lane(), fl32 = fl & 31, fhf = fl >> 5;
       const unsigned qb = lds_addr(smem + LDS_MAIN + wave * 32 * ROWB) + fl32 * ROWB +
                           16 * (fhf ^ (C::ksw(fl32) & 1)) + 32 * (C::ksw(fl32) >> 1);
@@ -1074,15 +1078,18 @@ void attn_fwd_bf16(KParams p_arg) {
     // need (S only, P.V only) and the dead last step dropped: in step 2n
     // group 1 adds its last P.V while group 0 stores its rows; the next item
     // starts with the barrier that ends step 2n, its first K and V tiles
-    // already in LDS.  Group 0 loads all tiles (on the first item also the
-    // first three) and stages the next item's Q in LDS right after its last
-    // S block, three steps ahead of its use; group 1 loads its Q at the
-    // item's start and first needs it in step 0, while group 0 runs S(0) and
-    // its softmax.  The vector memory counter retires in order, so
-    // group 0's waits for its tile loads leave the Q loads and stores issued
-    // after them in flight: nq_out counts those (8 per Q, 16 per set of
-    // stores).
-    constexpr int NST = 4 * NDB;
+    // already in LDS.  Group 0 loads the tiles in steps 2j+1 (on the first
+    // item also the first three), except the last two of the item, K(n+1)
+    // and V(n) (the next item's K(1) and V(0)): group 1 loads those in step
+    // 2n, so that group 0 stores with no loads in flight, and waits for them
+    // before the barrier that ends the next item's step 0.  Group 0 stages
+    // the next item's Q in LDS after its first block (its rows there are
+    // free once read at the item's start); group 1 loads its Q at the item's
+    // start and first needs it in step 0, while group 0 runs S(0) and its
+    // softmax.  The vector memory counter retires in order, so group 0's
+    // waits for its tile loads leave the Q loads and stores issued after
+    // them in flight: nq_out counts those (8 per Q, 8 per set of stores).
+    constexpr int NST = 2 * NDB;  // stores per wave (see the epilogue)
     // (each group defines its Q in its own part, so that no path shows the
     // compiler a load into those registers still in flight on the other)
     if (grp == 0) {
@@ -1119,10 +1126,14 @@ void attn_fwd_bf16(KParams p_arg) {
         __builtin_amdgcn_s_barrier();
         mfma_block(j, !tile_empty(j), j + 1, !tile_empty(j + 1), true, j + 2, (gofs + j) % NSTAGE);  // step 2j+1
         nq_out = 0;
+        // the next item's Q, early: its staging rows are free once read
+        if (j == 0 && id_n1 >= 0) {
+          stage_q(it_n1);
+          nq_out = NQL;
+        }
         __builtin_amdgcn_s_barrier();
       }
-      // the last S block is done: stage the next item's Q
-      if (id_n1 >= 0) {
+      if (n_it == 1 && id_n1 >= 0) {
         stage_q(it_n1);
         nq_out += NQL;
       }
@@ -1132,7 +1143,7 @@ void attn_fwd_bf16(KParams p_arg) {
         else zero_p();
         wait_tiles();
         __builtin_amdgcn_s_barrier();
-        mfma_block_m(ModeC<0>{}, j, !tile_empty(j), j, false, true, j + 2, (gofs + j) % NSTAGE);  // step 2n-1
+        mfma_block_m(ModeC<0>{}, j, !tile_empty(j), j, false, true, -1, 0);  // step 2n-1, no loads
         __builtin_amdgcn_s_barrier();
       }
     } else {
@@ -1140,15 +1151,24 @@ void attn_fwd_bf16(KParams p_arg) {
       __builtin_amdgcn_s_barrier();
       for (int j = 0; j < n_it; ++j) {
         mfma_block(j - 1, j >= 1 && !tile_empty(j - 1), j, !tile_empty(j), false, -1, 0);  // step 2j
+        // K(1), V(0), loaded by this group at the end of the previous item,
+        // landed before group 0 reads them in step 1
+        if (j == 0) __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
         __builtin_amdgcn_s_barrier();
         if (!tile_empty(j)) softmax(j);  // step 2j+1
         else zero_p();
         __builtin_amdgcn_s_barrier();
       }
-      mfma_block_m(ModeC<0>{}, n_it - 1, !tile_empty(n_it - 1), n_it - 1, false, false, -1, 0);  // step 2n
-      // (nothing of this group is in flight here; the wait tells the compiler
-      // so on every path, also where a skipped S(0) never waited for the Q)
-      __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+      // step 2n: the last P.V, with the stream's next two tiles K(n+1) and
+      // V(n) (the next item's K(1) and V(0)), whose stages were last read in
+      // step 2n-2; this group waits for them before the barrier that ends
+      // the next item's step 0
+      mfma_block_m(ModeC<0>{}, n_it - 1, !tile_empty(n_it - 1), n_it - 1, false, true, n_it + 1,
+                   (gofs + n_it - 1) % NSTAGE);
+      // (only those tile loads may be in flight here; the wait tells the
+      // compiler so on every path, also where a skipped S(0) never waited
+      // for the Q)
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * NGL));
     }
   } else if constexpr (NSTAGE == 2) {
     // Two stages of 128-key tiles (the four-stage schedule below with the
@@ -1239,15 +1259,27 @@ void attn_fwd_bf16(KParams p_arg) {
     const __amdgpu_buffer_rsrc_t r = uniform_rsrc(
         (char*)p.o + ((size_t)(it.b * s.Hq + a) * S + qa) * ROWB,
         wave_active ? (wqb - qa + 1) * ROWB : 0);
+    // Lane (row, h) holds dims 32*db + 8*g4 + 4*h + [0, 4) of its row.  For
+    // each pair g4 = 2*g2, 2*g2 + 1 one swap between the lane halves gives
+    // lane h the 8 dims 32*db + 16*g2 + 8*h + [0, 8): 16 bytes per store,
+    // 32 contiguous bytes of each row per instruction.
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 w;
+      for (int g2 = 0; g2 < 2; ++g2) {
+        bf16x4 wa, wb;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) w[t] = (__bf16)(oacc[db][g4 * 4 + t] * inv);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, w), r,
-                                              row_off + (db * 32 + g4 * 8) * 2 + (int)(lid >> 5) * 8, 0, 0);
+        for (int t = 0; t < 4; ++t) {
+          wa[t] = (__bf16)(oacc[db][(2 * g2) * 4 + t] * inv);
+          wb[t] = (__bf16)(oacc[db][(2 * g2 + 1) * 4 + t] * inv);
+        }
+        const u32x2 a2 = __builtin_bit_cast(u32x2, wa), b2 = __builtin_bit_cast(u32x2, wb);
+        // swap(a, b): lanes 0-31 get (a, a of lane + 32), lanes 32-63 (b of lane - 32, b)
+        const auto s0 = __builtin_amdgcn_permlane32_swap(a2[0], b2[0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(a2[1], b2[1], false, false);
+        const u32x4 c = {s0[0], s1[0], s0[1], s1[1]};
+        __builtin_amdgcn_raw_buffer_store_b128(c, r, row_off + (db * 32 + g2 * 16) * 2 + (int)(lid >> 5) * 16,
+                                               0, 0);
       }
   } else
   // ---- epilogue: O = O^T / l, round to bf16, store --------------------------
