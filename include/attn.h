@@ -71,8 +71,10 @@ typedef enum {
   ATTN_ERR_HIP = 8,         /* the kernel launch failed (hipGetLastError)          */
   ATTN_ERR_ALIAS = 9,       /* o overlaps q, k or v                                */
   ATTN_ERR_SCALE = 10,      /* scale is NaN or infinite                            */
-  ATTN_ERR_WORKSPACE = 11   /* attn_decode: workspace missing, smaller than
+  ATTN_ERR_WORKSPACE = 11,  /* attn_decode: workspace missing, smaller than
                                attn_decode_workspace reports, or not 16-byte aligned */
+  ATTN_ERR_SCRATCH = 12     /* attn_decode_noalloc: the call needs more than the
+                               library's static device scratch (ATTN_NOALLOC_SCRATCH_BYTES) */
 } attn_status;
 
 #define ATTN_MAX_GLOBAL 64
@@ -301,6 +303,35 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
  * depends on B, Hq, Hkv, Sq, Smax and D, not on the lengths. */
 int attn_decode_workspace(int B, int Hq, int Hkv, int Sq, int Smax, int D, int mask_kind,
                           int dtype, size_t* workspace_bytes);
+
+/* Bytes of the static device scratch behind attn_decode_noalloc (one array
+ * per GPU the library runs on, held until the process ends). */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device
+ * memory at all (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same arguments, kernels and results as
+ * attn_decode, without the workspace.  The key-split partials go to a static
+ * device array of ATTN_NOALLOC_SCRATCH_BYTES per GPU instead; the call
+ * allocates nothing (no hipMalloc, hipFree or allocating routine).
+ *
+ *   q, k_cache, v_cache, o, cache_len, B, Hq, Hkv, Sq, Smax, D, mask_kind,
+ *   scale, dtype, stream   as for attn_decode
+ *
+ * The first call on a GPU looks up that GPU's copy of the array (with the
+ * stream's device current for the lookup, restored afterwards).  Every call
+ * on a GPU shares that array and leaves the last call's partials in it:
+ * calls that may overlap on one GPU race and must be serialised by the
+ * caller (one stream, or events).  Returns ATTN_ERR_SCRATCH, before any
+ * launch, when attn_decode_workspace reports more than
+ * ATTN_NOALLOC_SCRATCH_BYTES for the arguments (no valid decode shape needs
+ * more than about 8.1 MiB), ATTN_ERR_HIP when the lookup fails, otherwise
+ * the status attn_decode would return.
+ */
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                        const int* cache_len, int B, int Hq, int Hkv, int Sq, int Smax, int D,
+                        int mask_kind, float scale, int dtype, void* stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* attn_status_string(int status);

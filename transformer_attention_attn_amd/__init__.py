@@ -24,6 +24,8 @@ from ._binding import (  # noqa: F401
     FwdArgs,
     check_devices,
     decode,
+    decode_noalloc,
+    decode_noalloc_raw,
     decode_raw,
     decode_workspace_bytes,
     decode_workspace_status,

@@ -29,9 +29,11 @@ STATUS = {
     4: "ATTN_ERR_UNSUPPORTED", 5: "ATTN_ERR_WINDOW", 6: "ATTN_ERR_GLOBAL",
     7: "ATTN_ERR_ALIGN", 8: "ATTN_ERR_HIP", 9: "ATTN_ERR_ALIAS", 10: "ATTN_ERR_SCALE",
     11: "ATTN_ERR_WORKSPACE",
+    12: "ATTN_ERR_SCRATCH",
 }
 
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_plan", "attn_decode", "attn_decode_workspace",
+           "attn_decode_noalloc",
            "attn_layout_strided", "attn_layout_fixed", "attn_layout_bigbird",
            "attn_status_string", "attn_version")
 
@@ -103,6 +105,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode.restype = i
     lib.attn_decode_workspace.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
     lib.attn_decode_workspace.restype = i
+    lib.attn_decode_noalloc.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, f, i, p]
+    lib.attn_decode_noalloc.restype = i
     u32p = ctypes.POINTER(ctypes.c_uint32)
     lib.attn_layout_strided.argtypes = [i, i, i, u32p]
     lib.attn_layout_strided.restype = i
@@ -389,6 +393,53 @@ def decode(q, k_cache, v_cache, cache_len=None, mask="causal", scale: Optional[f
         st = decode_raw(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
                         cache_len.data_ptr() if cache_len is not None else 0, B, Hq, Hkv, Sq,
                         Smax, D, mask, scale, DTYPE_BF16, ws_ptr, ws_bytes, handle)
+    if st != 0:
+        raise AttnError(st)
+    return out
+
+
+def decode_noalloc_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, len_ptr: int, B: int,
+                       Hq: int, Hkv: int, Sq: int, Smax: int, D: int, mask, scale: float,
+                       dtype: int, stream: int) -> int:
+    """Direct call of attn_decode_noalloc with raw device addresses; returns the status."""
+    return load().attn_decode_noalloc(q_ptr, k_ptr, v_ptr, o_ptr, len_ptr, B, Hq, Hkv, Sq, Smax,
+                                      D, _mask_id(mask), float(scale), dtype, stream)
+
+
+def decode_noalloc(q, k_cache, v_cache, cache_len=None, mask="causal",
+                   scale: Optional[float] = None, out=None, stream=None):
+    """decode() through attn_decode_noalloc: no workspace, the library's static
+    device scratch instead (calls that may overlap on one GPU race).  `out`
+    is allocated with torch when not given; pass it to allocate nothing."""
+    import torch
+
+    if q.dtype != torch.bfloat16:
+        raise TypeError("decode_noalloc takes bf16 tensors")
+    for t in (q, k_cache, v_cache):
+        if t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q and the caches must be contiguous 4-D bf16 GPU tensors")
+    B, Hq, Sq, D = q.shape
+    Hkv, Smax = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, Smax, D) or tuple(v_cache.shape) != (B, Hkv, Smax, D):
+        raise ValueError("caches must be [B, Hkv, Smax, D] matching q")
+    if cache_len is not None:
+        if (cache_len.dtype != torch.int32 or not cache_len.is_cuda or cache_len.numel() != B
+                or not cache_len.is_contiguous()):
+            raise ValueError("cache_len must be a contiguous int32 GPU tensor of B lengths")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped like q")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    check_devices(q, k_cache=k_cache, v_cache=v_cache, out=out, cache_len=cache_len)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = decode_noalloc_raw(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                out.data_ptr(), cache_len.data_ptr() if cache_len is not None else 0,
+                                B, Hq, Hkv, Sq, Smax, D, mask, scale, DTYPE_BF16, handle)
     if st != 0:
         raise AttnError(st)
     return out

@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/attn.h"
 #include "attn_kernels.h"
@@ -75,11 +76,15 @@ Checked check_args(int B, int Hq, int Hkv, int S, int D, int mask_kind, int wind
 
 // Compute units of the device a stream launches on (cached per device; 0 when
 // the runtime cannot tell, which keeps the one-workgroup-per-item launch).
+// The device a stream belongs to (the current device for the null stream).
+hipError_t stream_device(hipStream_t stream, int* dev) {
+  return stream ? hipStreamGetDevice(stream, dev) : hipGetDevice(dev);
+}
+
 int device_cus(hipStream_t stream) {
   static std::atomic<int> cache[64];
   int dev = -1;
-  if (stream ? hipStreamGetDevice(stream, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
-    return 0;
+  if (stream_device(stream, &dev) != hipSuccess) return 0;
   if (dev < 0 || dev >= 64) return 0;
   int n = cache[dev].load(std::memory_order_relaxed);
   if (n == 0) {
@@ -168,6 +173,92 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int Sq, int Smax, int D, int mask
                    ? (size_t)pairs * d.n_split * attn::kDecodeRows * (size_t)(D + 2) * sizeof(float)
                    : 0;
   return d;
+}
+
+}  // namespace
+
+// Static device scratch behind attn_decode_noalloc: one copy per GPU.  In
+// host code the array's name is only a stand-in; every use goes through the
+// address hipGetSymbolAddress returned for the device (kept in g_scratch).
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This device's address of `scratch`, looked up on the first call with the
+// device current (the caller's current device is restored).
+hipError_t scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      int cur = -1;
+      hipError_t e = hipGetDevice(&cur);
+      if (e != hipSuccess) return e;
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (cur != dev) {
+        const hipError_t e2 = hipSetDevice(cur);
+        if (e == hipSuccess) e = e2;
+      }
+      if (e != hipSuccess) return e;
+      if (!ptr) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return hipSuccess;
+}
+
+// attn_decode (static_scratch false: the caller's workspace) and
+// attn_decode_noalloc (true: this device's copy of `scratch`).
+int decode_call(const void* q, const void* k_cache, const void* v_cache, void* o,
+                const int* cache_len, int B, int Hq, int Hkv, int Sq, int Smax, int D,
+                int mask_kind, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                hipStream_t stream, bool static_scratch) {
+  if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULL;
+  const DecodePlan d = plan_decode(B, Hq, Hkv, Sq, Smax, D, mask_kind, dtype);
+  if (d.status != ATTN_OK) return d.status;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  for (const void* ptr : {q, k_cache, v_cache, (const void*)o})
+    if ((uintptr_t)ptr % 16 != 0) return ATTN_ERR_ALIGN;
+  if (cache_len && (uintptr_t)cache_len % 4 != 0) return ATTN_ERR_ALIGN;
+  const size_t nq = (size_t)B * Hq * Sq * D * 2, nkv = (size_t)B * Hkv * Smax * D * 2;
+  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k_cache, nkv) || overlaps(o, nq, v_cache, nkv))
+    return ATTN_ERR_ALIAS;
+  if (static_scratch && d.ws_bytes > 0) {
+    if (d.ws_bytes > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+    int dev = -1;
+    if (stream_device(stream, &dev) != hipSuccess) return ATTN_ERR_HIP;
+    if (scratch_address(dev, &workspace) != hipSuccess) return ATTN_ERR_HIP;
+    workspace_bytes = ATTN_NOALLOC_SCRATCH_BYTES;
+  }
+  if (d.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < d.ws_bytes || (uintptr_t)workspace % 16 != 0)
+      return ATTN_ERR_WORKSPACE;
+    if (overlaps(workspace, d.ws_bytes, o, nq) || overlaps(workspace, d.ws_bytes, q, nq) ||
+        overlaps(workspace, d.ws_bytes, k_cache, nkv) || overlaps(workspace, d.ws_bytes, v_cache, nkv))
+      return ATTN_ERR_ALIAS;
+  }
+
+  attn::DParams p{};
+  p.q = q; p.k = k_cache; p.v = v_cache; p.o = o;
+  p.cache_len = cache_len;
+  p.ws = d.ws_bytes > 0 ? (float*)workspace : nullptr;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Smax = Smax; p.G = Hq / Hkv;
+  p.n_split = d.n_split;
+  p.chunk = d.chunk;
+  p.causal = mask_kind == ATTN_MASK_CAUSAL ? 1 : 0;
+  p.c = std::fabs(scale) * 1.4426950408889634f;
+  p.qmode = scale > 0.f ? 0 : (scale < 0.f ? 1 : 2);
+  if (p.qmode == 2) p.c = 1.f;  // all visible scores equal: weights are uniform
+  hipError_t err = attn::launch_decode(p, D, stream);
+  return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 }  // namespace
@@ -367,37 +458,15 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
                 const int* cache_len, int B, int Hq, int Hkv, int Sq, int Smax, int D,
                 int mask_kind, float scale, int dtype, void* workspace, size_t workspace_bytes,
                 void* stream) {
-  if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULL;
-  const DecodePlan d = plan_decode(B, Hq, Hkv, Sq, Smax, D, mask_kind, dtype);
-  if (d.status != ATTN_OK) return d.status;
-  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
-  for (const void* ptr : {q, k_cache, v_cache, (const void*)o})
-    if ((uintptr_t)ptr % 16 != 0) return ATTN_ERR_ALIGN;
-  if (cache_len && (uintptr_t)cache_len % 4 != 0) return ATTN_ERR_ALIGN;
-  const size_t nq = (size_t)B * Hq * Sq * D * 2, nkv = (size_t)B * Hkv * Smax * D * 2;
-  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k_cache, nkv) || overlaps(o, nq, v_cache, nkv))
-    return ATTN_ERR_ALIAS;
-  if (d.ws_bytes > 0) {
-    if (!workspace || workspace_bytes < d.ws_bytes || (uintptr_t)workspace % 16 != 0)
-      return ATTN_ERR_WORKSPACE;
-    if (overlaps(workspace, d.ws_bytes, o, nq) || overlaps(workspace, d.ws_bytes, q, nq) ||
-        overlaps(workspace, d.ws_bytes, k_cache, nkv) || overlaps(workspace, d.ws_bytes, v_cache, nkv))
-      return ATTN_ERR_ALIAS;
-  }
+  return decode_call(q, k_cache, v_cache, o, cache_len, B, Hq, Hkv, Sq, Smax, D, mask_kind, scale,
+                     dtype, workspace, workspace_bytes, (hipStream_t)stream, false);
+}
 
-  attn::DParams p{};
-  p.q = q; p.k = k_cache; p.v = v_cache; p.o = o;
-  p.cache_len = cache_len;
-  p.ws = d.ws_bytes > 0 ? (float*)workspace : nullptr;
-  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Smax = Smax; p.G = Hq / Hkv;
-  p.n_split = d.n_split;
-  p.chunk = d.chunk;
-  p.causal = mask_kind == ATTN_MASK_CAUSAL ? 1 : 0;
-  p.c = std::fabs(scale) * 1.4426950408889634f;
-  p.qmode = scale > 0.f ? 0 : (scale < 0.f ? 1 : 2);
-  if (p.qmode == 2) p.c = 1.f;  // all visible scores equal: weights are uniform
-  hipError_t err = attn::launch_decode(p, D, (hipStream_t)stream);
-  return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                        const int* cache_len, int B, int Hq, int Hkv, int Sq, int Smax, int D,
+                        int mask_kind, float scale, int dtype, void* stream) {
+  return decode_call(q, k_cache, v_cache, o, cache_len, B, Hq, Hkv, Sq, Smax, D, mask_kind, scale,
+                     dtype, nullptr, 0, (hipStream_t)stream, true);
 }
 
 const char* attn_status_string(int status) {
@@ -414,6 +483,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS";
     case ATTN_ERR_SCALE: return "ATTN_ERR_SCALE";
     case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_SCRATCH: return "ATTN_ERR_SCRATCH";
     default: return "ATTN_ERR_UNKNOWN";
   }
 }
