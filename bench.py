@@ -60,6 +60,7 @@ KERNEL_SOURCES = ("kernel_bf16.hip", "gfx950_ops.h", "attn_kernels.h", "attn_sch
 # committed HBM-traffic summaries per workload, with the sources their kernel is built from
 TRAFFIC_SUMMARIES = {
     "causal_gqa_bf16_s8192": ("attn_fwd_bf16_causal_gqa_s8192_hbm_traffic.md", KERNEL_SOURCES),
+    "local_global_bf16_s8192": ("attn_fwd_bf16_local_global_s8192.md", KERNEL_SOURCES),
     "causal_gqa_fp8_s8192": ("attn_fwd_fp8_causal_gqa_s8192.md",
                              ("kernel_fp8.hip", "gfx950_ops.h", "attn_kernels.h", "attn_sched.h")),
 }
@@ -156,12 +157,18 @@ def inputs_sha256(*tensors) -> dict:
 
 class ClockSampler:
     """Samples the graphics clock with amd-smi in a background thread while
-    the GPU is busy (None where the tool or its output is unavailable)."""
+    the GPU is busy: up to `n` samples, each the mean over the XCDs of one
+    amd-smi call; a sample with any XCD in deep sleep (a momentary gap
+    between launches) is dropped.  result(): the median of the kept samples
+    in MHz, or None where the tool or its output is unavailable."""
 
-    def __init__(self):
+    def __init__(self, n: int = 6):
         import threading
 
+        self.n = n
         self.mhz = []
+        self.dropped = 0
+        self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
 
     @staticmethod
@@ -171,7 +178,7 @@ class ClockSampler:
                 if isinstance(key, str) and key.lower().startswith("gfx") and isinstance(val, dict):
                     clk = val.get("clk")
                     if isinstance(clk, dict) and isinstance(clk.get("value"), (int, float)):
-                        found.append(float(clk["value"]))
+                        found.append((float(clk["value"]), str(val.get("deep_sleep", "")).upper()))
                 ClockSampler._gfx_clocks(val, found)
         elif isinstance(node, list):
             for x in node:
@@ -180,16 +187,23 @@ class ClockSampler:
     def _run(self):
         import subprocess
 
-        try:
-            res = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"],
-                                 capture_output=True, text=True, timeout=10)
-            found = []
-            self._gfx_clocks(json.loads(res.stdout), found)
-            found = [x for x in found if x > 0]
-            if found:
-                self.mhz.append(sum(found) / len(found))
-        except Exception:  # noqa: BLE001 - the clock is an optional extra
-            pass
+        for _ in range(self.n):
+            if self._stop.is_set():
+                break
+            try:
+                res = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"],
+                                     capture_output=True, text=True, timeout=10)
+                found = []
+                self._gfx_clocks(json.loads(res.stdout), found)
+            except Exception:  # noqa: BLE001 - the clock is an optional extra
+                return
+            if not found:
+                return
+            if any(ds == "ENABLED" for _, ds in found):
+                self.dropped += 1
+            else:
+                self.mhz.append(sum(v for v, _ in found) / len(found))
+            time.sleep(0.05)
 
     def start(self):
         self._thread.start()
@@ -198,8 +212,12 @@ class ClockSampler:
         return self._thread.is_alive()
 
     def result(self):
+        self._stop.set()
         self._thread.join(timeout=15)
-        return self.mhz[0] if self.mhz else None
+        if not self.mhz:
+            return None
+        v = sorted(self.mhz)
+        return v[len(v) // 2]
 
 
 def calibration_copy(mib: int, dev):
@@ -393,9 +411,9 @@ def time_steps(step, stream, args):
         waiting = started and sampler.alive()
         if (el >= args.prewarm and not waiting) or el > args.prewarm + 15:
             break
-        for _ in range(5):
+        for _ in range(20):
             step()
-        prewarm_steps += 5
+        prewarm_steps += 20
         torch.cuda.synchronize()
         if sampler is not None and not started and el > 0.3:
             sampler.start()
@@ -413,6 +431,7 @@ def time_steps(step, stream, args):
     spread = {"median_ms": round(per[len(per) // 2], 6), "min_ms": round(per[0], 6)}
     if started:
         args.clock_mhz = sampler.result()
+        args.clock_samples = {"kept": len(sampler.mhz), "dropped_deep_sleep": sampler.dropped}
     return ev[0].elapsed_time(ev[-1]) / args.steps, prewarm_steps, spread
 
 
@@ -597,15 +616,16 @@ def bench_ex(args, name):
     return 0
 
 
-def clock_line(tflops, dtype, cus, mhz):
-    """The sampled graphics clock and the throughput as a percentage of the
-    dense matrix-core peak at that clock (CUs x FLOP/clk/CU x clock)."""
+def clock_line(tflops, dtype, cus, mhz, samples=None):
+    """The sampled graphics clock (median of the busy samples, mean over the
+    XCDs) and the throughput as a percentage of the dense matrix-core peak at
+    that clock (CUs x FLOP/clk/CU x clock)."""
     per_clk = {"bf16": 4096, "fp8": 8192}.get(dtype)
     if mhz is None or per_clk is None:
-        return {"sclk_mhz": mhz, "pct_of_peak_at_sclk": None}
+        return {"sclk_mhz": mhz, "pct_of_peak_at_sclk": None, "samples": samples}
     peak = cus * per_clk * mhz * 1e6 / 1e12
     return {"sclk_mhz": round(mhz, 1), "peak_at_sclk_tflops": round(peak, 1),
-            "pct_of_peak_at_sclk": round(100.0 * tflops / peak, 2)}
+            "pct_of_peak_at_sclk": round(100.0 * tflops / peak, 2), "samples": samples}
 
 
 def main(argv=None):
@@ -713,7 +733,8 @@ def main(argv=None):
         "gpu": torch.cuda.get_device_name(dev),
         "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
         "clock": clock_line(tflops, w.dtype, torch.cuda.get_device_properties(dev)
-                            .multi_processor_count, getattr(args, "clock_mhz", None)),
+                            .multi_processor_count, getattr(args, "clock_mhz", None),
+                            getattr(args, "clock_samples", None)),
         "inputs_sha256": inputs_sha256(q, k, v),
     }
 
