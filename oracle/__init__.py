@@ -25,6 +25,7 @@ from .decode import (  # noqa: F401
     decode_cache_bytes,
     decode_effective_flops,
     decode_visible_count,
+    decode_visible_range,
 )
 from .cross import (  # noqa: F401
     CROSS_MASK_KINDS,

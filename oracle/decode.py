@@ -26,6 +26,11 @@ Readings taken where the pages leave a step open:
   position L - Sq + i, already appended.  "causal" lets query i see cache
   positions 0 .. L - Sq + i; "full" lets every query see all L positions.
   With Sq = 1 the two coincide and equal the page's decode formula.
+* Sliding window in decode ("causal_window", window w >= 1) -- "Transformer
+  演进与变体", section 稀疏注意力 (Mistral's window of 4096): query i at
+  position p = L - Sq + i sees the cache positions j with p - w < j <= p,
+  the same visibility as the full-sequence oracle's causal_window mask, so
+  only the last w positions are read.
 * A query that sees no position (L - Sq + i < 0, or L = 0) has output zero.
 * Cache positions at or beyond a sequence's length L are not part of the
   sequence: whatever they hold (even NaN) never reaches the output.
@@ -34,9 +39,9 @@ Layout: q is [B][Hq][Sq][D]; the caches are [B][Hkv][Smax][D] with L_b <= Smax
 valid positions for sequence b.  All arithmetic is float64 on the exact input
 values.
 
-Pinned by tests/test_oracle.py (the full-sequence oracle's last rows, padding
-that must not leak, closed forms, a grouped-head reduction and a pure-Python
-loop).
+Pinned by tests/test_oracle_decode.py (the full-sequence oracle's last rows,
+also under the window; padding that must not leak; closed forms, a window of
+one position among them; a grouped-head reduction and a pure-Python loop).
 """
 from __future__ import annotations
 
@@ -44,23 +49,37 @@ import numpy as np
 
 FULL = "full"
 CAUSAL = "causal"
-DECODE_MASK_KINDS = (FULL, CAUSAL)
+CAUSAL_WINDOW = "causal_window"
+DECODE_MASK_KINDS = (FULL, CAUSAL, CAUSAL_WINDOW)
 
 
-def decode_visible_count(L, Sq, i, kind):
-    """Number of cache positions query i (of Sq new ones) sees in a cache of L."""
+def decode_visible_range(L, Sq, i, kind, window=0):
+    """Cache positions [lo, hi) that query i (of Sq new ones, at position
+    L - Sq + i) sees in a cache of L positions (lo == hi: none)."""
     if kind == FULL:
-        return L
+        return 0, L
+    p = L - Sq + i
     if kind == CAUSAL:
-        return max(0, min(L, L - Sq + i + 1))
+        return 0, max(0, min(L, p + 1))
+    if kind == CAUSAL_WINDOW:
+        if window < 1:
+            raise ValueError("causal_window needs window >= 1")
+        hi = max(0, min(L, p + 1))
+        return min(hi, max(0, p - window + 1)), hi
     raise ValueError(f"unknown decode mask kind {kind!r}")
 
 
-def decode_attention(q, k_cache, v_cache, kind, cache_len=None, scale=None):
+def decode_visible_count(L, Sq, i, kind, window=0):
+    """Number of cache positions query i (of Sq new ones) sees in a cache of L."""
+    lo, hi = decode_visible_range(L, Sq, i, kind, window)
+    return hi - lo
+
+
+def decode_attention(q, k_cache, v_cache, kind, cache_len=None, scale=None, window=0):
     """Decode attention output, float64, shape [B, Hq, Sq, D].
 
     q: [B, Hq, Sq, D]; k_cache, v_cache: [B, Hkv, Smax, D]; cache_len: B ints in
-    [0, Smax] (all Smax when None).
+    [0, Smax] (all Smax when None); window: the w of "causal_window".
     """
     q = np.asarray(q)
     kc = np.asarray(k_cache)
@@ -82,30 +101,36 @@ def decode_attention(q, k_cache, v_cache, kind, cache_len=None, scale=None):
         for a in range(Hq):
             h = a // G
             for i in range(Sq):
-                n = decode_visible_count(lens[b], Sq, i, kind)
-                if n == 0:
+                lo, hi = decode_visible_range(lens[b], Sq, i, kind, window)
+                if hi == lo:
                     continue
-                keys = kc[b, h, :n].astype(np.float64)
-                vals = vc[b, h, :n].astype(np.float64)
+                keys = kc[b, h, lo:hi].astype(np.float64)
+                vals = vc[b, h, lo:hi].astype(np.float64)
                 s = float(scale) * (keys @ q[b, a, i].astype(np.float64))
                 e = np.exp(s - s.max())
                 out[b, a, i] = (e / e.sum()) @ vals
     return out
 
 
-def decode_cache_bytes(B, Hkv, D, cache_len, elem_bytes):
-    """Bytes of the valid key and value cache entries that one call must read:
-    2 * Hkv * D * elem_bytes per cached position, summed over the sequences
-    (the per-layer payload of "Transformer 架构及其变体", section
-    预填充创建缓存，解码复用缓存)."""
-    return 2 * Hkv * D * elem_bytes * int(sum(int(x) for x in cache_len))
+def decode_cache_bytes(B, Hkv, D, cache_len, elem_bytes, Sq=1, kind=CAUSAL, window=0):
+    """Bytes of the key and value cache entries that one call must read: 2 *
+    Hkv * D * elem_bytes per cached position that some query sees, summed over
+    the sequences (the per-layer payload of "Transformer 架构及其变体", section
+    预填充创建缓存，解码复用缓存; under a window, the last window + Sq - 1
+    positions at most)."""
+    n = 0
+    for L in cache_len:
+        los, his = zip(*(decode_visible_range(int(L), Sq, i, kind, window) for i in range(Sq)))
+        lo, hi = min(los), max(his)
+        n += max(0, hi - lo)
+    return 2 * Hkv * D * elem_bytes * n
 
 
-def decode_effective_flops(Hq, Sq, D, cache_len, kind):
+def decode_effective_flops(Hq, Sq, D, cache_len, kind, window=0):
     """Two multiply-add chains of length D per visible (query, cache position)
     pair and query head, two FLOPs per multiply-add."""
     pairs = 0
     for L in cache_len:
         for i in range(Sq):
-            pairs += decode_visible_count(int(L), Sq, i, kind)
+            pairs += decode_visible_count(int(L), Sq, i, kind, window)
     return 4 * D * pairs * Hq

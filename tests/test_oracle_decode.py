@@ -144,10 +144,83 @@ def pin_counts():
     want = sum(max(0, L - Sq + i + 1) for L in lens for i in range(Sq))
     assert causal == 4 * D * Hq * want
     assert dec.decode_cache_bytes(3, Hkv, D, lens, 2) == 2 * Hkv * D * 2 * sum(lens)
+    for w in (1, 2, 5, 100):
+        win = dec.decode_effective_flops(Hq, Sq, D, lens, "causal_window", window=w)
+        want = sum(min(w, max(0, L - Sq + i + 1)) for L in lens for i in range(Sq))
+        assert win == 4 * D * Hq * want
+        # the union of the rows' windows: the last min(L, w + Sq - 1) positions
+        nb = dec.decode_cache_bytes(3, Hkv, D, lens, 2, Sq=Sq, kind="causal_window", window=w)
+        assert nb == 2 * Hkv * D * 2 * sum(min(L, w + Sq - 1) for L in lens)
+
+
+def pin_window_cache_equivalence():
+    """Under the sliding window, decoding the last Sq positions equals the
+    full-sequence oracle's causal_window mask on those rows, at windows below,
+    at and above the cache length."""
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, S, D = 2, 4, 2, 29, 8
+    q, k, v = randn(rng, B, Hq, S, D), randn(rng, B, Hkv, S, D), randn(rng, B, Hkv, S, D)
+    for Sq in (1, 4, S):
+        for w in (1, 3, 11, S, S + 5):
+            rows = list(range(S - Sq, S))
+            ref = oracle.attention(q, k, v, "causal_window", window=w, rows=rows)
+            got = dec.decode_attention(q[:, :, S - Sq:], k, v, "causal_window",
+                                       cache_len=[S] * B, window=w)
+            assert np.max(np.abs(got - ref)) < 1e-12, (Sq, w)
+
+
+def pin_window_reads_only_last_positions():
+    """Cache positions before a query's window never reach its output, even
+    when they hold NaN: the sequence equals the cache cut to its last
+    w + Sq - 1 positions; a window that covers the sequence equals causal."""
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, Smax, D, Sq, w = 3, 4, 1, 40, 8, 3, 6
+    lens = [40, 13, 4]
+    q = randn(rng, B, Hq, Sq, D)
+    k, v = randn(rng, B, Hkv, Smax, D), randn(rng, B, Hkv, Smax, D)
+    clean_k, clean_v = k.copy(), v.copy()
+    for b, L in enumerate(lens):
+        cut = max(0, L - Sq - w + 1)
+        k[b, :, :cut] = np.nan
+        v[b, :, :cut] = np.nan
+        k[b, :, L:] = np.nan
+        v[b, :, L:] = np.nan
+    got = dec.decode_attention(q, k, v, "causal_window", cache_len=lens, window=w)
+    assert np.all(np.isfinite(got))
+    for b, L in enumerate(lens):
+        cut = max(0, L - Sq - w + 1)
+        tail = dec.decode_attention(q[b:b + 1], clean_k[b:b + 1, :, cut:L],
+                                    clean_v[b:b + 1, :, cut:L], "causal_window", window=w)
+        assert np.max(np.abs(got[b] - tail[0])) < 1e-13
+    wide = dec.decode_attention(q, clean_k, clean_v, "causal_window", cache_len=lens, window=Smax)
+    causal = dec.decode_attention(q, clean_k, clean_v, "causal", cache_len=lens)
+    assert np.array_equal(wide, causal)
+
+
+def pin_window_closed_forms():
+    """Window of one position: the output is the value row at the query's own
+    position; scale 0: the mean of the value rows of p - w + 1 .. p."""
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, Smax, D, Sq = 2, 2, 1, 15, 4, 3
+    lens = [15, 9]
+    q = randn(rng, B, Hq, Sq, D)
+    k, v = randn(rng, B, Hkv, Smax, D), randn(rng, B, Hkv, Smax, D)
+    one = dec.decode_attention(q, k, v, "causal_window", cache_len=lens, window=1)
+    w = 4
+    mean = dec.decode_attention(q, k, v, "causal_window", cache_len=lens, scale=0.0, window=w)
+    for b, L in enumerate(lens):
+        for i in range(Sq):
+            p = L - Sq + i
+            for a in range(Hq):
+                assert np.max(np.abs(one[b, a, i] - v[b, 0, p])) < 1e-15
+                want = v[b, 0, p - w + 1:p + 1].mean(axis=0)
+                assert np.max(np.abs(mean[b, a, i] - want)) < 1e-13
 
 
 PINS = [pin_cache_equivalence, pin_ragged_padding_ignored, pin_scale_zero_is_mean,
-        pin_grouped_heads_are_repeated_heads, pin_brute_force_loop, pin_edge_rows, pin_counts]
+        pin_grouped_heads_are_repeated_heads, pin_brute_force_loop, pin_edge_rows, pin_counts,
+        pin_window_cache_equivalence, pin_window_reads_only_last_positions,
+        pin_window_closed_forms]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -159,27 +232,42 @@ def test_decode_pin(pin):
 # planted mistakes: each must make at least one pin fail
 # ----------------------------------------------------------------------------
 
-_ORIG_COUNT = dec.decode_visible_count
+_ORIG_RANGE = dec.decode_visible_range
 _ORIG_DECODE = dec.decode_attention
 
 
-def _mut_causal_excludes_own_position(L, Sq, i, kind):
-    n = _ORIG_COUNT(L, Sq, i, kind)
-    return max(0, n - 1) if kind == "causal" else n
+def _mut_causal_excludes_own_position(L, Sq, i, kind, window=0):
+    lo, hi = _ORIG_RANGE(L, Sq, i, kind, window)
+    return (lo, max(lo, hi - 1)) if kind != "full" else (lo, hi)
 
 
-def _mut_query_at_index(L, Sq, i, kind):
+def _mut_query_at_index(L, Sq, i, kind, window=0):
     # query i taken at position i instead of L - Sq + i
-    return min(L, i + 1) if kind == "causal" else L
+    return _ORIG_RANGE(L, L, i, kind, window) if L >= Sq else _ORIG_RANGE(L, Sq, i, kind, window)
 
 
-def _mut_ignores_length(q, k_cache, v_cache, kind, cache_len=None, scale=None):
-    return _ORIG_DECODE(q, k_cache, v_cache, kind, cache_len=None, scale=scale)
+def _mut_window_one_too_wide(L, Sq, i, kind, window=0):
+    lo, hi = _ORIG_RANGE(L, Sq, i, kind, window)
+    return (max(0, lo - 1), hi) if kind == "causal_window" else (lo, hi)
+
+
+def _mut_window_from_sequence_start(L, Sq, i, kind, window=0):
+    # the window taken as the first w positions rather than the last
+    lo, hi = _ORIG_RANGE(L, Sq, i, kind, window)
+    return (0, min(hi, window)) if kind == "causal_window" else (lo, hi)
+
+
+def _mut_window_ignored(L, Sq, i, kind, window=0):
+    return _ORIG_RANGE(L, Sq, i, "causal" if kind == "causal_window" else kind, window)
+
+
+def _mut_ignores_length(q, k_cache, v_cache, kind, cache_len=None, scale=None, window=0):
+    return _ORIG_DECODE(q, k_cache, v_cache, kind, cache_len=None, scale=scale, window=window)
 
 
 def _variant(head=None, normalise=True, use_scale=True):
     """A copy of decode_attention with one step changed."""
-    def f(q, k_cache, v_cache, kind, cache_len=None, scale=None):
+    def f(q, k_cache, v_cache, kind, cache_len=None, scale=None, window=0):
         q = np.asarray(q)
         kc, vc = np.asarray(k_cache), np.asarray(v_cache)
         B, Hq, Sq, D = q.shape
@@ -192,19 +280,22 @@ def _variant(head=None, normalise=True, use_scale=True):
             for a in range(Hq):
                 h = a // G if head is None else head(a, Hq, Hkv)
                 for i in range(Sq):
-                    n = dec.decode_visible_count(lens[b], Sq, i, kind)
-                    if n == 0:
+                    lo, hi = dec.decode_visible_range(lens[b], Sq, i, kind, window)
+                    if hi == lo:
                         continue
-                    s = sc * (kc[b, h, :n] @ q[b, a, i])
+                    s = sc * (kc[b, h, lo:hi] @ q[b, a, i])
                     e = np.exp(s - s.max())
-                    out[b, a, i] = ((e / e.sum()) if normalise else e) @ vc[b, h, :n]
+                    out[b, a, i] = ((e / e.sum()) if normalise else e) @ vc[b, h, lo:hi]
         return out
     return f
 
 
 MUTATIONS = {
-    "causal_excludes_own_position": ("decode_visible_count", _mut_causal_excludes_own_position),
-    "query_at_index_not_cache_end": ("decode_visible_count", _mut_query_at_index),
+    "causal_excludes_own_position": ("decode_visible_range", _mut_causal_excludes_own_position),
+    "query_at_index_not_cache_end": ("decode_visible_range", _mut_query_at_index),
+    "window_one_too_wide": ("decode_visible_range", _mut_window_one_too_wide),
+    "window_from_sequence_start": ("decode_visible_range", _mut_window_from_sequence_start),
+    "window_ignored": ("decode_visible_range", _mut_window_ignored),
     "cache_length_ignored": ("decode_attention", _mut_ignores_length),
     "head_map_modulo": ("decode_attention", _variant(head=lambda a, Hq, Hkv: a % Hkv)),
     "not_normalised": ("decode_attention", _variant(normalise=False)),
