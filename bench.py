@@ -247,7 +247,7 @@ def decode_cpu_baseline(w, inputs, lens, n_seq: int = 1):
     sub = [int(x) for x in lens[:n]]
     t0 = time.perf_counter()
     ref = oracle.decode_attention(inputs["q"][:n], inputs["k"][:n], inputs["v"][:n], w.mask,
-                                  cache_len=sub, scale=w.scale)
+                                  cache_len=sub, scale=w.scale, window=w.window)
     dt = time.perf_counter() - t0
     nbytes = decode_counts(w, sub)[0]
     return {
@@ -263,18 +263,23 @@ def decode_cpu_baseline(w, inputs, lens, n_seq: int = 1):
 
 
 def decode_counts(w, lens):
-    """(valid cache bytes, effective FLOPs) of one decode call over the given
-    sequence lengths: 2 * Hkv * D * 2 bytes per cached position; 4 * D FLOPs
-    per visible (query row, position) pair and query head."""
+    """(cache bytes read, effective FLOPs) of one decode call over the given
+    sequence lengths: 2 * Hkv * D * 2 bytes per cached position some new query
+    sees (under a window of w, the last min(L, w + Sq - 1) of a sequence); 4 * D
+    FLOPs per visible (query row, position) pair and query head."""
     import numpy as np
 
     L = np.asarray([int(x) for x in lens], dtype=np.int64)
-    cache_bytes = int(2 * w.Hkv * w.D * 2 * L.sum())
+    read = np.minimum(L, w.window + w.Sq - 1) if w.mask == "causal_window" else L
+    cache_bytes = int(2 * w.Hkv * w.D * 2 * read.sum())
     if w.mask == "full":
         pairs = int(w.Sq * L.sum())
-    else:  # new position i of Sq sees positions 0 .. L - Sq + i
+    else:  # new position i of Sq sits at p = L - Sq + i and sees positions .. p
         i = np.arange(w.Sq, dtype=np.int64)
-        pairs = int(np.clip(L[:, None] - w.Sq + i[None, :] + 1, 0, L[:, None]).sum())
+        p = L[:, None] - w.Sq + i[None, :]
+        hi = np.clip(p + 1, 0, L[:, None])
+        lo = np.clip(p - w.window + 1, 0, None) if w.mask == "causal_window" else 0
+        pairs = int(np.maximum(hi - lo, 0).sum())
     return cache_bytes, 4 * w.D * pairs * w.Hq
 
 
@@ -474,14 +479,14 @@ def bench_decode(args, name):
     lens = w.cache_len()
     cl = torch.from_numpy(lens).to(dev)
     out = torch.empty_like(q)
-    ws_n = attn.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Smax, w.D, w.mask)
+    ws_n = attn.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Smax, w.D, w.mask, w.window)
     ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     calibration_copy(args.calibrate_copy_mib, dev)
 
     def step():
         attn.decode(q, k, v, cache_len=cl, mask=w.mask, scale=w.scale, out=out, workspace=ws,
-                    stream=stream)
+                    stream=stream, window=w.window)
 
     ms, prewarm_steps, spread = time_steps(step, stream, args)
     cache_bytes, flops = decode_counts(w, lens)

@@ -259,11 +259,14 @@ int attn_plan(int B, int Hq, int Hkv, int S, int D, int mask_kind, int window,
  * cached values; "Transformer 架构及其变体", section 预填充创建缓存，解码复用缓存:
  * each step appends the new positions' keys and values to the cache, then the
  * new queries read the stored history; sequences may hold caches of
- * different lengths):
+ * different lengths; "Transformer 演进与变体", section 稀疏注意力: under a
+ * sliding window each position attends only to the last `window` positions
+ * up to itself):
  *
  *   for every batch b, query head a, new position i < Sq:
  *     h   = a / (Hq / Hkv),   L = cache_len[b],   p_i = L - Sq + i
- *     visible positions j:  j <= p_i (ATTN_MASK_CAUSAL)  or  j < L (ATTN_MASK_FULL)
+ *     visible positions j:  j <= p_i (ATTN_MASK_CAUSAL),  j < L (ATTN_MASK_FULL),
+ *                           p_i - window < j <= p_i (ATTN_MASK_CAUSAL_WINDOW)
  *     o[b][a][i][:] = softmax_j(scale * q[b][a][i] . k[b][h][j]) applied to v[b][h][j][:]
  *
  *   q           device [B][Hq][Sq][D] bf16: queries of the Sq newest positions
@@ -279,7 +282,11 @@ int attn_plan(int B, int Hq, int Hkv, int S, int D, int mask_kind, int window,
  *               (all query rows of one key/value head share one matrix-core tile)
  *   Smax        cache capacity per sequence, >= 1
  *   D           head width, 64 or 128
- *   mask_kind   ATTN_MASK_CAUSAL or ATTN_MASK_FULL (identical when Sq == 1)
+ *   mask_kind   ATTN_MASK_CAUSAL, ATTN_MASK_FULL (identical when Sq == 1) or
+ *               ATTN_MASK_CAUSAL_WINDOW (only the last window + Sq - 1
+ *               positions of a sequence are read)
+ *   window      >= 1 with ATTN_MASK_CAUSAL_WINDOW (a window of Smax or more
+ *               is the causal mask), 0 otherwise; else ATTN_ERR_WINDOW
  *   scale       multiplies q.k, used exactly as given
  *   dtype       ATTN_DTYPE_BF16 (fp32 returns ATTN_ERR_UNSUPPORTED); arithmetic
  *               as for attn_fwd's bf16 path
@@ -289,20 +296,26 @@ int attn_plan(int B, int Hq, int Hkv, int S, int D, int mask_kind, int window,
  *               calls that may run at the same time need separate workspaces
  *
  * A query that sees no position (p_i < 0, or L == 0) is written as zeros.
- * Returns ATTN_OK after enqueuing one or two kernels (the second merges key
- * splits); no synchronisation, no allocation.  Argument errors are detected on
- * the host before any launch.  Deterministic for a given input and length.
+ * The key ranges are cut into splits on the device from the lengths, in
+ * proportion to each sequence's range (a long sequence takes more
+ * workgroups than a short one).  Returns ATTN_OK after enqueuing one or two
+ * kernels (the second merges key splits); no synchronisation, no allocation.
+ * Argument errors are detected on the host before any launch.  Deterministic
+ * for a given input and lengths.
  */
 int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
                 const int* cache_len, int B, int Hq, int Hkv, int Sq, int Smax, int D,
-                int mask_kind, float scale, int dtype, void* workspace,
+                int mask_kind, int window, float scale, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream);
 
 /* Workspace bytes attn_decode needs for these arguments (0 when it needs
  * none); the same validation as attn_decode, no device access.  The size
- * depends on B, Hq, Hkv, Sq, Smax and D, not on the lengths. */
+ * depends on the shape, the mask and the window, not on the lengths or on
+ * whether they are given: about 4.1 MiB (D = 128) or 2.1 MiB (D = 64) of
+ * key-split partials plus 8 bytes per (sequence, key/value head) pair once a
+ * sequence's key range can exceed 256 positions, else 0. */
 int attn_decode_workspace(int B, int Hq, int Hkv, int Sq, int Smax, int D, int mask_kind,
-                          int dtype, size_t* workspace_bytes);
+                          int window, int dtype, size_t* workspace_bytes);
 
 /* Bytes of the static device scratch behind attn_decode_noalloc (one array
  * per GPU the library runs on, held until the process ends). */
@@ -317,7 +330,7 @@ int attn_decode_workspace(int B, int Hq, int Hkv, int Sq, int Smax, int D, int m
  * allocates nothing (no hipMalloc, hipFree or allocating routine).
  *
  *   q, k_cache, v_cache, o, cache_len, B, Hq, Hkv, Sq, Smax, D, mask_kind,
- *   scale, dtype, stream   as for attn_decode
+ *   window, scale, dtype, stream   as for attn_decode
  *
  * The first call on a GPU looks up that GPU's copy of the array (with the
  * stream's device current for the lookup, restored afterwards).  Every call
@@ -325,13 +338,13 @@ int attn_decode_workspace(int B, int Hq, int Hkv, int Sq, int Smax, int D, int m
  * calls that may overlap on one GPU race and must be serialised by the
  * caller (one stream, or events).  Returns ATTN_ERR_SCRATCH, before any
  * launch, when attn_decode_workspace reports more than
- * ATTN_NOALLOC_SCRATCH_BYTES for the arguments (no valid decode shape needs
- * more than about 8.1 MiB), ATTN_ERR_HIP when the lookup fails, otherwise
- * the status attn_decode would return.
+ * ATTN_NOALLOC_SCRATCH_BYTES for the arguments (more than about a million
+ * (sequence, key/value head) pairs), ATTN_ERR_HIP when the lookup fails,
+ * otherwise the status attn_decode would return.
  */
 int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
                         const int* cache_len, int B, int Hq, int Hkv, int Sq, int Smax, int D,
-                        int mask_kind, float scale, int dtype, void* stream);
+                        int mask_kind, int window, float scale, int dtype, void* stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* attn_status_string(int status);

@@ -17,17 +17,22 @@ def test_decode_counts_match_oracle(name):
     w = workloads.DECODE_WORKLOADS[name]
     lens = w.cache_len()
     nbytes, flops = bench.decode_counts(w, lens)
-    assert nbytes == oracle.decode_cache_bytes(w.B, w.Hkv, w.D, lens, 2)
-    assert flops == oracle.decode_effective_flops(w.Hq, w.Sq, w.D, lens, w.mask)
+    assert nbytes == oracle.decode_cache_bytes(w.B, w.Hkv, w.D, lens, 2, Sq=w.Sq, kind=w.mask,
+                                               window=w.window)
+    assert flops == oracle.decode_effective_flops(w.Hq, w.Sq, w.D, lens, w.mask, w.window)
 
 
-@pytest.mark.parametrize("mask", ["causal", "full"])
-def test_decode_counts_short_caches(mask):
-    """Lengths of zero and below the number of new positions."""
-    w = workloads.DecodeWorkload("t", 5, 8, 2, 4, 64, 64, mask, "full")
-    lens = [0, 1, 3, 4, 64]
-    assert bench.decode_counts(w, lens)[1] == oracle.decode_effective_flops(
-        w.Hq, w.Sq, w.D, lens, mask)
+@pytest.mark.parametrize("mask,window", [("causal", 0), ("full", 0), ("causal_window", 1),
+                                         ("causal_window", 3), ("causal_window", 50)])
+def test_decode_counts_short_caches(mask, window):
+    """Lengths of zero, below the number of new positions, and below and
+    above the window."""
+    w = workloads.DecodeWorkload("t", 7, 8, 2, 4, 64, 64, mask, "full", window=window)
+    lens = [0, 1, 3, 4, 6, 52, 64]
+    nbytes, flops = bench.decode_counts(w, lens)
+    assert flops == oracle.decode_effective_flops(w.Hq, w.Sq, w.D, lens, mask, window)
+    assert nbytes == oracle.decode_cache_bytes(w.B, w.Hkv, w.D, lens, 2, Sq=w.Sq, kind=mask,
+                                               window=window)
 
 
 @pytest.mark.parametrize("Sq,Skv", [(1, 1), (5, 3), (3, 5), (64, 1000), (300, 100)])

@@ -2,8 +2,9 @@
 
 GPU cases compare every element of the output with oracle.decode_attention on
 the same seeded inputs (bf16 tolerance 2e-2, as for the full-sequence path);
-cache positions beyond a sequence's length hold NaN, so any read of them into
-the result shows.  Host-only cases check the validation of the boundary.
+cache positions beyond a sequence's length, and under a sliding window those
+before the first position any new query sees, hold NaN, so any read of them
+into the result shows.  Host-only cases check the validation of the boundary.
 """
 import ctypes
 
@@ -18,26 +19,35 @@ attn = pytest.importorskip("transformer_attention_attn_amd")
 
 
 def run_decode(device, B, Hq, Hkv, Sq, Smax, D, mask, lens=None, seed=0, scale=None,
-               rows=None):
+               rows=None, window=0, ws_guard=False):
     import torch
 
-    print(f"decode case B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Smax={Smax} D={D} {mask} "
+    print(f"decode case B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Smax={Smax} D={D} {mask} w={window} "
           f"lens={None if lens is None else list(lens)[:8]} seed={seed}", flush=True)
     inp = workloads.make_decode_inputs(B, Hq, Hkv, Sq, Smax, D, seed)
     kb, vb = inp["k_bits"].copy(), inp["v_bits"].copy()
-    if lens is not None:
-        for b, L in enumerate(lens):  # positions past the length hold NaN
-            kb[b, :, L:] = 0x7FC0
-            vb[b, :, L:] = 0x7FC0
+    for b, L in enumerate([Smax] * B if lens is None else lens):
+        kb[b, :, L:] = 0x7FC0  # positions past the length hold NaN
+        vb[b, :, L:] = 0x7FC0
+        if window:  # and those before every new query's window
+            cut = max(0, L - Sq - window + 1)
+            kb[b, :, :cut] = 0x7FC0
+            vb[b, :, :cut] = 0x7FC0
     q = torch.from_numpy(inp["q_bits"].view(np.int16)).view(torch.bfloat16).to(device)
     k = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(device)
     v = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(device)
     cl = None if lens is None else torch.tensor(list(lens), dtype=torch.int32, device=device)
-    o = attn.decode(q, k, v, cache_len=cl, mask=mask, scale=scale)
+    ws = None
+    if ws_guard:  # the workspace the call asks for, then a guard region it must not touch
+        need = attn.decode_workspace_bytes(B, Hq, Hkv, Sq, Smax, D, mask, window)
+        ws = torch.full((need + 65536,), 0x5A, dtype=torch.uint8, device=device)
+    o = attn.decode(q, k, v, cache_len=cl, mask=mask, scale=scale, window=window, workspace=ws)
     torch.cuda.synchronize()
+    if ws_guard:
+        assert bool((ws[need:] == 0x5A).all()), "write past the workspace"
     got = o.float().cpu().numpy()
     ref = oracle.decode_attention(inp["q"], inp["k"], inp["v"], mask,
-                                  cache_len=lens, scale=scale)
+                                  cache_len=lens, scale=scale, window=window)
     if rows is not None:
         got = np.stack([got[b, a, i] for b, a, i in rows])
         ref = np.stack([ref[b, a, i] for b, a, i in rows])
@@ -55,15 +65,24 @@ for D in (64, 128):
                 lens = None
                 if _rng.integers(2) and Smax > 1:
                     lens = tuple(int(x) for x in _rng.integers(0, Smax + 1, size=B))
-                SWEEP.append((B, Hq, Hkv, Sq, Smax, D, mask, lens))
+                SWEEP.append((B, Hq, Hkv, Sq, Smax, D, mask, lens, 0))
+        # sliding window: one, a part of a tile, several tiles, about the cache
+        for Smax, window in ((300, 1), (300, 17), (2049, 100), (2049, 700), (2049, 2049)):
+            B = 1 + int(_rng.integers(3))
+            lens = None
+            if _rng.integers(2):
+                lens = tuple(int(x) for x in _rng.integers(0, Smax + 1, size=B))
+            SWEEP.append((B, Hq, Hkv, Sq, Smax, D, "causal_window", lens, window))
 
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"D{c[5]}-H{c[1]}x{c[2]}-Sq{c[3]}-S{c[4]}-"
-                                                      f"{c[6]}-{'ragged' if c[7] else 'full'}")
+                                                      f"{c[6]}{c[8] or ''}-"
+                                                      f"{'ragged' if c[7] else 'full'}")
 def test_decode_sweep(device, case):
-    B, Hq, Hkv, Sq, Smax, D, mask, lens = case
-    err = run_decode(device, B, Hq, Hkv, Sq, Smax, D, mask, lens, seed=Smax + 3 * Sq + D)
+    B, Hq, Hkv, Sq, Smax, D, mask, lens, window = case
+    err = run_decode(device, B, Hq, Hkv, Sq, Smax, D, mask, lens, seed=Smax + 3 * Sq + D,
+                     window=window)
     assert err <= TOL["bf16"], err
 
 
@@ -81,6 +100,33 @@ def test_decode_edge_lengths(device):
     lens = (0, 2, 4, 32, 33, 255, 256, 257, 1023, 1024, 4096)
     err = run_decode(device, len(lens), 8, 2, 4, 4096, 128, "causal", lens, seed=10)
     assert err <= TOL["bf16"], err
+    for window in (1, 3, 32, 253, 1021):
+        err = run_decode(device, len(lens), 8, 2, 4, 4096, 128, "causal_window", lens, seed=11,
+                         window=window)
+        assert err <= TOL["bf16"], (window, err)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", ["one_long", "many_short", "mqa_skew", "window_skew"])
+def test_decode_split_plan(device, case):
+    """Lengths that push the plan made from the device-side lengths: one long
+    sequence among empty and short ones (it takes nearly all splits), many
+    sequences (most take one split), a key/value head shared by 32 query
+    heads, and a window over skewed lengths.  The workspace is followed by a
+    guard region the call must leave alone."""
+    if case == "one_long":
+        args = (9, 8, 2, 1, 65536, 128, "causal", (0, 65536, 3, 100, 0, 1, 300, 2, 31), 0)
+    elif case == "many_short":
+        lens = tuple(int(x) for x in np.random.default_rng(3).integers(0, 4097, size=96))
+        args = (96, 8, 2, 2, 4096, 64, "causal", lens, 0)
+    elif case == "mqa_skew":
+        args = (3, 32, 1, 1, 40000, 128, "full", (40000, 257, 9999), 0)
+    else:
+        args = (5, 16, 4, 2, 30000, 128, "causal_window", (30000, 5000, 4097, 4095, 17), 4096)
+    B, Hq, Hkv, Sq, Smax, D, mask, lens, window = args
+    err = run_decode(device, B, Hq, Hkv, Sq, Smax, D, mask, lens, seed=12, window=window,
+                     ws_guard=True)
+    assert err <= TOL["bf16"], err
 
 
 @pytest.mark.gpu
@@ -95,7 +141,7 @@ def test_decode_workload_full_size(device, name):
         rows.add((int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.Sq))))
     lens = tuple(int(x) for x in w.cache_len()) if w.lengths != "full" else None
     err = run_decode(device, w.B, w.Hq, w.Hkv, w.Sq, w.Smax, w.D, w.mask, lens, seed=w.seed,
-                     rows=sorted(rows))
+                     rows=sorted(rows), window=w.window)
     print(f"{name}: max abs err {err:.3e}", flush=True)
     assert err <= TOL["bf16"], err
 
@@ -109,21 +155,27 @@ FAKE = 0x100000  # an aligned non-null address; never dereferenced (validation f
 
 def decode_status(B=1, Hq=8, Hkv=2, Sq=1, Smax=1000, D=128, mask="causal", scale=0.1,
                   dtype=attn.DTYPE_BF16, ws=0, ws_bytes=0, ptrs=(FAKE, FAKE * 3, FAKE * 5, FAKE * 7),
-                  cache_len=0):
+                  cache_len=0, window=0):
     q, k, v, o = ptrs
-    return attn.decode_raw(q, k, v, o, cache_len, B, Hq, Hkv, Sq, Smax, D, mask, scale, dtype,
-                           ws, ws_bytes, 0)
+    return attn.decode_raw(q, k, v, o, cache_len, B, Hq, Hkv, Sq, Smax, D, mask, window, scale,
+                           dtype, ws, ws_bytes, 0)
 
 
 def test_decode_workspace_plan():
-    # enough (b, kvh) pairs: no split, no workspace
-    st, n = attn.decode_workspace_status(64, 32, 8, 1, 8192, 128)
-    assert (st, n) == (0, 0)
-    # few pairs and a long cache: splits, 32 rows x (D + 2) floats per split
-    st, n = attn.decode_workspace_status(1, 32, 8, 1, 8192, 128)
-    assert st == 0 and n > 0 and n % (8 * 32 * 130 * 4) == 0
-    # the size does not depend on the mask kind
+    # key ranges of at most 256 positions (eight 32-key tiles) never split
+    assert attn.decode_workspace_status(64, 32, 8, 1, 256, 128) == (0, 0)
+    assert attn.decode_workspace_status(64, 32, 8, 4, 65536, 128, "causal_window",
+                                        window=253) == (0, 0)
+    # longer ranges: 256 partial slots of 32 rows x (D + 2) floats, then 8
+    # bytes per (sequence, key/value head) pair; independent of the lengths
+    for B, Hkv, D in ((1, 8, 128), (64, 8, 128), (3, 1, 64)):
+        st, n = attn.decode_workspace_status(B, 4 * Hkv, Hkv, 1, 8192, D)
+        assert st == 0 and n == 256 * 32 * (D + 2) * 4 + 8 * B * Hkv
+    # the same for every mask kind, and for a window whose range is 257 positions
+    n = attn.decode_workspace_status(1, 32, 8, 1, 8192, 128)[1]
     assert attn.decode_workspace_status(1, 32, 8, 1, 8192, 128, "full")[1] == n
+    assert attn.decode_workspace_status(1, 32, 8, 1, 8192, 128, "causal_window",
+                                        window=257)[1] == n
 
 
 def test_decode_rejects_bad_arguments():
@@ -136,7 +188,11 @@ def test_decode_rejects_bad_arguments():
     assert st(Hq=6, Hkv=4) == "ATTN_ERR_HEADS"
     assert st(D=96) == "ATTN_ERR_UNSUPPORTED"
     assert st(dtype=attn.DTYPE_FP32) == "ATTN_ERR_UNSUPPORTED"
-    assert st(mask="causal_window") == "ATTN_ERR_UNSUPPORTED"
+    assert st(mask="causal_window") == "ATTN_ERR_WINDOW"         # window 0
+    assert st(mask="causal_window", window=-3) == "ATTN_ERR_WINDOW"
+    assert st(mask="causal", window=5) == "ATTN_ERR_WINDOW"      # a window without its mask
+    assert st(mask="full", window=5) == "ATTN_ERR_WINDOW"
+    assert st(mask="local_global", window=5) == "ATTN_ERR_UNSUPPORTED"
     assert st(Hq=32, Hkv=1, Sq=2) == "ATTN_ERR_UNSUPPORTED"   # 64 query rows per key/value head
     assert st(scale=float("nan")) == "ATTN_ERR_SCALE"
     assert st(ptrs=(FAKE + 8, FAKE * 3, FAKE * 5, FAKE * 7)) == "ATTN_ERR_ALIGN"
@@ -150,5 +206,5 @@ def test_decode_rejects_bad_arguments():
 
 def test_decode_symbols_exported():
     lib = ctypes.CDLL(attn.LIB_PATH)
-    for name in ("attn_decode", "attn_decode_workspace"):
+    for name in ("attn_decode", "attn_decode_workspace", "attn_decode_noalloc"):
         assert hasattr(lib, name)

@@ -2,8 +2,8 @@
 attn_decode (caller's workspace): the same kernels and split plan, so the
 outputs must be bitwise equal.  Two calls in a row on one GPU, the second
 with a smaller input, so the second reads the shared scratch after the first
-left its partials there; plus a many-split MQA cache and a call that needs
-no scratch."""
+left its partials there; plus a many-split MQA cache, a sliding window and a
+call that needs no scratch."""
 import pytest
 
 torch = pytest.importorskip("torch")
@@ -23,10 +23,10 @@ def _case(B, Hq, Hkv, Sq, Smax, lengths, seed):
     return q, k, v, lens
 
 
-def _check(q, k, v, lens, mask="causal"):
-    ref = attn.decode(q, k, v, cache_len=lens, mask=mask)
+def _check(q, k, v, lens, mask="causal", window=0):
+    ref = attn.decode(q, k, v, cache_len=lens, mask=mask, window=window)
     out = torch.full_like(q, float("nan"))
-    got = attn.decode_noalloc(q, k, v, cache_len=lens, mask=mask, out=out)
+    got = attn.decode_noalloc(q, k, v, cache_len=lens, mask=mask, out=out, window=window)
     torch.cuda.synchronize()
     assert got.data_ptr() == out.data_ptr()
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
@@ -44,13 +44,16 @@ def test_noalloc_two_calls_second_smaller():
 
 
 def test_noalloc_many_splits_mqa_and_no_scratch():
-    # one key/value head, 65536 positions: 256 splits in the plan
+    # one key/value head, 50001 of 65536 positions: 196 splits of eight tiles
     q, k, v, lens = _case(1, 8, 1, 1, 65536, [50001], seed=13)
     assert attn.decode_workspace_bytes(1, 8, 1, 1, 65536, 128) > 0
     _check(q, k, v, lens)
-    # 256 (b, kvh) pairs: one split each, no scratch used
-    q, k, v, lens = _case(64, 16, 4, 1, 512, [(37 * i) % 512 + 1 for i in range(64)], seed=14)
-    assert attn.decode_workspace_bytes(64, 16, 4, 1, 512, 128) == 0
+    # a sliding window of 1000 positions over ragged caches
+    q, k, v, lens = _case(3, 16, 4, 2, 9000, [9000, 1200, 17], seed=16)
+    _check(q, k, v, lens, mask="causal_window", window=1000)
+    # caches of at most 256 positions: one split each, no scratch used
+    q, k, v, lens = _case(64, 16, 4, 1, 256, [(37 * i) % 256 + 1 for i in range(64)], seed=14)
+    assert attn.decode_workspace_bytes(64, 16, 4, 1, 256, 128) == 0
     _check(q, k, v, lens, mask="full")
 
 

@@ -101,11 +101,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_plan.restype = i
     lib.attn_fwd_ex.argtypes = [ctypes.POINTER(FwdArgs), p]
     lib.attn_fwd_ex.restype = i
-    lib.attn_decode.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, f, i, p, ctypes.c_size_t, p]
+    lib.attn_decode.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, i, f, i, p, ctypes.c_size_t, p]
     lib.attn_decode.restype = i
-    lib.attn_decode_workspace.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
+    lib.attn_decode_workspace.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]
     lib.attn_decode_workspace.restype = i
-    lib.attn_decode_noalloc.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, f, i, p]
+    lib.attn_decode_noalloc.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, i, f, i, p]
     lib.attn_decode_noalloc.restype = i
     u32p = ctypes.POINTER(ctypes.c_uint32)
     lib.attn_layout_strided.argtypes = [i, i, i, u32p]
@@ -324,37 +324,40 @@ def plan_status(B, Hq, Hkv, S, D, mask, window=0, global_idx=None, dtype=DTYPE_B
                          ctypes.byref(info))
 
 
-def decode_workspace_status(B, Hq, Hkv, Sq, Smax, D, mask="causal", dtype=DTYPE_BF16):
+def decode_workspace_status(B, Hq, Hkv, Sq, Smax, D, mask="causal", dtype=DTYPE_BF16, window=0):
     """(status, bytes) of attn_decode_workspace for these arguments (host only)."""
     lib = load()
     n = ctypes.c_size_t(0)
-    st = lib.attn_decode_workspace(B, Hq, Hkv, Sq, Smax, D, _mask_id(mask), dtype, ctypes.byref(n))
+    st = lib.attn_decode_workspace(B, Hq, Hkv, Sq, Smax, D, _mask_id(mask), window, dtype,
+                                   ctypes.byref(n))
     return st, int(n.value)
 
 
 def decode_workspace_bytes(B: int, Hq: int, Hkv: int, Sq: int, Smax: int, D: int,
-                           mask="causal") -> int:
+                           mask="causal", window: int = 0) -> int:
     """Device workspace bytes attn_decode needs (0 when it needs none)."""
-    st, n = decode_workspace_status(B, Hq, Hkv, Sq, Smax, D, mask)
+    st, n = decode_workspace_status(B, Hq, Hkv, Sq, Smax, D, mask, window=window)
     if st != 0:
         raise AttnError(st)
     return n
 
 
 def decode_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, len_ptr: int, B: int, Hq: int,
-               Hkv: int, Sq: int, Smax: int, D: int, mask, scale: float, dtype: int,
+               Hkv: int, Sq: int, Smax: int, D: int, mask, window: int, scale: float, dtype: int,
                ws_ptr: int, ws_bytes: int, stream: int) -> int:
     """Direct call of attn_decode with raw device addresses; returns the status."""
     return load().attn_decode(q_ptr, k_ptr, v_ptr, o_ptr, len_ptr, B, Hq, Hkv, Sq, Smax, D,
-                              _mask_id(mask), float(scale), dtype, ws_ptr, ws_bytes, stream)
+                              _mask_id(mask), window, float(scale), dtype, ws_ptr, ws_bytes,
+                              stream)
 
 
 def decode(q, k_cache, v_cache, cache_len=None, mask="causal", scale: Optional[float] = None,
-           out=None, workspace=None, stream=None):
+           out=None, workspace=None, stream=None, window: int = 0):
     """Decode attention of the Sq newest positions against key/value caches.
 
     q: [B, Hq, Sq, D] bf16; k_cache, v_cache: [B, Hkv, Smax, D] bf16, contiguous,
     on the GPU.  cache_len: int32 GPU tensor of B lengths (None: all Smax).
+    window: the w of mask "causal_window" (0 with the other masks).
     The workspace (a GPU tensor of at least decode_workspace_bytes bytes) is
     allocated with torch when not given.  Returns o shaped like q.
     """
@@ -379,7 +382,7 @@ def decode(q, k_cache, v_cache, cache_len=None, mask="causal", scale: Optional[f
         raise ValueError("out must be a contiguous tensor shaped like q")
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
-    need = decode_workspace_bytes(B, Hq, Hkv, Sq, Smax, D, mask)
+    need = decode_workspace_bytes(B, Hq, Hkv, Sq, Smax, D, mask, window)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     check_devices(q, k_cache=k_cache, v_cache=v_cache, out=out, cache_len=cache_len,
@@ -392,22 +395,22 @@ def decode(q, k_cache, v_cache, cache_len=None, mask="causal", scale: Optional[f
     with torch.cuda.device(q.device):
         st = decode_raw(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
                         cache_len.data_ptr() if cache_len is not None else 0, B, Hq, Hkv, Sq,
-                        Smax, D, mask, scale, DTYPE_BF16, ws_ptr, ws_bytes, handle)
+                        Smax, D, mask, window, scale, DTYPE_BF16, ws_ptr, ws_bytes, handle)
     if st != 0:
         raise AttnError(st)
     return out
 
 
 def decode_noalloc_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, len_ptr: int, B: int,
-                       Hq: int, Hkv: int, Sq: int, Smax: int, D: int, mask, scale: float,
-                       dtype: int, stream: int) -> int:
+                       Hq: int, Hkv: int, Sq: int, Smax: int, D: int, mask, window: int,
+                       scale: float, dtype: int, stream: int) -> int:
     """Direct call of attn_decode_noalloc with raw device addresses; returns the status."""
     return load().attn_decode_noalloc(q_ptr, k_ptr, v_ptr, o_ptr, len_ptr, B, Hq, Hkv, Sq, Smax,
-                                      D, _mask_id(mask), float(scale), dtype, stream)
+                                      D, _mask_id(mask), window, float(scale), dtype, stream)
 
 
 def decode_noalloc(q, k_cache, v_cache, cache_len=None, mask="causal",
-                   scale: Optional[float] = None, out=None, stream=None):
+                   scale: Optional[float] = None, out=None, stream=None, window: int = 0):
     """decode() through attn_decode_noalloc: no workspace, the library's static
     device scratch instead (calls that may overlap on one GPU race).  `out`
     is allocated with torch when not given; pass it to allocate nothing."""
@@ -439,7 +442,8 @@ def decode_noalloc(q, k_cache, v_cache, cache_len=None, mask="causal",
     with torch.cuda.device(q.device):
         st = decode_noalloc_raw(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                 out.data_ptr(), cache_len.data_ptr() if cache_len is not None else 0,
-                                B, Hq, Hkv, Sq, Smax, D, mask, scale, DTYPE_BF16, handle)
+                                B, Hq, Hkv, Sq, Smax, D, mask, window, scale, DTYPE_BF16,
+                                handle)
     if st != 0:
         raise AttnError(st)
     return out

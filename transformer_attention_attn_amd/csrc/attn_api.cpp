@@ -130,17 +130,27 @@ long long visible_pairs(int S, int mask, int window, const int* g, int ng) {
 
 struct DecodePlan {
   int status;
-  int n_split;
-  int chunk;
+  int window;        // the sliding window clamped to Smax, 0 without one
+  int uni_splits;    // splits of every pair when all sequences hold Smax positions
+  int grid_uniform;  // workgroups without lengths: pairs x uni_splits
+  int grid_ragged;   // workgroups with device lengths: max(kDecodeWorkgroups, pairs),
+                     // a bound on the items of the kernel's plan
+  size_t hdr_off;    // bytes from the workspace start to the per-pair header
   size_t ws_bytes;
 };
 
-// Validation and the key-split plan of a decode call.  Splits: enough
-// (b, kvh, split) workgroups to reach kDecodeWorkgroups, each split at least
-// kDecodeMinChunk keys of the cache capacity; the plan depends on the
-// capacity Smax only, so lengths may change from call to call (and live in
-// device memory) without changing the workspace.
-DecodePlan plan_decode(int B, int Hq, int Hkv, int Sq, int Smax, int D, int mask_kind, int dtype) {
+// Validation and the key-split plan of a decode call.  The key range of a
+// sequence is its last min(L, w + Sq - 1) positions under a window of w, all
+// L otherwise.  Splits hold at least kDecodeMinTiles tiles, and the work items
+// (pairs x splits) of a plan fit in kDecodeWorkgroups whenever the pairs do.
+// Without device lengths every pair holds the same tiles and the splits are
+// planned here; with them the kernel plans from the lengths, and the grid and
+// the workspace take the bounds of its plan: at most max(kDecodeWorkgroups,
+// pairs) items, and at most kDecodeWorkgroups partial slots (only pairs with
+// two or more splits take them).  Neither depends on the lengths, so they
+// may change from call to call without a new workspace.
+DecodePlan plan_decode(int B, int Hq, int Hkv, int Sq, int Smax, int D, int mask_kind,
+                       int window, int dtype) {
   DecodePlan d{};
   d.status = ATTN_OK;
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Smax < 1 || (long long)Smax > kMaxS) {
@@ -149,29 +159,38 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int Sq, int Smax, int D, int mask
   }
   if (dtype != ATTN_DTYPE_BF16) { d.status = ATTN_ERR_UNSUPPORTED; return d; }
   if (D != 64 && D != 128) { d.status = ATTN_ERR_UNSUPPORTED; return d; }
-  if (mask_kind != ATTN_MASK_FULL && mask_kind != ATTN_MASK_CAUSAL) {
+  if (mask_kind != ATTN_MASK_FULL && mask_kind != ATTN_MASK_CAUSAL &&
+      mask_kind != ATTN_MASK_CAUSAL_WINDOW) {
     d.status = ATTN_ERR_UNSUPPORTED;
+    return d;
+  }
+  if (mask_kind == ATTN_MASK_CAUSAL_WINDOW ? window < 1 : window != 0) {
+    d.status = ATTN_ERR_WINDOW;
     return d;
   }
   if (Hq % Hkv != 0) { d.status = ATTN_ERR_HEADS; return d; }
   if ((long long)(Hq / Hkv) * Sq > attn::kDecodeRows) { d.status = ATTN_ERR_UNSUPPORTED; return d; }
   const long double elems = (long double)B * std::max(Hq, Hkv) * std::max(Sq, Smax) * D;
   if (elems > 4.0e18L) { d.status = ATTN_ERR_SHAPE; return d; }
+  d.window = std::min(window, Smax);  // a window of Smax or more sees every causal position
   const long long pairs = (long long)B * Hkv;
-  const long long max_split = attn::cdiv(Smax, attn::kDecodeMinChunk);
-  long long ns = attn::cdiv((int)std::min<long long>(attn::kDecodeWorkgroups, 1LL << 30),
-                            (int)std::min<long long>(pairs, 1LL << 30));
-  ns = std::max<long long>(1, std::min(ns, max_split));
-  const int chunk = attn::cdiv(attn::cdiv(Smax, (int)ns), 32) * 32;
-  d.chunk = chunk;
-  d.n_split = attn::cdiv(Smax, chunk);
-  if (pairs * std::max<long long>(d.n_split, attn::kDecodeRows) > 0x7fffffffLL) {
+  const long long keys = d.window ? std::min<long long>(Smax, (long long)d.window + Sq - 1) : Smax;
+  const int tiles = (int)((keys + attn::kDecodeTile - 1) / attn::kDecodeTile);
+  d.uni_splits = (int)std::max<long long>(
+      1, std::min<long long>(attn::cdiv(tiles, attn::kDecodeMinTiles), attn::kDecodeWorkgroups / pairs));
+  const long long grid_u = pairs * d.uni_splits;
+  const long long grid_r = std::max<long long>(attn::kDecodeWorkgroups, pairs);
+  if (std::max(grid_u, grid_r) > 0x7fffffffLL || pairs * attn::kDecodeRows > 0x7fffffffLL) {
     d.status = ATTN_ERR_SHAPE;  // grid sizes of the two kernels
     return d;
   }
-  d.ws_bytes = d.n_split > 1
-                   ? (size_t)pairs * d.n_split * attn::kDecodeRows * (size_t)(D + 2) * sizeof(float)
-                   : 0;
+  d.grid_uniform = (int)grid_u;
+  d.grid_ragged = (int)grid_r;
+  if (tiles > attn::kDecodeMinTiles) {  // some pair may take two or more splits
+    const size_t slot = (size_t)attn::kDecodeRows * (size_t)(D + 2) * sizeof(float);
+    d.hdr_off = (size_t)attn::kDecodeWorkgroups * slot;
+    d.ws_bytes = d.hdr_off + (size_t)pairs * 2 * sizeof(int);
+  }
   return d;
 }
 
@@ -219,10 +238,10 @@ hipError_t scratch_address(int dev, void** out) {
 // attn_decode_noalloc (true: this device's copy of `scratch`).
 int decode_call(const void* q, const void* k_cache, const void* v_cache, void* o,
                 const int* cache_len, int B, int Hq, int Hkv, int Sq, int Smax, int D,
-                int mask_kind, float scale, int dtype, void* workspace, size_t workspace_bytes,
-                hipStream_t stream, bool static_scratch) {
+                int mask_kind, int window, float scale, int dtype, void* workspace,
+                size_t workspace_bytes, hipStream_t stream, bool static_scratch) {
   if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULL;
-  const DecodePlan d = plan_decode(B, Hq, Hkv, Sq, Smax, D, mask_kind, dtype);
+  const DecodePlan d = plan_decode(B, Hq, Hkv, Sq, Smax, D, mask_kind, window, dtype);
   if (d.status != ATTN_OK) return d.status;
   if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
   for (const void* ptr : {q, k_cache, v_cache, (const void*)o})
@@ -238,6 +257,7 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, void* o
     if (scratch_address(dev, &workspace) != hipSuccess) return ATTN_ERR_HIP;
     workspace_bytes = ATTN_NOALLOC_SCRATCH_BYTES;
   }
+  const bool split = cache_len ? d.ws_bytes > 0 : d.uni_splits > 1;
   if (d.ws_bytes > 0) {
     if (!workspace || workspace_bytes < d.ws_bytes || (uintptr_t)workspace % 16 != 0)
       return ATTN_ERR_WORKSPACE;
@@ -249,15 +269,17 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, void* o
   attn::DParams p{};
   p.q = q; p.k = k_cache; p.v = v_cache; p.o = o;
   p.cache_len = cache_len;
-  p.ws = d.ws_bytes > 0 ? (float*)workspace : nullptr;
+  p.ws = split ? (float*)workspace : nullptr;
+  p.hdr = split ? (int*)((char*)workspace + d.hdr_off) : nullptr;
+  p.max_slots = split ? attn::kDecodeWorkgroups : 0;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Smax = Smax; p.G = Hq / Hkv;
-  p.n_split = d.n_split;
-  p.chunk = d.chunk;
-  p.causal = mask_kind == ATTN_MASK_CAUSAL ? 1 : 0;
+  p.uni_splits = cache_len ? 0 : d.uni_splits;
+  p.causal = mask_kind != ATTN_MASK_FULL ? 1 : 0;
+  p.window = d.window;
   p.c = std::fabs(scale) * 1.4426950408889634f;
   p.qmode = scale > 0.f ? 0 : (scale < 0.f ? 1 : 2);
   if (p.qmode == 2) p.c = 1.f;  // all visible scores equal: weights are uniform
-  hipError_t err = attn::launch_decode(p, D, stream);
+  hipError_t err = attn::launch_decode(p, D, cache_len ? d.grid_ragged : d.grid_uniform, stream);
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -446,9 +468,9 @@ int attn_plan(int B, int Hq, int Hkv, int S, int D, int mask_kind, int window,
 }
 
 int attn_decode_workspace(int B, int Hq, int Hkv, int Sq, int Smax, int D, int mask_kind,
-                          int dtype, size_t* workspace_bytes) {
+                          int window, int dtype, size_t* workspace_bytes) {
   if (!workspace_bytes) return ATTN_ERR_NULL;
-  const DecodePlan d = plan_decode(B, Hq, Hkv, Sq, Smax, D, mask_kind, dtype);
+  const DecodePlan d = plan_decode(B, Hq, Hkv, Sq, Smax, D, mask_kind, window, dtype);
   if (d.status != ATTN_OK) return d.status;
   *workspace_bytes = d.ws_bytes;
   return ATTN_OK;
@@ -456,17 +478,17 @@ int attn_decode_workspace(int B, int Hq, int Hkv, int Sq, int Smax, int D, int m
 
 int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
                 const int* cache_len, int B, int Hq, int Hkv, int Sq, int Smax, int D,
-                int mask_kind, float scale, int dtype, void* workspace, size_t workspace_bytes,
-                void* stream) {
-  return decode_call(q, k_cache, v_cache, o, cache_len, B, Hq, Hkv, Sq, Smax, D, mask_kind, scale,
-                     dtype, workspace, workspace_bytes, (hipStream_t)stream, false);
+                int mask_kind, int window, float scale, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return decode_call(q, k_cache, v_cache, o, cache_len, B, Hq, Hkv, Sq, Smax, D, mask_kind, window,
+                     scale, dtype, workspace, workspace_bytes, (hipStream_t)stream, false);
 }
 
 int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
                         const int* cache_len, int B, int Hq, int Hkv, int Sq, int Smax, int D,
-                        int mask_kind, float scale, int dtype, void* stream) {
-  return decode_call(q, k_cache, v_cache, o, cache_len, B, Hq, Hkv, Sq, Smax, D, mask_kind, scale,
-                     dtype, nullptr, 0, (hipStream_t)stream, true);
+                        int mask_kind, int window, float scale, int dtype, void* stream) {
+  return decode_call(q, k_cache, v_cache, o, cache_len, B, Hq, Hkv, Sq, Smax, D, mask_kind, window,
+                     scale, dtype, nullptr, 0, (hipStream_t)stream, true);
 }
 
 const char* attn_status_string(int status) {

@@ -8,7 +8,10 @@
 // step, so it is bound by memory bandwidth, and the sequences of a batch hold
 // caches of different lengths).  Query i of the Sq new ones sits at cache
 // position L - Sq + i; the causal mask lets it see positions 0..L - Sq + i,
-// the full mask all L.
+// the full mask all L.  Under a sliding window of w positions ("Transformer
+// 演进与变体", section 稀疏注意力: each position attends to the w positions
+// up to itself) query i sees L - Sq + i - w < j <= L - Sq + i, so a sequence
+// reads only its last w + Sq - 1 positions.
 //
 // gfx950 mapping:
 //   * One workgroup of eight wave64 per (sequence b, key/value head, key
@@ -17,6 +20,13 @@
 //     most 32), so every cached key and value row is read from HBM once for
 //     all query heads that share it ("第 8 章 AI 算法Transformer大模型",
 //     section 8.2.1: shared key/value heads need one read instead of h).
+//   * Splits: a sequence's key range is cut into runs of at most `per`
+//     32-key tiles, with per as small as the rule "all work items fit in one
+//     wave of 256 workgroups (one per CU)" allows, so a long sequence takes
+//     more splits than a short one and no split is empty.  With the lengths
+//     on the device every workgroup derives the same plan from them (a
+//     search for per, then a scan that finds its (b, split)); without, all
+//     sequences are alike and the plan is the host's.
 //   * The split's keys are cut into 32-key tiles; wave w walks tiles w,
 //     w + 8, ... (so the eight waves stream neighbouring tiles of one
 //     contiguous range at any time) through a private LDS region (one K
@@ -59,6 +69,40 @@ struct DCfg {
   static_assert(NIG < 16, "vmcnt immediates below 16");
 };
 
+// Length of sequence b (lengths outside [0, Smax] are clamped).
+__device__ __forceinline__ int decode_len(const DParams& p, int b) {
+  const int L = p.cache_len[b];
+  return L < 0 ? 0 : (L > p.Smax ? p.Smax : L);
+}
+// Inclusive prefix sum (ADD) or prefix maximum of non-negative values over
+// the 64 lanes of a wave with DPP row moves (a few cycles each, no LDS):
+// shifts by 1, 2, 4 and 8 within each row of 16 lanes, then the last lane of
+// row 0 into row 1 and of row 2 into row 3, then the last lane of row 1 into
+// rows 2 and 3.  Lanes without a source read 0.
+template <bool ADD, typename T>
+__device__ __forceinline__ T wave_scan(T x) {
+  auto op = [](T a, T b) { return ADD ? a + b : (a > b ? a : b); };
+  x = op(x, __builtin_amdgcn_update_dpp((T)0, x, 0x111, 0xf, 0xf, true));  // row_shr:1
+  x = op(x, __builtin_amdgcn_update_dpp((T)0, x, 0x112, 0xf, 0xf, true));  // row_shr:2
+  x = op(x, __builtin_amdgcn_update_dpp((T)0, x, 0x114, 0xf, 0xf, true));  // row_shr:4
+  x = op(x, __builtin_amdgcn_update_dpp((T)0, x, 0x118, 0xf, 0xf, true));  // row_shr:8
+  x = op(x, __builtin_amdgcn_update_dpp((T)0, x, 0x142, 0xa, 0xf, false)); // row_bcast:15
+  x = op(x, __builtin_amdgcn_update_dpp((T)0, x, 0x143, 0xc, 0xf, false)); // row_bcast:31
+  return x;
+}
+// the scan's value in lane 63: the wave's total or maximum
+template <bool ADD, typename T>
+__device__ __forceinline__ T wave_all(T x) {
+  x = wave_scan<ADD>(x);
+  if constexpr (sizeof(T) == 8) {
+    const unsigned lo = __builtin_amdgcn_readlane((unsigned)x, 63);
+    const unsigned hi = __builtin_amdgcn_readlane((unsigned)((unsigned long long)x >> 32), 63);
+    return (T)(((unsigned long long)hi << 32) | lo);
+  } else {
+    return __builtin_amdgcn_readlane(x, 63);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
   using C = DCfg<D>;
@@ -73,15 +117,121 @@ __global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
   const int hf = lane >> 5;
 
   // ---- work item: (b, kvh, split) ---------------------------------------------
-  const int split = (int)blockIdx.x % p.n_split;
-  const int pair = (int)blockIdx.x / p.n_split;
-  const int b = pair / p.Hkv, kvh = pair % p.Hkv;
-  int L = p.Smax;
-  if (p.cache_len) {
-    L = p.cache_len[b];
-    L = L < 0 ? 0 : (L > p.Smax ? p.Smax : L);  // lengths outside [0, Smax] are clamped
+  int b, kvh, split, ns, slot, Lf;
+  if (p.uni_splits) {
+    // every sequence holds Smax positions: the host's split count
+    ns = p.uni_splits;
+    const int pair = (int)blockIdx.x / ns;
+    split = (int)blockIdx.x % ns;
+    b = pair / p.Hkv;
+    kvh = pair % p.Hkv;
+    slot = pair * ns;
+    Lf = p.Smax;
+  } else {
+    // The same plan in every wave of every workgroup, from the lengths (no
+    // LDS, no barrier): a split holds at most `per` tiles, per the smallest
+    // value found for which the items, Hkv * sum_b ceil(tiles_b / per), fit
+    // in kDecodeWorkgroups (one wave of workgroups); then item g is split
+    // g - Hkv * (s_0 + .. + s_{b-1}) of sequence b, in (kvh, split) order,
+    // and only pairs with two or more splits take partial slots.  Lanes hold
+    // sequences lane, lane + 64, ...; the first 64 lengths stay in a register.
+    const int nch = (p.B + 63) / 64;
+    const int L0 = lane < p.B ? decode_len(p, lane) : 0;
+    auto len_at = [&](int ch) {
+      const int bb = ch * 64 + lane;
+      return ch == 0 ? L0 : (bb < p.B ? decode_len(p, bb) : 0);
+    };
+    auto tiles_of = [&](int L) { return (L - decode_first_key(L, p.Sq, p.window) + DT - 1) / DT; };
+    // items of the plan with at most `per` tiles per split
+    auto items = [&](int per) {
+      long long n = 0;
+      for (int ch = 0; ch < nch; ++ch)
+        if (ch * 64 + lane < p.B) n += decode_splits(tiles_of(len_at(ch)), per);
+      return wave_all<true>(n) * p.Hkv;
+    };
+    long long ts = 0;
+    int tm = 0;
+    for (int ch = 0; ch < nch; ++ch) {
+      const int t = tiles_of(len_at(ch));
+      ts += t;
+      tm = t > tm ? t : tm;
+    }
+    const long long T = wave_all<true>(ts);
+    const int TM = wave_all<false>(tm);
+    const int K = kDecodeWorkgroups / p.Hkv;  // splits per key/value head
+    int per;
+    if (K <= p.B || T == 0) {
+      per = TM > kDecodeMinTiles ? TM : kDecodeMinTiles;  // one split each
+    } else {
+      // lower bound: Hkv * T / per items at least
+      const long long lo0 = (T * p.Hkv + kDecodeWorkgroups - 1) / kDecodeWorkgroups;
+      int lo = lo0 > kDecodeMinTiles ? (int)lo0 : kDecodeMinTiles;
+      if (items(lo) <= kDecodeWorkgroups) {
+        per = lo;
+      } else {
+        // upper bound: the proportional plan 1 + floor((K - B) tiles_b / T)
+        // holds at most K splits per head, its largest split `hi` tiles, and
+        // ceil(tiles_b / hi) never exceeds its split count
+        int hi = kDecodeMinTiles;
+        for (int ch = 0; ch < nch; ++ch) {
+          const int t = tiles_of(len_at(ch));
+          const int sb = 1 + (int)((long long)(K - p.B) * t / T);
+          const int h = (t + sb - 1) / sb;
+          hi = h > hi ? h : hi;
+        }
+        hi = wave_all<false>(hi);
+        hi = hi > lo ? hi : lo + 1;
+        // lo fails, hi fits: bisect, at most six steps (to a 64th of the
+        // first interval)
+        for (int step = 0; step < 6 && hi - lo > 1; ++step) {
+          const int mid = lo + (hi - lo) / 2;
+          if (items(mid) <= kDecodeWorkgroups) hi = mid;
+          else lo = mid;
+        }
+        per = hi;
+      }
+    }
+    // scan the split counts for the sequence that holds item g
+    const int g = (int)blockIdx.x;
+    int carry_s = 0, carry_q = 0, fb = -1, fs = 0, fe = 0, fq = 0, fl = 0;
+    for (int ch = 0; ch < nch; ++ch) {
+      const int bb = ch * 64 + lane;
+      const int Lb = len_at(ch);
+      const int sb = bb < p.B ? decode_splits(tiles_of(Lb), per) : 0;
+      const int qb = sb >= 2 ? sb : 0;
+      const int is = wave_scan<true>(sb), iq = wave_scan<true>(qb);  // inclusive
+      const int first = p.Hkv * (carry_s + is - sb);
+      const unsigned long long hit =
+          __builtin_amdgcn_ballot_w64(bb < p.B && g >= first && g < first + p.Hkv * sb);
+      if (hit) {
+        const int src = __builtin_ctzll(hit);
+        fb = ch * 64 + src;
+        fs = __builtin_amdgcn_readlane(sb, src);
+        fe = g - __builtin_amdgcn_readlane(first, src);
+        fq = carry_q + __builtin_amdgcn_readlane(iq - qb, src);
+        fl = __builtin_amdgcn_readlane(Lb, src);
+        break;
+      }
+      carry_s += __builtin_amdgcn_readlane(is, 63);
+      carry_q += __builtin_amdgcn_readlane(iq, 63);
+    }
+    if (fb < 0) return;  // past the last item (the grid is an upper bound)
+    b = fb;
+    ns = fs;
+    kvh = fe / ns;
+    split = fe % ns;
+    slot = p.Hkv * fq + kvh * ns;
+    Lf = fl;
   }
-  L = __builtin_amdgcn_readfirstlane(L);
+  b = __builtin_amdgcn_readfirstlane(b);
+  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  split = __builtin_amdgcn_readfirstlane(split);
+  ns = __builtin_amdgcn_readfirstlane(ns);
+  slot = __builtin_amdgcn_readfirstlane(slot);
+  // a plan whose partials would not fit the workspace is never carried out
+  if (ns >= 2 && (!p.ws || slot + ns > p.max_slots)) return;
+  const int L = __builtin_amdgcn_readfirstlane(Lf);
+  const int kfirst = decode_first_key(L, p.Sq, p.window);
 
   // ---- this lane's query row: head kvh*G + r / Sq, new position r % Sq ----------
   const int r = l32;
@@ -91,6 +241,7 @@ __global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
   const int qi = row_valid ? r % p.Sq : 0;
   // last visible cache position of this row (inclusive); -1 when it sees none
   const int lim = p.causal ? L - p.Sq + qi : L - 1;
+  // window: this row sees positions lim - w + 1 .. lim
 
   const size_t Smax = (size_t)p.Smax;
   const __bf16* kp = (const __bf16*)p.k + ((size_t)b * p.Hkv + kvh) * Smax * D;
@@ -113,8 +264,12 @@ __global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
   }
 
   // ---- the split's key range [k0, k1) in 32-key tiles -------------------------
-  const int k0 = split * p.chunk;
-  const int k1 = (k0 + p.chunk < L) ? k0 + p.chunk : L;
+  // the sequence's tiles from kfirst, cut into ns runs of equal length (the
+  // last one shorter); every run starts before L
+  const int seq_tiles = (L - kfirst + DT - 1) / DT;
+  const int tps = (seq_tiles + ns - 1) / ns;
+  const int k0 = kfirst + split * tps * DT;
+  const int k1 = (tps * DT < L - k0) ? k0 + tps * DT : L;
   const int ntile = k1 > k0 ? (k1 - k0 + DT - 1) / DT : 0;
 
   unsigned char* kreg = smem + wave * 2 * REG;
@@ -153,8 +308,12 @@ __global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
     for (int q = 0; q < 16; ++q) oacc[db][q] = 0.f;
   float m_run = -INFINITY, l_run0 = 0.f, l_run1 = 0.f;
   const float c = p.c;
-  // positions past which some row of the wave may be masked
+  // keys past lim_lo or before lo_hi are masked for some row of the wave
   const int lim_lo = p.causal ? L - p.Sq : L - 1;
+  const int lo_hi = p.window ? L - p.window : -(1 << 30);
+  // first position this row sees (0 without a window; no key loaded is below it
+  // then)
+  const int row_lo = (p.window && lim - p.window + 1 > 0) ? lim - p.window + 1 : 0;
 
   // wave w takes tiles w, w + 8, ...: at any time the eight waves stream
   // neighbouring tiles of one contiguous range
@@ -173,11 +332,16 @@ __global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // K operand reads done: the region may be refilled
     if (more) gload(kp, t + DWAVES, kreg, false);
     const int tk = k0 + t * DT;
-    if (tk + DT - 1 > lim_lo) {
-      // register q of the accumulator holds key tk + 8*(q/4) + 4*hf + q%4
+    if (tk + DT - 1 > lim_lo || tk < lo_hi) {
+      // register q of the accumulator holds key tk + 8*(q/4) + 4*hf + q%4; the
+      // row sees offsets rel - w + 1 .. rel
       const int rel = lim - tk - 4 * hf;
+      const int rlo = row_lo - tk - 4 * hf;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) sc[q] = (8 * (q >> 2) + (q & 3) <= rel) ? sc[q] : -INFINITY;
+      for (int q = 0; q < 16; ++q) {
+        const int off = 8 * (q >> 2) + (q & 3);
+        sc[q] = (off <= rel && off >= rlo) ? sc[q] : -INFINITY;
+      }
     }
     float mx = max3f(sc[0], sc[1], sc[2]);
     mx = max3f(mx, sc[3], sc[4]);
@@ -279,7 +443,9 @@ __global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
   // ---- wave 0: the workgroup's (m, l, O) of the 32 rows ---------------------------
   const float l_half = l_run0 + l_run1;
   const float l_tot = l_half + __uint_as_float(__shfl_xor((int)__float_as_uint(l_half), 32));
-  if (p.n_split == 1) {
+  if (p.ws && !p.uni_splits && split == 0 && lane == 0)
+    *(int2*)(p.hdr + 2 * (b * p.Hkv + kvh)) = int2{slot, ns};
+  if (ns == 1) {
     if (!row_valid) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;  // a row that sees nothing is zero
     __bf16* op = (__bf16*)p.o + (((size_t)b * p.Hq + a) * p.Sq + qi) * D;
@@ -296,7 +462,7 @@ __global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
   }
   // partial of this split: rows [32][D] fp32 (unnormalised O), then m (log2
   // units, -inf when the row saw nothing here) and l per row
-  float* ws = p.ws + (size_t)blockIdx.x * (32 * (D + 2));
+  float* ws = p.ws + (size_t)(slot + split) * (32 * (D + 2));
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -311,70 +477,125 @@ __global__ __launch_bounds__(DWAVES * 64) void attn_decode_bf16(DParams p) {
   }
 }
 
-// Merge the splits of one query row: one workgroup per (b, kvh, row) of
-// CG x D threads; thread (g, d) sums dimension d over the splits s = g mod CG,
-//   M = max_c m_c,  O[d] = sum_c 2^(m_c - M) O_c[d] / sum_c 2^(m_c - M) l_c
-// (zero if M = -inf), and the CG partial sums meet in LDS in a fixed order.
-constexpr int CG = 4;
+// Merge the splits of one query row: one workgroup of 512 threads per (b,
+// kvh, row) (pairs that took one split wrote their output already).  Thread
+// (g, c) holds dims 4c .. 4c + 3 and walks the splits s = g mod CG with the
+// online recurrence (running maximum M; numerator and denominator rescaled by
+// 2^(M_old - M_new) when it rises), so every partial is read once; the CG
+// groups then meet in LDS in a fixed order:
+//   M = max_s m_s,  O[d] = sum_s 2^(m_s - M) O_s[d] / sum_s 2^(m_s - M) l_s
+// (zero when no split saw a position).
+constexpr int kCombThreads = 512;
 template <int D>
-__global__ __launch_bounds__(CG * D) void attn_decode_combine(DParams p) {
+__global__ __launch_bounds__(kCombThreads) void attn_decode_combine(DParams p) {
   constexpr int STRIDE = 32 * (D + 2);
-  __shared__ float red[CG * D];
-  __shared__ float part[2][CG][D];
+  constexpr int TPR = D / 4;                 // threads per row
+  constexpr int CG = kCombThreads / TPR;     // split groups
+  __shared__ float4 pnum[CG][TPR];
+  __shared__ float2 pmd[CG];
   const int nrows = p.G * p.Sq;
   const int pair = (int)blockIdx.x / nrows, r = (int)blockIdx.x % nrows;
   const int b = pair / p.Hkv, kvh = pair % p.Hkv;
-  const int tid = threadIdx.x, d = tid % D, g = tid / D;
-  const float* base = p.ws + (size_t)pair * p.n_split * STRIDE;
-  float mloc = -INFINITY;
-  for (int s = tid; s < p.n_split; s += CG * D) mloc = fmaxf(mloc, base[(size_t)s * STRIDE + 32 * D + r]);
-  red[tid] = mloc;
-  __syncthreads();
-  for (int h = CG * D / 2; h > 0; h >>= 1) {
-    if (tid < h) red[tid] = fmaxf(red[tid], red[tid + h]);
-    __syncthreads();
+  const int tid = threadIdx.x, c = tid % TPR, g = tid / TPR;
+  int ns = p.uni_splits, slot = pair * ns;
+  if (!ns) {
+    const int2 h = *(const int2*)(p.hdr + 2 * pair);
+    slot = h.x;
+    ns = h.y;
   }
-  const float M = red[0];
-  float num = 0.f, den = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll 4
-    for (int s = g; s < p.n_split; s += CG) {
-      const float* w = base + (size_t)s * STRIDE;
-      const float ms = w[32 * D + r];
-      const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-      num += f * w[r * D + d];
-      den += f * w[32 * D + 32 + r];
+  if (ns < 2 || slot + ns > p.max_slots) return;
+  const float* base = p.ws + (size_t)slot * STRIDE;
+  float M = -INFINITY, den = 0.f;
+  float4 num = {0.f, 0.f, 0.f, 0.f};
+  // four of the thread's splits per round, all loads issued before any use
+  constexpr int U = 4;
+  for (int s0 = g; s0 < ns; s0 += U * CG) {
+    float ms[U], ls[U];
+    float4 os[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sp = s0 + u * CG;
+      ms[u] = -INFINITY;
+      ls[u] = 0.f;
+      os[u] = float4{0.f, 0.f, 0.f, 0.f};
+      if (sp < ns) {
+        const float* w = base + (size_t)sp * STRIDE;
+        ms[u] = w[32 * D + r];
+        ls[u] = w[32 * D + 32 + r];
+        os[u] = *(const float4*)(w + r * D + 4 * c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ms[u] == -INFINITY) continue;  // the split saw no position of the row
+      if (ms[u] > M) {
+        const float f = __builtin_amdgcn_exp2f(M - ms[u]);  // 0 while M is -inf
+        den *= f;
+        num.x *= f;
+        num.y *= f;
+        num.z *= f;
+        num.w *= f;
+        M = ms[u];
+      }
+      const float f = __builtin_amdgcn_exp2f(ms[u] - M);
+      den += f * ls[u];
+      num.x += f * os[u].x;
+      num.y += f * os[u].y;
+      num.z += f * os[u].z;
+      num.w += f * os[u].w;
     }
   }
-  part[0][g][d] = num;
-  part[1][g][d] = den;
+  pnum[g][c] = num;
+  if (c == 0) pmd[g] = float2{M, den};
   __syncthreads();
   if (g != 0) return;
+  float Mt = -INFINITY;
 #pragma unroll
-  for (int k = 1; k < CG; ++k) {
-    num += part[0][k][d];
-    den += part[1][k][d];
+  for (int k = 0; k < CG; ++k) Mt = fmaxf(Mt, pmd[k].x);
+  float4 o = {0.f, 0.f, 0.f, 0.f};
+  if (Mt != -INFINITY) {
+    float dt = 0.f;
+    float4 nt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < CG; ++k) {
+      const float2 md = pmd[k];
+      if (md.x == -INFINITY) continue;
+      const float f = __builtin_amdgcn_exp2f(md.x - Mt);
+      const float4 x = pnum[k][c];
+      dt += f * md.y;
+      nt.x += f * x.x;
+      nt.y += f * x.y;
+      nt.z += f * x.z;
+      nt.w += f * x.w;
+    }
+    if (dt > 0.f) {
+      const float inv = 1.f / dt;
+      o = float4{nt.x * inv, nt.y * inv, nt.z * inv, nt.w * inv};
+    }
   }
-  const float out = den > 0.f ? num / den : 0.f;
   const int a = kvh * p.G + r / p.Sq, qi = r % p.Sq;
-  ((__bf16*)p.o)[(((size_t)b * p.Hq + a) * p.Sq + qi) * D + d] = (__bf16)out;
+  bf16x4 w4;
+  w4[0] = (__bf16)o.x;
+  w4[1] = (__bf16)o.y;
+  w4[2] = (__bf16)o.z;
+  w4[3] = (__bf16)o.w;
+  *(bf16x4*)((__bf16*)p.o + (((size_t)b * p.Hq + a) * p.Sq + qi) * D + 4 * c) = w4;
 }
 
 template <int D>
-hipError_t launch_decode_d(const DParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((long long)p.B * p.Hkv * p.n_split));
-  hipLaunchKernelGGL(attn_decode_bf16<D>, grid, dim3(DWAVES * 64), 0, stream, p);
+hipError_t launch_decode_d(const DParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(attn_decode_bf16<D>, dim3((unsigned)grid), dim3(DWAVES * 64), 0, stream, p);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || p.n_split == 1) return err;
+  if (err != hipSuccess || !p.ws) return err;
   const long long rows = (long long)p.B * p.Hkv * p.G * p.Sq;
-  hipLaunchKernelGGL(attn_decode_combine<D>, dim3((unsigned)rows), dim3(CG * D), 0, stream, p);
+  hipLaunchKernelGGL(attn_decode_combine<D>, dim3((unsigned)rows), dim3(kCombThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DParams& p, int D, hipStream_t stream) {
-  return D == 64 ? launch_decode_d<64>(p, stream) : launch_decode_d<128>(p, stream);
+hipError_t launch_decode(const DParams& p, int D, int grid, hipStream_t stream) {
+  return D == 64 ? launch_decode_d<64>(p, grid, stream) : launch_decode_d<128>(p, grid, stream);
 }
 
 }  // namespace attn

@@ -129,10 +129,11 @@ class DecodeWorkload:
     Sq: int
     Smax: int
     D: int
-    mask: str      # "causal" or "full"
+    mask: str      # "causal", "full" or "causal_window"
     lengths: str   # "full": every cache holds Smax positions; "ragged": seeded in [Smax/4, Smax]
     seed: int = 0
     dtype: str = "bf16"
+    window: int = 0  # the w of "causal_window"
 
     @property
     def scale(self) -> float:
@@ -159,6 +160,10 @@ DECODE_WORKLOADS = {
                        "ragged", seed=7),
         DecodeWorkload("decode_mqa_bf16_b4_l65536", 4, 32, 1, 1, 65536, 128, MASK_CAUSAL, "full",
                        seed=8),
+        # a 4096-position sliding window (Mistral's, "Transformer 演进与变体", section
+        # 稀疏注意力) over caches of 8192 to 32768 positions
+        DecodeWorkload("decode_window_gqa_bf16_b16_w4096_l32768", 16, 32, 8, 1, 32768, 128,
+                       MASK_CAUSAL_WINDOW, "ragged", seed=9, window=4096),
     )
 }
 DECODE_HEADLINE = "decode_gqa_bf16_b16_l8192"
