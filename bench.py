@@ -57,12 +57,17 @@ PEAK_FP32_TFLOPS = 157.3   # vector fp32
 PEAK_FP8_TFLOPS = 5033.2   # 256 CU x 2.4 GHz x 8192 dense FP8 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 KERNEL_SOURCES = ("kernel_bf16.hip", "gfx950_ops.h", "attn_kernels.h", "attn_sched.h")
+DECODE_SOURCES = ("kernel_decode.hip", "gfx950_ops.h", "attn_decode.h", "attn_sched.h")
 # committed HBM-traffic summaries per workload, with the sources their kernel is built from
 TRAFFIC_SUMMARIES = {
     "causal_gqa_bf16_s8192": ("attn_fwd_bf16_causal_gqa_s8192_hbm_traffic.md", KERNEL_SOURCES),
     "local_global_bf16_s8192": ("attn_fwd_bf16_local_global_s8192.md", KERNEL_SOURCES),
     "causal_gqa_fp8_s8192": ("attn_fwd_fp8_causal_gqa_s8192.md",
                              ("kernel_fp8.hip", "gfx950_ops.h", "attn_kernels.h", "attn_sched.h")),
+    "decode_gqa_bf16_b16_l8192": ("attn_decode_bf16_gqa_b16_l8192.md", DECODE_SOURCES),
+    "decode_gqa_bf16_b8_sq4_l16384": ("attn_decode_bf16_ragged_b8_sq4_l16384.md", DECODE_SOURCES),
+    "decode_window_gqa_bf16_b16_w4096_l32768": ("attn_decode_bf16_window_b16_w4096_l32768.md",
+                                                DECODE_SOURCES),
 }
 
 
@@ -519,7 +524,7 @@ def bench_decode(args, name):
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": committed_traffic(name),
         },
         "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
         "prewarm_steps": prewarm_steps,

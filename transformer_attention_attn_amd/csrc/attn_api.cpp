@@ -10,6 +10,7 @@
 #include <mutex>
 
 #include "../../include/attn.h"
+#include "attn_decode.h"
 #include "attn_kernels.h"
 
 namespace {

@@ -43,7 +43,7 @@
 //   * A plain streaming read of 1 GiB reaches about 6.0-6.3 TB/s on MI355X
 //     (LDS-direct or vector loads); that, not the 8 TB/s peak, is the
 //     practical ceiling of this kernel.
-#include "attn_kernels.h"
+#include "attn_decode.h"
 #include "gfx950_ops.h"
 
 namespace attn {
