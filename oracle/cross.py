@@ -21,6 +21,13 @@ at key position p_i = i + Skv - Sq.  Visibility:
     full           every key j < Skv
     causal         j <= p_i
     causal_window  p_i - w < j <= p_i
+    local_global   |p_i - j| <= w, or p_i is a global position, or j is one
+                   ("Transformer 演进与变体", section 稀疏注意力, the Longformer
+                   paragraph: a sliding window plus global tokens that see
+                   and are seen by every position).  Reading: the global
+                   indices are key positions (sequence positions), the same
+                   for every sequence of the batch; a sequence holding fewer
+                   keys has no global token at or past its end.
 
 A query that sees no key (p_i < 0, which needs Skv < Sq) has output zero.
 With Sq == Skv this is the square attention of reference.py.
@@ -57,7 +64,8 @@ import numpy as np
 FULL = "full"
 CAUSAL = "causal"
 CAUSAL_WINDOW = "causal_window"
-CROSS_MASK_KINDS = (FULL, CAUSAL, CAUSAL_WINDOW)
+LOCAL_GLOBAL = "local_global"
+CROSS_MASK_KINDS = (FULL, CAUSAL, CAUSAL_WINDOW, LOCAL_GLOBAL)
 
 
 def cross_visible_range(Sq, Skv, i, kind, window=0):
@@ -72,6 +80,21 @@ def cross_visible_range(Sq, Skv, i, kind, window=0):
             raise ValueError("causal_window needs window >= 1")
         return max(0, p - window + 1), max(0, min(Skv, p + 1))
     raise ValueError(f"unknown mask kind {kind!r}")
+
+
+def cross_visible_keys(Sq, Skv, i, kind, window=0, global_idx=()):
+    """Visible key positions of query i, ascending (an int64 array)."""
+    if kind != LOCAL_GLOBAL:
+        lo, hi = cross_visible_range(Sq, Skv, i, kind, window)
+        return np.arange(lo, max(lo, hi), dtype=np.int64)
+    if window < 0:
+        raise ValueError("local_global needs window >= 0")
+    p = i + Skv - Sq
+    g = sorted({int(x) for x in global_idx if 0 <= int(x) < Skv})
+    if p in g:
+        return np.arange(Skv, dtype=np.int64)
+    band = set(range(max(0, p - window), min(Skv, p + window + 1)))
+    return np.array(sorted(band | set(g)), dtype=np.int64)
 
 
 def alibi_penalty(slope, p, j):
@@ -95,11 +118,12 @@ def sequence_lengths(Sq, Skv, q_len, kv_len, b):
 
 
 def cross_attention(q, k, v, kind, window=0, scale=None, rows=None, alibi_slopes=None,
-                    q_len=None, kv_len=None):
+                    q_len=None, kv_len=None, global_idx=()):
     """Attention output, float64, shape [B, Hq, Sq, D]; with `rows` (query row
     indices) only those rows, shape [B, Hq, len(rows), D].  `alibi_slopes`: Hq
     slopes (None: no bias); `q_len`, `kv_len`: B valid lengths each (None: all
-    Sq / Skv rows valid)."""
+    Sq / Skv rows valid); `global_idx`: the global key positions of
+    "local_global"."""
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
@@ -124,24 +148,22 @@ def cross_attention(q, k, v, kind, window=0, scale=None, rows=None, alibi_slopes
             for r, i in enumerate(rows):
                 if i >= sq_b:
                     continue  # padded query row
-                lo, hi = cross_visible_range(sq_b, skv_b, i, kind, window)
-                if hi <= lo:
+                js = cross_visible_keys(sq_b, skv_b, i, kind, window, global_idx)
+                if js.size == 0:
                     continue
-                kk = k[b, h, lo:hi].astype(np.float64)
-                vv = v[b, h, lo:hi].astype(np.float64)
+                kk = k[b, h, js].astype(np.float64)
+                vv = v[b, h, js].astype(np.float64)
                 s = float(scale) * (kk @ q[b, a, i].astype(np.float64))
                 if slopes is not None:
-                    s = s - alibi_penalty(head_slope(slopes, a, G), i + skv_b - sq_b,
-                                          np.arange(lo, hi))
+                    s = s - alibi_penalty(head_slope(slopes, a, G), i + skv_b - sq_b, js)
                 e = np.exp(s - s.max())
                 out[b, a, r] = (e / e.sum()) @ vv
     return out
 
 
-def cross_visible_pairs(Sq, Skv, kind, window=0):
+def cross_visible_pairs(Sq, Skv, kind, window=0, global_idx=()):
     """Visible (query, key) pairs of one head."""
     tot = 0
     for i in range(Sq):
-        lo, hi = cross_visible_range(Sq, Skv, i, kind, window)
-        tot += max(0, hi - lo)
+        tot += cross_visible_keys(Sq, Skv, i, kind, window, global_idx).size
     return tot

@@ -238,10 +238,79 @@ def pin_pair_counts():
     assert cr.cross_visible_pairs(6, 3, "causal") == 1 + 2 + 3
 
 
+def pin_local_global_square_and_chunk():
+    """local_global: Sq == Skv is the square oracle's local+global mask, and a
+    chunk of the last Sq queries gives the square oracle's last Sq rows of the
+    whole sequence (a global position inside the chunk and one before it)."""
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, S, D = 1, 4, 2, 40, 8
+    q, k, v = randn(rng, B, Hq, S, D), randn(rng, B, Hkv, S, D), randn(rng, B, Hkv, S, D)
+    for w, g in ((3, (0, 17, 33)), (0, (5,)), (6, ())):
+        got = cr.cross_attention(q, k, v, "local_global", w, global_idx=g)
+        ref = oracle.attention(q, k, v, "local_global", w, g)
+        assert np.max(np.abs(got - ref)) < 1e-12, (w, g)
+        Sq = 11
+        got = cr.cross_attention(q[:, :, S - Sq:], k, v, "local_global", w, global_idx=g)
+        ref = oracle.attention(q, k, v, "local_global", w, g, rows=list(range(S - Sq, S)))
+        assert np.max(np.abs(got - ref)) < 1e-12, (w, g, Sq)
+
+
+def pin_local_global_ragged():
+    """local_global on a padded batch: each sequence is the square oracle on
+    its own positions with the global positions it holds; padded rows are
+    zero and padded content (NaN) never leaks, also where a global position
+    lies past a sequence's end."""
+    rng = np.random.default_rng(23)
+    B, Hq, Hkv, Sq, Skv, D, w = 3, 2, 1, 9, 30, 8, 2
+    g = (1, 12, 25)
+    q = randn(rng, B, Hq, Sq, D)
+    k, v = randn(rng, B, Hkv, Skv, D), randn(rng, B, Hkv, Skv, D)
+    q_len, kv_len = [9, 4, 6], [30, 14, 6]
+    for b in range(B):
+        q[b, :, q_len[b]:] = np.nan
+        k[b, :, kv_len[b]:] = np.nan
+        v[b, :, kv_len[b]:] = np.nan
+    got = cr.cross_attention(q, k, v, "local_global", w, q_len=q_len, kv_len=kv_len,
+                             global_idx=g)
+    assert np.all(np.isfinite(got))
+    for b in range(B):
+        nq, nk = q_len[b], kv_len[b]
+        assert np.all(got[b, :, nq:] == 0.0)
+        gb = [x for x in g if x < nk]
+        qf = np.concatenate([randn(rng, 1, Hq, nk - nq, D), q[b:b + 1, :, :nq]], axis=2)
+        ref = oracle.attention(qf, k[b:b + 1, :, :nk], v[b:b + 1, :, :nk], "local_global", w, gb,
+                               rows=list(range(nk - nq, nk)))
+        assert np.max(np.abs(got[b:b + 1, :, :nq] - ref)) < 1e-12, b
+
+
+def pin_local_global_brute_force():
+    """Pure-Python loops with the visibility rule written out: |p - j| <= w, or
+    p global, or j global."""
+    rng = np.random.default_rng(24)
+    Hq, Sq, Skv, D, w, scale = 1, 5, 12, 3, 1, 0.9
+    g = {2, 7}
+    q, k, v = randn(rng, 1, Hq, Sq, D), randn(rng, 1, 1, Skv, D), randn(rng, 1, 1, Skv, D)
+    got = cr.cross_attention(q, k, v, "local_global", w, scale=scale, global_idx=sorted(g))
+    for i in range(Sq):
+        p = i + Skv - Sq
+        js = [j for j in range(Skv) if abs(p - j) <= w or p in g or j in g]
+        sc = [scale * math.fsum(q[0, 0, i, d] * k[0, 0, j, d] for d in range(D)) for j in js]
+        m = max(sc)
+        e = [math.exp(x - m) for x in sc]
+        for d in range(D):
+            want = math.fsum(e[t] * v[0, 0, j, d] for t, j in enumerate(js)) / math.fsum(e)
+            assert abs(got[0, 0, i, d] - want) < 1e-13
+    assert cr.cross_visible_pairs(Sq, Skv, "local_global", w, sorted(g)) == sum(
+        len([j for j in range(Skv) if abs(i + Skv - Sq - j) <= w or i + Skv - Sq in g or j in g])
+        for i in range(Sq))
+
+
 PINS = [pin_square_case, pin_chunk_is_last_rows, pin_matches_decode_oracle,
         pin_fewer_keys_than_queries, pin_brute_force_loop, pin_row_selection,
         pin_alibi_closed_form, pin_alibi_as_extra_dimension, pin_ragged_matches_decode_oracle,
-        pin_ragged_queries_are_last_rows, pin_alibi_ragged_brute_force, pin_pair_counts]
+        pin_ragged_queries_are_last_rows, pin_alibi_ragged_brute_force, pin_pair_counts,
+        pin_local_global_square_and_chunk, pin_local_global_ragged,
+        pin_local_global_brute_force]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -267,6 +336,21 @@ def _mut_full_is_causal(Sq, Skv, i, kind, window=0):
 
 
 _ORIG_PEN, _ORIG_SLOPE, _ORIG_LENS = cr.alibi_penalty, cr.head_slope, cr.sequence_lengths
+_ORIG_KEYS = cr.cross_visible_keys
+
+
+def _lg_variant(global_query_by_index=False, global_keys=True, one_sided=False, keep_past_end=False):
+    """cross_visible_keys with one step of the local_global rule changed."""
+    def f(Sq, Skv, i, kind, window=0, global_idx=()):
+        if kind != "local_global":
+            return _ORIG_KEYS(Sq, Skv, i, kind, window, global_idx)
+        p = i + Skv - Sq
+        g = sorted({int(x) for x in global_idx if keep_past_end or int(x) < Skv})
+        if (i if global_query_by_index else p) in g:
+            return np.arange(Skv, dtype=np.int64)
+        band = set(range(max(0, p - window), min(Skv, p + (0 if one_sided else window) + 1)))
+        return np.array(sorted(band | (set(g) if global_keys else set())), dtype=np.int64)
+    return f
 
 MUTATIONS = {
     "top_left_alignment": ("cross_visible_range", _mut_top_left),
@@ -283,6 +367,10 @@ MUTATIONS = {
     "alibi_slope_by_kv_head": ("head_slope", lambda sl, a, G: sl[(a // G) * G]),
     # padding ignored: every key and query row valid
     "padding_ignored": ("sequence_lengths", lambda Sq, Skv, ql, kl, b: (Sq, Skv)),
+    "lg_global_query_by_row_index": ("cross_visible_keys", _lg_variant(global_query_by_index=True)),
+    "lg_global_keys_ignored": ("cross_visible_keys", _lg_variant(global_keys=False)),
+    "lg_band_one_sided": ("cross_visible_keys", _lg_variant(one_sided=True)),
+    "lg_globals_past_end_kept": ("cross_visible_keys", _lg_variant(keep_past_end=True)),
     # valid query rows counted, but aligned as if all Sq rows were valid
     "ragged_queries_misaligned": ("sequence_lengths",
                                   lambda Sq, Skv, ql, kl, b: (
