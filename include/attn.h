@@ -189,14 +189,19 @@ typedef struct {
   long long k_stride[3];
   long long v_stride[3];
   long long o_stride[3];
-  int mask_kind;          /* ATTN_MASK_FULL, _CAUSAL or _CAUSAL_WINDOW     */
-  int window;             /* CAUSAL_WINDOW: >= 1                          */
+  int mask_kind;          /* ATTN_MASK_FULL, _CAUSAL, _CAUSAL_WINDOW or
+                             _LOCAL_GLOBAL (not with ALiBi or a layout)    */
+  int window;             /* CAUSAL_WINDOW: >= 1; LOCAL_GLOBAL: >= 0       */
   float scale;
   int dtype;              /* ATTN_DTYPE_BF16                              */
   const float* alibi_slopes;  /* device [Hq] fp32, or NULL                */
   const int* q_len;           /* device [B] int32, or NULL (all Sq valid)  */
   const int* kv_len;          /* device [B] int32, or NULL (all Skv valid) */
   const uint32_t* block_layout; /* device block-sparse layout, or NULL       */
+  const int* global_idx;  /* LOCAL_GLOBAL: host array of n_global global key
+                             positions in [0, Skv) (duplicates allowed), or
+                             NULL when n_global is 0                        */
+  int n_global;           /* 0..ATTN_MAX_GLOBAL                            */
 } attn_fwd_args;
 
 /* Enqueue attn_fwd_ex on `stream`; same return and error conventions as

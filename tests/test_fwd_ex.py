@@ -1,5 +1,5 @@
-"""attn_fwd_ex (Sq != Skv, strided layouts, ALiBi, padded batches) against
-the fp64 oracle.
+"""attn_fwd_ex (Sq != Skv, strided layouts, ALiBi, padded batches, local +
+global tokens) against the fp64 oracle.
 
 GPU cases compare every output element with oracle.cross_attention (queries
 aligned to the end of the keys) at the bf16 tolerance, over head-major,
@@ -8,6 +8,8 @@ without ALiBi slopes and per-sequence lengths (NaN in every padded position);
 with Sq == Skv and dense layouts the result must equal attn_fwd's bit for
 bit.  Host-only cases check the validation.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -46,14 +48,14 @@ def empty_out(B, H, S, D, layout, device):
 
 
 def run_ex(device, B, Hq, Hkv, Sq, Skv, D, mask, window=0, layout="bhsd", out_layout="bhsd",
-           seed=0, scale=None, slopes=None, q_len=None, kv_len=None):
+           seed=0, scale=None, slopes=None, q_len=None, kv_len=None, global_idx=()):
     """Max abs error of attn_fwd_ex against the oracle.  With lengths, the
     padded query rows, keys and values hold NaN (bf16 0x7FC0)."""
     import torch
 
     print(f"fwd_ex case B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} {mask} w={window} "
           f"{layout}->{out_layout} seed={seed} scale={scale} alibi={slopes is not None} "
-          f"q_len={q_len} kv_len={kv_len}", flush=True)
+          f"q_len={q_len} kv_len={kv_len} globals={list(global_idx)}", flush=True)
     rng = np.random.default_rng(seed)
     bits = {}
     vals = {}
@@ -71,11 +73,12 @@ def run_ex(device, B, Hq, Hkv, Sq, Skv, D, mask, window=0, layout="bhsd", out_la
     dev_arr = lambda x, dt: None if x is None else torch.tensor(list(x), dtype=dt, device=device)  # noqa: E731
     attn.fwd_ex(q, k, v, mask=mask, window=window, scale=scale, out=o,
                 alibi_slopes=dev_arr(slopes, torch.float32), q_len=dev_arr(q_len, torch.int32),
-                kv_len=dev_arr(kv_len, torch.int32))
+                kv_len=dev_arr(kv_len, torch.int32), global_idx=list(global_idx) or None)
     torch.cuda.synchronize()
     got = o.float().cpu().numpy()
     ref = oracle.cross_attention(vals["q"], vals["k"], vals["v"], mask, window, scale=scale,
-                                 alibi_slopes=slopes, q_len=q_len, kv_len=kv_len)
+                                 alibi_slopes=slopes, q_len=q_len, kv_len=kv_len,
+                                 global_idx=global_idx)
     assert np.all(np.isfinite(got))
     return float(np.max(np.abs(got.astype(np.float64) - ref)))
 
@@ -197,6 +200,56 @@ def test_fwd_ex_full_lengths_equal_no_lengths(device):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), mask
 
 
+LG_SWEEP = []
+_rng = np.random.default_rng(93)
+for D in (64, 128):
+    for (Sq, Skv) in ((257, 257), (100, 300), (300, 100), (1, 500), (64, 1000), (513, 2049)):
+        for window in (0, 3, 200):
+            g = sorted({int(x) for x in _rng.integers(0, Skv, size=int(_rng.integers(0, 5)))}
+                       | ({Skv - 1} if _rng.integers(2) else set()))
+            Hq, Hkv = [(8, 2), (4, 4), (8, 1)][int(_rng.integers(3))]
+            layout = ["bhsd", "bshd", "padded"][int(_rng.integers(3))]
+            out_layout = ["bhsd", "bshd", "padded"][int(_rng.integers(3))]
+            LG_SWEEP.append((1 + int(_rng.integers(2)), Hq, Hkv, Sq, Skv, D, window, tuple(g),
+                             layout, out_layout))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", LG_SWEEP, ids=lambda c: f"D{c[5]}-Sq{c[3]}-Skv{c[4]}-w{c[6]}-"
+                                                         f"g{len(c[7])}-{c[8]}-{c[9]}")
+def test_fwd_ex_local_global_sweep(device, case):
+    """Local + global tokens with the queries at the end of the keys (global
+    indices are key positions), every layout, windows 0 to 200."""
+    B, Hq, Hkv, Sq, Skv, D, window, g, layout, out_layout = case
+    err = run_ex(device, B, Hq, Hkv, Sq, Skv, D, "local_global", window, layout, out_layout,
+                 seed=Sq + 7 * Skv + D + window, global_idx=g)
+    assert err <= TOL["bf16"], err
+
+
+LG_PADDED = [
+    # (B, Hq, Hkv, Sq, Skv, D, window, globals, q_len, kv_len)
+    (3, 8, 2, 600, 600, 64, 64, (0, 100, 450, 599), (600, 300, 0), (600, 300, 0)),
+    (3, 4, 4, 700, 700, 128, 32, (3, 650), (700, 500, 650), (700, 500, 651)),
+    (2, 8, 1, 256, 900, 128, 100, (0, 700, 899), (256, 100), (900, 750)),
+    (2, 12, 12, 1100, 1100, 64, 512, (0, 1000), (1100, 999), (1100, 999)),
+    # more queries than keys, a window wider than the keys, huge window
+    (2, 8, 2, 300, 100, 128, 200, (13, 99), (300, 120), (100, 40)),
+    (1, 4, 1, 400, 150, 64, 2 ** 31 - 1, (7,), (400,), (150,)),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", LG_PADDED, ids=lambda c: f"D{c[5]}-Sq{c[3]}-Skv{c[4]}-w{c[6]}")
+def test_fwd_ex_local_global_padded(device, case):
+    """Padded Longformer batches: per-sequence lengths with global positions
+    past a sequence's end, on a padded query row's position, and in empty
+    sequences; padded positions hold NaN and padded rows must come out zero."""
+    B, Hq, Hkv, Sq, Skv, D, window, g, q_len, kv_len = case
+    err = run_ex(device, B, Hq, Hkv, Sq, Skv, D, "local_global", window, "bshd", "bhsd",
+                 seed=Sq + D + window, q_len=q_len, kv_len=kv_len, global_idx=g)
+    assert err <= TOL["bf16"], err
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("D", [64, 128])
 def test_fwd_ex_square_dense_equals_fwd(device, D):
@@ -205,9 +258,10 @@ def test_fwd_ex_square_dense_equals_fwd(device, D):
 
     inp = workloads.make_inputs(2, 8, 2, 700, D, "bf16", seed=21)
     q, k, v = workloads.to_torch(inp, "bf16", device)
-    for mask, w in (("causal", 0), ("causal_window", 100), ("full", 0)):
-        a = attn.fwd(q, k, v, mask=mask, window=w)
-        b = attn.fwd_ex(q, k, v, mask=mask, window=w)
+    for mask, w, g in (("causal", 0, None), ("causal_window", 100, None), ("full", 0, None),
+                       ("local_global", 64, [0, 333, 699])):
+        a = attn.fwd(q, k, v, mask=mask, window=w, global_idx=g)
+        b = attn.fwd_ex(q, k, v, mask=mask, window=w, global_idx=g)
         torch.cuda.synchronize()
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), mask
 
@@ -271,7 +325,7 @@ def test_fwd_ex_workload_full_size(device, name):
 
 def ex_status(**kw):
     a = attn.FwdArgs()
-    a.alibi_slopes, a.q_len, a.kv_len = None, None, None
+    a.alibi_slopes, a.q_len, a.kv_len, a.global_idx, a.n_global = None, None, None, None, 0
     base = 0x1000000
     a.q, a.k, a.v, a.o = base, base * 3, base * 5, base * 7
     a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = 1, 8, 2, 100, 300, 128
@@ -296,7 +350,20 @@ def test_fwd_ex_rejects_bad_arguments():
     assert ex_status(Hq=6, Hkv=4) == "ATTN_ERR_HEADS"
     assert ex_status(D=96) == "ATTN_ERR_UNSUPPORTED"
     assert ex_status(dtype=attn.DTYPE_FP32) == "ATTN_ERR_UNSUPPORTED"
-    assert ex_status(mask_kind=3) == "ATTN_ERR_UNSUPPORTED"
+    assert ex_status(mask_kind=4) == "ATTN_ERR_UNSUPPORTED"
+    assert ex_status(mask_kind=3, alibi_slopes=0x2000000) == "ATTN_ERR_UNSUPPORTED"
+    assert ex_status(mask_kind=3, block_layout=0x2000000) == "ATTN_ERR_UNSUPPORTED"
+    assert ex_status(mask_kind=3, window=-1) == "ATTN_ERR_WINDOW"
+    assert ex_status(mask_kind=3, Sq=1 << 29, Skv=1 << 29) == "ATTN_ERR_SHAPE"
+    g = (ctypes.c_int * 65)(*range(65))
+    gp = ctypes.cast(g, ctypes.c_void_p).value
+    assert ex_status(mask_kind=1, global_idx=gp, n_global=1) == "ATTN_ERR_GLOBAL"
+    assert ex_status(mask_kind=3, global_idx=None, n_global=1) == "ATTN_ERR_GLOBAL"
+    assert ex_status(mask_kind=3, global_idx=gp, n_global=65) == "ATTN_ERR_GLOBAL"
+    assert ex_status(mask_kind=3, global_idx=gp, n_global=-1) == "ATTN_ERR_GLOBAL"
+    big = (ctypes.c_int * 2)(5, 300)  # 300 is not a key position when Skv = 300
+    assert ex_status(mask_kind=3, global_idx=ctypes.cast(big, ctypes.c_void_p).value,
+                     n_global=2) == "ATTN_ERR_GLOBAL"
     assert ex_status(mask_kind=2, window=0) == "ATTN_ERR_WINDOW"
     assert ex_status(scale=float("inf")) == "ATTN_ERR_SCALE"
     assert ex_status(q=0x1000008) == "ATTN_ERR_ALIGN"

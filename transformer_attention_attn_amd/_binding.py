@@ -60,6 +60,7 @@ class FwdArgs(ctypes.Structure):
         ("scale", ctypes.c_float), ("dtype", ctypes.c_int),
         ("alibi_slopes", ctypes.c_void_p), ("q_len", ctypes.c_void_p),
         ("kv_len", ctypes.c_void_p), ("block_layout", ctypes.c_void_p),
+        ("global_idx", ctypes.c_void_p), ("n_global", ctypes.c_int),
     ]
 
 
@@ -241,7 +242,8 @@ def layout_bigbird(nb: int, radius_blocks: int, n_global_blocks: int, rand_block
 
 
 def fwd_ex(q, k, v, mask="causal", window: int = 0, scale: Optional[float] = None, out=None,
-           stream=None, alibi_slopes=None, q_len=None, kv_len=None, block_layout=None):
+           stream=None, alibi_slopes=None, q_len=None, kv_len=None, block_layout=None,
+           global_idx=None):
     """Forward pass with Sq != Skv and strided layouts (bf16).
 
     q: [B, Hq, Sq, D], k, v: [B, Hkv, Skv, D] as torch views of any strides
@@ -252,7 +254,8 @@ def fwd_ex(q, k, v, mask="causal", window: int = 0, scale: Optional[float] = Non
     alibi_slopes float32 [Hq] (ALiBi), q_len and kv_len int32 [B] (valid rows
     and keys per sequence of a right-padded batch; padded rows come out zero),
     block_layout int32 [nb, words] (a layout_* bitmask on the GPU: block-sparse
-    attention over blocks of 64 positions).
+    attention over blocks of 64 positions).  global_idx: host sequence of
+    global key positions for mask "local_global".
     """
     import torch
 
@@ -292,6 +295,8 @@ def fwd_ex(q, k, v, mask="causal", window: int = 0, scale: Optional[float] = Non
             raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {shape} on "
                              "q's device")
         setattr(a, name, t.data_ptr())
+    garr, a.n_global = _globals(global_idx)  # garr stays referenced until the call returns
+    a.global_idx = ctypes.cast(garr, ctypes.c_void_p) if garr is not None else None
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)

@@ -341,11 +341,28 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
     return ATTN_ERR_SHAPE;
   if (a->dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
   if (a->D != 64 && a->D != 128) return ATTN_ERR_UNSUPPORTED;
-  if (a->mask_kind != ATTN_MASK_FULL && a->mask_kind != ATTN_MASK_CAUSAL &&
-      a->mask_kind != ATTN_MASK_CAUSAL_WINDOW)
+  if (a->mask_kind < ATTN_MASK_FULL || a->mask_kind > ATTN_MASK_LOCAL_GLOBAL)
+    return ATTN_ERR_UNSUPPORTED;
+  // local+global: not with ALiBi or a block-sparse layout
+  if (a->mask_kind == ATTN_MASK_LOCAL_GLOBAL && (a->alibi_slopes || a->block_layout))
     return ATTN_ERR_UNSUPPORTED;
   if (a->Hq % a->Hkv != 0) return ATTN_ERR_HEADS;
   if (a->mask_kind == ATTN_MASK_CAUSAL_WINDOW && a->window < 1) return ATTN_ERR_WINDOW;
+  if (a->mask_kind == ATTN_MASK_LOCAL_GLOBAL && a->window < 0) return ATTN_ERR_WINDOW;
+  // local+global: positions -Sq .. Skv - 1 and windows up to Sq + Skv in 32 bits
+  if (a->mask_kind == ATTN_MASK_LOCAL_GLOBAL && (long long)a->Sq + a->Skv >= (1LL << 30))
+    return ATTN_ERR_SHAPE;
+  // global key positions: local+global only, in [0, Skv), sorted and made distinct
+  if (a->n_global < 0 || a->n_global > ATTN_MAX_GLOBAL) return ATTN_ERR_GLOBAL;
+  if (a->n_global > 0 && (a->mask_kind != ATTN_MASK_LOCAL_GLOBAL || a->global_idx == nullptr))
+    return ATTN_ERR_GLOBAL;
+  int gpos[ATTN_MAX_GLOBAL];
+  for (int i = 0; i < a->n_global; ++i) {
+    if (a->global_idx[i] < 0 || a->global_idx[i] >= a->Skv) return ATTN_ERR_GLOBAL;
+    gpos[i] = a->global_idx[i];
+  }
+  std::sort(gpos, gpos + a->n_global);
+  const int n_global = (int)(std::unique(gpos, gpos + a->n_global) - gpos);
   if (!std::isfinite(a->scale)) return ATTN_ERR_SCALE;
   for (const void* ptr : {a->q, a->k, a->v, (const void*)a->o})
     if ((uintptr_t)ptr % 16 != 0) return ATTN_ERR_ALIGN;
@@ -394,11 +411,15 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
     return ATTN_ERR_ALIAS;
 
   // A window of Skv keys or more admits every key at or before the query (a
-  // query's key position is at most Skv - 1), so larger windows are clamped to
-  // Skv: the kernels then form position - window (positions down to -Sq) in
-  // 32-bit arithmetic without overflow.
-  const int window = a->mask_kind == ATTN_MASK_CAUSAL_WINDOW ? std::min(a->window, a->Skv) : 0;
-  Sched s = attn::make_sched(a->B, a->Hq, a->Hkv, a->Sq, a->mask_kind, window, 0,
+  // query's key position is at most Skv - 1), so larger causal windows are
+  // clamped to Skv; a band of radius Sq + Skv holds every key of every query
+  // (positions run from -Sq to Skv - 1), so larger local+global windows are
+  // clamped to that (such calls have Sq + Skv below 2^30).  The kernels then
+  // form position +- window in 32-bit arithmetic without overflow.
+  const int window = a->mask_kind == ATTN_MASK_CAUSAL_WINDOW ? std::min(a->window, a->Skv)
+                     : a->mask_kind == ATTN_MASK_LOCAL_GLOBAL ? std::min(a->window, a->Sq + a->Skv)
+                                                              : 0;
+  Sched s = attn::make_sched(a->B, a->Hq, a->Hkv, a->Sq, a->mask_kind, window, n_global,
                              attn::kBf16Rows, attn::bf16_keys_per_tile(a->D), 1,
                              attn::kBf16GlobalRows);
   if (s.n_items > 0x7fffffffLL) return ATTN_ERR_SHAPE;
@@ -419,6 +440,7 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
   p.alibi_k = a->scale != 0.f ? 1.f / std::fabs(a->scale) : 1.4426950408889634f;
   p.layout = a->block_layout;
   p.lay_nw = lay_nw;
+  std::copy(gpos, gpos + n_global, p.gpos);
   for (int d = 0; d < 3; ++d) {
     p.qs[d] = a->q_stride[d];
     p.ks[d] = a->k_stride[d];

@@ -235,8 +235,9 @@ constexpr int kWavesPerEu = HD == 64 ? 4 : 2;
 // GEN = 0: attn_fwd's dense square layout.  GEN = 1: the general form behind
 // attn_fwd_ex -- Sq query rows (s.S) against Sk keys (s.Sk), query i at key
 // position i + s.off, element strides for the batch, head and row dimensions
-// of each tensor, optional per-sequence lengths (right padding); the
-// local+global mask is not offered there.  GEN = 2: GEN = 1 plus the ALiBi
+// of each tensor, optional per-sequence lengths (right padding); under the
+// local+global mask the global indices are key positions (a global query is
+// row gpos - off of its sequence).  GEN = 2: GEN = 1 plus the ALiBi
 // bias.  GEN = 3: GEN = 1 with a block-sparse layout (square, no lengths).
 // LDS for the global token positions, only in kernels of the local+global
 // mask (the persistent kernels use all 160 KB otherwise)
@@ -348,10 +349,13 @@ void attn_fwd_bf16(KParams p_arg) {
     wqb = imin(q0 + 31, SQ - 1);
   } else {
     // every wave of a head holds the head's (up to) 32 global rows; the waves
-    // split the keys instead (see the global-row path below)
+    // split the keys instead (see the global-row path below).  The global
+    // indices are key positions: query row gpos - OFF, present when that row
+    // and that key exist in this sequence.
     const int slot = it.blk * kBf16GlobalRows + l32;
-    row_valid = slot < s.n_global;
-    q_row = row_valid ? gpos_s[slot] : 0;
+    const int gp = slot < s.n_global ? gpos_s[slot] : -1;
+    row_valid = gp >= 0 && gp < SK && gp - OFF >= 0 && gp - OFF < SQ;
+    q_row = row_valid ? gp - OFF : 0;
   }
   const bool wave_active = wqa <= wqb;
   // key positions of the wave's first and last valid rows
@@ -452,9 +456,15 @@ void attn_fwd_bf16(KParams p_arg) {
   if constexpr (SPARSE) {
   } else if constexpr (GEN) {
     // keys seen by the valid rows r0..r1 at key positions r0 + OFF .. r1 + OFF
+    // (local+global: the band part; the global keys come in the strip tile)
     const int pa = r0 + OFF, pb = r1 + OFF;
-    klo = MASK == MASK_CAUSAL_WINDOW ? imax(0, pa - s.window + 1) : 0;
-    khi = MASK == MASK_FULL ? SK - 1 : imin(pb, SK - 1);
+    if (MASK == MASK_LOCAL_GLOBAL) {
+      klo = it.is_global ? 0 : imax(0, pa - s.window);
+      khi = it.is_global ? SK - 1 : (int)(pb + (long long)s.window < SK ? pb + s.window : SK - 1);
+    } else {
+      klo = MASK == MASK_CAUSAL_WINDOW ? imax(0, pa - s.window + 1) : 0;
+      khi = MASK == MASK_FULL ? SK - 1 : imin(pb, SK - 1);
+    }
   } else {
     key_range(s, it.is_global, r0, r1, &klo, &khi);
   }
@@ -481,8 +491,13 @@ void attn_fwd_bf16(KParams p_arg) {
     }
   }
   const int has_strip = (MASK == MASK_LOCAL_GLOBAL && !it.is_global && s.n_global > 0) ? 1 : 0;
+  // GEN: an item of padded rows, or of a sequence without keys, visits
+  // nothing; rows that see no band key (positions before the first key)
+  // still visit the strip of global keys
   const int n_it = SPARSE ? n_list
-                          : (GEN && (khi < klo || r1 < r0)) ? 0 : (kt_hi - kt_lo + 1) + has_strip;
+                   : !GEN ? (kt_hi - kt_lo + 1) + has_strip
+                   : (r1 < r0 || SK == 0) ? 0
+                   : (khi < klo ? 0 : kt_hi - kt_lo + 1) + has_strip;
   auto tile_kt = [&](int iter) -> int {
     if constexpr (SPARSE) return (int)(entry(iter) & 0xffffu);
     return kt_lo + iter - has_strip;
@@ -509,12 +524,14 @@ void attn_fwd_bf16(KParams p_arg) {
   const int k_col = (sphys ^ C::ksw(srow)) * 16;
   const int v_col = (sphys ^ ((srow & 3) << VSH)) * 16;
   // Load n of this wave for tile iter of K (isk) or V into stage st.  Rows past
-  // S (tail tile) or past n_global (strip) repeat a valid row: their scores are
-  // masked, so they carry zero weight.  Tiles past the end of the range load
-  // clamped rows into a stage that is not read again.
+  // the sequence's keys (tail tile; strip entries past n_global, or GEN: at a
+  // padded position) repeat a valid row: their scores are masked, so they
+  // carry zero weight, and what padding holds is never multiplied in.  Tiles
+  // past the end of the range load clamped rows into a stage that is not read
+  // again.
   auto dma = [&](bool isk, int iter, int st, int n) {
     int row;
-    if (is_strip(iter)) row = gpos_s[imin(srow + n * RSTEP, s.n_global - 1)];
+    if (is_strip(iter)) row = imin(gpos_s[imin(srow + n * RSTEP, s.n_global - 1)], SKA - 1);
     else row = imin(tile_kt(iter) * BN + srow + n * RSTEP, SKA - 1);
     const char* src = (const char*)(isk ? kp : vp) + (size_t)row * (isk ? KRB : VRB) + (isk ? k_col : v_col);
     dma16_global(src, smem + (isk ? 0 : NSTAGE * REG) + st * REG + (n * 4 + gw) * 1024);
@@ -597,7 +614,7 @@ void attn_fwd_bf16(KParams p_arg) {
     if (!wave_active || is_strip(iter) || wave_pad) return true;
     if (SPARSE && wave_code(iter) != 3u) return true;  // one 64-key half only
     const int kt = tile_kt(iter);
-    if (it.is_global) return kt * BN + BN > s.S;
+    if (it.is_global) return kt * BN + BN > SK;
     return classify_tile(MASK, s.window, SK, wpa, wpb, kt * BN, BN) != TILE_FULL;
   };
   auto tile_empty = [&](int j) -> bool {
@@ -662,8 +679,11 @@ void attn_fwd_bf16(KParams p_arg) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kbk * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const int dist = q_row - gpos_s[key < kMaxGlobal ? key : 0];
-          const bool vis = key < s.n_global && (dist > s.window || -dist > s.window);
+          const int gk = gpos_s[key < kMaxGlobal ? key : 0];
+          const int dist = q_pos - gk;
+          // (GEN: padded query rows see nothing, also here)
+          const bool vis = key < s.n_global && gk < SK && (dist > s.window || -dist > s.window) &&
+                           (!GEN || row_valid);
           sc[kbk][r] = vis ? sc[kbk][r] : -INFINITY;
         }
       return;
@@ -672,7 +692,7 @@ void attn_fwd_bf16(KParams p_arg) {
     // indices, shifted by the lane half so each test is against an immediate:
     // lo <= 32*kbk + 8*(r/4) + r%4 <= hi
     long long lo, hi;
-    if (it.is_global) { lo = 0; hi = (long long)s.S - 1; }
+    if (it.is_global) { lo = 0; hi = (long long)SK - 1; }
     else row_interval(MASK, s.window, SK, q_pos, &lo, &hi);
     if (!wave_active || (GEN && !row_valid)) hi = lo - 1;
     const long long base = (long long)tile_kt(iter) * BN + 4 * (PERS ? (int)(fresh_lane() >> 5) : hf);
@@ -718,7 +738,7 @@ void attn_fwd_bf16(KParams p_arg) {
     constexpr int RPI = 1024 / ROWB;    // tile rows per 1 KiB load
     unsigned char* kreg = smem + wave * 2 * GREG;
     unsigned char* vreg = kreg + GREG;
-    const int ntile = cdiv(s.S, GK);
+    const int ntile = cdiv(SK, GK);
     const int t_lo = (int)((long long)ntile * rpart / wph);
     const int t_hi = (int)((long long)ntile * (rpart + 1) / wph);
     const int lrow = lane * 16 / ROWB, lphys = (lane * 16 % ROWB) / 16;
@@ -726,9 +746,10 @@ void attn_fwd_bf16(KParams p_arg) {
 #pragma unroll
       for (int n = 0; n < NIG; ++n) {
         const int row = n * RPI + lrow;
-        const int key = imin(t * GK + row, s.S - 1);  // tail rows repeat a valid row (masked)
+        const int key = imin(t * GK + row, SKA - 1);  // tail rows repeat a valid row (masked)
         const int sw = is_v ? ((row & 3) << VSH) : C::ksw(row);
-        dma16_global((const char*)base + (size_t)key * ROWB + (lphys ^ sw) * 16, dst + n * 1024);
+        dma16_global((const char*)base + (size_t)key * (is_v ? VRB : KRB) + (lphys ^ sw) * 16,
+                     dst + n * 1024);
       }
     };
     if (t_lo < t_hi) {
@@ -745,9 +766,9 @@ void attn_fwd_bf16(KParams p_arg) {
       for (int dc = 0; dc < NDC; ++dc) sc = mfma32(k_frag(kreg, 0, dc), qf[dc], sc);
       __builtin_amdgcn_s_waitcnt(0xc07f);  // K operand reads done: the region may be refilled
       if (more) gload(kp, t + 1, kreg, false);
-      if ((t + 1) * GK > s.S) {
-        // tail tile: keys at or beyond S carry no weight
-        const int lim = s.S - t * GK - 4 * hf;
+      if ((t + 1) * GK > SK) {
+        // tail tile: keys at or beyond SK carry no weight
+        const int lim = SK - t * GK - 4 * hf;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[r] = (8 * (r >> 2) + (r & 3) < lim) ? sc[r] : -INFINITY;
       }
@@ -1290,9 +1311,12 @@ void attn_fwd_bf16(KParams p_arg) {
     const float l_tot = l_run + l_other;
     // global items: the first wave of each head holds the merged result
     // (GEN: padded query rows and rows that see no key are written as zero)
-    bool store = GEN ? q_row < s.S : row_valid && (it.is_global ? rpart == 0 : wave_active);
-    if (MASK == MASK_LOCAL_GLOBAL && !it.is_global && store) {
-      for (int g = 0; g < s.n_global; ++g) store = store && (gpos_s[g] != q_row);
+    bool store = it.is_global ? row_valid && rpart == 0
+                              : (GEN ? q_row < s.S : row_valid && wave_active);
+    // band items leave the rows of global queries to the global items (GEN:
+    // padded rows, which no global item owns, are still written as zero)
+    if (MASK == MASK_LOCAL_GLOBAL && !it.is_global && store && (!GEN || q_row < SQ)) {
+      for (int g = 0; g < s.n_global; ++g) store = store && (gpos_s[g] != q_pos);
     }
     if (store) {
       const float inv = GEN ? (l_tot > 0.f ? 1.f / l_tot : 0.f) : 1.f / l_tot;
@@ -1334,7 +1358,8 @@ hipError_t launch_d(const KParams& p, hipStream_t stream) {
     switch (p.s.mask) {
       case MASK_FULL: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_FULL, 1>), grid, block, 0, stream, p); break;
       case MASK_CAUSAL: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL, 1>), grid, block, 0, stream, p); break;
-      default: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL_WINDOW, 1>), grid, block, 0, stream, p); break;
+      case MASK_CAUSAL_WINDOW: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL_WINDOW, 1>), grid, block, 0, stream, p); break;
+      default: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_LOCAL_GLOBAL, 1>), grid, block, 0, stream, p); break;
     }
     return hipGetLastError();
   }
