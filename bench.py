@@ -288,7 +288,7 @@ def decode_counts(w, lens):
     return cache_bytes, 4 * w.D * pairs * w.Hq
 
 
-def ex_visible_pairs(Sq, Skv, mask, window=0) -> int:
+def ex_visible_pairs(Sq, Skv, mask, window=0, global_idx=()) -> int:
     """Visible (query, key) pairs of one query head of one sequence of an
     attn_fwd_ex call: query i sits at key position p = i + Skv - Sq."""
     import numpy as np
@@ -296,6 +296,16 @@ def ex_visible_pairs(Sq, Skv, mask, window=0) -> int:
     if mask == "full":
         return Sq * Skv
     p = np.arange(Sq, dtype=np.int64) + (Skv - Sq)
+    if mask == "local_global":
+        # the band |p - j| <= w, the global keys outside it, and every key for
+        # a global query
+        g = np.array(sorted({int(x) for x in global_idx if 0 <= int(x) < Skv}), dtype=np.int64)
+        band = np.maximum(np.minimum(p + window, Skv - 1) - np.maximum(p - window, 0) + 1, 0)
+        outside = (np.abs(p[:, None] - g[None, :]) > window).sum(axis=1) if g.size else 0
+        n = band + outside
+        if g.size:
+            n = np.where(np.isin(p, g), Skv, n)
+        return int(n.sum())
     hi = np.clip(p + 1, 0, Skv)
     lo = np.zeros_like(hi) if mask == "causal" else np.clip(p - window + 1, 0, Skv)
     return int(np.maximum(hi - lo, 0).sum())
@@ -348,7 +358,7 @@ def ex_effective_flops(w, batches=None) -> float:
     for b in (range(w.B) if batches is None else batches):
         sq = w.Sq if q_len is None else int(q_len[b])
         skv = w.Skv if kv_len is None else int(kv_len[b])
-        total += ex_visible_pairs(sq, skv, w.mask, w.window)
+        total += ex_visible_pairs(sq, skv, w.mask, w.window, w.global_idx)
     return 4.0 * w.D * total * w.Hq
 
 
@@ -384,7 +394,7 @@ def ex_cpu_baseline(w, inputs, seconds: float = 10.0):
             w.mask, w.window, scale=w.scale,
             alibi_slopes=None if slopes is None else slopes[a:a + 1].astype(np.float64),
             q_len=None if q_len is None else q_len[:1],
-            kv_len=None if kv_len is None else kv_len[:1]))
+            kv_len=None if kv_len is None else kv_len[:1], global_idx=w.global_idx))
     dt = time.perf_counter() - t0
     n = len(refs)
     flops = ex_effective_flops(w, batches=[0]) / w.Hq * n
@@ -578,7 +588,7 @@ def bench_ex(args, name):
     def step():
         attn.fwd_ex(q, k, v, mask=w.mask, window=w.window, scale=w.scale, out=out,
                     stream=stream, alibi_slopes=slopes_d, q_len=q_len_d, kv_len=kv_len_d,
-                    block_layout=layout_d)
+                    block_layout=layout_d, global_idx=list(w.global_idx) or None)
 
     ms, prewarm_steps, spread = time_steps(step, stream, args)
     tflops = flops / (ms * 1e-3) / 1e12

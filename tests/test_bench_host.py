@@ -43,6 +43,14 @@ def test_ex_pairs_match_oracle(Sq, Skv, mask, window):
         Sq, Skv, mask, window)
 
 
+@pytest.mark.parametrize("Sq,Skv", [(1, 1), (5, 3), (3, 5), (64, 1000), (300, 100), (700, 700)])
+@pytest.mark.parametrize("window,g", [(0, ()), (2, (0,)), (37, (1, 2, 60, 299, 699)),
+                                      (1000, (5,))])
+def test_ex_local_global_pairs_match_oracle(Sq, Skv, window, g):
+    assert bench.ex_visible_pairs(Sq, Skv, "local_global", window, g) == cr.cross_visible_pairs(
+        Sq, Skv, "local_global", window, g)
+
+
 @pytest.mark.parametrize("name", list(workloads.EX_WORKLOADS))
 def test_ex_workload_flops(name):
     w = workloads.EX_WORKLOADS[name]
@@ -61,7 +69,7 @@ def test_ex_workload_flops(name):
     for b in range(w.B):
         pairs += cr.cross_visible_pairs(w.Sq if q_len is None else int(q_len[b]),
                                         w.Skv if kv_len is None else int(kv_len[b]),
-                                        w.mask, w.window)
+                                        w.mask, w.window, w.global_idx)
     assert bench.ex_effective_flops(w) == 4.0 * w.D * pairs * w.Hq
 
 

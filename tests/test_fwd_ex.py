@@ -299,12 +299,14 @@ def test_fwd_ex_workload_full_size(device, name):
     q_len, kv_len = w.lengths_qkv()
     dev = lambda x: None if x is None else torch.from_numpy(x).to(device)  # noqa: E731
     attn.fwd_ex(q, k, v, mask=w.mask, window=w.window, scale=w.scale, out=o,
-                alibi_slopes=dev(slopes), q_len=dev(q_len), kv_len=dev(kv_len))
+                alibi_slopes=dev(slopes), q_len=dev(q_len), kv_len=dev(kv_len),
+                global_idx=list(w.global_idx) or None)
     torch.cuda.synchronize()
     got = o.float().cpu().numpy()
     rng = np.random.default_rng(w.seed + 5)
     rows = sorted({0, 1, 127, 128, w.Sq // 2, w.Sq - 1}
-                  | {int(x) for x in rng.integers(w.Sq, size=10)})
+                  | {int(x) for x in rng.integers(w.Sq, size=10)}
+                  | {int(g) for g in w.global_idx if g < w.Sq})
     G = w.Hq // w.Hkv
     for b, a in {(0, 0), (w.B - 1, w.Hq - 1), (int(rng.integers(w.B)), int(rng.integers(w.Hq)))}:
         h = a // G
@@ -313,7 +315,7 @@ def test_fwd_ex_workload_full_size(device, name):
             w.mask, w.window, scale=w.scale, rows=rows,
             alibi_slopes=None if slopes is None else slopes[a:a + 1].astype(np.float64),
             q_len=None if q_len is None else q_len[b:b + 1],
-            kv_len=None if kv_len is None else kv_len[b:b + 1])
+            kv_len=None if kv_len is None else kv_len[b:b + 1], global_idx=w.global_idx)
         err = float(np.max(np.abs(got[b, a, rows].astype(np.float64) - ref[0, 0])))
         print(f"{name} b={b} a={a}: max abs err {err:.3e}", flush=True)
         assert err <= TOL["bf16"], (b, a, err)

@@ -191,6 +191,7 @@ class ExWorkload:
     # local, stride), "fixed" (chunk) or "bigbird" (radius, n_global, n_random)
     pattern: str = ""
     pattern_args: Tuple[int, ...] = ()
+    global_idx: Tuple[int, ...] = ()  # local_global: global key positions
 
     @property
     def scale(self) -> float:
@@ -218,6 +219,7 @@ class ExWorkload:
     def describe(self) -> dict:
         d = dataclasses.asdict(self)
         d["pattern_args"] = list(self.pattern_args)
+        d["global_idx"] = list(self.global_idx)
         ql, kl = self.lengths_qkv()
         if ql is not None:
             d["q_len"], d["kv_len"] = [int(x) for x in ql], [int(x) for x in kl]
@@ -242,6 +244,12 @@ EX_WORKLOADS = {
         # Sparse Transformer strided pattern on the grouped-query head shapes
         ExWorkload("strided_causal_gqa_bf16_s8192", 1, 32, 8, 8192, 8192, 128, MASK_CAUSAL,
                    "bhsd", seed=13, pattern="strided", pattern_args=(7, 8)),
+        # Longformer ("Transformer 演进与变体", section 稀疏注意力: 8192 tokens, a
+        # 512-position window, globals at 0, 1000, 3000, 6000) over a right-padded
+        # batch of four sequences, sequence-major tensors
+        ExWorkload("longformer_padded_bf16_b4_s8192_bshd", 4, 12, 12, 8192, 8192, 64,
+                   MASK_LOCAL_GLOBAL, "bshd", window=512, seed=14, lengths="ragged",
+                   global_idx=(0, 1000, 3000, 6000)),
     )
 }
 
