@@ -36,9 +36,25 @@ unrounded weights, O - O_exact = sum_j (p~_j - p_j) v_j / L, hence
 
     |O - O_exact| <= b = sum_j e_j |v_j| / L.
 
-``fp8_error_bound`` returns b per output element.  ``fp8_tolerance`` adds the
-kernel's other roundings, each bounded from the arithmetic it does (first
-order in the fp32 unit u = 2^-24):
+``fp8_error_bound`` returns b per output element.
+
+With the denominator summed from the ROUNDED weights as well (both sums then
+run on the matrix cores: P~ times V and P~ times a column of ones), the output
+is the exact weighted mean under the rounded weights p~_j, and since
+sum_j p_j (v_j - O_exact) = 0,
+
+    O - O_exact = sum_j (p~_j - p_j) (v_j - O_exact) / sum_j p~_j,
+
+with sum_j p~_j >= L - sum_j e_j, hence
+
+    |O - O_exact| <= b' = sum_j e_j |v_j - O_exact| / (L - sum_j e_j)
+
+(no bound when sum_j e_j >= L).  In the normalised weights w_j = p_j / L of
+the oracle (w_max = 1 / L, as p_max = 1) e_j / L = u w_j + 2^-10 w_max.
+``fp8_error_bound(..., rounded_denominator=True)`` returns b'.
+
+``fp8_tolerance`` adds the kernel's other roundings, each bounded from the
+arithmetic it does (first order in the fp32 unit u = 2^-24):
 
 * fp32 scores and exponent.  A score is an fp32 sum of D exact E4M3 products
   (a product of two 4-bit significands fits fp32), error <= D u A_j with
@@ -53,7 +69,9 @@ order in the fp32 unit u = 2^-24):
   rescales and the final division), error <= (n_vis / 16 + 48) u
   sum_j p_j |v_j| / L; the denominator is a chain of at most n_vis fp32
   additions of positive weights, relative error <= (n_vis + 8) u, which moves
-  O by that fraction of |O|.
+  O by that fraction of |O|; a denominator summed on the matrix cores (the
+  rounded weights times ones) is a chain of the numerator's kind, relative
+  error <= (n_vis / 16 + 48) u.
 * bf16 output.  O is rounded once to bf16 (8-bit significand, nearest even):
   at most 2^-8 of the rounded value, i.e. 2^-8 (|O| + the bounds above).
 
@@ -93,9 +111,12 @@ def fp8_attention(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=No
                                kind, window, (), scale=scale, rows=rows)
 
 
-def fp8_error_bound(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=None):
-    """Per-element bound b (float64, shaped like the output) on the error the
-    E4M3 rounding of P can cause."""
+def fp8_error_bound(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=None,
+                    rounded_denominator=False):
+    """Per-element bound (float64, shaped like the output) on the error the
+    E4M3 rounding of P can cause: b with the denominator summed from the
+    unrounded weights, b' with the denominator summed from the rounded ones
+    (``rounded_denominator``; inf where sum_j e_j >= L)."""
     q = e4m3_decode(q_codes)
     k = e4m3_decode(k_codes)
     v = e4m3_decode(v_codes)
@@ -112,17 +133,24 @@ def fp8_error_bound(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=
             wmax = w.max(axis=1, keepdims=True)
             # w = p / L with p_max = 1, so p = w / wmax and 1 / L = wmax
             e = np.where(w > 0, U_E4M3 * w + ABS_E4M3 * wmax, 0.0)
-            out[b, a] = e @ np.abs(v[b, h])
+            if not rounded_denominator:
+                out[b, a] = e @ np.abs(v[b, h])
+                continue
+            o = w @ v[b, h]                                   # O_exact of these rows
+            num = np.einsum("rj,rjd->rd", e, np.abs(v[b, h][None, :, :] - o[:, None, :]))
+            den = 1.0 - e.sum(axis=1, keepdims=True)
+            out[b, a] = np.where(den > 0, num / np.where(den > 0, den, 1.0), np.inf)
     return out
 
 
 def fp8_tolerance(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=None,
-                  exact_weights=False, bf16_output=True):
+                  exact_weights=False, bf16_output=True, rounded_denominator=False):
     """Per-element bound (float64, shaped like the output) on |O_kernel -
     O_exact|: the E4M3 rounding of P (``fp8_error_bound``, left out when
     ``exact_weights``), the fp32 score, exponent and accumulation errors and,
     when ``bf16_output``, the bf16 rounding of the output (derivation in the
-    module docstring)."""
+    module docstring).  ``rounded_denominator``: the kernel sums the
+    denominator from the rounded weights on the matrix cores."""
     q = e4m3_decode(q_codes)
     k = e4m3_decode(k_codes)
     v = e4m3_decode(v_codes)
@@ -136,7 +164,8 @@ def fp8_tolerance(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=No
     n_vis = vis.sum(axis=1, keepdims=True).astype(np.float64)
     exact = reference.attention(q, k, v, kind, window, (), scale=scale, rows=rows)
     b = np.zeros_like(exact) if exact_weights else \
-        fp8_error_bound(q_codes, k_codes, v_codes, kind, window, scale, rows)
+        fp8_error_bound(q_codes, k_codes, v_codes, kind, window, scale, rows, rounded_denominator)
+    den_chain = (n_vis / 16 + 48) if rounded_denominator else (n_vis + 8)
     out = np.empty_like(exact)
     for bb in range(B):
         for a in range(Hq):
@@ -150,7 +179,7 @@ def fp8_tolerance(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=No
                 ew = np.log(2.0) * (D + 4) * U_F32 * c * amag.max(axis=1, keepdims=True) \
                     + 2 * U_F32
             f = (2 * ew * (1 + 2 * ew) + (n_vis / 16 + 48) * U_F32) * mean_abs \
-                + (n_vis + 8) * U_F32 * np.abs(exact[bb, a])
+                + den_chain * U_F32 * np.abs(exact[bb, a])
             out[bb, a] = b[bb, a] + f
     if bf16_output:
         out = out + U_BF16 * (np.abs(exact) + out)

@@ -4,15 +4,18 @@ e4m3_decode is checked against hand-decoded codes and against torch's own
 float8_e4m3fn type for all 256 codes.  fp8_error_bound is checked against a
 simulation of what it bounds: the weights of real rows rounded to E4M3 (by
 torch's conversion, round to nearest even) at several reference maxima below
-the true one, the output formed with the unrounded denominator; the bound
+the true one, the output formed with the unrounded denominator (bound b) and
+with the denominator summed from the rounded weights (bound b'); each bound
 must hold everywhere and must not be vacuous.  Planted mistakes in the bound
-(a smaller relative unit, no subnormal term) make the simulation exceed it.
+(a smaller relative unit, no subnormal term) make the simulation exceed it,
+in both forms.
 
 fp8_tolerance (the bound plus the kernel's fp32 and bf16 roundings) is checked
 against a simulation of the kernel's whole arithmetic: fp32 scores and
 exponentials, weights rounded to E4M3, fp32 accumulation in 16-key chunks and a
-sequential fp32 denominator, an fp32 division and a bf16 output (nearest
-even).  With all queries zero the weights are exact, so the fp32 and bf16
+sequential fp32 denominator (or, for the matrix-core denominator, the rounded
+weights summed in the numerator's 16-key chunks), an fp32 division and a bf16
+output (nearest even).  With all queries zero the weights are exact, so the fp32 and bf16
 terms alone must cover the simulated error; planting a zero bf16 or fp32 unit
 makes the simulation exceed the tolerance.
 """
@@ -57,9 +60,10 @@ def random_codes(rng, shape, spread=1.0):
     return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
-def simulate(q, k, v, kind, window, scale, shift):
+def simulate(q, k, v, kind, window, scale, shift, rounded_den=False):
     """Output of the FP8 method with P rounded to E4M3 while the reference
-    maximum sits `shift` (log2 units) below the row maximum."""
+    maximum sits `shift` (log2 units) below the row maximum; the denominator
+    from the unrounded weights, or from the rounded ones (`rounded_den`)."""
     qd, kd, vd = (f8.e4m3_decode(x) for x in (q, k, v))
     B, Hq, S, D = qd.shape
     Hkv = kd.shape[1]
@@ -71,11 +75,12 @@ def simulate(q, k, v, kind, window, scale, shift):
             w = ref.weights(qd[b, a], kd[b, h], rows, kind, window, (), scale)
             p = w / w.max(axis=1, keepdims=True)           # p_max = 1
             pk = e4m3_round(p * 2.0 ** shift) / 2.0 ** shift
-            out[b, a] = (pk @ vd[b, h]) / p.sum(axis=1, keepdims=True)
+            den = (pk if rounded_den else p).sum(axis=1, keepdims=True)
+            out[b, a] = (pk @ vd[b, h]) / den
     return out
 
 
-def check_bound_holds(spread):
+def check_bound_holds(spread, rounded_den=False):
     rng = np.random.default_rng(60)
     B, Hq, Hkv, S, D = 1, 4, 2, 96, 16
     q, k, v = (random_codes(rng, s, sp) for s, sp in (((B, Hq, S, D), spread),
@@ -84,19 +89,36 @@ def check_bound_holds(spread):
     worst = 0.0
     for kind, w in (("causal", 0), ("full", 0), ("causal_window", 9)):
         exact = f8.fp8_attention(q, k, v, kind, w, scale=0.5)
-        bound = f8.fp8_error_bound(q, k, v, kind, w, scale=0.5)
+        bound = f8.fp8_error_bound(q, k, v, kind, w, scale=0.5, rounded_denominator=rounded_den)
+        assert np.all(np.isfinite(bound))
         for shift in (0.0, 0.37, 3.0, 7.9):
-            err = np.abs(simulate(q, k, v, kind, w, 0.5, shift) - exact)
+            err = np.abs(simulate(q, k, v, kind, w, 0.5, shift, rounded_den) - exact)
             assert np.all(err <= bound * (1 + 1e-9) + 1e-12), (kind, shift, float((err - bound).max()))
             worst = max(worst, float((err / bound).max()))
     return worst
 
 
-def test_bound_holds_and_is_not_vacuous():
+@pytest.mark.parametrize("rounded_den", [False, True])
+def test_bound_holds_and_is_not_vacuous(rounded_den):
     pytest.importorskip("torch")
-    worst = check_bound_holds(1.0)
+    worst = check_bound_holds(1.0, rounded_den)
     assert worst > 0.05, worst          # the bound is within 20x of a real error
-    check_bound_holds(3.0)              # peaked rows: many weights in the subnormal range
+    check_bound_holds(3.0, rounded_den)  # peaked rows: many weights in the subnormal range
+
+
+def test_rounded_denominator_bound_vs_unrounded():
+    """b' uses |v_j - O| where b uses |v_j|: on values with a large common
+    offset b' is the smaller bound (the offset cancels in a weighted mean)."""
+    rng = np.random.default_rng(63)
+    q = random_codes(rng, (1, 1, 40, 16))
+    k = random_codes(rng, (1, 1, 40, 16))
+    v = (f8.e4m3_decode(random_codes(rng, (1, 1, 40, 16))) * 0.1 + 8.0).astype(np.float32)
+    import torch
+
+    v = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    b = f8.fp8_error_bound(q, k, v, "causal", scale=0.5)
+    b2 = f8.fp8_error_bound(q, k, v, "causal", scale=0.5, rounded_denominator=True)
+    assert np.all(b2 < b)
 
 
 def test_zero_queries_give_the_mean_of_visible_values():
@@ -112,8 +134,9 @@ def test_zero_queries_give_the_mean_of_visible_values():
         assert np.max(np.abs(got[0, :, i] - want)) < 1e-12
 
 
+@pytest.mark.parametrize("rounded_den", [False, True])
 @pytest.mark.parametrize("mutation", ["unit_halved", "no_subnormal_term"])
-def test_planted_bound_mistakes_are_caught(monkeypatch, mutation):
+def test_planted_bound_mistakes_are_caught(monkeypatch, mutation, rounded_den):
     pytest.importorskip("torch")
     if mutation == "unit_halved":
         monkeypatch.setattr(f8, "U_E4M3", 2.0 ** -5)
@@ -122,7 +145,7 @@ def test_planted_bound_mistakes_are_caught(monkeypatch, mutation):
     caught = False
     for spread in (1.0, 3.0):
         try:
-            check_bound_holds(spread)
+            check_bound_holds(spread, rounded_den)
         except AssertionError:
             caught = True
     assert caught, mutation
@@ -136,7 +159,8 @@ def bf16_round(x):
         torch.bfloat16).float().numpy().astype(np.float64)
 
 
-def simulate_kernel(q, k, v, kind, window, scale, shift, round_p=True, bf16_out=True):
+def simulate_kernel(q, k, v, kind, window, scale, shift, round_p=True, bf16_out=True,
+                    rounded_den=False):
     """The FP8 forward's arithmetic in float32 on the decoded inputs: scores,
     exponent argument and 2^x in float32, weights against a reference maximum
     `shift` log2 units below the row maximum, P rounded to E4M3 (unless
@@ -163,14 +187,19 @@ def simulate_kernel(q, k, v, kind, window, scale, shift, round_p=True, bf16_out=
                 num = (num + (pr[:, j0:j0 + 16].astype(np.float64)
                               @ vd[b, h, j0:j0 + 16].astype(np.float64)).astype(np.float32))
             den = np.zeros((S, 1), dtype=np.float32)
-            for j in range(S):
-                den = (den + p[:, j:j + 1]).astype(np.float32)
+            if rounded_den:  # the rounded weights in the numerator's 16-key chunks
+                for j0 in range(0, S, 16):
+                    den = (den + pr[:, j0:j0 + 16].astype(np.float64).sum(
+                        axis=1, keepdims=True)).astype(np.float32)
+            else:
+                for j in range(S):
+                    den = (den + p[:, j:j + 1]).astype(np.float32)
             o = (num / den).astype(np.float32)
             out[b, a] = bf16_round(o) if bf16_out else o
     return out
 
 
-def check_tolerance(spread, exact_weights=False, bf16_out=True, scale=0.5):
+def check_tolerance(spread, exact_weights=False, bf16_out=True, scale=0.5, rounded_den=False):
     rng = np.random.default_rng(62)
     B, Hq, Hkv, S, D = 1, 2, 1, 80, 32
     q = np.zeros((B, Hq, S, D), dtype=np.uint8) if exact_weights else \
@@ -181,39 +210,42 @@ def check_tolerance(spread, exact_weights=False, bf16_out=True, scale=0.5):
     for kind, w in (("causal", 0), ("full", 0), ("causal_window", 9)):
         exact = f8.fp8_attention(q, k, v, kind, w, scale=scale)
         tol = f8.fp8_tolerance(q, k, v, kind, w, scale=scale, exact_weights=exact_weights,
-                               bf16_output=bf16_out)
+                               bf16_output=bf16_out, rounded_denominator=rounded_den)
         for shift in ((0.0,) if exact_weights else (0.0, 0.37, 3.0, 7.9)):
             got = simulate_kernel(q, k, v, kind, w, scale, shift, round_p=not exact_weights,
-                                  bf16_out=bf16_out)
+                                  bf16_out=bf16_out, rounded_den=rounded_den)
             err = np.abs(got - exact)
             assert np.all(err <= tol), (kind, shift, float((err - tol).max()))
             worst = max(worst, float((err / tol).max()))
     return worst
 
 
-def test_tolerance_covers_the_kernel_arithmetic():
+@pytest.mark.parametrize("rounded_den", [False, True])
+def test_tolerance_covers_the_kernel_arithmetic(rounded_den):
     pytest.importorskip("torch")
-    assert check_tolerance(1.0) > 0.05
-    check_tolerance(3.0)
-    check_tolerance(1.0, scale=-0.3)
+    assert check_tolerance(1.0, rounded_den=rounded_den) > 0.05
+    check_tolerance(3.0, rounded_den=rounded_den)
+    check_tolerance(1.0, scale=-0.3, rounded_den=rounded_den)
 
 
-def test_tolerance_with_exact_weights():
+@pytest.mark.parametrize("rounded_den", [False, True])
+def test_tolerance_with_exact_weights(rounded_den):
     pytest.importorskip("torch")
     # the bf16 output rounding is the dominant part: a real error reaches it
-    assert check_tolerance(1.0, exact_weights=True) > 0.2
+    assert check_tolerance(1.0, exact_weights=True, rounded_den=rounded_den) > 0.2
     # without the output rounding only the fp32 terms remain, and they hold
-    check_tolerance(1.0, exact_weights=True, bf16_out=False)
+    check_tolerance(1.0, exact_weights=True, bf16_out=False, rounded_den=rounded_den)
 
 
+@pytest.mark.parametrize("rounded_den", [False, True])
 @pytest.mark.parametrize("mutation", ["no_bf16_term", "no_fp32_term"])
-def test_planted_tolerance_mistakes_are_caught(monkeypatch, mutation):
+def test_planted_tolerance_mistakes_are_caught(monkeypatch, mutation, rounded_den):
     pytest.importorskip("torch")
     if mutation == "no_bf16_term":
         monkeypatch.setattr(f8, "U_BF16", 0.0)
         with pytest.raises(AssertionError):
-            check_tolerance(1.0, exact_weights=True)
+            check_tolerance(1.0, exact_weights=True, rounded_den=rounded_den)
     else:
         monkeypatch.setattr(f8, "U_F32", 0.0)
         with pytest.raises(AssertionError):
-            check_tolerance(1.0, exact_weights=True, bf16_out=False)
+            check_tolerance(1.0, exact_weights=True, bf16_out=False, rounded_den=rounded_den)
