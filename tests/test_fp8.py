@@ -2,7 +2,8 @@
 
 GPU cases compare every output element with oracle.fp8_attention (exact
 attention on the decoded E4M3 inputs, fp64) within the per-element bound
-oracle.fp8_tolerance derives for the method's rounding of P to E4M3, its fp32
+oracle.fp8_tolerance derives for the method's rounding of P to E4M3 (the denominator
+summed from the rounded weights, as the kernel does on the matrix cores), its fp32
 scores, exponentials and accumulation, and the bf16 rounding of the output.
 With all queries zero every visible weight is exactly 1, so the output is the
 mean of the visible value rows and must match to the output's bf16 rounding:
@@ -42,7 +43,8 @@ def run_fp8(device, B, Hq, Hkv, S, mask, window=0, seed=0, scale=None, zero_q=Fa
     if rows is not None:
         got = got[:, :, rows]
     assert np.all(np.isfinite(got))
-    tol = oracle.fp8_tolerance(*codes, mask, window, scale=scale, rows=rows, exact_weights=zero_q)
+    tol = oracle.fp8_tolerance(*codes, mask, window, scale=scale, rows=rows, exact_weights=zero_q,
+                               rounded_denominator=True)
     return got, ref, tol
 
 

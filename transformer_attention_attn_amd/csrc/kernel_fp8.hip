@@ -6,13 +6,17 @@
 //   * S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit
 //     scales, fp32 accumulation): 64 dims per instruction.
 //   * Online softmax in fp32, as in the bf16 kernel (log2 units, lazy
-//     reference maximum, denominator summed from the fp32 weights), except
-//     that the weights come first and the row maximum is computed only when
-//     their per-lane sum shows a weight above 2^8 (and on a row's first tile).
-//   * P is rounded to E4M3 (v_cvt_pk_fp8_f32, round to nearest even; P <= 2^8
-//     stays far below the E4M3 maximum) and O^T += V^T P^T runs on the same
+//     reference maximum), except that the weights come first and the row
+//     maximum is computed only when one of them rounds to 2^8 or more (and on
+//     a row's first tile).
+//   * P is rounded to E4M3 (v_cvt_pk_fp8_f32, round to nearest even; P < 2^8
+//     stays below the E4M3 maximum) and O^T += V^T P^T runs on the same
 //     instruction, 64 keys per instruction; O is accumulated in fp32 and
 //     written as bf16.
+//   * The denominator is summed on the matrix cores too: l += 1 P^T with an
+//     all-ones E4M3 operand (two more instructions per tile), i.e. from the
+//     rounded weights, so O is the exact weighted mean under them; the
+//     vector ALUs, this kernel's bottleneck, do no sum at all.
 //
 // gfx950 operand layouts used (checked on the hardware): for the 32x32x64
 // FP8 product, lane l holds row (A) or column (B) l % 32 and the 32
@@ -56,8 +60,7 @@ constexpr int F8_ROWB = F8_D;             // bytes per K or V row
 constexpr int F8_REG = F8_BN * F8_ROWB;   // one K or V tile (16 KB)
 constexpr int F8_NSTAGE = 2;
 constexpr int F8_LOADS = F8_REG / 1024 / 4;  // 1 KiB direct loads per loading wave per tile
-constexpr float kLazyF8 = 8.f;
-constexpr float kLazyWF8 = 256.f;  // 2^kLazyF8
+constexpr unsigned kE4M3One = 0x38383838u;  // four E4M3 ones
 static_assert(F8_LOADS * 4 * 1024 == F8_REG, "tile split into 1 KiB loads of four waves");
 
 __device__ __forceinline__ int kswz(int row) { return ((row >> 1) & 3) | (((row >> 4) & 1) << 2); }
@@ -251,7 +254,13 @@ void attn_fwd_fp8(KParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_run = -INFINITY;
-  float l_run0 = 0.f, l_run1 = 0.f;
+  // denominator l = P 1: every register of the accumulator holds the row sum
+  // of the lane's query (column l32)
+  f32x16 lacc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
+  const i32x8 ones8 = {(int)kE4M3One, (int)kE4M3One, (int)kE4M3One, (int)kE4M3One,
+                       (int)kE4M3One, (int)kE4M3One, (int)kE4M3One, (int)kE4M3One};
   const float c = p.c;
 
   // ---- the matrix block of one step: O^T += V(jv)^T P^T, then S(js) = K(js) Q^T
@@ -266,7 +275,9 @@ void attn_fwd_fp8(KParams p) {
       const unsigned vbase[4] = {vb + v_off[0], vb + v_off[1], vb + v_off[2], vb + v_off[3]};
       i32x8 vo[2];
       vo[0] = lds_tr8x4<vrow_off(0, 0), vrow_off(0, 1), vrow_off(0, 2), vrow_off(0, 3)>(vbase[0]);
+      lacc = mfma_fp8(ones8, pf[0], lacc);
       pv_steps<0>(vo, vbase, pf, oacc);
+      lacc = mfma_fp8(ones8, pf[1], lacc);
     }
     if (do_s) {
       const unsigned kb = lds_addr(smem + (js & 1) * 2 * F8_REG);
@@ -299,12 +310,11 @@ void attn_fwd_fp8(KParams p) {
         }
     }
     // Weights first, against the current reference maximum, when every row of
-    // the wave has one; the per-lane sum of the tile's weights bounds each of
-    // them, so the row maximum (and the rescale) is only needed on a row's
-    // first tile and when that sum exceeds 2^kLazyF8, and the weights are then
-    // recomputed.  Weights stay <= 2^8, inside the E4M3 range.
+    // the wave has one; the row maximum (and the rescale) is only needed on a
+    // row's first tile and when a weight rounds to 2^8 or more (an E4M3 code
+    // with exponent field 15, or the NaN code), and the weights are then
+    // recomputed.  Weights stay below 2^8, inside the E4M3 range.
     bool with_max = __builtin_amdgcn_ballot_w64(row_valid && m_run == -INFINITY) != 0;
-    float t0, t1;
 #pragma nounroll
     for (;;) {
       if (with_max) {
@@ -327,8 +337,8 @@ void attn_fwd_fp8(KParams p) {
           const float m_new = fmaxf(m_run, mx);
           const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
           m_run = m_new;
-          l_run0 *= alpha;
-          l_run1 *= alpha;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
 #pragma unroll
           for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -336,8 +346,9 @@ void attn_fwd_fp8(KParams p) {
         }
       }
       const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-      t0 = 0.f;
-      t1 = 0.f;
+      // bit 7 of a byte of (code + 8) is set exactly for codes 0x78..0x7F
+      // (weights are positive: codes below 0x80, no carry between bytes)
+      unsigned big = 0u;
       // weights of 64-key step sk: bytes 16*(kbk - 2*sk) + r, four per dword
 #pragma unroll
       for (int kbk = 0; kbk < 4; ++kbk)
@@ -347,17 +358,15 @@ void attn_fwd_fp8(KParams p) {
           const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 1], c, -mc));
           const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 2], c, -mc));
           const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 3], c, -mc));
-          t0 += e0 + e1;
-          t1 += e2 + e3;
           int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
           w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
+          big |= (unsigned)w + 0x08080808u;
           pf[kbk >> 1][4 * (kbk & 1) + r / 4] = w;
         }
-      if (with_max || __builtin_amdgcn_ballot_w64(row_valid && !(t0 + t1 <= kLazyWF8)) == 0) break;
+      if (with_max || __builtin_amdgcn_ballot_w64(row_valid && (big & 0x80808080u) != 0u) == 0)
+        break;
       with_max = true;
     }
-    l_run0 += t0;
-    l_run1 += t1;
   };
   auto zero_p = [&]() {
 #pragma unroll
@@ -409,9 +418,7 @@ void attn_fwd_fp8(KParams p) {
 
   // ---- epilogue: O = O^T / l, round to bf16, store --------------------------
   {
-    const float l_run = l_run0 + l_run1;
-    const float l_other = __uint_as_float(__shfl_xor((int)__float_as_uint(l_run), 32));
-    const float l_tot = l_run + l_other;
+    const float l_tot = lacc[0];
     if (row_valid && wave_active) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       __bf16* op = (__bf16*)p.o + ((size_t)(it.b * s.Hq + a) * S + q_row) * F8_D;
