@@ -61,6 +61,9 @@ constexpr int F8_REG = F8_BN * F8_ROWB;   // one K or V tile (16 KB)
 constexpr int F8_NSTAGE = 2;
 constexpr int F8_LOADS = F8_REG / 1024 / 4;  // 1 KiB direct loads per loading wave per tile
 constexpr unsigned kE4M3One = 0x38383838u;  // four E4M3 ones
+#ifndef F8_OPDEPTH
+#define F8_OPDEPTH 3  // LDS operands in flight + 1 in the matrix block
+#endif
 static_assert(F8_LOADS * 4 * 1024 == F8_REG, "tile split into 1 KiB loads of four waves");
 
 __device__ __forceinline__ int kswz(int row) { return ((row >> 1) & 3) | (((row >> 4) & 1) << 2); }
@@ -95,45 +98,72 @@ __device__ __forceinline__ void lds_wait8(i32x8& f) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f) : "i"(N));
 }
 
-// S^T = K Q^T, 32-key blocks KBK..3 (two 64-dim MFMAs each).  On entry op[0]
-// holds the reads of (KBK, dim step 0) in flight; a_dc_c are the per-lane K
-// read addresses of dim step dc, chunk c (block 0).
-template <int KBK>
-__device__ __forceinline__ void s_blocks(i32x8 (&op)[2], unsigned a00, unsigned a01, unsigned a10,
-                                         unsigned a11, const i32x8 (&qf)[2], f32x16 (&sc)[4]) {
-  constexpr int OFF = KBK * 32 * F8_ROWB;
-  op[1] = lds_read32<OFF>(a10, a11);
-  lds_wait8<2>(op[0]);
-  sc[KBK] = mfma_fp8(op[0], qf[0], f32x16{});
-  if constexpr (KBK < 3) {
-    op[0] = lds_read32<OFF + 32 * F8_ROWB>(a00, a01);
-    lds_wait8<2>(op[1]);
-  } else {
-    lds_wait8<0>(op[1]);
-  }
-  sc[KBK] = mfma_fp8(op[1], qf[1], sc[KBK]);
-  if constexpr (KBK < 3) s_blocks<KBK + 1>(op, a00, a01, a10, a11, qf, sc);
-}
-
 // Row offset (bytes) of transposed read t of 64-key step SK.
 constexpr int vrow_off(int SK, int t) { return (64 * SK + 32 * (t >> 1) + 8 * (t & 1)) * F8_ROWB; }
 
-// O^T += V^T P^T, steps I..7 (I = 2 * dim block + key step).  On entry vo[I & 1]
-// holds the reads of step I in flight; vbase[db] is the per-lane V^T read base
-// of dim block db.
-template <int I>
-__device__ __forceinline__ void pv_steps(i32x8 (&vo)[2], const unsigned (&vbase)[4],
-                                         const i32x8 (&pf)[2], f32x16 (&oacc)[4]) {
-  constexpr int DB = I >> 1, SK = I & 1;
-  if constexpr (I < 7) {
-    constexpr int ND = (I + 1) >> 1, NS = (I + 1) & 1;
-    vo[(I + 1) & 1] = lds_tr8x4<vrow_off(NS, 0), vrow_off(NS, 1), vrow_off(NS, 2), vrow_off(NS, 3)>(vbase[ND]);
-    lds_wait8<4>(vo[I & 1]);
+// The matrix block of one step as operand pipelines: operands 0..NV-1 are
+// V^T (I = 2 * dim block + 64-key step: O^T += V^T P^T), operands NV..N-1 are
+// K (I - NV = 2 * 32-key block + 64-dim step: S^T = K Q^T); the kernel runs
+// the P.V part and the S part as two of them.  The LDS reads of
+// operand I + DEPTH - 1 are issued before the product of operand I, so
+// DEPTH - 1 operands are in flight behind each product; the wait for operand
+// I lets the reads issued after it stay outstanding (V: four reads, K: two).
+struct BlockOps {
+  unsigned vbase[4];            // per-lane V^T read base of each dim block
+  unsigned a00, a01, a10, a11;  // per-lane K read addresses (dim step, chunk)
+};
+template <int NV>
+constexpr int reads_of(int i) { return i < NV ? 4 : 2; }
+template <int NV>
+constexpr int reads_after(int i, int last) {
+  int n = 0;
+  for (int j = i + 1; j <= last; ++j) n += reads_of<NV>(j);
+  return n;
+}
+template <int I, int NV>
+__device__ __forceinline__ i32x8 block_read(const BlockOps& o) {
+  if constexpr (I < NV) {
+    constexpr int DB = I >> 1, SK = I & 1;
+    return lds_tr8x4<vrow_off(SK, 0), vrow_off(SK, 1), vrow_off(SK, 2), vrow_off(SK, 3)>(o.vbase[DB]);
   } else {
-    lds_wait8<0>(vo[I & 1]);
+    constexpr int KBK = (I - NV) >> 1, DC = (I - NV) & 1;
+    return DC == 0 ? lds_read32<KBK * 32 * F8_ROWB>(o.a00, o.a01)
+                   : lds_read32<KBK * 32 * F8_ROWB>(o.a10, o.a11);
   }
-  oacc[DB] = mfma_fp8(vo[I & 1], pf[SK], oacc[DB]);
-  if constexpr (I < 7) pv_steps<I + 1>(vo, vbase, pf, oacc);
+}
+template <int I, int NV, int N, int DEPTH>
+__device__ __forceinline__ void block_step(i32x8 (&op)[DEPTH], const BlockOps& o, const i32x8 (&pf)[2],
+                                           const i32x8 (&qf)[2], const i32x8& ones, f32x16 (&oacc)[4],
+                                           f32x16& lacc, f32x16 (&sc)[4]) {
+  constexpr int J = I + DEPTH - 1;
+  if constexpr (J < N) op[J % DEPTH] = block_read<J, NV>(o);
+  constexpr int LAST = J < N ? J : N - 1;
+  lds_wait8<reads_after<NV>(I, LAST)>(op[I % DEPTH]);
+  if constexpr (I < NV) {
+    oacc[I >> 1] = mfma_fp8(op[I % DEPTH], pf[I & 1], oacc[I >> 1]);
+    // the denominator (no LDS operand) in the shadow of the first reads
+    if constexpr (I < 2) lacc = mfma_fp8(ones, pf[I], lacc);
+  } else {
+    constexpr int K = I - NV;
+    sc[K >> 1] = mfma_fp8(op[I % DEPTH], qf[K & 1], (K & 1) ? sc[K >> 1] : f32x16{});
+  }
+  if constexpr (I + 1 < N) block_step<I + 1, NV, N, DEPTH>(op, o, pf, qf, ones, oacc, lacc, sc);
+}
+template <int NV, int N, int DEPTH, int I = 0>
+__device__ __forceinline__ void block_prime(i32x8 (&op)[DEPTH], const BlockOps& o) {
+  if constexpr (I < DEPTH - 1 && I < N) {
+    op[I] = block_read<I, NV>(o);
+    block_prime<NV, N, DEPTH, I + 1>(op, o);
+  }
+}
+template <bool PV, bool S>
+__device__ __forceinline__ void run_block(const BlockOps& o, const i32x8 (&pf)[2], const i32x8 (&qf)[2],
+                                          const i32x8& ones, f32x16 (&oacc)[4], f32x16& lacc,
+                                          f32x16 (&sc)[4]) {
+  constexpr int NV = PV ? 8 : 0, N = NV + (S ? 8 : 0), DEPTH = F8_OPDEPTH;
+  i32x8 op[DEPTH];
+  block_prime<NV, N, DEPTH>(op, o);
+  block_step<0, NV, N, DEPTH>(op, o, pf, qf, ones, oacc, lacc, sc);
 }
 
 template <int MASK>
@@ -270,23 +300,18 @@ void attn_fwd_fp8(KParams p) {
   for (int i = 0; i < 2; ++i) pf[i] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
   auto mfma_block = [&](int jv, bool do_pv, int js, bool do_s) {
     __builtin_amdgcn_s_setprio(1);
-    if (do_pv) {
-      const unsigned vb = lds_addr(smem + (jv & 1) * 2 * F8_REG);
-      const unsigned vbase[4] = {vb + v_off[0], vb + v_off[1], vb + v_off[2], vb + v_off[3]};
-      i32x8 vo[2];
-      vo[0] = lds_tr8x4<vrow_off(0, 0), vrow_off(0, 1), vrow_off(0, 2), vrow_off(0, 3)>(vbase[0]);
-      lacc = mfma_fp8(ones8, pf[0], lacc);
-      pv_steps<0>(vo, vbase, pf, oacc);
-      lacc = mfma_fp8(ones8, pf[1], lacc);
-    }
-    if (do_s) {
-      const unsigned kb = lds_addr(smem + (js & 1) * 2 * F8_REG);
-      const unsigned a00 = kb + k_off[0][0], a01 = kb + k_off[0][1];
-      const unsigned a10 = kb + k_off[1][0], a11 = kb + k_off[1][1];
-      i32x8 op[2];
-      op[0] = lds_read32<0>(a00, a01);
-      s_blocks<0>(op, a00, a01, a10, a11, qf, sc);
-    }
+    BlockOps o;
+    const unsigned vb = lds_addr(smem + (jv & 1) * 2 * F8_REG);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o.vbase[db] = vb + v_off[db];
+    const unsigned kb = lds_addr(smem + (js & 1) * 2 * F8_REG);
+    o.a00 = kb + k_off[0][0];
+    o.a01 = kb + k_off[0][1];
+    o.a10 = kb + k_off[1][0];
+    o.a11 = kb + k_off[1][1];
+    // two regions (one pipeline over both would hold too many registers live)
+    if (do_pv) run_block<true, false>(o, pf, qf, ones8, oacc, lacc, sc);
+    if (do_s) run_block<false, true>(o, pf, qf, ones8, oacc, lacc, sc);
     __builtin_amdgcn_s_setprio(0);
   };
 
