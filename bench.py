@@ -10,7 +10,8 @@ kernel is launched on.  Prints one JSON line:
 
   value     effective TFLOP/s = unmasked FLOPs (4*D per visible (query, key)
             pair per query head) / time per step
-  roofline  matrix-core bound: achieved TFLOP/s of the attention kernel (its
+  roofline  matrix-core bound (vector-ALU bound for fp32 workloads):
+            achieved TFLOP/s of the attention kernel (its
             algorithmic FLOPs per launch / its average launch duration, which
             is the event-timed time per step: a step is exactly one launch of
             that kernel; the committed rocprofv3 kernel trace of the same
@@ -737,7 +738,8 @@ def main(argv=None):
                    "effective_flops": flops, "parallelism": "none"},
         "pct_peak": round(100.0 * tflops / peak, 2),
         "roofline": {
-            "bound": "mfma",
+            # the fp32 kernel runs on the vector ALUs (peak: the fp32 vector rate)
+            "bound": "alu" if w.dtype == "fp32" else "mfma",
             "achieved": round(tflops, 3),
             "peak": peak,
             "unit": "TFLOP/s",

@@ -108,7 +108,7 @@ def test_plan_matches_oracle_counts(case):
                                           2 if G % 2 == 0 else 1)
         assert rows * info["heads_per_item"] == 256
     else:
-        assert (rows, info["heads_per_item"], info["keys_per_tile"]) == (64, 1, 32)
+        assert (rows, info["heads_per_item"], info["keys_per_tile"]) == (16, 1, 32)
 
 
 def test_plan_skips_masked_tiles():

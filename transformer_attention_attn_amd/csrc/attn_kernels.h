@@ -39,7 +39,7 @@ struct KParams {
 constexpr int kSparseMaxKeys = 8192;
 
 // Workgroup shapes used by the two kernels.
-constexpr int kF32Rows = 64;   // query rows per fp32 work item (one head)
+constexpr int kF32Rows = 16;   // query rows per fp32 work item (one head, 16 lanes per row)
 constexpr int kF32Keys = 32;   // keys per fp32 tile
 constexpr int kBf16Rows = 32 * kBf16Waves;  // query rows per bf16 work item (heads packed)
 constexpr int kBf16GlobalRows = 32;          // global rows per query head in a bf16 global item
