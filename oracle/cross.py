@@ -43,6 +43,18 @@ Optional parts of the same call:
   it equals p_i - j on every key a causal or causal-window query sees), and
   the bias is added after the 1/sqrt(d) scaling, not scaled itself.  Slopes
   are inputs (the pages fix none; any real value is accepted).
+* Distance bias -- "Trasformer 浅析", the closing section on the unified view
+  (sequence attention, positional biases and graph attention as one formula):
+  the logit is the scaled score plus a term b_ij, and what distinguishes the
+  priors is where b_ij comes from (position, distance or graph structure).
+  Reading for the distance case: b_ij is a function f_a of the signed
+  distance d = j - p_i (key position minus query position), one function
+  per query head, given as a table over every distance a call can produce:
+  row a holds Sq + Skv - 1 values and entry d + Skv - 1 is f_a(d), for
+  d in [-(Skv - 1), Sq - 1] (the table's length and offset come from the
+  call's Sq and Skv, also in padded batches, where each sequence uses the
+  distances of its own positions).  The term is added after the scaling and
+  is not scaled itself.  ALiBi is the table -m_a |d|.
 * Padded (ragged) batches -- "Trasformer 浅析", section 填充掩码与因果掩码:
   short sequences of a batch are padded and the padded positions are masked
   out.  Reading: sequence b holds q_len[b] valid query rows and kv_len[b]
@@ -55,7 +67,8 @@ Optional parts of the same call:
 Layout: q [B][Hq][Sq][D], k and v [B][Hkv][Skv][D] (logical layout; strided
 device layouts are a matter of the tests).  float64 on the exact inputs.
 
-Pinned by tests/test_oracle_cross.py (ALiBi and padded batches included).
+Pinned by tests/test_oracle_cross.py (ALiBi, the distance bias and padded
+batches included).
 """
 from __future__ import annotations
 
@@ -108,6 +121,18 @@ def head_slope(slopes, a, G):
     return slopes[a]
 
 
+def head_bias_row(table, a, G):
+    """Distance-bias table row of query head a (G query heads per key/value
+    head)."""
+    return table[a]
+
+
+def distance_bias(row, p, j, Skv):
+    """The distance-bias term of query position p and key positions j: entry
+    (j - p) + Skv - 1 of the head's table row (Skv: the call's key count)."""
+    return np.asarray(row, dtype=np.float64)[np.asarray(j, dtype=np.int64) - p + Skv - 1]
+
+
 def sequence_lengths(Sq, Skv, q_len, kv_len, b):
     """Valid query rows and keys of sequence b."""
     sq_b = Sq if q_len is None else int(q_len[b])
@@ -118,12 +143,13 @@ def sequence_lengths(Sq, Skv, q_len, kv_len, b):
 
 
 def cross_attention(q, k, v, kind, window=0, scale=None, rows=None, alibi_slopes=None,
-                    q_len=None, kv_len=None, global_idx=()):
+                    q_len=None, kv_len=None, global_idx=(), dist_bias=None):
     """Attention output, float64, shape [B, Hq, Sq, D]; with `rows` (query row
     indices) only those rows, shape [B, Hq, len(rows), D].  `alibi_slopes`: Hq
     slopes (None: no bias); `q_len`, `kv_len`: B valid lengths each (None: all
     Sq / Skv rows valid); `global_idx`: the global key positions of
-    "local_global"."""
+    "local_global"; `dist_bias`: the [Hq][Sq + Skv - 1] distance-bias table
+    (None: no such term)."""
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
@@ -140,6 +166,9 @@ def cross_attention(q, k, v, kind, window=0, scale=None, rows=None, alibi_slopes
     slopes = None if alibi_slopes is None else np.asarray(alibi_slopes, dtype=np.float64)
     if slopes is not None and slopes.shape != (Hq,):
         raise ValueError("alibi_slopes needs one slope per query head")
+    table = None if dist_bias is None else np.asarray(dist_bias, dtype=np.float64)
+    if table is not None and table.shape != (Hq, Sq + Skv - 1):
+        raise ValueError("dist_bias needs Hq rows of Sq + Skv - 1 values")
     out = np.zeros((B, Hq, len(rows), D), dtype=np.float64)
     for b in range(B):
         sq_b, skv_b = sequence_lengths(Sq, Skv, q_len, kv_len, b)
@@ -156,6 +185,8 @@ def cross_attention(q, k, v, kind, window=0, scale=None, rows=None, alibi_slopes
                 s = float(scale) * (kk @ q[b, a, i].astype(np.float64))
                 if slopes is not None:
                     s = s - alibi_penalty(head_slope(slopes, a, G), i + skv_b - sq_b, js)
+                if table is not None:
+                    s = s + distance_bias(head_bias_row(table, a, G), i + skv_b - sq_b, js, Skv)
                 e = np.exp(s - s.max())
                 out[b, a, r] = (e / e.sum()) @ vv
     return out

@@ -4,8 +4,11 @@ oracle/cross.py is tied to independent routines: the square oracle
 (reference.py) when Sq == Skv or on the last rows of a longer sequence, the
 decode oracle (decode.py) for causal and full masks, and a pure-Python loop.
 ALiBi is tied to a closed form (geometric weights when all scores are zero)
-and to the square oracle with one extra dimension; padded batches to the
-decode oracle's cache lengths and the square oracle per sequence.
+and to the square oracle with one extra dimension; the distance bias to a
+one-distance selection (zero queries), the softmax of the bias when all
+scores are zero, ALiBi as a table, and a pure-Python loop over a padded
+batch; padded batches to the decode oracle's cache lengths and the square
+oracle per sequence.
 ``test_planted_cross_mistakes_are_caught`` plants plausible mistakes and checks
 that a pin fails for each.
 """
@@ -231,6 +234,100 @@ def pin_alibi_ragged_brute_force():
                     assert abs(got[b, a, i, d] - want) < 1e-13
 
 
+def _bias_table(fs, Sq, Skv):
+    """Distance-bias table whose row a holds f_a(d) for d = -(Skv - 1) .. Sq - 1."""
+    return np.array([[f(t - (Skv - 1)) for t in range(Sq + Skv - 1)] for f in fs])
+
+
+def pin_dist_bias_selects_distance():
+    """Zero queries and a bias of 0 at one distance and -80 elsewhere: row i
+    takes the value row at key position p_i + d when that key is visible, and
+    the mean of its visible values otherwise (all weights equal)."""
+    rng = np.random.default_rng(31)
+    D = 3
+    for Sq, Skv, kind, d in ((5, 9, "full", 1), (9, 9, "full", 1), (9, 4, "full", -1),
+                             (6, 11, "causal", -2), (7, 7, "causal_window", -3)):
+        q = np.zeros((1, 1, Sq, D))
+        k, v = randn(rng, 1, 1, Skv, D), randn(rng, 1, 1, Skv, D)
+        table = _bias_table([lambda x, d=d: 0.0 if x == d else -80.0], Sq, Skv)
+        got = cr.cross_attention(q, k, v, kind, 4, scale=0.8, dist_bias=table)
+        for i in range(Sq):
+            p = i + Skv - Sq
+            if kind == "full":
+                vis = list(range(Skv))
+            elif kind == "causal":
+                vis = list(range(0, min(Skv, p + 1)))
+            else:
+                vis = list(range(max(0, p - 3), min(Skv, p + 1)))
+            if not vis:
+                assert np.all(got[0, 0, i] == 0.0)
+                continue
+            want = v[0, 0, p + d] if (p + d) in vis else v[0, 0, vis].mean(axis=0)
+            assert np.max(np.abs(got[0, 0, i] - want)) < 1e-12, (Sq, Skv, kind, i)
+
+
+def pin_dist_bias_zero_scores():
+    """With zero scores the weights are the softmax of f_a(j - p_i) over the
+    visible keys, whatever the scale (the term is not scaled)."""
+    rng = np.random.default_rng(32)
+    Sq, Skv, D, G = 4, 7, 2, 2
+    fs = [lambda x: 0.3 * x - 0.05 * x * x, lambda x: -0.7 * abs(x + 1) + 0.2 * (x > 2)]
+    table = _bias_table(fs, Sq, Skv)
+    q = np.zeros((1, G, Sq, D))
+    k, v = randn(rng, 1, 1, Skv, D), randn(rng, 1, 1, Skv, D)
+    for scale in (1.0, 0.37, -2.0):
+        got = cr.cross_attention(q, k, v, "causal", scale=scale, dist_bias=table)
+        for a in range(G):
+            for i in range(Sq):
+                p = i + Skv - Sq
+                js = list(range(p + 1))
+                e = [math.exp(fs[a](j - p)) for j in js]
+                for dd in range(D):
+                    want = math.fsum(e[n] * v[0, 0, j, dd] for n, j in enumerate(js)) / math.fsum(e)
+                    assert abs(got[0, a, i, dd] - want) < 1e-13, (scale, a, i)
+
+
+def pin_dist_bias_as_alibi():
+    """The table -m_a |d| is ALiBi with slopes m_a (the oracle's ALiBi path,
+    pinned above), for every mask, with grouped heads."""
+    rng = np.random.default_rng(33)
+    B, Hq, Hkv, Sq, Skv, D = 1, 4, 2, 6, 10, 4
+    slopes = [0.25, 0.9, 0.05, 1.7]
+    q, k, v = randn(rng, B, Hq, Sq, D), randn(rng, B, Hkv, Skv, D), randn(rng, B, Hkv, Skv, D)
+    table = _bias_table([lambda x, m=m: -m * abs(x) for m in slopes], Sq, Skv)
+    for kind, w in (("full", 0), ("causal", 0), ("causal_window", 3)):
+        got = cr.cross_attention(q, k, v, kind, w, dist_bias=table)
+        ref = cr.cross_attention(q, k, v, kind, w, alibi_slopes=slopes)
+        assert np.max(np.abs(got - ref)) < 1e-12, kind
+
+
+def pin_dist_bias_ragged_brute_force():
+    """Pure-Python loops: a distance bias on a padded batch (each sequence
+    uses the distances of its own positions), grouped heads."""
+    rng = np.random.default_rng(34)
+    B, Hq, Sq, Skv, D, scale = 2, 2, 4, 6, 3, 0.6
+    fs = [lambda x: math.sin(0.9 * x) + 0.1 * x, lambda x: -0.4 * abs(x) + (0.5 if x == 0 else 0.0)]
+    table = _bias_table(fs, Sq, Skv)
+    q, k, v = randn(rng, B, Hq, Sq, D), randn(rng, B, 1, Skv, D), randn(rng, B, 1, Skv, D)
+    q_len, kv_len = [3, 4], [5, 6]
+    for kind in ("full", "causal"):
+        got = cr.cross_attention(q, k, v, kind, scale=scale, q_len=q_len, kv_len=kv_len,
+                                 dist_bias=table)
+        for b in range(B):
+            assert np.all(got[b, :, q_len[b]:] == 0.0)
+            for a in range(Hq):
+                for i in range(q_len[b]):
+                    p = i + kv_len[b] - q_len[b]
+                    js = [j for j in range(kv_len[b]) if kind == "full" or j <= p]
+                    sc = [scale * math.fsum(q[b, a, i, d] * k[b, 0, j, d] for d in range(D))
+                          + fs[a](j - p) for j in js]
+                    m = max(sc)
+                    e = [math.exp(x - m) for x in sc]
+                    for d in range(D):
+                        want = math.fsum(e[n] * v[b, 0, j, d] for n, j in enumerate(js)) / math.fsum(e)
+                        assert abs(got[b, a, i, d] - want) < 1e-13, (kind, b, a, i)
+
+
 def pin_pair_counts():
     assert cr.cross_visible_pairs(4, 10, "full") == 40
     assert cr.cross_visible_pairs(4, 10, "causal") == 7 + 8 + 9 + 10
@@ -310,7 +407,8 @@ PINS = [pin_square_case, pin_chunk_is_last_rows, pin_matches_decode_oracle,
         pin_alibi_closed_form, pin_alibi_as_extra_dimension, pin_ragged_matches_decode_oracle,
         pin_ragged_queries_are_last_rows, pin_alibi_ragged_brute_force, pin_pair_counts,
         pin_local_global_square_and_chunk, pin_local_global_ragged,
-        pin_local_global_brute_force]
+        pin_local_global_brute_force, pin_dist_bias_selects_distance, pin_dist_bias_zero_scores,
+        pin_dist_bias_as_alibi, pin_dist_bias_ragged_brute_force]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -336,6 +434,7 @@ def _mut_full_is_causal(Sq, Skv, i, kind, window=0):
 
 
 _ORIG_PEN, _ORIG_SLOPE, _ORIG_LENS = cr.alibi_penalty, cr.head_slope, cr.sequence_lengths
+_ORIG_DB = cr.distance_bias
 _ORIG_KEYS = cr.cross_visible_keys
 
 
@@ -365,6 +464,18 @@ MUTATIONS = {
     "alibi_scaled": ("alibi_penalty", lambda m, p, j: 0.5 * _ORIG_PEN(m, p, j)),
     # slope of the key/value head instead of the query head
     "alibi_slope_by_kv_head": ("head_slope", lambda sl, a, G: sl[(a // G) * G]),
+    # distance measured from the key to the query
+    "dist_bias_sign": ("distance_bias",
+                       lambda row, p, j, Skv: np.asarray(row, dtype=np.float64)[
+                           p - np.asarray(j, dtype=np.int64) + Skv - 1]),
+    # table offset taken from the query count (Sq - 1) instead of Skv - 1
+    "dist_bias_offset_by_queries": ("distance_bias",
+                                    lambda row, p, j, Skv: np.asarray(row, dtype=np.float64)[
+                                        np.asarray(j, dtype=np.int64) - p + len(row) - Skv]),
+    # the term scaled like the scores
+    "dist_bias_scaled": ("distance_bias", lambda row, p, j, Skv: 0.5 * _ORIG_DB(row, p, j, Skv)),
+    # row of the key/value head's first query head
+    "dist_bias_row_by_kv_head": ("head_bias_row", lambda t, a, G: t[(a // G) * G]),
     # padding ignored: every key and query row valid
     "padding_ignored": ("sequence_lengths", lambda Sq, Skv, ql, kl, b: (Sq, Skv)),
     "lg_global_query_by_row_index": ("cross_visible_keys", _lg_variant(global_query_by_index=True)),
