@@ -135,6 +135,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o,
  *   CAUSAL          keys j <= p_i
  *   CAUSAL_WINDOW   keys p_i - window < j <= p_i
  *   FULL            every key
+ *   LOCAL_GLOBAL    keys |p_i - j| <= window, every key when p_i is a global
+ *                   position, and the global positions themselves (global_idx
+ *                   holds key positions, the same for every sequence;
+ *                   "Transformer 演进与变体", section 稀疏注意力, Longformer)
  * A query that sees no key (p_i < 0, possible when Skv < Sq) is written as
  * zeros.  With Sq == Skv and dense strides this is attn_fwd.
  *
@@ -144,7 +148,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o,
  * {H*S*D, S*D, D}; [B][S][H][D] (sequence-major) has {S*H*D, D, H*D}.
  * Strides must be non-negative multiples of 8 elements (16-byte rows), row
  * strides at most 2^23 elements; o's rows must not overlap each other or the
- * inputs.  LOCAL_GLOBAL and fp32 return ATTN_ERR_UNSUPPORTED here.
+ * inputs.  fp32 returns ATTN_ERR_UNSUPPORTED here.
  *
  * Optional parts (NULL pointers leave them out):
  *   alibi_slopes  device, Hq fp32 slopes m_a: query head a adds -m_a * |p_i - j|
@@ -175,6 +179,23 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o,
  *                 no lengths (else ATTN_ERR_UNSUPPORTED).  The attn_layout_*
  *                 builders below write the pages' patterns; any layout works.
  *                 A query whose row sees no key is written as zeros.
+ *   dist_bias     device, Hq x (Sq + Skv - 1) fp32, row a contiguous: a bias
+ *                 that is a function of the signed distance d = j - p_i (key
+ *                 position minus query position), one per query head.  Entry
+ *                 d + Skv - 1 of row a is added to query head a's scaled
+ *                 score of every pair at distance d, before the softmax (the
+ *                 unified view of "Trasformer 浅析", closing section: every
+ *                 positional prior is a term b_ij added to the scaled logits;
+ *                 here b_ij depends on the distance only).  In padded batches
+ *                 the distances are those of each sequence's own positions,
+ *                 so the same table serves every sequence.  ALiBi is the table
+ *                 -m_a |d|; a bucketed or clipped relative bias is written out
+ *                 per distance.  Masks FULL, CAUSAL and CAUSAL_WINDOW, not with
+ *                 ALiBi or a layout (else ATTN_ERR_UNSUPPORTED); Sq + Skv at
+ *                 most 2^29 (else ATTN_ERR_SHAPE); the same scale limit as
+ *                 ALiBi.  Values are read by the kernel, entries of masked
+ *                 pairs never reach the result, and NaN/Inf entries of
+ *                 visible pairs propagate.
  */
 typedef struct {
   const void* q;
@@ -202,6 +223,7 @@ typedef struct {
                              positions in [0, Skv) (duplicates allowed), or
                              NULL when n_global is 0                        */
   int n_global;           /* 0..ATTN_MAX_GLOBAL                            */
+  const float* dist_bias; /* device [Hq][Sq + Skv - 1] fp32, or NULL      */
 } attn_fwd_args;
 
 /* Enqueue attn_fwd_ex on `stream`; same return and error conventions as

@@ -48,14 +48,17 @@ def empty_out(B, H, S, D, layout, device):
 
 
 def run_ex(device, B, Hq, Hkv, Sq, Skv, D, mask, window=0, layout="bhsd", out_layout="bhsd",
-           seed=0, scale=None, slopes=None, q_len=None, kv_len=None, global_idx=()):
-    """Max abs error of attn_fwd_ex against the oracle.  With lengths, the
-    padded query rows, keys and values hold NaN (bf16 0x7FC0)."""
+           seed=0, scale=None, slopes=None, q_len=None, kv_len=None, global_idx=(),
+           dist_bias=None, rel=0.0):
+    """Max abs error of attn_fwd_ex against the oracle, less rel * |oracle| per
+    element.  With lengths, the padded query rows, keys and values hold NaN
+    (bf16 0x7FC0)."""
     import torch
 
     print(f"fwd_ex case B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} {mask} w={window} "
           f"{layout}->{out_layout} seed={seed} scale={scale} alibi={slopes is not None} "
-          f"q_len={q_len} kv_len={kv_len} globals={list(global_idx)}", flush=True)
+          f"q_len={q_len} kv_len={kv_len} globals={list(global_idx)} "
+          f"dist_bias={dist_bias is not None}", flush=True)
     rng = np.random.default_rng(seed)
     bits = {}
     vals = {}
@@ -73,14 +76,15 @@ def run_ex(device, B, Hq, Hkv, Sq, Skv, D, mask, window=0, layout="bhsd", out_la
     dev_arr = lambda x, dt: None if x is None else torch.tensor(list(x), dtype=dt, device=device)  # noqa: E731
     attn.fwd_ex(q, k, v, mask=mask, window=window, scale=scale, out=o,
                 alibi_slopes=dev_arr(slopes, torch.float32), q_len=dev_arr(q_len, torch.int32),
-                kv_len=dev_arr(kv_len, torch.int32), global_idx=list(global_idx) or None)
+                kv_len=dev_arr(kv_len, torch.int32), global_idx=list(global_idx) or None,
+                dist_bias=None if dist_bias is None else torch.from_numpy(dist_bias).to(device))
     torch.cuda.synchronize()
     got = o.float().cpu().numpy()
     ref = oracle.cross_attention(vals["q"], vals["k"], vals["v"], mask, window, scale=scale,
                                  alibi_slopes=slopes, q_len=q_len, kv_len=kv_len,
-                                 global_idx=global_idx)
+                                 global_idx=global_idx, dist_bias=dist_bias)
     assert np.all(np.isfinite(got))
-    return float(np.max(np.abs(got.astype(np.float64) - ref)))
+    return float(np.max(np.abs(got.astype(np.float64) - ref) - rel * np.abs(ref)))
 
 
 SWEEP = []
@@ -142,6 +146,74 @@ def test_fwd_ex_alibi_scales(device, scale, mask):
     assert err <= TOL["bf16"], err
 
 
+DIST_SWEEP = []
+_rng = np.random.default_rng(93)
+for D in (64, 128):
+    for (Sq, Skv) in ((100, 300), (300, 100), (257, 257), (1, 500), (513, 2049), (129, 128)):
+        for mask in ("full", "causal", "causal_window"):
+            Hq, Hkv = [(8, 2), (4, 4), (8, 1)][int(_rng.integers(3))]
+            window = int(_rng.choice([1, 63, 200])) if mask == "causal_window" else 0
+            layout = ["bhsd", "bshd", "padded"][int(_rng.integers(3))]
+            DIST_SWEEP.append((1 + int(_rng.integers(2)), Hq, Hkv, Sq, Skv, D, mask, window,
+                               layout))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", DIST_SWEEP, ids=lambda c: f"D{c[5]}-Sq{c[3]}-Skv{c[4]}-{c[6]}-"
+                                                           f"{c[8]}")
+def test_fwd_ex_distance_bias_sweep(device, case):
+    """A bucketed distance-bias table (distinct per query head, also inside
+    one group), every element against the oracle."""
+    B, Hq, Hkv, Sq, Skv, D, mask, window, layout = case
+    table = workloads.make_distance_bias(Hq, Sq, Skv, seed=Sq + Skv + D)
+    err = run_ex(device, B, Hq, Hkv, Sq, Skv, D, mask, window, layout, layout,
+                 seed=Sq + 5 * Skv + D, dist_bias=table)
+    assert err <= TOL["bf16"], err
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("scale", [0.0, -0.1, 0.5])
+@pytest.mark.parametrize("D", [64, 128])
+def test_fwd_ex_distance_bias_scales_and_steep(device, scale, D):
+    """Zero and negative scales, and a steep table (a row's weight sits on a
+    few distances, -30 elsewhere), so the bias alone picks the keys.  Outputs
+    are then close to single value rows (|O| up to about 4.5), where rounding
+    O to bf16 alone (P rounded to bf16, O rounded once, to nearest even) may
+    be off by half a unit in the last place, 2^-8 |O|: the check allows that
+    on top of the bf16 tolerance."""
+    rng = np.random.default_rng(41)
+    Sq, Skv = 130, 700
+    table = (rng.standard_normal((4, Sq + Skv - 1)) * 4.0).astype(np.float32)
+    table[:, rng.random(Sq + Skv - 1) < 0.8] = -30.0
+    for mask in ("full", "causal"):
+        err = run_ex(device, 1, 4, 2, Sq, Skv, D, mask, seed=37, scale=scale, dist_bias=table,
+                     rel=2.0 ** -8)
+        assert err <= TOL["bf16"], (mask, err)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("D", [64, 128])
+def test_fwd_ex_distance_bias_as_alibi(device, D):
+    """The table -m_a |d| gives ALiBi's result (two kernels, same inputs)."""
+    import torch
+
+    B, Hq, Hkv, Sq, Skv = 2, 8, 2, 200, 333
+    slopes = workloads.make_alibi_slopes(Hq)
+    d = np.arange(Sq + Skv - 1) - (Skv - 1)
+    table = (-slopes[:, None].astype(np.float64) * np.abs(d)[None, :]).astype(np.float32)
+    rng = np.random.default_rng(42)
+    q = torch.from_numpy(workloads.draw((B, Hq, Sq, D), rng)).to(torch.bfloat16).to(device)
+    k = torch.from_numpy(workloads.draw((B, Hkv, Skv, D), rng)).to(torch.bfloat16).to(device)
+    v = torch.from_numpy(workloads.draw((B, Hkv, Skv, D), rng)).to(torch.bfloat16).to(device)
+    for mask in ("full", "causal", "causal_window"):
+        a = attn.fwd_ex(q, k, v, mask=mask, window=77,
+                        alibi_slopes=torch.from_numpy(slopes).to(device))
+        b = attn.fwd_ex(q, k, v, mask=mask, window=77, dist_bias=torch.from_numpy(table).to(device))
+        torch.cuda.synchronize()
+        err = (a.float() - b.float()).abs().max().item()
+        assert err <= TOL["bf16"], (mask, err)
+
+
 RAGGED = [
     # (B, Hq, Hkv, Sq, Skv, D, mask, window, q_len, kv_len, alibi)
     (4, 8, 2, 300, 300, 128, "causal", 0, (300, 1, 129, 0), (300, 1, 129, 0), False),
@@ -171,6 +243,18 @@ def test_fwd_ex_padded_batches(device, case):
         err = run_ex(device, B, Hq, Hkv, Sq, Skv, D, mask, window, layout, layout,
                      seed=Sq + Skv + B, slopes=slopes, q_len=q_len, kv_len=kv_len)
         assert err <= TOL["bf16"], (layout, err)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: f"D{c[5]}-Sq{c[3]}-Skv{c[4]}-{c[6]}")
+def test_fwd_ex_distance_bias_padded_batches(device, case):
+    """The distance bias on the same padded batches (each sequence's own
+    positions index the table)."""
+    B, Hq, Hkv, Sq, Skv, D, mask, window, q_len, kv_len, _ = case
+    table = workloads.make_distance_bias(Hq, Sq, Skv, seed=B + D)
+    err = run_ex(device, B, Hq, Hkv, Sq, Skv, D, mask, window, "bshd", "bhsd",
+                 seed=Sq + Skv + B + 1, q_len=q_len, kv_len=kv_len, dist_bias=table)
+    assert err <= TOL["bf16"], err
 
 
 @pytest.mark.gpu
@@ -328,6 +412,7 @@ def test_fwd_ex_workload_full_size(device, name):
 def ex_status(**kw):
     a = attn.FwdArgs()
     a.alibi_slopes, a.q_len, a.kv_len, a.global_idx, a.n_global = None, None, None, None, 0
+    a.dist_bias = None
     base = 0x1000000
     a.q, a.k, a.v, a.o = base, base * 3, base * 5, base * 7
     a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = 1, 8, 2, 100, 300, 128
@@ -380,3 +465,13 @@ def test_fwd_ex_rejects_bad_arguments():
     assert ex_status(alibi_slopes=0x2000000, scale=1e-30) == "ATTN_ERR_SCALE"
     assert ex_status(alibi_slopes=0x7000000 + 64) == "ATTN_ERR_ALIAS"  # slopes inside o
     assert ex_status(kv_len=0x7000000) == "ATTN_ERR_ALIAS"             # lengths inside o
+    # distance bias: general masks only, not with ALiBi or a layout
+    assert ex_status(dist_bias=0x2000000, mask_kind=3) == "ATTN_ERR_UNSUPPORTED"
+    assert ex_status(dist_bias=0x2000000, alibi_slopes=0x3000000) == "ATTN_ERR_UNSUPPORTED"
+    assert ex_status(dist_bias=0x2000000, block_layout=0x3000000) == "ATTN_ERR_UNSUPPORTED"
+    assert ex_status(dist_bias=0x2000002) == "ATTN_ERR_ALIGN"
+    assert ex_status(dist_bias=0x2000000, scale=1e-30) == "ATTN_ERR_SCALE"
+    assert ex_status(dist_bias=0x7000000 + 4096) == "ATTN_ERR_ALIAS"  # table inside o
+    assert ex_status(dist_bias=0x6FFFF00) == "ATTN_ERR_ALIAS"         # table runs into o
+    assert ex_status(dist_bias=0x2000000, Sq=1 << 28, Skv=(1 << 28) + 1,
+                     q_stride=[0, 0, 128], o_stride=[0, 0, 128]) == "ATTN_ERR_SHAPE"

@@ -61,6 +61,7 @@ class FwdArgs(ctypes.Structure):
         ("alibi_slopes", ctypes.c_void_p), ("q_len", ctypes.c_void_p),
         ("kv_len", ctypes.c_void_p), ("block_layout", ctypes.c_void_p),
         ("global_idx", ctypes.c_void_p), ("n_global", ctypes.c_int),
+        ("dist_bias", ctypes.c_void_p),
     ]
 
 
@@ -243,7 +244,7 @@ def layout_bigbird(nb: int, radius_blocks: int, n_global_blocks: int, rand_block
 
 def fwd_ex(q, k, v, mask="causal", window: int = 0, scale: Optional[float] = None, out=None,
            stream=None, alibi_slopes=None, q_len=None, kv_len=None, block_layout=None,
-           global_idx=None):
+           global_idx=None, dist_bias=None):
     """Forward pass with Sq != Skv and strided layouts (bf16).
 
     q: [B, Hq, Sq, D], k, v: [B, Hkv, Skv, D] as torch views of any strides
@@ -254,7 +255,9 @@ def fwd_ex(q, k, v, mask="causal", window: int = 0, scale: Optional[float] = Non
     alibi_slopes float32 [Hq] (ALiBi), q_len and kv_len int32 [B] (valid rows
     and keys per sequence of a right-padded batch; padded rows come out zero),
     block_layout int32 [nb, words] (a layout_* bitmask on the GPU: block-sparse
-    attention over blocks of 64 positions).  global_idx: host sequence of
+    attention over blocks of 64 positions), dist_bias float32 [Hq, Sq + Skv - 1]
+    (entry d + Skv - 1 of row a is added to head a's scaled scores at signed
+    distance d = key position - query position).  global_idx: host sequence of
     global key positions for mask "local_global".
     """
     import torch
@@ -273,7 +276,7 @@ def fwd_ex(q, k, v, mask="causal", window: int = 0, scale: Optional[float] = Non
     elif tuple(out.shape) != (B, Hq, Sq, D) or out.dtype != q.dtype or out.stride(3) != 1:
         raise ValueError("out must be shaped like q with a contiguous last dim")
     check_devices(q, k=k, v=v, out=out, alibi_slopes=alibi_slopes, q_len=q_len,
-                  kv_len=kv_len, block_layout=block_layout)
+                  kv_len=kv_len, block_layout=block_layout, dist_bias=dist_bias)
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
     a = FwdArgs()
@@ -287,7 +290,8 @@ def fwd_ex(q, k, v, mask="causal", window: int = 0, scale: Optional[float] = Non
                                ("q_len", q_len, torch.int32, (B,)),
                                ("kv_len", kv_len, torch.int32, (B,)),
                                ("block_layout", block_layout, torch.int32,
-                                (nb, layout_words(nb)))):
+                                (nb, layout_words(nb))),
+                               ("dist_bias", dist_bias, torch.float32, (Hq, Sq + Skv - 1))):
         if t is None:
             setattr(a, name, None)
             continue

@@ -343,9 +343,14 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
   if (a->D != 64 && a->D != 128) return ATTN_ERR_UNSUPPORTED;
   if (a->mask_kind < ATTN_MASK_FULL || a->mask_kind > ATTN_MASK_LOCAL_GLOBAL)
     return ATTN_ERR_UNSUPPORTED;
-  // local+global: not with ALiBi or a block-sparse layout
-  if (a->mask_kind == ATTN_MASK_LOCAL_GLOBAL && (a->alibi_slopes || a->block_layout))
+  // local+global: not with ALiBi, a block-sparse layout or a distance bias;
+  // a distance bias: not with ALiBi or a layout either
+  if (a->mask_kind == ATTN_MASK_LOCAL_GLOBAL &&
+      (a->alibi_slopes || a->block_layout || a->dist_bias))
     return ATTN_ERR_UNSUPPORTED;
+  if (a->dist_bias && (a->alibi_slopes || a->block_layout)) return ATTN_ERR_UNSUPPORTED;
+  // distance-bias rows of Sq + Skv - 1 fp32 values, byte offsets in 31 bits
+  if (a->dist_bias && (long long)a->Sq + a->Skv > (1LL << 29)) return ATTN_ERR_SHAPE;
   if (a->Hq % a->Hkv != 0) return ATTN_ERR_HEADS;
   if (a->mask_kind == ATTN_MASK_CAUSAL_WINDOW && a->window < 1) return ATTN_ERR_WINDOW;
   if (a->mask_kind == ATTN_MASK_LOCAL_GLOBAL && a->window < 0) return ATTN_ERR_WINDOW;
@@ -367,7 +372,8 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
   for (const void* ptr : {a->q, a->k, a->v, (const void*)a->o})
     if ((uintptr_t)ptr % 16 != 0) return ATTN_ERR_ALIGN;
   for (const void* ptr : {(const void*)a->alibi_slopes, (const void*)a->q_len,
-                          (const void*)a->kv_len, (const void*)a->block_layout})
+                          (const void*)a->kv_len, (const void*)a->block_layout,
+                          (const void*)a->dist_bias})
     if ((uintptr_t)ptr % 4 != 0) return ATTN_ERR_ALIGN;
   // block-sparse layouts: square, at most ATTN_SPARSE_MAX_BLOCKS blocks, full or
   // causal mask, no bias or lengths
@@ -375,8 +381,9 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
       (a->Sq != a->Skv || a->Sq > ATTN_SPARSE_MAX_BLOCKS * ATTN_SPARSE_BLOCK ||
        a->mask_kind == ATTN_MASK_CAUSAL_WINDOW || a->alibi_slopes || a->q_len || a->kv_len))
     return ATTN_ERR_UNSUPPORTED;
-  // ALiBi slopes are turned into score units by 1 / |scale|
-  if (a->alibi_slopes && a->scale != 0.f && std::fabs(a->scale) < 0x1p-60f) return ATTN_ERR_SCALE;
+  // ALiBi slopes and distance biases are turned into score units by 1 / |scale|
+  if ((a->alibi_slopes || a->dist_bias) && a->scale != 0.f && std::fabs(a->scale) < 0x1p-60f)
+    return ATTN_ERR_SCALE;
   const long long* strides[4] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride};
   for (const long long* st : strides) {
     for (int d = 0; d < 3; ++d)
@@ -397,7 +404,9 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
     return ATTN_ERR_ALIAS;
   if ((a->alibi_slopes && overlaps(a->o, no, a->alibi_slopes, (size_t)a->Hq * 4)) ||
       (a->q_len && overlaps(a->o, no, a->q_len, (size_t)a->B * 4)) ||
-      (a->kv_len && overlaps(a->o, no, a->kv_len, (size_t)a->B * 4)))
+      (a->kv_len && overlaps(a->o, no, a->kv_len, (size_t)a->B * 4)) ||
+      (a->dist_bias &&
+       overlaps(a->o, no, a->dist_bias, (size_t)a->Hq * ((size_t)a->Sq + a->Skv - 1) * 4)))
     return ATTN_ERR_ALIAS;
   const int lay_nb = (a->Sq + ATTN_SPARSE_BLOCK - 1) / ATTN_SPARSE_BLOCK;
   const int lay_nw = ATTN_LAYOUT_WORDS(lay_nb);
@@ -437,7 +446,9 @@ int attn_fwd_ex(const attn_fwd_args* a, void* stream) {
   p.qlen = a->q_len;
   p.kvlen = a->kv_len;
   p.slopes = a->alibi_slopes;
-  p.alibi_k = a->scale != 0.f ? 1.f / std::fabs(a->scale) : 1.4426950408889634f;
+  p.bias_k = a->scale != 0.f ? 1.f / std::fabs(a->scale) : 1.4426950408889634f;
+  p.bias = a->dist_bias;
+  p.bias_len = a->Sq + a->Skv - 1;
   p.layout = a->block_layout;
   p.lay_nw = lay_nw;
   std::copy(gpos, gpos + n_global, p.gpos);

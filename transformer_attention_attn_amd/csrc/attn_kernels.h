@@ -30,7 +30,12 @@ struct KParams {
   const int* qlen;       // device, B valid query rows per sequence, or null (all Sq)
   const int* kvlen;      // device, B valid keys per sequence, or null (all Skv)
   const float* slopes;   // device, Hq ALiBi slopes, or null (no bias)
-  float alibi_k;         // slope -> score units: 1 / |scale|, or log2(e) for scale 0
+  float bias_k;          // ALiBi slope or distance bias -> score units: 1 / |scale|,
+                         // or log2(e) for scale 0
+  const float* bias;     // device [Hq][bias_len] distance-bias table, or null: entry
+                         // d + Skv - 1 of row a is added to query head a's logits at
+                         // signed distance d = key position - query position
+  int bias_len;          // Sq + Skv - 1
   const unsigned* layout;  // device block-sparse layout (64-position blocks), or null
   int lay_nw;              // words per layout row
 };

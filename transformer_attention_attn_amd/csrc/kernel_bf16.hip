@@ -239,6 +239,8 @@ constexpr int kWavesPerEu = HD == 64 ? 4 : 2;
 // local+global mask the global indices are key positions (a global query is
 // row gpos - off of its sequence).  GEN = 2: GEN = 1 plus the ALiBi
 // bias.  GEN = 3: GEN = 1 with a block-sparse layout (square, no lengths).
+// GEN = 4: GEN = 1 plus a distance-bias table (masks FULL, CAUSAL and
+// CAUSAL_WINDOW).
 // LDS for the global token positions, only in kernels of the local+global
 // mask (the persistent kernels use all 160 KB otherwise)
 template <bool LG>
@@ -257,6 +259,7 @@ void attn_fwd_bf16(KParams p_arg) {
   using C = Cfg<D>;
   constexpr bool ALIBI = GEN == 2;
   constexpr bool SPARSE = GEN == 3;
+  constexpr bool DBIAS = GEN == 4;
   constexpr int NDC = C::NDC, NDB = C::NDB, ROWB = C::ROWB, REG = C::REG, BUF = C::BUF,
                 NGL = C::NGL, RSTEP = C::RSTEP, NSTAGE = C::NSTAGE, VSH = C::VSH;
 
@@ -266,9 +269,15 @@ void attn_fwd_bf16(KParams p_arg) {
   // PERS: the next item's Q of wave group 0 (32 rows per wave, laid out like
   // the first 32 rows of a K tile)
   constexpr int LDS_Q = PERS ? 4 * 32 * ROWB : 0;
-  static_assert(LDS_MAIN + LDS_Q + (MASK == MASK_LOCAL_GLOBAL ? kMaxGlobal * 4 : 0) <= 160 * 1024,
+  // DBIAS: per wave, the table entries one tile's scores of its 32 rows use
+  // (BN + 31 consecutive distances), loaded 64 entries per direct load
+  constexpr int NBD = (BN + 31 + 63) / 64;
+  constexpr int LDS_B = DBIAS ? kBf16Waves * NBD * 256 : 0;
+  static_assert(LDS_MAIN + LDS_Q + LDS_B + (MASK == MASK_LOCAL_GLOBAL ? kMaxGlobal * 4 : 0) <=
+                    160 * 1024,
                 "LDS budget of one CU");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_MAIN + LDS_Q];
+  static_assert(!DBIAS || (!PERS && MASK != MASK_LOCAL_GLOBAL), "distance bias: general masks");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_MAIN + LDS_Q + LDS_B];
   int* const gpos_s = gpos_storage<MASK == MASK_LOCAL_GLOBAL>();
 
   const int tid = threadIdx.x;
@@ -365,7 +374,7 @@ void attn_fwd_bf16(KParams p_arg) {
   // ALiBi: the head's slope in units of the scores below (q.k, or log2 units
   // when the scale is zero), and this lane's query position
   float slope_u = 0.f;
-  if constexpr (ALIBI) slope_u = p.slopes[a] * p.alibi_k;
+  if constexpr (ALIBI) slope_u = p.slopes[a] * p.bias_k;
   const int q_pos = q_row + OFF;
 
   const size_t S = (size_t)s.S;
@@ -893,6 +902,9 @@ void attn_fwd_bf16(KParams p_arg) {
       for (int t = 0; t < 8; ++t) pb[pc][t] = (__bf16)0.f;
   };
   zero_p();
+  // DBIAS: direct loads issued after this wave's table entries of the last S
+  // it computed (its next softmax waits for all but these)
+  int bias_after = 0;
 
   // ---- the matrix block of one step --------------------------------------
   // O^T += V(jv)^T P(jv)^T (if do_pv), then S(js) = K(js) Q^T (if do_s), as
@@ -904,7 +916,8 @@ void attn_fwd_bf16(KParams p_arg) {
   // V(dj - 1) into its own stage.  No loads where dj < 0.
   constexpr int NDMA = NSTAGE == 2 ? 2 * NGL : NGL;
   // mode: ModeC<2> (P.V then S), ModeC<0> (P.V only) or ModeC<1> (S only)
-  auto mfma_block_m = [&](auto mode, int jv, bool do_pv, int js, bool do_s, bool dk, int dj, int dst) {
+  auto mfma_block_m = [&](auto mode, int jv, bool do_pv, int js, bool do_s, bool dk, int dj,
+                          int dst) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode)::value;
     if constexpr (MODE == 0) do_s = false;
     if constexpr (MODE == 1) do_pv = false;
@@ -930,6 +943,24 @@ void attn_fwd_bf16(KParams p_arg) {
       do_dma(NDMA);
       return;
     }
+    if constexpr (DBIAS) {
+      if (do_s) {
+        // the table entries of S(js) into this wave's region, before the tile
+        // loads of the block: entry t0 + x lands in slot x, where t0 belongs to
+        // the tile's first key and the wave's last row.  Entries are clamped
+        // into the head's row; only masked pairs ever use a clamped one.
+        const int t0 = tile_kt(js) * BN - (wqa + 31 + OFF) + s.Sk - 1;
+        const __amdgpu_buffer_rsrc_t br =
+            uniform_rsrc(p.bias + (size_t)a * p.bias_len, p.bias_len * 4);
+        unsigned char* bdst = smem + LDS_MAIN + LDS_Q + wave * NBD * 256;
+#pragma unroll
+        for (int n = 0; n < NBD; ++n) {
+          const int t = imin(imax(t0 + 64 * n + lane, 0), p.bias_len - 1);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void_t*)(bdst + n * 256), 4, t * 4, 0, 0, 0);
+        }
+        bias_after = dj >= 0 ? NDMA : 0;
+      }
+    }
     __builtin_amdgcn_s_setprio(1);
     // One sequence for every block of a mode.  Where P.V is not needed, P is
     // zero (the softmax of that tile was skipped) and its operands are read
@@ -952,12 +983,28 @@ void attn_fwd_bf16(KParams p_arg) {
     block_run<MODE, ROWB, NDB, NDC, NKB, NDMA>(vbd, kbd, pb, qf, oacc, scur, do_dma);
     __builtin_amdgcn_s_setprio(0);
   };
-  auto mfma_block = [&](int jv, bool do_pv, int js, bool do_s, bool dk, int dj, int dst) {
+  auto mfma_block = [&](int jv, bool do_pv, int js, bool do_s, bool dk, int dj,
+                        int dst) __attribute__((always_inline)) {
     mfma_block_m(ModeC<2>{}, jv, do_pv, js, do_s, dk, dj, dst);
   };
 
   // ---- online softmax of S(j): mask, running maximum, weights P(j) and l -----
-  auto softmax = [&](int j) {
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    if constexpr (DBIAS) {
+      // the table entries of S(j) have landed once only the tile loads issued
+      // after them may be in flight; register r of block kbk (key 32*kbk +
+      // 8*(r/4) + 4*hf + r%4 of the tile) takes slot key + 31 - l32.  Added
+      // before the mask, which overwrites every pair it hides.
+      if (bias_after == 0) __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_enc(NDMA));
+      const float* bl =
+          (const float*)(smem + LDS_MAIN + LDS_Q + wave * NBD * 256) + (31 - l32) + 4 * hf;
+#pragma unroll
+      for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          scur[kbk][r] = __builtin_fmaf(bl[kbk * 32 + 8 * (r >> 2) + (r & 3)], p.bias_k, scur[kbk][r]);
+    }
     if (tile_partial(j)) {
       asm volatile("");  // keep this a branch: full tiles skip it
       apply_mask(scur, j);
@@ -1344,6 +1391,14 @@ hipError_t launch_d(const KParams& p, hipStream_t stream) {
   if (p.general && p.layout) {
     if (p.s.mask == MASK_FULL) hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_FULL, 3>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL, 3>), grid, block, 0, stream, p);
+    return hipGetLastError();
+  }
+  if (p.general && p.bias) {
+    switch (p.s.mask) {
+      case MASK_FULL: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_FULL, 4>), grid, block, 0, stream, p); break;
+      case MASK_CAUSAL: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL, 4>), grid, block, 0, stream, p); break;
+      default: hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL_WINDOW, 4>), grid, block, 0, stream, p); break;
+    }
     return hipGetLastError();
   }
   if (p.general && p.slopes) {

@@ -270,6 +270,27 @@ def make_alibi_slopes(H: int) -> np.ndarray:
     return np.exp2(-8.0 * (np.arange(H, dtype=np.float64) + 1.0) / H).astype(np.float32)
 
 
+def make_distance_bias(Hq: int, Sq: int, Skv: int, seed: int, buckets: int = 32,
+                       max_distance: int = 128) -> np.ndarray:
+    """Synthetic distance-bias table, float32 [Hq][Sq + Skv - 1]: entry
+    d + Skv - 1 of row a holds the value of the bucket of the signed distance
+    d, as a learned relative-position bias would (the pages fix no values;
+    this is an input recipe).  Half the buckets serve d < 0, half d >= 0;
+    within each half, |d| < 8 get a bucket each, longer distances share
+    log-spaced buckets up to max_distance, beyond which all share the last.
+    Bucket values are N(0, 1.5^2) from default_rng(seed + 3000)."""
+    rng = np.random.default_rng(seed + 3000)
+    vals = rng.standard_normal((Hq, buckets)) * 1.5
+    half = buckets // 2
+    exact = half // 2
+    d = np.arange(Sq + Skv - 1, dtype=np.int64) - (Skv - 1)
+    n = np.abs(d)
+    logb = exact + np.floor(np.log(np.maximum(n, 1) / exact) / np.log(max_distance / exact)
+                            * (half - exact)).astype(np.int64)
+    b = np.where(n < exact, n, np.minimum(logb, half - 1)) + np.where(d >= 0, half, 0)
+    return np.ascontiguousarray(vals[:, b], dtype=np.float32)
+
+
 def make_ragged_lengths(B: int, Sq: int, Skv: int, seed: int):
     """Per-sequence valid lengths of a right-padded batch, drawn uniformly from
     [Skv/4, Skv] for the keys with default_rng(seed + 2000); the query count is
