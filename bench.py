@@ -373,6 +373,7 @@ def ex_cpu_baseline(w, inputs, seconds: float = 10.0):
     threads = host_threads()
     G = w.Hq // w.Hkv
     slopes = w.alibi_slopes()
+    table = w.distance_bias()
     q_len, kv_len = w.lengths_qkv()
     lay = None
     if w.pattern:  # the oracle's own layout of the pattern
@@ -395,7 +396,8 @@ def ex_cpu_baseline(w, inputs, seconds: float = 10.0):
             w.mask, w.window, scale=w.scale,
             alibi_slopes=None if slopes is None else slopes[a:a + 1].astype(np.float64),
             q_len=None if q_len is None else q_len[:1],
-            kv_len=None if kv_len is None else kv_len[:1], global_idx=w.global_idx))
+            kv_len=None if kv_len is None else kv_len[:1], global_idx=w.global_idx,
+            dist_bias=None if table is None else table[a:a + 1]))
     dt = time.perf_counter() - t0
     n = len(refs)
     flops = ex_effective_flops(w, batches=[0]) / w.Hq * n
@@ -573,8 +575,8 @@ def bench_ex(args, name):
     q, k, v = (place(inputs[n + "_bits"]) for n in ("q", "k", "v"))
     slopes = w.alibi_slopes()
     q_len, kv_len = w.lengths_qkv()
-    slopes_d, q_len_d, kv_len_d = (None if x is None else torch.from_numpy(x).to(dev)
-                                   for x in (slopes, q_len, kv_len))
+    slopes_d, q_len_d, kv_len_d, bias_d = (None if x is None else torch.from_numpy(x).to(dev)
+                                           for x in (slopes, q_len, kv_len, w.distance_bias()))
     words = ex_layout_words(w)
     layout_d = None if words is None else torch.from_numpy(words.view(np.int32)).to(dev)
     if w.layout == "bshd":
@@ -589,7 +591,8 @@ def bench_ex(args, name):
     def step():
         attn.fwd_ex(q, k, v, mask=w.mask, window=w.window, scale=w.scale, out=out,
                     stream=stream, alibi_slopes=slopes_d, q_len=q_len_d, kv_len=kv_len_d,
-                    block_layout=layout_d, global_idx=list(w.global_idx) or None)
+                    block_layout=layout_d, global_idx=list(w.global_idx) or None,
+                    dist_bias=bias_d)
 
     ms, prewarm_steps, spread = time_steps(step, stream, args)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -611,7 +614,8 @@ def bench_ex(args, name):
         "data": "synthetic",
         "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq,
                    "Skv": w.Skv, "D": w.D, "mask": w.mask, "window": w.window,
-                   "layout": w.layout, "alibi": w.alibi, "lengths": w.lengths,
+                   "layout": w.layout, "alibi": w.alibi, "dist_bias": w.dist_bias,
+                   "lengths": w.lengths,
                    "pattern": w.pattern, "pattern_args": list(w.pattern_args),
                    "effective_flops": flops, "parallelism": "none"},
         "pct_peak": round(100.0 * tflops / peak, 2),

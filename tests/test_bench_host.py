@@ -97,3 +97,20 @@ def test_layout_pairs_match_oracle(S, causal):
         for J in np.nonzero(lay[I])[0]:
             words[I, J // 32] |= np.uint32(1) << np.uint32(J % 32)
     assert bench.layout_pairs(words, S, causal) == sp.block_sparse_pairs(S, lay, 64, causal)
+
+
+def test_distance_bias_recipe():
+    """The bucketed distance-bias input: per-head rows over d = -(Skv-1) ..
+    Sq-1, one value per distance below 8 on each side, shared log buckets
+    further out, a single value past the maximum distance on each side."""
+    import numpy as np
+
+    Sq, Skv, Hq = 300, 700, 3
+    t = workloads.make_distance_bias(Hq, Sq, Skv, seed=4)
+    assert t.shape == (Hq, Sq + Skv - 1) and t.dtype == np.float32 and t.flags["C_CONTIGUOUS"]
+    at = lambda d: t[:, d + Skv - 1]  # noqa: E731
+    near = [tuple(at(d)) for d in range(-7, 8)]
+    assert len(set(near)) == 15  # distinct buckets for |d| < 8 on either side (and 0)
+    assert np.array_equal(at(200), at(Sq - 1)) and np.array_equal(at(-200), at(-(Skv - 1)))
+    assert not np.array_equal(at(200), at(-200))
+    assert np.array_equal(workloads.make_distance_bias(Hq, Sq, Skv, seed=4), t)

@@ -380,11 +380,12 @@ def test_fwd_ex_workload_full_size(device, name):
     q, k, v = (place(inp[n + "_bits"], w.layout, device) for n in ("q", "k", "v"))
     o = empty_out(w.B, w.Hq, w.Sq, w.D, w.layout, device)
     slopes = w.alibi_slopes()
+    table = w.distance_bias()
     q_len, kv_len = w.lengths_qkv()
     dev = lambda x: None if x is None else torch.from_numpy(x).to(device)  # noqa: E731
     attn.fwd_ex(q, k, v, mask=w.mask, window=w.window, scale=w.scale, out=o,
                 alibi_slopes=dev(slopes), q_len=dev(q_len), kv_len=dev(kv_len),
-                global_idx=list(w.global_idx) or None)
+                global_idx=list(w.global_idx) or None, dist_bias=dev(table))
     torch.cuda.synchronize()
     got = o.float().cpu().numpy()
     rng = np.random.default_rng(w.seed + 5)
@@ -399,7 +400,8 @@ def test_fwd_ex_workload_full_size(device, name):
             w.mask, w.window, scale=w.scale, rows=rows,
             alibi_slopes=None if slopes is None else slopes[a:a + 1].astype(np.float64),
             q_len=None if q_len is None else q_len[b:b + 1],
-            kv_len=None if kv_len is None else kv_len[b:b + 1], global_idx=w.global_idx)
+            kv_len=None if kv_len is None else kv_len[b:b + 1], global_idx=w.global_idx,
+            dist_bias=None if table is None else table[a:a + 1])
         err = float(np.max(np.abs(got[b, a, rows].astype(np.float64) - ref[0, 0])))
         print(f"{name} b={b} a={a}: max abs err {err:.3e}", flush=True)
         assert err <= TOL["bf16"], (b, a, err)

@@ -192,6 +192,7 @@ class ExWorkload:
     pattern: str = ""
     pattern_args: Tuple[int, ...] = ()
     global_idx: Tuple[int, ...] = ()  # local_global: global key positions
+    dist_bias: bool = False  # a distance-bias table, that of distance_bias()
 
     @property
     def scale(self) -> float:
@@ -200,6 +201,11 @@ class ExWorkload:
     def alibi_slopes(self):
         """Hq slopes (float32) when alibi is set, else None."""
         return make_alibi_slopes(self.Hq) if self.alibi else None
+
+    def distance_bias(self):
+        """The [Hq][Sq + Skv - 1] float32 distance-bias table when dist_bias is
+        set, else None."""
+        return make_distance_bias(self.Hq, self.Sq, self.Skv, self.seed) if self.dist_bias else None
 
     def n_blocks(self) -> int:
         return -(-self.Sq // SPARSE_BLOCK)
@@ -238,6 +244,10 @@ EX_WORKLOADS = {
         # causal prefill of a right-padded batch with ALiBi instead of positions in q/k
         ExWorkload("alibi_padded_mha_bf16_b8_s4096", 8, 32, 32, 4096, 4096, 128, MASK_CAUSAL,
                    "bhsd", seed=11, alibi=True, lengths="ragged"),
+        # the same padded causal prefill with a bucketed relative-position bias
+        # per head (one learned value per distance bucket) instead of ALiBi
+        ExWorkload("relbias_padded_mha_bf16_b8_s4096", 8, 32, 32, 4096, 4096, 128, MASK_CAUSAL,
+                   "bhsd", seed=15, lengths="ragged", dist_bias=True),
         # Big Bird: window of 3 blocks, 2 global blocks, 3 random blocks per row
         ExWorkload("bigbird_bf16_b4_h12_s4096", 4, 12, 12, 4096, 4096, 64, MASK_FULL, "bhsd",
                    seed=12, pattern="bigbird", pattern_args=(1, 2, 3)),
