@@ -80,11 +80,11 @@ typedef enum {
 #define ATTN_MAX_GLOBAL 64
 
 /* Block-sparse layouts (attn_fwd_ex's block_layout): blocks of 64 positions,
- * at most 128 blocks (8192 positions); row I of a layout holds
+ * at most 512 blocks (32768 positions); row I of a layout holds
  * ATTN_LAYOUT_WORDS(nb) uint32 words, bit J % 32 of word J / 32 set when query
  * block I may look at key block J. */
 #define ATTN_SPARSE_BLOCK 64
-#define ATTN_SPARSE_MAX_BLOCKS 128
+#define ATTN_SPARSE_MAX_BLOCKS 512
 #define ATTN_LAYOUT_WORDS(nb) (((nb) + 31) / 32)
 
 /*
@@ -175,7 +175,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o,
  *                 section 8.3: sparse patterns, run as block-sparse products
  *                 per 8.3.4).  Key j is visible from query i only when bit
  *                 j / 64 of row i / 64 is set, in addition to the mask kind.
- *                 Needs Sq == Skv <= 8192, mask FULL or CAUSAL, no ALiBi and
+ *                 Needs Sq == Skv <= 32768, mask FULL or CAUSAL, no ALiBi and
  *                 no lengths (else ATTN_ERR_UNSUPPORTED).  The attn_layout_*
  *                 builders below write the pages' patterns; any layout works.
  *                 A query whose row sees no key is written as zeros.

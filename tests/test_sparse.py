@@ -56,7 +56,7 @@ def test_builders_match_oracle(nb):
 
 
 def test_builders_reject_bad_arguments():
-    for call in (lambda: attn.layout_strided(0, 1, 1), lambda: attn.layout_strided(129, 1, 1),
+    for call in (lambda: attn.layout_strided(0, 1, 1), lambda: attn.layout_strided(513, 1, 1),
                  lambda: attn.layout_strided(8, -1, 1), lambda: attn.layout_strided(8, 1, 0),
                  lambda: attn.layout_fixed(8, 0),
                  lambda: attn.layout_bigbird(8, 1, 1, np.full((8, 1), 8)),
@@ -91,7 +91,7 @@ def test_block_layout_validation():
     assert sparse_status(mask_kind=2, window=10) == "ATTN_ERR_UNSUPPORTED"
     assert sparse_status(alibi_slopes=0x2000000) == "ATTN_ERR_UNSUPPORTED"
     assert sparse_status(q_len=0x2000000) == "ATTN_ERR_UNSUPPORTED"
-    S = 8256
+    S = 32768 + 64  # one block past the longest layout
     assert sparse_status(Sq=S, Skv=S, q_stride=[8 * S * 128, S * 128, 128],
                          k_stride=[2 * S * 128, S * 128, 128], v_stride=[2 * S * 128, S * 128, 128],
                          o_stride=[8 * S * 128, S * 128, 128]) == "ATTN_ERR_UNSUPPORTED"
@@ -206,6 +206,25 @@ def test_all_ones_layout_equals_dense(device, D):
         b = attn.fwd_ex(q, k, v, mask=mask, block_layout=ones)
         torch.cuda.synchronize()
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), mask
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("S,mask,density", [(32768, "full", 0.45), (32768, "causal", 0.9),
+                                            (20001, "full", 0.8), (12345, "causal", 0.35)])
+def test_sparse_long_sequences(device, D, S, mask, density):
+    """Layouts up to the 512-block limit (32768 positions), dense enough that
+    an item's tile list fills several list registers (up to 256 tiles of 128
+    keys, 512 of 64); sampled rows of every head against the oracle,
+    including the first and last rows of blocks and the ragged tail."""
+    nb = sp.n_blocks(S, 64)
+    rng = np.random.default_rng(S + D)
+    lay = random_layout(rng, nb, density, mask == "causal")
+    lay[np.arange(nb), np.arange(nb)] = True  # every row sees its own block
+    rows = sorted({0, 63, 64, 4095, 8192, S // 2, S - 65, S - 64, S - 1}
+                  | {int(x) for x in rng.integers(S, size=6)})
+    err = run_sparse(device, 1, 8, 2, S, D, mask, lay, seed=S % 997, rows=rows)
+    assert err <= TOL["bf16"], err
 
 
 def workload_layout_bool(w):

@@ -38,7 +38,7 @@ EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_plan", "attn_decode", "attn_decode_w
            "attn_status_string", "attn_version")
 
 SPARSE_BLOCK = 64          # positions per block of a block-sparse layout
-SPARSE_MAX_BLOCKS = 128    # longest block-sparse sequence: 8192 positions
+SPARSE_MAX_BLOCKS = 512    # longest block-sparse sequence: 32768 positions
 
 
 class AttnError(RuntimeError):

@@ -40,8 +40,10 @@ struct KParams {
   int lay_nw;              // words per layout row
 };
 
-// Longest sequence of a block-sparse call (its tile list lives in registers).
-constexpr int kSparseMaxKeys = 8192;
+// Longest sequence of a block-sparse call (its tile list lives in registers,
+// 64 tiles per register), and the longest the short-list kernels take.
+constexpr int kSparseMaxKeys = 32768;
+constexpr int kSparseShortKeys = 8192;
 
 // Workgroup shapes used by the two kernels.
 constexpr int kF32Rows = 16;   // query rows per fp32 work item (one head, 16 lanes per row)

@@ -238,7 +238,9 @@ constexpr int kWavesPerEu = HD == 64 ? 4 : 2;
 // of each tensor, optional per-sequence lengths (right padding); under the
 // local+global mask the global indices are key positions (a global query is
 // row gpos - off of its sequence).  GEN = 2: GEN = 1 plus the ALiBi
-// bias.  GEN = 3: GEN = 1 with a block-sparse layout (square, no lengths).
+// bias.  GEN = 3: GEN = 1 with a block-sparse layout (square, no lengths,
+// at most kSparseShortKeys positions); GEN = 5: the same up to kSparseMaxKeys
+// (a longer tile list).
 // GEN = 4: GEN = 1 plus a distance-bias table (masks FULL, CAUSAL and
 // CAUSAL_WINDOW).
 // LDS for the global token positions, only in kernels of the local+global
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(kBf16Threads) __attribute__((amdgpu_waves_per_eu(kW
 void attn_fwd_bf16(KParams p_arg) {
   using C = Cfg<D>;
   constexpr bool ALIBI = GEN == 2;
-  constexpr bool SPARSE = GEN == 3;
+  constexpr bool SPARSE = GEN == 3 || GEN == 5;
   constexpr bool DBIAS = GEN == 4;
   constexpr int NDC = C::NDC, NDB = C::NDB, ROWB = C::ROWB, REG = C::REG, BUF = C::BUF,
                 NGL = C::NGL, RSTEP = C::RSTEP, NSTAGE = C::NSTAGE, VSH = C::VSH;
@@ -418,7 +420,7 @@ void attn_fwd_bf16(KParams p_arg) {
   // 64-key halves that block may see, at bits 16 + 2*slot (both bits for a
   // 64-key tile).  Tiles past the item's last row are left out under the
   // causal mask.  Every wave builds the same list (no LDS, no barrier).
-  constexpr int NLV = SPARSE ? (kSparseMaxKeys / BN + 63) / 64 : 1;
+  constexpr int NLV = SPARSE ? ((GEN == 5 ? kSparseMaxKeys : kSparseShortKeys) / BN + 63) / 64 : 1;
   unsigned lv[NLV];
   int n_lv[NLV];
   int n_list = 0;
@@ -452,11 +454,21 @@ void attn_fwd_bf16(KParams p_arg) {
       n_list += cnt;
     }
   }
-  // list entry of iteration iter (past the end: the last one; tile 0 if none)
+  // list entry of iteration iter (past the end: the last one; tile 0 if none):
+  // register c holds entries [sum of n_lv below c, + n_lv[c]) in its first lanes
   auto entry = [&](int iter) -> unsigned {
-    const int t = imax(imin(iter, n_list - 1), 0);
-    if (NLV == 1 || t < n_lv[0]) return (unsigned)__builtin_amdgcn_readlane((int)lv[0], t);
-    return (unsigned)__builtin_amdgcn_readlane((int)lv[NLV - 1], t - n_lv[0]);
+    int t = imax(imin(iter, n_list - 1), 0);
+    if constexpr (NLV <= 2) {
+      if (NLV == 1 || t < n_lv[0]) return (unsigned)__builtin_amdgcn_readlane((int)lv[0], t);
+      return (unsigned)__builtin_amdgcn_readlane((int)lv[NLV - 1], t - n_lv[0]);
+    }
+    unsigned e = (unsigned)__builtin_amdgcn_readlane((int)lv[0], imin(t, 63));
+#pragma unroll
+    for (int c = 1; c < NLV; ++c) {
+      t -= n_lv[c - 1];
+      if (t >= 0 && t < n_lv[c]) e = (unsigned)__builtin_amdgcn_readlane((int)lv[c], t);
+    }
+    return e;
   };
   auto wave_code = [&](int iter) -> unsigned { return (entry(iter) >> (16 + 2 * wslot)) & 3u; };
 
@@ -1389,8 +1401,14 @@ template <int D>
 hipError_t launch_d(const KParams& p, hipStream_t stream) {
   dim3 grid((unsigned)p.s.n_items), block(kBf16Threads);
   if (p.general && p.layout) {
-    if (p.s.mask == MASK_FULL) hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_FULL, 3>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL, 3>), grid, block, 0, stream, p);
+    const bool full = p.s.mask == MASK_FULL;
+    if (p.s.S <= kSparseShortKeys) {
+      if (full) hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_FULL, 3>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL, 3>), grid, block, 0, stream, p);
+    } else {
+      if (full) hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_FULL, 5>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((attn_fwd_bf16<D, MASK_CAUSAL, 5>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
   }
   if (p.general && p.bias) {
