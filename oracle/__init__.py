@@ -41,7 +41,10 @@ from .sparse import (  # noqa: F401
     strided_layout,
 )
 from .fp8 import (  # noqa: F401
+    FP8_FORMATS,
     e4m3_decode,
+    e5m2_decode,
+    fp8_decode,
     fp8_attention,
     fp8_error_bound,
     fp8_tolerance,

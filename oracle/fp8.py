@@ -18,6 +18,16 @@ taken at face value.
   of that format (the OCP 8-bit float: 1 sign bit, 4 exponent bits with bias
   7, 3 mantissa bits, subnormals below 2^-6, no infinities, 0x7F / 0xFF NaN),
   written from the bit layout.
+* Or E5M2 codes (the page names both FP8 formats; ``fmt="e5m2"``):
+  ``e5m2_decode`` is that format's plain definition (OCP: 1 sign bit, 5
+  exponent bits with bias 15, 2 mantissa bits, subnormals below 2^-14,
+  exponent field 31 is infinity with a zero mantissa and NaN otherwise).
+  Reading: the weights P are still rounded to E4M3 for the P.V product (the
+  weights lie in [0, 1] after the row maximum is taken out, where E4M3's
+  extra mantissa bit is the better choice and E5M2's range is not needed),
+  so the bound below is the same for both input formats; a product of two
+  E5M2 values (3-bit significands) is as exact in fp32 as one of E4M3
+  values, so the score terms are unchanged too.
 * The reference output is exact masked attention (reference.py) on the decoded
   values: the score product of E4M3 inputs is exact, so the only rounding of
   the method that the oracle does not carry out is the E4M3 rounding of the
@@ -105,21 +115,47 @@ def e4m3_decode(codes):
     return np.where((c & 0x7F) == 0x7F, np.nan, val)
 
 
-def fp8_attention(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=None):
-    """Exact masked attention (float64) on the decoded E4M3 inputs."""
-    return reference.attention(e4m3_decode(q_codes), e4m3_decode(k_codes), e4m3_decode(v_codes),
-                               kind, window, (), scale=scale, rows=rows)
+def e5m2_decode(codes):
+    """Values (float64) of E5M2 codes (uint8 array)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 2) & 0x1F
+    m = c & 0x3
+    normal = sign * (1.0 + m / 4.0) * np.exp2(e - 15.0)
+    sub = sign * (m / 4.0) * 2.0 ** -14
+    val = np.where(e == 0, sub, normal)
+    val = np.where((e == 31) & (m == 0), sign * np.inf, val)
+    return np.where((e == 31) & (m != 0), np.nan, val)
+
+
+FP8_FORMATS = ("e4m3", "e5m2")
+
+
+def fp8_decode(codes, fmt="e4m3"):
+    """Values (float64) of FP8 codes in the given input format."""
+    if fmt == "e4m3":
+        return e4m3_decode(codes)
+    if fmt == "e5m2":
+        return e5m2_decode(codes)
+    raise ValueError(f"unknown FP8 format {fmt!r}")
+
+
+def fp8_attention(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=None, fmt="e4m3"):
+    """Exact masked attention (float64) on the decoded FP8 inputs."""
+    return reference.attention(fp8_decode(q_codes, fmt), fp8_decode(k_codes, fmt),
+                               fp8_decode(v_codes, fmt), kind, window, (), scale=scale, rows=rows)
 
 
 def fp8_error_bound(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=None,
-                    rounded_denominator=False):
+                    rounded_denominator=False, fmt="e4m3"):
     """Per-element bound (float64, shaped like the output) on the error the
     E4M3 rounding of P can cause: b with the denominator summed from the
     unrounded weights, b' with the denominator summed from the rounded ones
-    (``rounded_denominator``; inf where sum_j e_j >= L)."""
-    q = e4m3_decode(q_codes)
-    k = e4m3_decode(k_codes)
-    v = e4m3_decode(v_codes)
+    (``rounded_denominator``; inf where sum_j e_j >= L).  ``fmt``: the input
+    format of the codes."""
+    q = fp8_decode(q_codes, fmt)
+    k = fp8_decode(k_codes, fmt)
+    v = fp8_decode(v_codes, fmt)
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     if scale is None:
@@ -144,16 +180,17 @@ def fp8_error_bound(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=
 
 
 def fp8_tolerance(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=None,
-                  exact_weights=False, bf16_output=True, rounded_denominator=False):
+                  exact_weights=False, bf16_output=True, rounded_denominator=False, fmt="e4m3"):
     """Per-element bound (float64, shaped like the output) on |O_kernel -
     O_exact|: the E4M3 rounding of P (``fp8_error_bound``, left out when
     ``exact_weights``), the fp32 score, exponent and accumulation errors and,
     when ``bf16_output``, the bf16 rounding of the output (derivation in the
     module docstring).  ``rounded_denominator``: the kernel sums the
-    denominator from the rounded weights on the matrix cores."""
-    q = e4m3_decode(q_codes)
-    k = e4m3_decode(k_codes)
-    v = e4m3_decode(v_codes)
+    denominator from the rounded weights on the matrix cores.  ``fmt``: the
+    input format of the codes."""
+    q = fp8_decode(q_codes, fmt)
+    k = fp8_decode(k_codes, fmt)
+    v = fp8_decode(v_codes, fmt)
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     if scale is None:
@@ -164,7 +201,8 @@ def fp8_tolerance(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=No
     n_vis = vis.sum(axis=1, keepdims=True).astype(np.float64)
     exact = reference.attention(q, k, v, kind, window, (), scale=scale, rows=rows)
     b = np.zeros_like(exact) if exact_weights else \
-        fp8_error_bound(q_codes, k_codes, v_codes, kind, window, scale, rows, rounded_denominator)
+        fp8_error_bound(q_codes, k_codes, v_codes, kind, window, scale, rows, rounded_denominator,
+                        fmt)
     den_chain = (n_vis / 16 + 48) if rounded_denominator else (n_vis + 8)
     out = np.empty_like(exact)
     for bb in range(B):

@@ -1,7 +1,8 @@
 """Pins for the FP8 oracle (CPU only).
 
-e4m3_decode is checked against hand-decoded codes and against torch's own
-float8_e4m3fn type for all 256 codes.  fp8_error_bound is checked against a
+e4m3_decode and e5m2_decode are checked against hand-decoded codes and against
+torch's own float8_e4m3fn and float8_e5m2 types for all 256 codes; the
+simulations below decode their inputs with torch, and run for both formats.  fp8_error_bound is checked against a
 simulation of what it bounds: the weights of real rows rounded to E4M3 (by
 torch's conversion, round to nearest even) at several reference maxima below
 the true one, the output formed with the unrounded denominator (bound b) and
@@ -46,6 +47,39 @@ def test_e4m3_decode_matches_torch():
     assert np.array_equal(got[ok], t[ok])
 
 
+def test_e5m2_decode_by_hand():
+    codes = np.array([0x3C, 0x7B, 0x01, 0x03, 0x04, 0xC0, 0x00, 0x80, 0x3D, 0x4E], dtype=np.uint8)
+    want = [1.0, 57344.0, 2.0 ** -16, 3 * 2.0 ** -16, 2.0 ** -14, -2.0, 0.0, -0.0, 1.25, 24.0]
+    got = f8.e5m2_decode(codes)
+    assert list(got) == want
+    assert list(f8.e5m2_decode(np.array([0x7C, 0xFC], dtype=np.uint8))) == [np.inf, -np.inf]
+    assert np.isnan(f8.e5m2_decode(np.array([0x7D, 0x7E, 0x7F, 0xFF], dtype=np.uint8))).all()
+
+
+def test_e5m2_decode_matches_torch():
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    t = torch.from_numpy(codes).view(torch.float8_e5m2).float().numpy().astype(np.float64)
+    got = f8.e5m2_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(t))
+    ok = ~np.isnan(t)
+    assert np.array_equal(got[ok], t[ok])
+
+
+def _tdtype(fmt):
+    import torch
+
+    return {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[fmt]
+
+
+def torch_decode(codes, fmt):
+    """Input values by torch's own FP8 types (independent of the oracle)."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(_tdtype(fmt)).float().numpy() \
+        .astype(np.float64)
+
+
 def e4m3_round(x):
     import torch
 
@@ -53,18 +87,19 @@ def e4m3_round(x):
         torch.float8_e4m3fn).float().numpy().astype(np.float64)
 
 
-def random_codes(rng, shape, spread=1.0):
+def random_codes(rng, shape, spread=1.0, fmt="e4m3"):
     import torch
 
     x = (rng.standard_normal(shape) * spread).astype(np.float32)
-    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return torch.from_numpy(x).to(_tdtype(fmt)).view(torch.uint8).numpy()
 
 
-def simulate(q, k, v, kind, window, scale, shift, rounded_den=False):
+def simulate(q, k, v, kind, window, scale, shift, rounded_den=False, fmt="e4m3"):
     """Output of the FP8 method with P rounded to E4M3 while the reference
     maximum sits `shift` (log2 units) below the row maximum; the denominator
-    from the unrounded weights, or from the rounded ones (`rounded_den`)."""
-    qd, kd, vd = (f8.e4m3_decode(x) for x in (q, k, v))
+    from the unrounded weights, or from the rounded ones (`rounded_den`);
+    inputs in format `fmt`, decoded by torch."""
+    qd, kd, vd = (torch_decode(x, fmt) for x in (q, k, v))
     B, Hq, S, D = qd.shape
     Hkv = kd.shape[1]
     out = np.empty((B, Hq, S, D))
@@ -80,30 +115,32 @@ def simulate(q, k, v, kind, window, scale, shift, rounded_den=False):
     return out
 
 
-def check_bound_holds(spread, rounded_den=False):
+def check_bound_holds(spread, rounded_den=False, fmt="e4m3"):
     rng = np.random.default_rng(60)
     B, Hq, Hkv, S, D = 1, 4, 2, 96, 16
-    q, k, v = (random_codes(rng, s, sp) for s, sp in (((B, Hq, S, D), spread),
-                                                         ((B, Hkv, S, D), spread),
-                                                         ((B, Hkv, S, D), 1.0)))
+    q, k, v = (random_codes(rng, s, sp, fmt) for s, sp in (((B, Hq, S, D), spread),
+                                                              ((B, Hkv, S, D), spread),
+                                                              ((B, Hkv, S, D), 1.0)))
     worst = 0.0
     for kind, w in (("causal", 0), ("full", 0), ("causal_window", 9)):
-        exact = f8.fp8_attention(q, k, v, kind, w, scale=0.5)
-        bound = f8.fp8_error_bound(q, k, v, kind, w, scale=0.5, rounded_denominator=rounded_den)
+        exact = f8.fp8_attention(q, k, v, kind, w, scale=0.5, fmt=fmt)
+        bound = f8.fp8_error_bound(q, k, v, kind, w, scale=0.5, rounded_denominator=rounded_den,
+                                   fmt=fmt)
         assert np.all(np.isfinite(bound))
         for shift in (0.0, 0.37, 3.0, 7.9):
-            err = np.abs(simulate(q, k, v, kind, w, 0.5, shift, rounded_den) - exact)
+            err = np.abs(simulate(q, k, v, kind, w, 0.5, shift, rounded_den, fmt) - exact)
             assert np.all(err <= bound * (1 + 1e-9) + 1e-12), (kind, shift, float((err - bound).max()))
             worst = max(worst, float((err / bound).max()))
     return worst
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("rounded_den", [False, True])
-def test_bound_holds_and_is_not_vacuous(rounded_den):
+def test_bound_holds_and_is_not_vacuous(rounded_den, fmt):
     pytest.importorskip("torch")
-    worst = check_bound_holds(1.0, rounded_den)
+    worst = check_bound_holds(1.0, rounded_den, fmt)
     assert worst > 0.05, worst          # the bound is within 20x of a real error
-    check_bound_holds(3.0, rounded_den)  # peaked rows: many weights in the subnormal range
+    check_bound_holds(3.0, rounded_den, fmt)  # peaked rows: many weights in the subnormal range
 
 
 def test_rounded_denominator_bound_vs_unrounded():
@@ -160,14 +197,14 @@ def bf16_round(x):
 
 
 def simulate_kernel(q, k, v, kind, window, scale, shift, round_p=True, bf16_out=True,
-                    rounded_den=False):
+                    rounded_den=False, fmt="e4m3"):
     """The FP8 forward's arithmetic in float32 on the decoded inputs: scores,
     exponent argument and 2^x in float32, weights against a reference maximum
     `shift` log2 units below the row maximum, P rounded to E4M3 (unless
     round_p is False), the numerator accumulated in float32 16 keys at a time,
     the denominator summed key by key in float32 from the unrounded weights,
     one float32 division, the result rounded to bf16 when bf16_out."""
-    qd, kd, vd = (f8.e4m3_decode(x).astype(np.float32) for x in (q, k, v))
+    qd, kd, vd = (torch_decode(x, fmt).astype(np.float32) for x in (q, k, v))
     B, Hq, S, D = qd.shape
     Hkv = kd.shape[1]
     c = np.float32(abs(scale) / math.log(2.0))
@@ -199,33 +236,50 @@ def simulate_kernel(q, k, v, kind, window, scale, shift, round_p=True, bf16_out=
     return out
 
 
-def check_tolerance(spread, exact_weights=False, bf16_out=True, scale=0.5, rounded_den=False):
+def check_tolerance(spread, exact_weights=False, bf16_out=True, scale=0.5, rounded_den=False,
+                    fmt="e4m3"):
     rng = np.random.default_rng(62)
     B, Hq, Hkv, S, D = 1, 2, 1, 80, 32
     q = np.zeros((B, Hq, S, D), dtype=np.uint8) if exact_weights else \
-        random_codes(rng, (B, Hq, S, D), spread)
-    k = random_codes(rng, (B, Hkv, S, D), spread)
-    v = random_codes(rng, (B, Hkv, S, D), 1.0)
+        random_codes(rng, (B, Hq, S, D), spread, fmt)
+    k = random_codes(rng, (B, Hkv, S, D), spread, fmt)
+    v = random_codes(rng, (B, Hkv, S, D), 1.0, fmt)
     worst = 0.0
     for kind, w in (("causal", 0), ("full", 0), ("causal_window", 9)):
-        exact = f8.fp8_attention(q, k, v, kind, w, scale=scale)
+        exact = f8.fp8_attention(q, k, v, kind, w, scale=scale, fmt=fmt)
         tol = f8.fp8_tolerance(q, k, v, kind, w, scale=scale, exact_weights=exact_weights,
-                               bf16_output=bf16_out, rounded_denominator=rounded_den)
+                               bf16_output=bf16_out, rounded_denominator=rounded_den, fmt=fmt)
         for shift in ((0.0,) if exact_weights else (0.0, 0.37, 3.0, 7.9)):
             got = simulate_kernel(q, k, v, kind, w, scale, shift, round_p=not exact_weights,
-                                  bf16_out=bf16_out, rounded_den=rounded_den)
+                                  bf16_out=bf16_out, rounded_den=rounded_den, fmt=fmt)
             err = np.abs(got - exact)
             assert np.all(err <= tol), (kind, shift, float((err - tol).max()))
             worst = max(worst, float((err / tol).max()))
     return worst
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("rounded_den", [False, True])
-def test_tolerance_covers_the_kernel_arithmetic(rounded_den):
+def test_tolerance_covers_the_kernel_arithmetic(rounded_den, fmt):
     pytest.importorskip("torch")
-    assert check_tolerance(1.0, rounded_den=rounded_den) > 0.05
-    check_tolerance(3.0, rounded_den=rounded_den)
-    check_tolerance(1.0, scale=-0.3, rounded_den=rounded_den)
+    assert check_tolerance(1.0, rounded_den=rounded_den, fmt=fmt) > 0.05
+    check_tolerance(3.0, rounded_den=rounded_den, fmt=fmt)
+    check_tolerance(1.0, scale=-0.3, rounded_den=rounded_den, fmt=fmt)
+
+
+@pytest.mark.parametrize("mutation", ["e5m2_read_as_e4m3", "e5m2_bias_16"])
+def test_planted_e5m2_mistakes_are_caught(monkeypatch, mutation):
+    """The oracle's E5M2 decoding with a wrong format or exponent bias: its
+    exact output then leaves the simulation (torch's decoding) outside the
+    bound."""
+    pytest.importorskip("torch")
+    if mutation == "e5m2_read_as_e4m3":
+        monkeypatch.setattr(f8, "e5m2_decode", f8.e4m3_decode)
+    else:
+        orig = f8.e5m2_decode
+        monkeypatch.setattr(f8, "e5m2_decode", lambda c: orig(c) * 0.5)
+    with pytest.raises(AssertionError):
+        check_bound_holds(1.0, True, "e5m2")
 
 
 @pytest.mark.parametrize("rounded_den", [False, True])
