@@ -55,7 +55,12 @@ typedef enum {
    * run on the FP8 matrix cores with fp32 accumulation; P is rounded to E4M3
    * (nearest even) for the second.  Per-tensor scale factors stay with the
    * caller: fold q's and k's into `scale`, multiply o by v's. */
-  ATTN_DTYPE_FP8_E4M3 = 2
+  ATTN_DTYPE_FP8_E4M3 = 2,
+  /* the same with q, k, v as OCP E5M2 bytes (the other FP8 format that
+   * paragraph names: two mantissa bits, five exponent bits, infinities); the
+   * weights P stay E4M3 for the P.V product (they lie in [0, 2^8), where
+   * E4M3's extra mantissa bit counts and E5M2's range does not) */
+  ATTN_DTYPE_FP8_E5M2 = 3
 } attn_dtype;
 
 typedef enum {
@@ -105,9 +110,9 @@ typedef enum {
  *   scale       multiplies q.k; used exactly as given (0 gives uniform weights;
  *               the usual choice is 1/sqrt(D), "Trasformer 浅析", section
  *               缩放因子的必要性)
- *   dtype       attn_dtype of all four tensors (ATTN_DTYPE_FP8_E4M3: q, k, v
- *               one byte per element, o bf16; D = 128 and no global tokens,
- *               else ATTN_ERR_UNSUPPORTED)
+ *   dtype       attn_dtype of all four tensors (ATTN_DTYPE_FP8_E4M3 and _E5M2:
+ *               q, k, v one byte per element, o bf16; D = 128 and no global
+ *               tokens, else ATTN_ERR_UNSUPPORTED)
  *   stream      hipStream_t to launch on (NULL = the default stream)
  *
  * Returns ATTN_OK after enqueuing one kernel; the call does not synchronise.

@@ -1,4 +1,4 @@
-"""FP8 (E4M3) forward pass against the FP8 oracle.
+"""FP8 (E4M3 and E5M2 inputs) forward pass against the FP8 oracle.
 
 GPU cases compare every output element with oracle.fp8_attention (exact
 attention on the decoded E4M3 inputs, fp64) within the per-element bound
@@ -19,32 +19,40 @@ import workloads
 attn = pytest.importorskip("transformer_attention_attn_amd")
 
 
-def fp8_inputs(B, Hq, Hkv, S, seed, zero_q=False):
-    inp = workloads.make_inputs(B, Hq, Hkv, S, 128, "fp8", seed)
+def fp8_inputs(B, Hq, Hkv, S, seed, zero_q=False, fmt="e4m3", spread=1.0):
+    inp = workloads.make_inputs(B, Hq, Hkv, S, 128, "fp8" if fmt == "e4m3" else "fp8_e5m2", seed)
+    if spread != 1.0:  # re-encode the same draws scaled (E5M2's range)
+        for n in ("q", "k", "v"):
+            inp[n + "_codes"] = workloads.e4m3_codes(
+                oracle.fp8_decode(inp[n + "_codes"], fmt) * spread,
+                "fp8" if fmt == "e4m3" else "fp8_e5m2")
+            inp[n] = workloads.codes_to_float(inp[n + "_codes"],
+                                              "fp8" if fmt == "e4m3" else "fp8_e5m2")
     if zero_q:
         inp["q_codes"][:] = 0
         inp["q"][:] = 0.0
     return inp
 
 
-def run_fp8(device, B, Hq, Hkv, S, mask, window=0, seed=0, scale=None, zero_q=False, rows=None):
+def run_fp8(device, B, Hq, Hkv, S, mask, window=0, seed=0, scale=None, zero_q=False, rows=None,
+            fmt="e4m3", spread=1.0):
     import torch
 
     print(f"fp8 case B={B} Hq={Hq} Hkv={Hkv} S={S} {mask} w={window} seed={seed} scale={scale} "
-          f"zero_q={zero_q}", flush=True)
-    inp = fp8_inputs(B, Hq, Hkv, S, seed, zero_q)
-    q, k, v = workloads.to_torch(inp, "fp8", device)
+          f"zero_q={zero_q} fmt={fmt} spread={spread}", flush=True)
+    inp = fp8_inputs(B, Hq, Hkv, S, seed, zero_q, fmt, spread)
+    q, k, v = workloads.to_torch(inp, "fp8" if fmt == "e4m3" else "fp8_e5m2", device)
     o = attn.fwd(q, k, v, mask=mask, window=window, scale=scale)
     torch.cuda.synchronize()
     assert o.dtype == torch.bfloat16
     got = o.float().cpu().numpy().astype(np.float64)
     codes = (inp["q_codes"], inp["k_codes"], inp["v_codes"])
-    ref = oracle.fp8_attention(*codes, mask, window, scale=scale, rows=rows)
+    ref = oracle.fp8_attention(*codes, mask, window, scale=scale, rows=rows, fmt=fmt)
     if rows is not None:
         got = got[:, :, rows]
     assert np.all(np.isfinite(got))
     tol = oracle.fp8_tolerance(*codes, mask, window, scale=scale, rows=rows, exact_weights=zero_q,
-                               rounded_denominator=True)
+                               rounded_denominator=True, fmt=fmt)
     return got, ref, tol
 
 
@@ -88,6 +96,32 @@ def test_fp8_scales(device, scale):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"S{c[3]}-{c[4]}-H{c[1]}x{c[2]}")
+def test_fp8_e5m2_sweep(device, case):
+    """E5M2 inputs (the instruction's operand formats switched for q, k and
+    v; the weights stay E4M3) over the same shapes."""
+    B, Hq, Hkv, S, mask, window = case
+    worst = check(*run_fp8(device, B, Hq, Hkv, S, mask, window, seed=S + Hq + 1, fmt="e5m2"))
+    print(f"worst error / tolerance {worst:.3f}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", SWEEP[1::3], ids=lambda c: f"S{c[3]}-{c[4]}-H{c[1]}x{c[2]}")
+def test_fp8_e5m2_zero_queries_exact_means(device, case):
+    B, Hq, Hkv, S, mask, window = case
+    check(*run_fp8(device, B, Hq, Hkv, S, mask, window, seed=S + 8, zero_q=True, fmt="e5m2"))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("scale", [0.0, -0.002, 0.01])
+def test_fp8_e5m2_wide_range(device, scale):
+    """Inputs 300 times wider than the others (most beyond E4M3's 448, up to
+    about 1500), which only E5M2 holds; small and negative scales keep the
+    scores finite and the weights spread."""
+    check(*run_fp8(device, 1, 8, 2, 700, "causal", seed=6, scale=scale, fmt="e5m2", spread=300.0))
+
+
+@pytest.mark.gpu
 def test_fp8_workload_full_size(device):
     """The FP8 workload at full size, sampled rows, in the benchmark's launch
     configuration."""
@@ -122,3 +156,10 @@ def test_fp8_validation():
     assert fp8_status(ptrs=(FAKE, FAKE * 3, FAKE * 5, FAKE + nq - 16)) == "ATTN_ERR_ALIAS"
     info = attn.plan(1, 32, 8, 8192, 128, "causal", dtype="fp8")
     assert info["kernel"] == 2 and info["keys_per_tile"] == 128
+    info = attn.plan(1, 32, 8, 8192, 128, "causal", dtype="fp8_e5m2")
+    assert info["kernel"] == 2 and info["keys_per_tile"] == 128
+    assert attn.status_string(attn.fwd_raw(FAKE, FAKE * 3, FAKE * 5, FAKE * 7, 1, 8, 2, 1000, 64,
+                                           "causal", 0, None, 0.1, attn.DTYPE_FP8_E5M2, 0)) \
+        == "ATTN_ERR_UNSUPPORTED"
+    assert attn.status_string(attn.fwd_raw(FAKE, FAKE * 3, FAKE * 5, FAKE * 7, 1, 8, 2, 1000, 128,
+                                           "causal", 0, None, 0.1, 4, 0)) == "ATTN_ERR_UNSUPPORTED"

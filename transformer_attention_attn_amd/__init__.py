@@ -9,6 +9,7 @@ from ._binding import (  # noqa: F401
     DTYPE_BF16,
     DTYPE_FP32,
     DTYPE_FP8,
+    DTYPE_FP8_E5M2,
     EXPORTS,
     LIB_PATH,
     MASK_CAUSAL,

@@ -14,7 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn.so")
 
 MASK_FULL, MASK_CAUSAL, MASK_CAUSAL_WINDOW, MASK_LOCAL_GLOBAL = 0, 1, 2, 3
-DTYPE_FP32, DTYPE_BF16, DTYPE_FP8 = 0, 1, 2
+DTYPE_FP32, DTYPE_BF16, DTYPE_FP8, DTYPE_FP8_E5M2 = 0, 1, 2, 3
 MAX_GLOBAL = 64
 
 MASKS = {
@@ -165,7 +165,8 @@ def fwd(q, k, v, mask="causal", window: int = 0, global_idx=None, scale: Optiona
     """Attention forward on torch device tensors.
 
     q: [B, Hq, S, D], k, v: [B, Hkv, S, D], contiguous, bf16, fp32 or FP8
-    (torch.float8_e4m3fn: E4M3 codes; the output is then bf16), on the GPU.
+    (torch.float8_e4m3fn or torch.float8_e5m2 codes; the output is then
+    bf16), on the GPU.
     Returns o shaped like q (allocated with torch unless `out` is given).
     The kernel runs on `stream` (default: torch's current stream).
     """
@@ -177,6 +178,8 @@ def fwd(q, k, v, mask="causal", window: int = 0, global_idx=None, scale: Optiona
         dt, odt = DTYPE_FP32, torch.float32
     elif q.dtype == torch.float8_e4m3fn:
         dt, odt = DTYPE_FP8, torch.bfloat16
+    elif q.dtype == torch.float8_e5m2:
+        dt, odt = DTYPE_FP8_E5M2, torch.bfloat16
     else:
         raise TypeError(f"unsupported dtype {q.dtype}")
     for t in (q, k, v):
@@ -317,7 +320,8 @@ def plan(B: int, Hq: int, Hkv: int, S: int, D: int, mask="causal", window: int =
     lib = load()
     garr, ng = _globals(global_idx)
     info = PlanInfo()
-    dt = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32, "fp8": DTYPE_FP8}[dtype]
+    dt = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32, "fp8": DTYPE_FP8,
+          "fp8_e5m2": DTYPE_FP8_E5M2}[dtype]
     st = lib.attn_plan(B, Hq, Hkv, S, D, _mask_id(mask), window, garr, ng, dt, ctypes.byref(info))
     if st != 0:
         raise AttnError(st)

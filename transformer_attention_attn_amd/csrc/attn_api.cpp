@@ -33,13 +33,14 @@ Checked check_args(int B, int Hq, int Hkv, int S, int D, int mask_kind, int wind
   Checked c{};
   c.status = ATTN_OK;
   if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || (long long)S > kMaxS) { c.status = ATTN_ERR_SHAPE; return c; }
-  if (dtype != ATTN_DTYPE_FP32 && dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP8_E4M3) {
+  const bool fp8 = dtype == ATTN_DTYPE_FP8_E4M3 || dtype == ATTN_DTYPE_FP8_E5M2;
+  if (dtype != ATTN_DTYPE_FP32 && dtype != ATTN_DTYPE_BF16 && !fp8) {
     c.status = ATTN_ERR_UNSUPPORTED;
     return c;
   }
   if (D != 64 && D != 128) { c.status = ATTN_ERR_UNSUPPORTED; return c; }
   // FP8: D = 128, masks without global tokens
-  if (dtype == ATTN_DTYPE_FP8_E4M3 && (D != 128 || mask_kind == ATTN_MASK_LOCAL_GLOBAL)) {
+  if (fp8 && (D != 128 || mask_kind == ATTN_MASK_LOCAL_GLOBAL)) {
     c.status = ATTN_ERR_UNSUPPORTED;
     return c;
   }
@@ -327,7 +328,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq
   } else {
     err = dtype == ATTN_DTYPE_BF16
               ? (D == 64 ? attn::launch_bf16_d64(p, st) : attn::launch_bf16_d128(p, st))
-          : dtype == ATTN_DTYPE_FP8_E4M3 ? attn::launch_fp8_d128(p, st)
+          : dtype != ATTN_DTYPE_FP32 ? attn::launch_fp8_d128(p, dtype == ATTN_DTYPE_FP8_E5M2, st)
                                          : attn::launch_fp32(p, D, st);
   }
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -474,7 +475,7 @@ int attn_plan(int B, int Hq, int Hkv, int S, int D, int mask_kind, int window,
   r.rows_per_item = s.BMh;
   r.heads_per_item = s.HP;
   r.keys_per_tile = s.BN;
-  r.kernel = dtype == ATTN_DTYPE_BF16 ? 1 : dtype == ATTN_DTYPE_FP8_E4M3 ? 2 : 0;
+  r.kernel = dtype == ATTN_DTYPE_BF16 ? 1 : dtype == ATTN_DTYPE_FP32 ? 0 : 2;
   // Walk one pair's items (all pairs are alike) and scale by the pair count.
   long long visits = 0, partial = 0;
   for (long long id = 0; id < s.n_items; id += s.P) {

@@ -1,18 +1,22 @@
-// kernel_fp8.hip -- FP8 (E4M3) fused attention forward on gfx950 matrix cores.
+// kernel_fp8.hip -- FP8 (E4M3 or E5M2 inputs) fused attention forward on gfx950
+// matrix cores.
 //
 // The FP8 variant of the tiled online-softmax attention ("Transformer 演进与变
 // 体", section Flash Attention, the FlashAttention-3 paragraph: FP8 operands for
 // the two matrix products, softmax and accumulation in higher precision):
-//   * S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit
-//     scales, fp32 accumulation): 64 dims per instruction.
+//   * S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (inputs in E4M3 or
+//     E5M2, the instruction's operand formats set to match; unit scales, fp32
+//     accumulation): 64 dims per instruction.
 //   * Online softmax in fp32, as in the bf16 kernel (log2 units, lazy
 //     reference maximum), except that the weights come first and the row
 //     maximum is computed only when one of them rounds to 2^8 or more (and on
 //     a row's first tile).
 //   * P is rounded to E4M3 (v_cvt_pk_fp8_f32, round to nearest even; P < 2^8
 //     stays below the E4M3 maximum) and O^T += V^T P^T runs on the same
-//     instruction, 64 keys per instruction; O is accumulated in fp32 and
-//     written as bf16.
+//     instruction (V in the input format, P in E4M3 whatever the inputs:
+//     the weights lie in [0, 2^8), where E4M3's third mantissa bit serves
+//     and E5M2's range is not needed), 64 keys per instruction; O is
+//     accumulated in fp32 and written as bf16.
 //   * The denominator is summed on the matrix cores too: l += 1 P^T with an
 //     all-ones E4M3 operand (two more instructions per tile), i.e. from the
 //     rounded weights, so O is the exact weighted mean under them; the
@@ -69,8 +73,11 @@ static_assert(F8_LOADS * 4 * 1024 == F8_REG, "tile split into 1 KiB loads of fou
 __device__ __forceinline__ int kswz(int row) { return ((row >> 1) & 3) | (((row >> 4) & 1) << 2); }
 __device__ __forceinline__ int vswz(int row) { return 2 * ((row >> 1) & 3); }
 
+// Operand formats of the f8f6f4 product: 0 = E4M3, 1 = E5M2 (A, then B).
+constexpr int kFmtE4M3 = 0, kFmtE5M2 = 1;
+template <int FA, int FB>
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
 }
 
 // Two 16-byte LDS reads at a0 + OFF and a1 + OFF (a 32-byte A operand), as
@@ -131,7 +138,7 @@ __device__ __forceinline__ i32x8 block_read(const BlockOps& o) {
                    : lds_read32<KBK * 32 * F8_ROWB>(o.a10, o.a11);
   }
 }
-template <int I, int NV, int N, int DEPTH>
+template <int I, int NV, int N, int DEPTH, int FMT>
 __device__ __forceinline__ void block_step(i32x8 (&op)[DEPTH], const BlockOps& o, const i32x8 (&pf)[2],
                                            const i32x8 (&qf)[2], const i32x8& ones, f32x16 (&oacc)[4],
                                            f32x16& lacc, f32x16 (&sc)[4]) {
@@ -140,14 +147,14 @@ __device__ __forceinline__ void block_step(i32x8 (&op)[DEPTH], const BlockOps& o
   constexpr int LAST = J < N ? J : N - 1;
   lds_wait8<reads_after<NV>(I, LAST)>(op[I % DEPTH]);
   if constexpr (I < NV) {
-    oacc[I >> 1] = mfma_fp8(op[I % DEPTH], pf[I & 1], oacc[I >> 1]);
+    oacc[I >> 1] = mfma_fp8<FMT, kFmtE4M3>(op[I % DEPTH], pf[I & 1], oacc[I >> 1]);
     // the denominator (no LDS operand) in the shadow of the first reads
-    if constexpr (I < 2) lacc = mfma_fp8(ones, pf[I], lacc);
+    if constexpr (I < 2) lacc = mfma_fp8<kFmtE4M3, kFmtE4M3>(ones, pf[I], lacc);
   } else {
     constexpr int K = I - NV;
-    sc[K >> 1] = mfma_fp8(op[I % DEPTH], qf[K & 1], (K & 1) ? sc[K >> 1] : f32x16{});
+    sc[K >> 1] = mfma_fp8<FMT, FMT>(op[I % DEPTH], qf[K & 1], (K & 1) ? sc[K >> 1] : f32x16{});
   }
-  if constexpr (I + 1 < N) block_step<I + 1, NV, N, DEPTH>(op, o, pf, qf, ones, oacc, lacc, sc);
+  if constexpr (I + 1 < N) block_step<I + 1, NV, N, DEPTH, FMT>(op, o, pf, qf, ones, oacc, lacc, sc);
 }
 template <int NV, int N, int DEPTH, int I = 0>
 __device__ __forceinline__ void block_prime(i32x8 (&op)[DEPTH], const BlockOps& o) {
@@ -156,17 +163,18 @@ __device__ __forceinline__ void block_prime(i32x8 (&op)[DEPTH], const BlockOps& 
     block_prime<NV, N, DEPTH, I + 1>(op, o);
   }
 }
-template <bool PV, bool S>
+template <bool PV, bool S, int FMT>
 __device__ __forceinline__ void run_block(const BlockOps& o, const i32x8 (&pf)[2], const i32x8 (&qf)[2],
                                           const i32x8& ones, f32x16 (&oacc)[4], f32x16& lacc,
                                           f32x16 (&sc)[4]) {
   constexpr int NV = PV ? 8 : 0, N = NV + (S ? 8 : 0), DEPTH = F8_OPDEPTH;
   i32x8 op[DEPTH];
   block_prime<NV, N, DEPTH>(op, o);
-  block_step<0, NV, N, DEPTH>(op, o, pf, qf, ones, oacc, lacc, sc);
+  block_step<0, NV, N, DEPTH, FMT>(op, o, pf, qf, ones, oacc, lacc, sc);
 }
 
-template <int MASK>
+// FMT: the input format of q, k and v (kFmtE4M3 or kFmtE5M2)
+template <int MASK, int FMT>
 __global__ __launch_bounds__(kBf16Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_fp8(KParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[F8_NSTAGE * 2 * F8_REG];
@@ -310,8 +318,8 @@ void attn_fwd_fp8(KParams p) {
     o.a10 = kb + k_off[1][0];
     o.a11 = kb + k_off[1][1];
     // two regions (one pipeline over both would hold too many registers live)
-    if (do_pv) run_block<true, false>(o, pf, qf, ones8, oacc, lacc, sc);
-    if (do_s) run_block<false, true>(o, pf, qf, ones8, oacc, lacc, sc);
+    if (do_pv) run_block<true, false, FMT>(o, pf, qf, ones8, oacc, lacc, sc);
+    if (do_s) run_block<false, true, FMT>(o, pf, qf, ones8, oacc, lacc, sc);
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -462,14 +470,19 @@ void attn_fwd_fp8(KParams p) {
 
 }  // namespace
 
-hipError_t launch_fp8_d128(const KParams& p, hipStream_t stream) {
+template <int FMT>
+hipError_t launch_fmt(const KParams& p, hipStream_t stream) {
   dim3 grid((unsigned)p.s.n_items), block(kBf16Threads);
   switch (p.s.mask) {
-    case MASK_FULL: hipLaunchKernelGGL((attn_fwd_fp8<MASK_FULL>), grid, block, 0, stream, p); break;
-    case MASK_CAUSAL: hipLaunchKernelGGL((attn_fwd_fp8<MASK_CAUSAL>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((attn_fwd_fp8<MASK_CAUSAL_WINDOW>), grid, block, 0, stream, p); break;
+    case MASK_FULL: hipLaunchKernelGGL((attn_fwd_fp8<MASK_FULL, FMT>), grid, block, 0, stream, p); break;
+    case MASK_CAUSAL: hipLaunchKernelGGL((attn_fwd_fp8<MASK_CAUSAL, FMT>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((attn_fwd_fp8<MASK_CAUSAL_WINDOW, FMT>), grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_fp8_d128(const KParams& p, bool e5m2, hipStream_t stream) {
+  return e5m2 ? launch_fmt<kFmtE5M2>(p, stream) : launch_fmt<kFmtE4M3>(p, stream);
 }
 
 }  // namespace attn

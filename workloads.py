@@ -332,19 +332,26 @@ def draw(shape, rng: np.random.Generator) -> np.ndarray:
     return rng.standard_normal(shape, dtype=np.float32)
 
 
-def e4m3_codes(x: np.ndarray) -> np.ndarray:
+def _fp8_torch_dtype(dtype: str):
+    import torch
+
+    return {"fp8": torch.float8_e4m3fn, "fp8_e5m2": torch.float8_e5m2}[dtype]
+
+
+def e4m3_codes(x: np.ndarray, dtype: str = "fp8") -> np.ndarray:
     """Round float32 values to the nearest E4M3 value (ties to even, OCP
-    format) with torch's own conversion; return the uint8 codes."""
+    format; or E5M2 for dtype "fp8_e5m2") with torch's own conversion; return
+    the uint8 codes."""
     import torch
 
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return t.to(_fp8_torch_dtype(dtype)).view(torch.uint8).numpy().copy()
 
 
 def make_inputs(B, Hq, Hkv, S, D, dtype, seed):
     """Return dict with float32 arrays 'q','k','v' holding the values the kernel sees,
     plus (for bf16) the uint16 bit patterns under 'q_bits','k_bits','v_bits' or
-    (for fp8) the E4M3 codes under 'q_codes','k_codes','v_codes'."""
+    (for fp8, fp8_e5m2) the E4M3 / E5M2 codes under 'q_codes','k_codes','v_codes'."""
     rng = np.random.default_rng(seed)
     q = draw((B, Hq, S, D), rng)
     k = draw((B, Hkv, S, D), rng)
@@ -355,10 +362,10 @@ def make_inputs(B, Hq, Hkv, S, D, dtype, seed):
             bits = bf16_round_bits(x)
             out[name + "_bits"] = bits
             out[name] = bf16_bits_to_float(bits)
-        elif dtype == "fp8":
-            codes = e4m3_codes(x)
+        elif dtype in ("fp8", "fp8_e5m2"):
+            codes = e4m3_codes(x, dtype)
             out[name + "_codes"] = codes
-            out[name] = codes_to_float(codes)
+            out[name] = codes_to_float(codes, dtype)
         elif dtype == "fp32":
             out[name] = x
         else:
@@ -394,10 +401,10 @@ def make_trend_inputs(B, Hq, Hkv, S, D, dtype, seed, pattern, amp=16.0):
             bits = bf16_round_bits(x)
             out[name + "_bits"] = bits
             out[name] = bf16_bits_to_float(bits)
-        elif dtype == "fp8":
-            codes = e4m3_codes(x)
+        elif dtype in ("fp8", "fp8_e5m2"):
+            codes = e4m3_codes(x, dtype)
             out[name + "_codes"] = codes
-            out[name] = codes_to_float(codes)
+            out[name] = codes_to_float(codes, dtype)
         else:
             raise ValueError(f"unknown dtype {dtype!r}")
     return out
@@ -429,11 +436,13 @@ def ex_workload_inputs(w: ExWorkload):
     return make_decode_inputs(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.seed)
 
 
-def codes_to_float(codes: np.ndarray) -> np.ndarray:
-    """E4M3 codes widened exactly to float32 (torch's decoding)."""
+def codes_to_float(codes: np.ndarray, dtype: str = "fp8") -> np.ndarray:
+    """E4M3 (or, for "fp8_e5m2", E5M2) codes widened exactly to float32
+    (torch's decoding)."""
     import torch
 
-    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).float().numpy()
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(_fp8_torch_dtype(dtype)).float() \
+        .numpy()
 
 
 def to_torch(inputs: dict, dtype: str, device):
@@ -444,8 +453,8 @@ def to_torch(inputs: dict, dtype: str, device):
     for name in ("q", "k", "v"):
         if dtype == "bf16":
             t = torch.from_numpy(inputs[name + "_bits"].view(np.int16)).view(torch.bfloat16)
-        elif dtype == "fp8":
-            t = torch.from_numpy(inputs[name + "_codes"]).view(torch.float8_e4m3fn)
+        elif dtype in ("fp8", "fp8_e5m2"):
+            t = torch.from_numpy(inputs[name + "_codes"]).view(_fp8_torch_dtype(dtype))
         else:
             t = torch.from_numpy(inputs[name])
         res.append(t.to(device).contiguous())
