@@ -1,4 +1,4 @@
-"""FP8 (E4M3 and E5M2 inputs) forward pass against the FP8 oracle.
+"""FP8 (E4M3 and E5M2 inputs, D = 64 and 128) forward pass against the FP8 oracle.
 
 GPU cases compare every output element with oracle.fp8_attention (exact
 attention on the decoded E4M3 inputs, fp64) within the per-element bound
@@ -19,8 +19,8 @@ import workloads
 attn = pytest.importorskip("transformer_attention_attn_amd")
 
 
-def fp8_inputs(B, Hq, Hkv, S, seed, zero_q=False, fmt="e4m3", spread=1.0):
-    inp = workloads.make_inputs(B, Hq, Hkv, S, 128, "fp8" if fmt == "e4m3" else "fp8_e5m2", seed)
+def fp8_inputs(B, Hq, Hkv, S, seed, zero_q=False, fmt="e4m3", spread=1.0, D=128):
+    inp = workloads.make_inputs(B, Hq, Hkv, S, D, "fp8" if fmt == "e4m3" else "fp8_e5m2", seed)
     if spread != 1.0:  # re-encode the same draws scaled (E5M2's range)
         for n in ("q", "k", "v"):
             inp[n + "_codes"] = workloads.e4m3_codes(
@@ -35,12 +35,12 @@ def fp8_inputs(B, Hq, Hkv, S, seed, zero_q=False, fmt="e4m3", spread=1.0):
 
 
 def run_fp8(device, B, Hq, Hkv, S, mask, window=0, seed=0, scale=None, zero_q=False, rows=None,
-            fmt="e4m3", spread=1.0):
+            fmt="e4m3", spread=1.0, D=128):
     import torch
 
-    print(f"fp8 case B={B} Hq={Hq} Hkv={Hkv} S={S} {mask} w={window} seed={seed} scale={scale} "
-          f"zero_q={zero_q} fmt={fmt} spread={spread}", flush=True)
-    inp = fp8_inputs(B, Hq, Hkv, S, seed, zero_q, fmt, spread)
+    print(f"fp8 case B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} {mask} w={window} seed={seed} "
+          f"scale={scale} zero_q={zero_q} fmt={fmt} spread={spread}", flush=True)
+    inp = fp8_inputs(B, Hq, Hkv, S, seed, zero_q, fmt, spread, D)
     q, k, v = workloads.to_torch(inp, "fp8" if fmt == "e4m3" else "fp8_e5m2", device)
     o = attn.fwd(q, k, v, mask=mask, window=window, scale=scale)
     torch.cuda.synchronize()
@@ -97,6 +97,26 @@ def test_fp8_scales(device, scale):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"S{c[3]}-{c[4]}-H{c[1]}x{c[2]}")
+def test_fp8_d64_sweep(device, case):
+    """Head dimension 64 (half the matrix instructions per tile; the LDS rows
+    keep their 128-byte layout), E4M3 inputs, the same shapes."""
+    B, Hq, Hkv, S, mask, window = case
+    worst = check(*run_fp8(device, B, Hq, Hkv, S, mask, window, seed=S + Hq + 2, D=64))
+    print(f"worst error / tolerance {worst:.3f}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", SWEEP[::3], ids=lambda c: f"S{c[3]}-{c[4]}-H{c[1]}x{c[2]}")
+def test_fp8_d64_zero_queries_and_e5m2(device, case):
+    B, Hq, Hkv, S, mask, window = case
+    check(*run_fp8(device, B, Hq, Hkv, S, mask, window, seed=S + 9, zero_q=True, D=64))
+    check(*run_fp8(device, B, Hq, Hkv, S, mask, window, seed=S + 10, fmt="e5m2", D=64))
+    check(*run_fp8(device, B, Hq, Hkv, S, mask, window, seed=S + 11, zero_q=True, fmt="e5m2",
+                   D=64))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"S{c[3]}-{c[4]}-H{c[1]}x{c[2]}")
 def test_fp8_e5m2_sweep(device, case):
     """E5M2 inputs (the instruction's operand formats switched for q, k and
     v; the weights stay E4M3) over the same shapes."""
@@ -122,14 +142,15 @@ def test_fp8_e5m2_wide_range(device, scale):
 
 
 @pytest.mark.gpu
-def test_fp8_workload_full_size(device):
-    """The FP8 workload at full size, sampled rows, in the benchmark's launch
+@pytest.mark.parametrize("name", [n for n, w in workloads.WORKLOADS.items() if w.dtype == "fp8"])
+def test_fp8_workload_full_size(device, name):
+    """The FP8 workloads at full size, sampled rows, in the benchmark's launch
     configuration."""
     from tests.test_parity import sample_rows
 
-    w = workloads.WORKLOADS["causal_gqa_fp8_s8192"]
+    w = workloads.WORKLOADS[name]
     rows = sample_rows(w)
-    got, ref, tol = run_fp8(device, w.B, w.Hq, w.Hkv, w.S, w.mask, seed=w.seed, rows=rows)
+    got, ref, tol = run_fp8(device, w.B, w.Hq, w.Hkv, w.S, w.mask, seed=w.seed, rows=rows, D=w.D)
     print(f"fp8 full size: worst error / tolerance {check(got, ref, tol):.3f}", flush=True)
 
 
@@ -148,7 +169,7 @@ def fp8_status(D=128, mask="causal", window=0, g=None, ptrs=(FAKE, FAKE * 3, FAK
 
 
 def test_fp8_validation():
-    assert fp8_status(D=64) == "ATTN_ERR_UNSUPPORTED"
+    assert fp8_status(D=96) == "ATTN_ERR_UNSUPPORTED"
     assert fp8_status(mask="local_global", window=10, g=[0]) == "ATTN_ERR_UNSUPPORTED"
     assert fp8_status(ptrs=(FAKE + 8, FAKE * 3, FAKE * 5, FAKE * 7)) == "ATTN_ERR_ALIGN"
     # o (bf16, 2 bytes per element) overlapping the end of q (1 byte per element)
@@ -159,7 +180,7 @@ def test_fp8_validation():
     info = attn.plan(1, 32, 8, 8192, 128, "causal", dtype="fp8_e5m2")
     assert info["kernel"] == 2 and info["keys_per_tile"] == 128
     assert attn.status_string(attn.fwd_raw(FAKE, FAKE * 3, FAKE * 5, FAKE * 7, 1, 8, 2, 1000, 64,
-                                           "causal", 0, None, 0.1, attn.DTYPE_FP8_E5M2, 0)) \
-        == "ATTN_ERR_UNSUPPORTED"
+                                           "local_global", 10, [0], 0.1, attn.DTYPE_FP8_E5M2,
+                                           0)) == "ATTN_ERR_UNSUPPORTED"
     assert attn.status_string(attn.fwd_raw(FAKE, FAKE * 3, FAKE * 5, FAKE * 7, 1, 8, 2, 1000, 128,
                                            "causal", 0, None, 0.1, 4, 0)) == "ATTN_ERR_UNSUPPORTED"

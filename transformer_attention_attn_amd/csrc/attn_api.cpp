@@ -39,8 +39,8 @@ Checked check_args(int B, int Hq, int Hkv, int S, int D, int mask_kind, int wind
     return c;
   }
   if (D != 64 && D != 128) { c.status = ATTN_ERR_UNSUPPORTED; return c; }
-  // FP8: D = 128, masks without global tokens
-  if (fp8 && (D != 128 || mask_kind == ATTN_MASK_LOCAL_GLOBAL)) {
+  // FP8: masks without global tokens
+  if (fp8 && mask_kind == ATTN_MASK_LOCAL_GLOBAL) {
     c.status = ATTN_ERR_UNSUPPORTED;
     return c;
   }
@@ -328,7 +328,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq
   } else {
     err = dtype == ATTN_DTYPE_BF16
               ? (D == 64 ? attn::launch_bf16_d64(p, st) : attn::launch_bf16_d128(p, st))
-          : dtype != ATTN_DTYPE_FP32 ? attn::launch_fp8_d128(p, dtype == ATTN_DTYPE_FP8_E5M2, st)
+          : dtype != ATTN_DTYPE_FP32 ? attn::launch_fp8(p, D, dtype == ATTN_DTYPE_FP8_E5M2, st)
                                          : attn::launch_fp32(p, D, st);
   }
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

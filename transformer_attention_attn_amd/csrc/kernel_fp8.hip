@@ -58,7 +58,7 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int F8_D = 128;                 // head dimension
+constexpr int F8_D = 128;                 // widest head dimension: bytes of an LDS row
 constexpr int F8_BN = 128;                // keys per tile
 constexpr int F8_ROWB = F8_D;             // bytes per K or V row
 constexpr int F8_REG = F8_BN * F8_ROWB;   // one K or V tile (16 KB)
@@ -127,23 +127,23 @@ constexpr int reads_after(int i, int last) {
   for (int j = i + 1; j <= last; ++j) n += reads_of<NV>(j);
   return n;
 }
-template <int I, int NV>
+template <int I, int NV, int NDC>
 __device__ __forceinline__ i32x8 block_read(const BlockOps& o) {
   if constexpr (I < NV) {
     constexpr int DB = I >> 1, SK = I & 1;
     return lds_tr8x4<vrow_off(SK, 0), vrow_off(SK, 1), vrow_off(SK, 2), vrow_off(SK, 3)>(o.vbase[DB]);
   } else {
-    constexpr int KBK = (I - NV) >> 1, DC = (I - NV) & 1;
+    constexpr int KBK = (I - NV) / NDC, DC = (I - NV) % NDC;
     return DC == 0 ? lds_read32<KBK * 32 * F8_ROWB>(o.a00, o.a01)
                    : lds_read32<KBK * 32 * F8_ROWB>(o.a10, o.a11);
   }
 }
-template <int I, int NV, int N, int DEPTH, int FMT>
+template <int I, int NV, int N, int DEPTH, int FMT, int NDC>
 __device__ __forceinline__ void block_step(i32x8 (&op)[DEPTH], const BlockOps& o, const i32x8 (&pf)[2],
                                            const i32x8 (&qf)[2], const i32x8& ones, f32x16 (&oacc)[4],
                                            f32x16& lacc, f32x16 (&sc)[4]) {
   constexpr int J = I + DEPTH - 1;
-  if constexpr (J < N) op[J % DEPTH] = block_read<J, NV>(o);
+  if constexpr (J < N) op[J % DEPTH] = block_read<J, NV, NDC>(o);
   constexpr int LAST = J < N ? J : N - 1;
   lds_wait8<reads_after<NV>(I, LAST)>(op[I % DEPTH]);
   if constexpr (I < NV) {
@@ -152,29 +152,33 @@ __device__ __forceinline__ void block_step(i32x8 (&op)[DEPTH], const BlockOps& o
     if constexpr (I < 2) lacc = mfma_fp8<kFmtE4M3, kFmtE4M3>(ones, pf[I], lacc);
   } else {
     constexpr int K = I - NV;
-    sc[K >> 1] = mfma_fp8<FMT, FMT>(op[I % DEPTH], qf[K & 1], (K & 1) ? sc[K >> 1] : f32x16{});
+    sc[K / NDC] = mfma_fp8<FMT, FMT>(op[I % DEPTH], qf[K % NDC], (K % NDC) ? sc[K / NDC] : f32x16{});
   }
-  if constexpr (I + 1 < N) block_step<I + 1, NV, N, DEPTH, FMT>(op, o, pf, qf, ones, oacc, lacc, sc);
+  if constexpr (I + 1 < N) block_step<I + 1, NV, N, DEPTH, FMT, NDC>(op, o, pf, qf, ones, oacc, lacc, sc);
 }
-template <int NV, int N, int DEPTH, int I = 0>
+template <int NV, int N, int DEPTH, int NDC, int I = 0>
 __device__ __forceinline__ void block_prime(i32x8 (&op)[DEPTH], const BlockOps& o) {
   if constexpr (I < DEPTH - 1 && I < N) {
-    op[I] = block_read<I, NV>(o);
-    block_prime<NV, N, DEPTH, I + 1>(op, o);
+    op[I] = block_read<I, NV, NDC>(o);
+    block_prime<NV, N, DEPTH, NDC, I + 1>(op, o);
   }
 }
-template <bool PV, bool S, int FMT>
+// D: the head dimension (128, or 64: half the P.V and S instructions; the
+// LDS rows keep 128 bytes, the upper 64 never read)
+template <bool PV, bool S, int FMT, int D>
 __device__ __forceinline__ void run_block(const BlockOps& o, const i32x8 (&pf)[2], const i32x8 (&qf)[2],
                                           const i32x8& ones, f32x16 (&oacc)[4], f32x16& lacc,
                                           f32x16 (&sc)[4]) {
-  constexpr int NV = PV ? 8 : 0, N = NV + (S ? 8 : 0), DEPTH = F8_OPDEPTH;
+  constexpr int NDC = D / 64, NV = PV ? 2 * (D / 32) : 0, N = NV + (S ? 4 * NDC : 0);
+  constexpr int DEPTH = F8_OPDEPTH;
   i32x8 op[DEPTH];
-  block_prime<NV, N, DEPTH>(op, o);
-  block_step<0, NV, N, DEPTH, FMT>(op, o, pf, qf, ones, oacc, lacc, sc);
+  block_prime<NV, N, DEPTH, NDC>(op, o);
+  block_step<0, NV, N, DEPTH, FMT, NDC>(op, o, pf, qf, ones, oacc, lacc, sc);
 }
 
-// FMT: the input format of q, k and v (kFmtE4M3 or kFmtE5M2)
-template <int MASK, int FMT>
+// FMT: the input format of q, k and v (kFmtE4M3 or kFmtE5M2); D: 64 or 128
+// (in memory; in LDS every row takes 128 bytes)
+template <int MASK, int FMT, int D>
 __global__ __launch_bounds__(kBf16Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_fp8(KParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[F8_NSTAGE * 2 * F8_REG];
@@ -199,9 +203,11 @@ void attn_fwd_fp8(KParams p) {
   const bool wave_active = wqa <= wqb;
 
   const size_t S = (size_t)s.S;
-  const unsigned char* qp = (const unsigned char*)p.q + (size_t)(it.b * s.Hq + a) * S * F8_D;
-  const unsigned char* kp = (const unsigned char*)p.k + (size_t)(it.b * s.Hkv + it.kvh) * S * F8_D;
-  const unsigned char* vp = (const unsigned char*)p.v + (size_t)(it.b * s.Hkv + it.kvh) * S * F8_D;
+  static_assert(D == 64 || D == 128, "head dimension");
+  constexpr int NDB = D / 32, NCH = D / 16;  // 32-dim output blocks, 16-byte chunks per row
+  const unsigned char* qp = (const unsigned char*)p.q + (size_t)(it.b * s.Hq + a) * S * D;
+  const unsigned char* kp = (const unsigned char*)p.k + (size_t)(it.b * s.Hkv + it.kvh) * S * D;
+  const unsigned char* vp = (const unsigned char*)p.v + (size_t)(it.b * s.Hkv + it.kvh) * S * D;
 
   // ---- Q^T operand: lane holds query q_row, dims 64*dc + 32*hf + [0, 32) ----
   i32x8 qf[2];
@@ -211,8 +217,8 @@ void attn_fwd_fp8(KParams p) {
 #pragma unroll
     for (int dc = 0; dc < 2; ++dc) {
       u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
-      if (!zero) {
-        const unsigned char* src = qp + (size_t)q_row * F8_D + dc * 64 + hf * 32;
+      if (!zero && dc < D / 64) {
+        const unsigned char* src = qp + (size_t)q_row * D + dc * 64 + hf * 32;
         x0 = *(const u32x4*)src;
         x1 = *(const u32x4*)(src + 16);
       }
@@ -232,9 +238,10 @@ void attn_fwd_fp8(KParams p) {
   // Direct loads, issued by the four waves of group 0: load n of wave gw fills
   // 1 KiB slot sl = gw * F8_LOADS + n of the tile, lane l the 16-byte chunk at
   // row 8 * sl + l / 8, physical chunk l % 8 (its source: that row's logical
-  // chunk).  Rows past S repeat the last row (their scores are masked), so
-  // tiles past the end of the range load valid memory into a stage that is not
-  // read again.
+  // chunk; at D = 64 logical chunks 4-7 are never read, and their lanes load
+  // chunk (logical % 4) of the row, valid memory).  Rows past S repeat the last
+  // row (their scores are masked), so tiles past the end of the range load
+  // valid memory into a stage that is not read again.
   const int gw = wave & 3;
   const int drow = lane >> 3, dphys = lane & 7;
   auto dma_k = [&](int iter, int st) {
@@ -243,7 +250,7 @@ void attn_fwd_fp8(KParams p) {
     for (int n = 0; n < F8_LOADS; ++n) {
       const int trow = 8 * (gw * F8_LOADS + n) + drow;
       const int row = imin(kt * F8_BN + trow, s.S - 1);
-      dma16_global(kp + (size_t)row * F8_ROWB + 16 * (dphys ^ kswz(trow)),
+      dma16_global(kp + (size_t)row * D + 16 * ((dphys ^ kswz(trow)) & (NCH - 1)),
                    smem + st * 2 * F8_REG + (gw * F8_LOADS + n) * 1024);
     }
   };
@@ -253,7 +260,7 @@ void attn_fwd_fp8(KParams p) {
     for (int n = 0; n < F8_LOADS; ++n) {
       const int trow = 8 * (gw * F8_LOADS + n) + drow;
       const int row = imin(kt * F8_BN + trow, s.S - 1);
-      dma16_global(vp + (size_t)row * F8_ROWB + 16 * (dphys ^ vswz(trow)),
+      dma16_global(vp + (size_t)row * D + 16 * ((dphys ^ vswz(trow)) & (NCH - 1)),
                    smem + st * 2 * F8_REG + F8_REG + (gw * F8_LOADS + n) * 1024);
     }
   };
@@ -318,8 +325,8 @@ void attn_fwd_fp8(KParams p) {
     o.a10 = kb + k_off[1][0];
     o.a11 = kb + k_off[1][1];
     // two regions (one pipeline over both would hold too many registers live)
-    if (do_pv) run_block<true, false, FMT>(o, pf, qf, ones8, oacc, lacc, sc);
-    if (do_s) run_block<false, true, FMT>(o, pf, qf, ones8, oacc, lacc, sc);
+    if (do_pv) run_block<true, false, FMT, D>(o, pf, qf, ones8, oacc, lacc, sc);
+    if (do_s) run_block<false, true, FMT, D>(o, pf, qf, ones8, oacc, lacc, sc);
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -373,7 +380,7 @@ void attn_fwd_fp8(KParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
 #pragma unroll
-          for (int db = 0; db < 4; ++db)
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
@@ -454,9 +461,9 @@ void attn_fwd_fp8(KParams p) {
     const float l_tot = lacc[0];
     if (row_valid && wave_active) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      __bf16* op = (__bf16*)p.o + ((size_t)(it.b * s.Hq + a) * S + q_row) * F8_D;
+      __bf16* op = (__bf16*)p.o + ((size_t)(it.b * s.Hq + a) * S + q_row) * D;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           bf16x4 w;
@@ -470,19 +477,20 @@ void attn_fwd_fp8(KParams p) {
 
 }  // namespace
 
-template <int FMT>
+template <int FMT, int D>
 hipError_t launch_fmt(const KParams& p, hipStream_t stream) {
   dim3 grid((unsigned)p.s.n_items), block(kBf16Threads);
   switch (p.s.mask) {
-    case MASK_FULL: hipLaunchKernelGGL((attn_fwd_fp8<MASK_FULL, FMT>), grid, block, 0, stream, p); break;
-    case MASK_CAUSAL: hipLaunchKernelGGL((attn_fwd_fp8<MASK_CAUSAL, FMT>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((attn_fwd_fp8<MASK_CAUSAL_WINDOW, FMT>), grid, block, 0, stream, p); break;
+    case MASK_FULL: hipLaunchKernelGGL((attn_fwd_fp8<MASK_FULL, FMT, D>), grid, block, 0, stream, p); break;
+    case MASK_CAUSAL: hipLaunchKernelGGL((attn_fwd_fp8<MASK_CAUSAL, FMT, D>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((attn_fwd_fp8<MASK_CAUSAL_WINDOW, FMT, D>), grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_d128(const KParams& p, bool e5m2, hipStream_t stream) {
-  return e5m2 ? launch_fmt<kFmtE5M2>(p, stream) : launch_fmt<kFmtE4M3>(p, stream);
+hipError_t launch_fp8(const KParams& p, int D, bool e5m2, hipStream_t stream) {
+  if (D == 64) return e5m2 ? launch_fmt<kFmtE5M2, 64>(p, stream) : launch_fmt<kFmtE4M3, 64>(p, stream);
+  return e5m2 ? launch_fmt<kFmtE5M2, 128>(p, stream) : launch_fmt<kFmtE4M3, 128>(p, stream);
 }
 
 }  // namespace attn
