@@ -115,3 +115,68 @@ def test_graph_fwd_ex_replays_with_new_lengths_and_layout(device):
         ref = attn.fwd_ex(q, k, v, mask="causal", block_layout=lay.clone())
         torch.cuda.synchronize()
         assert torch.equal(out2.view(torch.int16), ref.view(torch.int16)), rep
+
+
+@pytest.mark.gpu
+def test_graph_distance_bias_replays_with_new_table(device):
+    import torch
+
+    print("graph: attn_fwd_ex with a distance-bias table, padded", flush=True)
+    B, Hq, Hkv, S, D = 2, 8, 2, 500, 128
+    inp = workloads.make_decode_inputs(B, Hq, Hkv, S, S, D, seed=54)
+    q, k, v = (bf16_tensor(inp[n + "_bits"], device) for n in ("q", "k", "v"))
+    table = torch.from_numpy(workloads.make_distance_bias(Hq, S, S, seed=55)).to(device)
+    ql = torch.tensor([500, 200], dtype=torch.int32, device=device)
+    out = torch.empty_like(q)
+    g = capture(lambda: attn.fwd_ex(q, k, v, mask="causal_window", window=130, out=out,
+                                    q_len=ql, kv_len=ql, dist_bias=table))
+    for rep in range(3):
+        table.copy_(torch.from_numpy(workloads.make_distance_bias(Hq, S, S, seed=56 + rep)))
+        ql.copy_(torch.tensor([500 - 100 * rep, 200 + rep], dtype=torch.int32))
+        g.replay()
+        torch.cuda.synchronize()
+        ref = attn.fwd_ex(q, k, v, mask="causal_window", window=130, q_len=ql.clone(),
+                          kv_len=ql.clone(), dist_bias=table.clone())
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
+
+
+@pytest.mark.gpu
+def test_graph_fp8_e5m2_d64_replays(device):
+    import torch
+
+    print("graph: attn_fwd FP8 E5M2 D=64 causal", flush=True)
+    inp = workloads.make_inputs(1, 8, 2, 700, 64, "fp8_e5m2", seed=57)
+    q, k, v = workloads.to_torch(inp, "fp8_e5m2", device)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=device)
+    g = capture(lambda: attn.fwd(q, k, v, mask="causal", out=out))
+    for rep in range(3):
+        new = workloads.make_inputs(1, 8, 2, 700, 64, "fp8_e5m2", seed=58 + rep)
+        q.copy_(torch.from_numpy(new["q_codes"]).view(torch.float8_e5m2).to(device))
+        g.replay()
+        torch.cuda.synchronize()
+        ref = attn.fwd(q, k, v, mask="causal")
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
+
+
+@pytest.mark.gpu
+def test_graph_windowed_decode_replays_with_new_lengths(device):
+    import torch
+
+    print("graph: attn_decode causal_window w=1000 B=4 Smax=8192 with a workspace", flush=True)
+    inp = workloads.make_decode_inputs(4, 32, 8, 2, 8192, 128, seed=59)
+    q, k, v = (bf16_tensor(inp[n + "_bits"], device) for n in ("q", "k", "v"))
+    lens = torch.tensor([8192, 1500, 2, 999], dtype=torch.int32, device=device)
+    n_ws = attn.decode_workspace_bytes(4, 32, 8, 2, 8192, 128, mask="causal_window", window=1000)
+    ws = torch.empty(max(n_ws, 16), dtype=torch.uint8, device=device)
+    out = torch.empty_like(q)
+    g = capture(lambda: attn.decode(q, k, v, cache_len=lens, mask="causal_window", window=1000,
+                                    out=out, workspace=ws))
+    for rep, new in enumerate(([8192, 1500, 2, 999], [2, 8000, 1001, 4096], [1000, 1000, 1000, 3])):
+        lens.copy_(torch.tensor(new, dtype=torch.int32))
+        g.replay()
+        torch.cuda.synchronize()
+        ref = attn.decode(q, k, v, cache_len=lens.clone(), mask="causal_window", window=1000)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
