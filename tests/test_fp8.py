@@ -179,6 +179,9 @@ def test_fp8_validation():
     assert info["kernel"] == 2 and info["keys_per_tile"] == 128
     info = attn.plan(1, 32, 8, 8192, 128, "causal", dtype="fp8_e5m2")
     assert info["kernel"] == 2 and info["keys_per_tile"] == 128
+    info = attn.plan(1, 12, 12, 8192, 64, "causal", dtype="fp8")
+    assert info["kernel"] == 2 and info["keys_per_tile"] == 128
+    assert info["tile_visits"] == 12 * sum(2 * b + 2 for b in range(32))  # 256 rows, 128-key tiles
     assert attn.status_string(attn.fwd_raw(FAKE, FAKE * 3, FAKE * 5, FAKE * 7, 1, 8, 2, 1000, 64,
                                            "local_global", 10, [0], 0.1, attn.DTYPE_FP8_E5M2,
                                            0)) == "ATTN_ERR_UNSUPPORTED"

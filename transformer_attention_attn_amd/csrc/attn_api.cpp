@@ -69,9 +69,9 @@ Checked check_args(int B, int Hq, int Hkv, int S, int D, int mask_kind, int wind
   if (dtype == ATTN_DTYPE_FP32)
     c.s = attn::make_sched(B, Hq, Hkv, S, mask_kind, window, nd, attn::kF32Rows, attn::kF32Keys, 0,
                            attn::kF32Rows);
-  else
+  else  // (the FP8 kernel's tiles are 128 keys at either head width)
     c.s = attn::make_sched(B, Hq, Hkv, S, mask_kind, window, nd, attn::kBf16Rows,
-                           attn::bf16_keys_per_tile(D), 1, attn::kBf16GlobalRows);
+                           fp8 ? 128 : attn::bf16_keys_per_tile(D), 1, attn::kBf16GlobalRows);
   if (c.s.n_items > 0x7fffffffLL) { c.status = ATTN_ERR_SHAPE; return c; }
   return c;
 }
