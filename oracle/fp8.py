@@ -169,14 +169,17 @@ def fp8_decode(codes, fmt="e4m3"):
     raise ValueError(f"unknown FP8 format {fmt!r}")
 
 
-def fp8_attention(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=None, fmt="e4m3"):
-    """Exact masked attention (float64) on the decoded FP8 inputs."""
+def fp8_attention(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=None, fmt="e4m3",
+                  global_idx=()):
+    """Exact masked attention (float64) on the decoded FP8 inputs (global_idx:
+    the global positions of "local_global")."""
     return reference.attention(fp8_decode(q_codes, fmt), fp8_decode(k_codes, fmt),
-                               fp8_decode(v_codes, fmt), kind, window, (), scale=scale, rows=rows)
+                               fp8_decode(v_codes, fmt), kind, window, global_idx, scale=scale,
+                               rows=rows)
 
 
 def fp8_error_bound(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=None,
-                    rounded_denominator=False, fmt="e4m3"):
+                    rounded_denominator=False, fmt="e4m3", global_idx=()):
     """Per-element bound (float64, shaped like the output) on the error the
     E4M3 rounding of P can cause: b with the denominator summed from the
     unrounded weights, b' with the denominator summed from the rounded ones
@@ -194,7 +197,7 @@ def fp8_error_bound(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=
     for b in range(B):
         for a in range(Hq):
             h = reference.kv_head(a, Hq, Hkv)
-            w = reference.weights(q[b, a, rows], k[b, h], rows, kind, window, (), scale)
+            w = reference.weights(q[b, a, rows], k[b, h], rows, kind, window, global_idx, scale)
             wmax = w.max(axis=1, keepdims=True)
             # w = p / L with p_max = 1, so p = w / wmax and 1 / L = wmax
             e = np.where(w > 0, U_E4M3 * w + ABS_E4M3 * wmax, 0.0)
@@ -209,7 +212,8 @@ def fp8_error_bound(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=
 
 
 def fp8_tolerance(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=None,
-                  exact_weights=False, bf16_output=True, rounded_denominator=False, fmt="e4m3"):
+                  exact_weights=False, bf16_output=True, rounded_denominator=False, fmt="e4m3",
+                  global_idx=()):
     """Per-element bound (float64, shaped like the output) on |O_kernel -
     O_exact|: the E4M3 rounding of P (``fp8_error_bound``, left out when
     ``exact_weights``), the fp32 score, exponent and accumulation errors and,
@@ -226,12 +230,12 @@ def fp8_tolerance(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=No
         scale = 1.0 / np.sqrt(D)
     c = abs(float(scale)) / np.log(2.0)
     rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
-    vis = reference.visibility(rows, S, kind, window)
+    vis = reference.visibility(rows, S, kind, window, global_idx)
     n_vis = vis.sum(axis=1, keepdims=True).astype(np.float64)
-    exact = reference.attention(q, k, v, kind, window, (), scale=scale, rows=rows)
+    exact = reference.attention(q, k, v, kind, window, global_idx, scale=scale, rows=rows)
     b = np.zeros_like(exact) if exact_weights else \
         fp8_error_bound(q_codes, k_codes, v_codes, kind, window, scale, rows, rounded_denominator,
-                        fmt)
+                        fmt, global_idx)
     um = u_mfma()
     den_rel = (n_vis + 8) * U_F32
     if rounded_denominator:
@@ -240,7 +244,7 @@ def fp8_tolerance(q_codes, k_codes, v_codes, kind, window=0, scale=None, rows=No
     for bb in range(B):
         for a in range(Hq):
             h = reference.kv_head(a, Hq, Hkv)
-            w = reference.weights(q[bb, a, rows], k[bb, h], rows, kind, window, (), scale)
+            w = reference.weights(q[bb, a, rows], k[bb, h], rows, kind, window, global_idx, scale)
             mean_abs = w @ np.abs(v[bb, h])               # sum_j p_j |v_j| / L
             if exact_weights:
                 ew = np.zeros((rows.size, 1))

@@ -32,6 +32,10 @@ from oracle import fp8 as f8
 from oracle import reference as ref
 
 
+# the global positions the local_global cases use (rows 0..79 or 0..95)
+GLOBALS = {"local_global": (3, 40, 77)}
+
+
 def test_e4m3_decode_by_hand():
     codes = np.array([0x38, 0x7E, 0x01, 0x08, 0x07, 0xC0, 0x00, 0x80, 0x39, 0x58], dtype=np.uint8)
     want = [1.0, 448.0, 2.0 ** -9, 2.0 ** -6, 7 * 2.0 ** -9, -2.0, 0.0, -0.0, 1.125, 16.0]
@@ -110,7 +114,7 @@ def simulate(q, k, v, kind, window, scale, shift, rounded_den=False, fmt="e4m3")
     for b in range(B):
         for a in range(Hq):
             h = ref.kv_head(a, Hq, Hkv)
-            w = ref.weights(qd[b, a], kd[b, h], rows, kind, window, (), scale)
+            w = ref.weights(qd[b, a], kd[b, h], rows, kind, window, GLOBALS.get(kind, ()), scale)
             p = w / w.max(axis=1, keepdims=True)           # p_max = 1
             pk = e4m3_round(p * 2.0 ** shift) / 2.0 ** shift
             den = (pk if rounded_den else p).sum(axis=1, keepdims=True)
@@ -125,10 +129,11 @@ def check_bound_holds(spread, rounded_den=False, fmt="e4m3"):
                                                               ((B, Hkv, S, D), spread),
                                                               ((B, Hkv, S, D), 1.0)))
     worst = 0.0
-    for kind, w in (("causal", 0), ("full", 0), ("causal_window", 9)):
-        exact = f8.fp8_attention(q, k, v, kind, w, scale=0.5, fmt=fmt)
+    for kind, w in (("causal", 0), ("full", 0), ("causal_window", 9), ("local_global", 5)):
+        g = GLOBALS.get(kind, ())
+        exact = f8.fp8_attention(q, k, v, kind, w, scale=0.5, fmt=fmt, global_idx=g)
         bound = f8.fp8_error_bound(q, k, v, kind, w, scale=0.5, rounded_denominator=rounded_den,
-                                   fmt=fmt)
+                                   fmt=fmt, global_idx=g)
         assert np.all(np.isfinite(bound))
         for shift in (0.0, 0.37, 3.0, 7.9):
             err = np.abs(simulate(q, k, v, kind, w, 0.5, shift, rounded_den, fmt) - exact)
@@ -232,7 +237,7 @@ def simulate_kernel(q, k, v, kind, window, scale, shift, round_p=True, bf16_out=
     c = np.float32(abs(scale) / math.log(2.0))
     sign = 1.0 if scale >= 0 else -1.0
     out = np.empty((B, Hq, S, D))
-    vis = ref.visibility(np.arange(S), S, kind, window)
+    vis = ref.visibility(np.arange(S), S, kind, window, GLOBALS.get(kind, ()))
     for b in range(B):
         for a in range(Hq):
             h = ref.kv_head(a, Hq, Hkv)
@@ -275,10 +280,12 @@ def check_tolerance(spread, exact_weights=False, bf16_out=True, scale=0.5, round
              * np.exp2(rng.uniform(-14, 2, size=(B, Hkv, S, D)))).astype(np.float32)
         v = torch.from_numpy(x).to(_tdtype(fmt)).view(torch.uint8).numpy()
     worst = 0.0
-    for kind, w in (("causal", 0), ("full", 0), ("causal_window", 9)):
-        exact = f8.fp8_attention(q, k, v, kind, w, scale=scale, fmt=fmt)
+    for kind, w in (("causal", 0), ("full", 0), ("causal_window", 9), ("local_global", 5)):
+        g = GLOBALS.get(kind, ())
+        exact = f8.fp8_attention(q, k, v, kind, w, scale=scale, fmt=fmt, global_idx=g)
         tol = f8.fp8_tolerance(q, k, v, kind, w, scale=scale, exact_weights=exact_weights,
-                               bf16_output=bf16_out, rounded_denominator=rounded_den, fmt=fmt)
+                               bf16_output=bf16_out, rounded_denominator=rounded_den, fmt=fmt,
+                               global_idx=g)
         for shift in ((0.0,) if exact_weights else (0.0, 0.37, 3.0, 7.9)):
             got = simulate_kernel(q, k, v, kind, w, scale, shift, round_p=not exact_weights,
                                   bf16_out=bf16_out, rounded_den=rounded_den, fmt=fmt)
