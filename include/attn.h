@@ -48,8 +48,8 @@ typedef enum {
 typedef enum {
   ATTN_DTYPE_FP32 = 0,
   ATTN_DTYPE_BF16 = 1,
-  /* q, k, v as OCP E4M3 bytes, o as bf16: attn_fwd only, D = 64 or 128, masks FULL,
-   * CAUSAL and CAUSAL_WINDOW ("Transformer 演进与变体", section Flash
+  /* q, k, v as OCP E4M3 bytes, o as bf16: attn_fwd only, D = 64 or 128, every
+   * mask ("Transformer 演进与变体", section Flash
    * Attention, the FlashAttention-3 paragraph: FP8 operands for both matrix
    * products, softmax and accumulation in higher precision).  Both products
    * run on the FP8 matrix cores (the instruction truncates the smaller
@@ -112,8 +112,7 @@ typedef enum {
  *               the usual choice is 1/sqrt(D), "Trasformer 浅析", section
  *               缩放因子的必要性)
  *   dtype       attn_dtype of all four tensors (ATTN_DTYPE_FP8_E4M3 and _E5M2:
- *               q, k, v one byte per element, o bf16; no global tokens, else
- *               ATTN_ERR_UNSUPPORTED)
+ *               q, k, v one byte per element, o bf16)
  *   stream      hipStream_t to launch on (NULL = the default stream)
  *
  * Returns ATTN_OK after enqueuing one kernel; the call does not synchronise.

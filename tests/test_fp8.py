@@ -35,24 +35,27 @@ def fp8_inputs(B, Hq, Hkv, S, seed, zero_q=False, fmt="e4m3", spread=1.0, D=128)
 
 
 def run_fp8(device, B, Hq, Hkv, S, mask, window=0, seed=0, scale=None, zero_q=False, rows=None,
-            fmt="e4m3", spread=1.0, D=128):
+            fmt="e4m3", spread=1.0, D=128, global_idx=()):
     import torch
 
     print(f"fp8 case B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} {mask} w={window} seed={seed} "
-          f"scale={scale} zero_q={zero_q} fmt={fmt} spread={spread}", flush=True)
+          f"scale={scale} zero_q={zero_q} fmt={fmt} spread={spread} globals={list(global_idx)}",
+          flush=True)
     inp = fp8_inputs(B, Hq, Hkv, S, seed, zero_q, fmt, spread, D)
     q, k, v = workloads.to_torch(inp, "fp8" if fmt == "e4m3" else "fp8_e5m2", device)
-    o = attn.fwd(q, k, v, mask=mask, window=window, scale=scale)
+    o = attn.fwd(q, k, v, mask=mask, window=window, scale=scale,
+                 global_idx=list(global_idx) or None)
     torch.cuda.synchronize()
     assert o.dtype == torch.bfloat16
     got = o.float().cpu().numpy().astype(np.float64)
     codes = (inp["q_codes"], inp["k_codes"], inp["v_codes"])
-    ref = oracle.fp8_attention(*codes, mask, window, scale=scale, rows=rows, fmt=fmt)
+    ref = oracle.fp8_attention(*codes, mask, window, scale=scale, rows=rows, fmt=fmt,
+                               global_idx=global_idx)
     if rows is not None:
         got = got[:, :, rows]
     assert np.all(np.isfinite(got))
     tol = oracle.fp8_tolerance(*codes, mask, window, scale=scale, rows=rows, exact_weights=zero_q,
-                               rounded_denominator=True, fmt=fmt)
+                               rounded_denominator=True, fmt=fmt, global_idx=global_idx)
     return got, ref, tol
 
 
@@ -115,6 +118,44 @@ def test_fp8_d64_zero_queries_and_e5m2(device, case):
                    D=64))
 
 
+LG_SWEEP = []
+_rng = np.random.default_rng(95)
+for D in (64, 128):
+    for S in (64, 129, 300, 1000, 2049):
+        Hq, Hkv = [(8, 2), (4, 4), (16, 2), (12, 12)][int(_rng.integers(4))]
+        window = int(_rng.choice([0, 16, 100, 600]))
+        n_g = int(_rng.choice([1, 3, 8, 64]))
+        g = sorted({int(x) for x in _rng.integers(0, S, size=n_g)} | ({0} if _rng.integers(2) else set())
+                   | ({S - 1} if _rng.integers(2) else set()))[:64]
+        LG_SWEEP.append((1 + int(_rng.integers(2)), Hq, Hkv, S, D, window, tuple(g)))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", LG_SWEEP, ids=lambda c: f"D{c[4]}-S{c[3]}-w{c[5]}-g{len(c[6])}-H{c[1]}x{c[2]}")
+def test_fp8_local_global_sweep(device, case):
+    """Local + global tokens: the band, the strip of global keys outside it,
+    and the global rows (keys shared out over the waves of a head and merged),
+    up to 64 globals, windows 0 to 600."""
+    B, Hq, Hkv, S, D, window, g = case
+    worst = check(*run_fp8(device, B, Hq, Hkv, S, "local_global", window, seed=S + D + window,
+                           D=D, global_idx=g))
+    print(f"worst error / tolerance {worst:.3f}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_local_global_exact_means_and_e5m2(device, D):
+    """Zero queries (each output the mean of its visible values: the band, the
+    strip and the global rows tightly) and E5M2 inputs, with globals at both
+    ends, next to each other and inside the band."""
+    g = (0, 1, 2, 90, 500, 699)
+    for window in (0, 5, 1000):
+        check(*run_fp8(device, 2, 8, 2, 700, "local_global", window, seed=60 + window, D=D,
+                       zero_q=True, global_idx=g))
+    check(*run_fp8(device, 1, 12, 12, 700, "local_global", 50, seed=61, D=D, fmt="e5m2",
+                   global_idx=g))
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"S{c[3]}-{c[4]}-H{c[1]}x{c[2]}")
 def test_fp8_e5m2_sweep(device, case):
@@ -150,7 +191,8 @@ def test_fp8_workload_full_size(device, name):
 
     w = workloads.WORKLOADS[name]
     rows = sample_rows(w)
-    got, ref, tol = run_fp8(device, w.B, w.Hq, w.Hkv, w.S, w.mask, seed=w.seed, rows=rows, D=w.D)
+    got, ref, tol = run_fp8(device, w.B, w.Hq, w.Hkv, w.S, w.mask, w.window, seed=w.seed,
+                            rows=rows, D=w.D, global_idx=w.global_idx)
     print(f"fp8 full size: worst error / tolerance {check(got, ref, tol):.3f}", flush=True)
 
 
@@ -170,7 +212,6 @@ def fp8_status(D=128, mask="causal", window=0, g=None, ptrs=(FAKE, FAKE * 3, FAK
 
 def test_fp8_validation():
     assert fp8_status(D=96) == "ATTN_ERR_UNSUPPORTED"
-    assert fp8_status(mask="local_global", window=10, g=[0]) == "ATTN_ERR_UNSUPPORTED"
     assert fp8_status(ptrs=(FAKE + 8, FAKE * 3, FAKE * 5, FAKE * 7)) == "ATTN_ERR_ALIGN"
     # o (bf16, 2 bytes per element) overlapping the end of q (1 byte per element)
     nq = 8 * 1000 * 128
@@ -183,7 +224,7 @@ def test_fp8_validation():
     assert info["kernel"] == 2 and info["keys_per_tile"] == 128
     assert info["tile_visits"] == 12 * sum(2 * b + 2 for b in range(32))  # 256 rows, 128-key tiles
     assert attn.status_string(attn.fwd_raw(FAKE, FAKE * 3, FAKE * 5, FAKE * 7, 1, 8, 2, 1000, 64,
-                                           "local_global", 10, [0], 0.1, attn.DTYPE_FP8_E5M2,
-                                           0)) == "ATTN_ERR_UNSUPPORTED"
+                                           "local_global", -1, [0], 0.1, attn.DTYPE_FP8_E5M2,
+                                           0)) == "ATTN_ERR_WINDOW"
     assert attn.status_string(attn.fwd_raw(FAKE, FAKE * 3, FAKE * 5, FAKE * 7, 1, 8, 2, 1000, 128,
                                            "causal", 0, None, 0.1, 4, 0)) == "ATTN_ERR_UNSUPPORTED"

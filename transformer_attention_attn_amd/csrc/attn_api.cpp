@@ -39,11 +39,6 @@ Checked check_args(int B, int Hq, int Hkv, int S, int D, int mask_kind, int wind
     return c;
   }
   if (D != 64 && D != 128) { c.status = ATTN_ERR_UNSUPPORTED; return c; }
-  // FP8: masks without global tokens
-  if (fp8 && mask_kind == ATTN_MASK_LOCAL_GLOBAL) {
-    c.status = ATTN_ERR_UNSUPPORTED;
-    return c;
-  }
   if (mask_kind < ATTN_MASK_FULL || mask_kind > ATTN_MASK_LOCAL_GLOBAL) { c.status = ATTN_ERR_UNSUPPORTED; return c; }
   if (Hq % Hkv != 0) { c.status = ATTN_ERR_HEADS; return c; }
   // total elements and the flat index of the last element must fit in 63 bits

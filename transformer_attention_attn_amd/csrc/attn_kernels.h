@@ -59,8 +59,8 @@ hipError_t launch_bf16_d128(const KParams& p, hipStream_t stream);  // kernel_bf
 // persistent form of the D = 128 dense square kernel (masks FULL, CAUSAL,
 // CAUSAL_WINDOW): `grid` workgroups walk the s.n_items work items
 hipError_t launch_bf16_pers_d128(const KParams& p, int grid, hipStream_t stream);
-// FP8 inputs, bf16 output, D = 64 or 128, masks without global tokens (e5m2:
-// q, k, v in E5M2 instead of E4M3)
+// FP8 inputs, bf16 output, D = 64 or 128, every mask (e5m2: q, k, v in E5M2
+// instead of E4M3)
 hipError_t launch_fp8(const KParams& p, int D, bool e5m2, hipStream_t stream);  // kernel_fp8.hip
 
 }  // namespace attn

@@ -176,12 +176,37 @@ __device__ __forceinline__ void run_block(const BlockOps& o, const i32x8 (&pf)[2
   block_step<0, NV, N, DEPTH, FMT, NDC>(op, o, pf, qf, ones, oacc, lacc, sc);
 }
 
+// LDS for the global token positions, only in kernels of the local+global mask
+template <bool LG>
+__device__ __forceinline__ int* f8_gpos_storage() {
+  if constexpr (LG) {
+    __shared__ int gpos[kMaxGlobal];
+    return gpos;
+  } else {
+    return nullptr;
+  }
+}
+
 // FMT: the input format of q, k and v (kFmtE4M3 or kFmtE5M2); D: 64 or 128
-// (in memory; in LDS every row takes 128 bytes)
+// (in memory; in LDS every row takes 128 bytes).  MASK_LOCAL_GLOBAL: band
+// items see the band |i - j| <= window through their key tiles plus one strip
+// tile that gathers the global keys (outside the band only); global-row items
+// hold the head's (up to) 32 global rows in every wave of the head, the waves
+// take the key tiles in turn (tile kt goes to wave kt % waves-per-head), and
+// their partial (m, l, O) merge through LDS in a fixed pairing.
 template <int MASK, int FMT, int D>
 __global__ __launch_bounds__(kBf16Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_fp8(KParams p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[F8_NSTAGE * 2 * F8_REG];
+  constexpr bool LG = MASK == MASK_LOCAL_GLOBAL;
+  static_assert(D == 64 || D == 128, "head dimension");
+  constexpr int NDB = D / 32, NCH = D / 16;  // 32-dim output blocks, 16-byte chunks per row
+  // local+global: a merge slot holds one wave's O (16-byte chunks [chunk][lane])
+  // and (m, l) per lane; at most four are written at once
+  constexpr int SLOT = NDB * 4 * 64 * 16 + 64 * 8;
+  constexpr int TILES_B = F8_NSTAGE * 2 * F8_REG;
+  constexpr int SMEM_B = (LG && 4 * SLOT > TILES_B) ? 4 * SLOT : TILES_B;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM_B];
+  int* const gpos_s = f8_gpos_storage<LG>();
   const Sched& s = p.s;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -189,22 +214,26 @@ void attn_fwd_fp8(KParams p) {
   const int l32 = lane & 31;
   const int hf = lane >> 5;
   const Item it = decode_item(s, blockIdx.x);
+  if constexpr (LG) {
+    if (tid < kMaxGlobal) gpos_s[tid] = tid < s.n_global ? p.gpos[tid] : 0;
+    __syncthreads();
+  }
+  const bool gitem = LG && it.is_global;  // a global-row item (workgroup-uniform)
 
   // ---- rows of this wave ------------------------------------------------
   const int wph = kBf16Waves / s.HP;
   const int a = it.kvh * s.G + it.hg * s.HP + wave / wph;
   const int rpart = wave % wph;
-  const int r0 = it.blk * s.BMh;
-  const int r1 = imin(r0 + s.BMh, s.S) - 1;
+  const int r0 = gitem ? 0 : it.blk * s.BMh;
+  const int r1 = gitem ? s.S - 1 : imin(r0 + s.BMh, s.S) - 1;
   const int q0 = r0 + rpart * 32;
-  const int q_row = q0 + l32;
-  const bool row_valid = q_row < s.S;
-  const int wqa = q0, wqb = imin(q0 + 31, s.S - 1);
+  const int gslot = it.blk * kBf16GlobalRows + l32;  // global items: the lane's global row
+  const int q_row = gitem ? (gslot < s.n_global ? gpos_s[gslot] : 0) : q0 + l32;
+  const bool row_valid = gitem ? gslot < s.n_global : q_row < s.S;
+  const int wqa = gitem ? 0 : q0, wqb = gitem ? s.S - 1 : imin(q0 + 31, s.S - 1);
   const bool wave_active = wqa <= wqb;
 
   const size_t S = (size_t)s.S;
-  static_assert(D == 64 || D == 128, "head dimension");
-  constexpr int NDB = D / 32, NCH = D / 16;  // 32-dim output blocks, 16-byte chunks per row
   const unsigned char* qp = (const unsigned char*)p.q + (size_t)(it.b * s.Hq + a) * S * D;
   const unsigned char* kp = (const unsigned char*)p.k + (size_t)(it.b * s.Hkv + it.kvh) * S * D;
   const unsigned char* vp = (const unsigned char*)p.v + (size_t)(it.b * s.Hkv + it.kvh) * S * D;
@@ -230,10 +259,14 @@ void attn_fwd_fp8(KParams p) {
   }
 
   // ---- key tiles --------------------------------------------------------
+  // (local+global band items: iteration 0 is the strip of global keys)
   int klo, khi;
-  key_range(s, 0, r0, r1, &klo, &khi);
+  key_range(s, gitem ? 1 : 0, r0, r1, &klo, &khi);
   const int kt_lo = klo / F8_BN, kt_hi = khi / F8_BN;
-  const int n_it = kt_hi - kt_lo + 1;
+  const int has_strip = (LG && !gitem && s.n_global > 0) ? 1 : 0;
+  const int n_it = kt_hi - kt_lo + 1 + has_strip;
+  auto tile_kt = [&](int iter) -> int { return kt_lo + iter - has_strip; };
+  auto is_strip = [&](int iter) -> bool { return LG && has_strip && iter == 0; };
 
   // Direct loads, issued by the four waves of group 0: load n of wave gw fills
   // 1 KiB slot sl = gw * F8_LOADS + n of the tile, lane l the 16-byte chunk at
@@ -244,22 +277,26 @@ void attn_fwd_fp8(KParams p) {
   // valid memory into a stage that is not read again.
   const int gw = wave & 3;
   const int drow = lane >> 3, dphys = lane & 7;
+  // (the strip: row t of the tile is global position t, later rows repeat the
+  // last one and are masked)
+  auto tile_row = [&](int iter, int trow) -> int {
+    if (is_strip(iter)) return gpos_s[imin(trow, s.n_global - 1)];
+    return imin(tile_kt(iter) * F8_BN + trow, s.S - 1);
+  };
   auto dma_k = [&](int iter, int st) {
-    const int kt = kt_lo + iter;
 #pragma unroll
     for (int n = 0; n < F8_LOADS; ++n) {
       const int trow = 8 * (gw * F8_LOADS + n) + drow;
-      const int row = imin(kt * F8_BN + trow, s.S - 1);
+      const int row = tile_row(iter, trow);
       dma16_global(kp + (size_t)row * D + 16 * ((dphys ^ kswz(trow)) & (NCH - 1)),
                    smem + st * 2 * F8_REG + (gw * F8_LOADS + n) * 1024);
     }
   };
   auto dma_v = [&](int iter, int st) {
-    const int kt = kt_lo + iter;
 #pragma unroll
     for (int n = 0; n < F8_LOADS; ++n) {
       const int trow = 8 * (gw * F8_LOADS + n) + drow;
-      const int row = imin(kt * F8_BN + trow, s.S - 1);
+      const int row = tile_row(iter, trow);
       dma16_global(vp + (size_t)row * D + 16 * ((dphys ^ vswz(trow)) & (NCH - 1)),
                    smem + st * 2 * F8_REG + F8_REG + (gw * F8_LOADS + n) * 1024);
     }
@@ -267,7 +304,15 @@ void attn_fwd_fp8(KParams p) {
 
   auto tile_class = [&](int iter) -> int {
     if (!wave_active) return TILE_EMPTY;
-    return classify_tile(MASK, s.window, s.S, wqa, wqb, (kt_lo + iter) * F8_BN, F8_BN);
+    if constexpr (LG) {
+      if (gitem) {  // every key, the wave's share of the tiles
+        const int kt = tile_kt(iter);
+        if (kt % wph != rpart) return TILE_EMPTY;
+        return kt * F8_BN + F8_BN > s.S ? TILE_PARTIAL : TILE_FULL;
+      }
+      if (is_strip(iter)) return TILE_PARTIAL;
+    }
+    return classify_tile(MASK, s.window, s.S, wqa, wqb, tile_kt(iter) * F8_BN, F8_BN);
   };
 
   // ---- per-lane LDS read offsets ------------------------------------------
@@ -332,12 +377,29 @@ void attn_fwd_fp8(KParams p) {
 
   // ---- online softmax of S(j) into the weights pf (E4M3) and l ---------------
   auto softmax = [&](int j, int cls) {
-    if (cls == TILE_PARTIAL) {
+    if (LG && is_strip(j)) {
+      // slot t of the strip is global key gpos[t]: seen when it exists and
+      // lies outside the row's band (inside, the band tiles hold it)
+#pragma unroll
+      for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbk * 32 + 16 * hf + r;
+          const int dist = q_row - gpos_s[imin(key, kMaxGlobal - 1)];
+          const bool vis = row_valid && key < s.n_global && (dist > s.window || -dist > s.window);
+          sc[kbk][r] = vis ? sc[kbk][r] : -INFINITY;
+        }
+    } else if (cls == TILE_PARTIAL) {
       // register r of block kbk holds key 32*kbk + 16*hf + r of the tile
       long long lo, hi;
-      row_interval(MASK, s.window, s.S, q_row, &lo, &hi);
+      if (gitem) {
+        lo = 0;  // a global row sees every key
+        hi = (long long)s.S - 1;
+      } else {
+        row_interval(MASK, s.window, s.S, q_row, &lo, &hi);
+      }
       if (!row_valid) hi = lo - 1;
-      const long long base = (long long)(kt_lo + j) * F8_BN + 16 * hf;
+      const long long base = (long long)tile_kt(j) * F8_BN + 16 * hf;
       const long long hi_a = hi < (long long)s.S - 1 ? hi : (long long)s.S - 1;
       const int lo_r = (int)(lo - base < -1 ? -1 : (lo - base > F8_BN ? F8_BN : lo - base));
       const int hi_r = (int)(hi_a - base < -1 ? -1 : (hi_a - base > F8_BN ? F8_BN : hi_a - base));
@@ -456,10 +518,67 @@ void attn_fwd_fp8(KParams p) {
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // no direct load may land after the workgroup ends
 
+  // ---- local+global, global-row items: merge the waves' partial (m, l, O) ----
+  // Fixed pairing (wave part r takes part r + half, half = wph/2, wph/4, ...),
+  // so results are bitwise reproducible; every wave of a head holds the same
+  // rows in the same lanes, so partials combine lane by lane:
+  //   m = max(m1, m2),  X = X1 * 2^((m1 - m) c) + X2 * 2^((m2 - m) c)  for X in {l, O}.
+  // The first barrier also orders the slots after every wave's last tile read
+  // and after every direct load has landed (each wave waited for its own).
+  bool store_rows = row_valid && wave_active;
+  if constexpr (LG) {
+    if (gitem) {
+      const int hh = wave / wph;
+      for (int half = wph >> 1; half >= 1; half >>= 1) {
+        __syncthreads();
+        if (rpart >= half && rpart < 2 * half) {
+          unsigned char* sl = smem + (hh * (wph >> 1) + rpart - half) * SLOT;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const float4 x = {oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2],
+                                oacc[db][4 * g4 + 3]};
+              *(float4*)(sl + ((4 * db + g4) * 64 + lane) * 16) = x;
+            }
+          *(float2*)(sl + NDB * 4 * 64 * 16 + lane * 8) = float2{m_run, lacc[0]};
+        }
+        __syncthreads();
+        if (rpart < half) {
+          const unsigned char* sl = smem + (hh * (wph >> 1) + rpart) * SLOT;
+          const float2 ml = *(const float2*)(sl + NDB * 4 * 64 * 16 + lane * 8);
+          const float m_new = fmaxf(m_run, ml.x);
+          if (m_new != -INFINITY) {
+            const float fa = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+            const float fb = __builtin_amdgcn_exp2f((ml.x - m_new) * c);
+            const float l_new = lacc[0] * fa + ml.y * fb;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) lacc[r] = l_new;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+              for (int g4 = 0; g4 < 4; ++g4) {
+                const float4 x = *(const float4*)(sl + ((4 * db + g4) * 64 + lane) * 16);
+                oacc[db][4 * g4] = oacc[db][4 * g4] * fa + x.x * fb;
+                oacc[db][4 * g4 + 1] = oacc[db][4 * g4 + 1] * fa + x.y * fb;
+                oacc[db][4 * g4 + 2] = oacc[db][4 * g4 + 2] * fa + x.z * fb;
+                oacc[db][4 * g4 + 3] = oacc[db][4 * g4 + 3] * fa + x.w * fb;
+              }
+            m_run = m_new;
+          }
+        }
+      }
+      store_rows = row_valid && rpart == 0;  // the head's first wave holds the merged rows
+    } else {
+      // band items leave the rows of global queries to the global items
+      for (int g = 0; g < s.n_global; ++g) store_rows = store_rows && (gpos_s[g] != q_row);
+    }
+  }
+
   // ---- epilogue: O = O^T / l, round to bf16, store --------------------------
   {
     const float l_tot = lacc[0];
-    if (row_valid && wave_active) {
+    if (store_rows) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       __bf16* op = (__bf16*)p.o + ((size_t)(it.b * s.Hq + a) * S + q_row) * D;
 #pragma unroll
@@ -483,7 +602,8 @@ hipError_t launch_fmt(const KParams& p, hipStream_t stream) {
   switch (p.s.mask) {
     case MASK_FULL: hipLaunchKernelGGL((attn_fwd_fp8<MASK_FULL, FMT, D>), grid, block, 0, stream, p); break;
     case MASK_CAUSAL: hipLaunchKernelGGL((attn_fwd_fp8<MASK_CAUSAL, FMT, D>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((attn_fwd_fp8<MASK_CAUSAL_WINDOW, FMT, D>), grid, block, 0, stream, p); break;
+    case MASK_CAUSAL_WINDOW: hipLaunchKernelGGL((attn_fwd_fp8<MASK_CAUSAL_WINDOW, FMT, D>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((attn_fwd_fp8<MASK_LOCAL_GLOBAL, FMT, D>), grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
 }

@@ -24,6 +24,8 @@ Workloads (shapes follow the examples on the pages):
   output.  The N(0, 1) draws are rounded to E4M3 (nearest even).
 * ``causal_mha_fp8_d64_s8192`` -- E4M3 inputs at head width 64: 12 heads of
   the local+global workload's shape, B=1 S=8192, causal mask.
+* ``local_global_fp8_s8192`` -- the local+global workload (window 512,
+  globals {0, 1000, 3000, 6000}) with E4M3 inputs.
 
 Decode workloads (the Sq newest positions of each sequence against its
 key/value cache, "Transformer 架构及其变体", section 预填充创建缓存，解码复用缓存):
@@ -117,6 +119,9 @@ WORKLOADS = {
         Workload("causal_gqa_fp8_s8192", 1, 32, 8, 8192, 128, "fp8", MASK_CAUSAL, seed=14),
         # FP8 at head width 64 (the local+global workload's heads, causal mask)
         Workload("causal_mha_fp8_d64_s8192", 1, 12, 12, 8192, 64, "fp8", MASK_CAUSAL, seed=17),
+        # the local+global workload with E4M3 inputs
+        Workload("local_global_fp8_s8192", 1, 12, 12, 8192, 64, "fp8", MASK_LOCAL_GLOBAL,
+                 window=512, global_idx=(0, 1000, 3000, 6000), seed=18),
     )
 }
 
