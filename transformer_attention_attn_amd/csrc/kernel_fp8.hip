@@ -204,7 +204,10 @@ void attn_fwd_fp8(KParams p) {
   // and (m, l) per lane; at most four are written at once
   constexpr int SLOT = NDB * 4 * 64 * 16 + 64 * 8;
   constexpr int TILES_B = F8_NSTAGE * 2 * F8_REG;
-  constexpr int SMEM_B = (LG && 4 * SLOT > TILES_B) ? 4 * SLOT : TILES_B;
+  // local+global, global-row items: one private 64-key K tile and V tile per wave
+  constexpr int GT = 64, GREG = GT * F8_ROWB, GLOADS = GREG / 1024;
+  constexpr int LG_B = (4 * SLOT > kBf16Waves * 2 * GREG) ? 4 * SLOT : kBf16Waves * 2 * GREG;
+  constexpr int SMEM_B = (LG && LG_B > TILES_B) ? LG_B : TILES_B;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM_B];
   int* const gpos_s = f8_gpos_storage<LG>();
   const Sched& s = p.s;
@@ -485,6 +488,119 @@ void attn_fwd_fp8(KParams p) {
   // 2j+1 (K(j) was last read in step 2j by group 1, V(j-1) in step 2j by group
   // 1) and waits for them at the end of step 2j+2, before the barrier into step
   // 2j+3, the first that reads them.  Group 1 loads nothing.
+  // ---- local+global, global-row items: private key walks ------------------
+  // Each wave walks its own contiguous run of 64-key tiles through a private
+  // LDS region (one K tile and one V tile, the ring's row layout and
+  // swizzles), so the waves of a head work on different keys at once and the
+  // walk needs no workgroup barrier.  K(t+1) loads during the softmax of tile
+  // t, V(t+1) after its P.V; the exact weights use the row maximum of every
+  // tile (weights at most 1).
+  if (gitem) {
+    {
+      unsigned char* kreg = smem + wave * 2 * GREG;
+      unsigned char* vreg = kreg + GREG;
+      const int nt = cdiv(s.S, GT);
+      const int t_lo = (int)((long long)nt * rpart / wph);
+      const int t_hi = (int)((long long)nt * (rpart + 1) / wph);
+      auto gload = [&](int t, bool is_v) {
+#pragma unroll
+        for (int n = 0; n < GLOADS; ++n) {
+          const int trow = 8 * n + drow;
+          const int row = imin(t * GT + trow, s.S - 1);
+          const int ch = (dphys ^ (is_v ? vswz(trow) : kswz(trow))) & (NCH - 1);
+          dma16_global((is_v ? vp : kp) + (size_t)row * D + 16 * ch, (is_v ? vreg : kreg) + n * 1024);
+        }
+      };
+      const unsigned kb = lds_addr(kreg);
+      const unsigned ka0 = kb + k_off[0][0], ka1 = kb + k_off[0][1];
+      const unsigned kc0 = kb + k_off[1][0], kc1 = kb + k_off[1][1];
+      // (v_off counts from the ring's V tile, F8_REG into a stage)
+      const unsigned vb = lds_addr(vreg) - (unsigned)F8_REG;
+      if (t_lo < t_hi) {
+        gload(t_lo, false);
+        gload(t_lo, true);
+      }
+      for (int t = t_lo; t < t_hi; ++t) {
+        const bool more = t + 1 < t_hi;
+        __builtin_amdgcn_s_waitcnt(0x0f70 | GLOADS);  // K(t) landed; V(t) may be in flight
+        {
+          const f32x16 zero = {};
+          i32x8 k00 = lds_read32<0>(ka0, ka1);
+          i32x8 k10 = lds_read32<32 * F8_ROWB>(ka0, ka1);
+          lds_wait8<0>(k00);
+          lds_wait8<0>(k10);
+          sc[0] = mfma_fp8<FMT, FMT>(k00, qf[0], zero);
+          sc[1] = mfma_fp8<FMT, FMT>(k10, qf[0], zero);
+          if constexpr (D == 128) {
+            i32x8 k01 = lds_read32<0>(kc0, kc1);
+            i32x8 k11 = lds_read32<32 * F8_ROWB>(kc0, kc1);
+            lds_wait8<0>(k01);
+            lds_wait8<0>(k11);
+            sc[0] = mfma_fp8<FMT, FMT>(k01, qf[1], sc[0]);
+            sc[1] = mfma_fp8<FMT, FMT>(k11, qf[1], sc[1]);
+          }
+        }
+        if (more) gload(t + 1, false);  // the K operand reads are done
+        // register r of block kbk holds key 32*kbk + 16*hf + r of the tile;
+        // keys at or beyond S, and rows past the global count, carry no weight
+        const int lim = row_valid ? s.S - t * GT - 16 * hf : 0;
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[kbk][r] = (kbk * 32 + r < lim) ? sc[kbk][r] : -INFINITY;
+        float mx;
+        {
+          float t4[4];
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const int kbk = c4 >> 1, rb = (c4 & 1) * 8;
+            float x = max3f(sc[kbk][rb], sc[kbk][rb + 1], sc[kbk][rb + 2]);
+            x = max3f(x, sc[kbk][rb + 3], sc[kbk][rb + 4]);
+            x = max3f(x, sc[kbk][rb + 5], sc[kbk][rb + 6]);
+            t4[c4] = fmaxf(x, sc[kbk][rb + 7]);
+          }
+          mx = max3f(max3f(t4[0], t4[1], t4[2]), t4[3], t4[3]);
+        }
+        mx = pair_max(mx);
+        if (__builtin_amdgcn_ballot_w64(mx * c > m_run * c) != 0) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
+          m_run = m_new;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+        i32x8 pw;
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+          for (int r = 0; r < 16; r += 4) {
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r], c, -mc));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 1], c, -mc));
+            const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 2], c, -mc));
+            const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kbk][r + 3], c, -mc));
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
+            pw[4 * kbk + r / 4] = w;
+          }
+        if (more) __builtin_amdgcn_s_waitcnt(0x0f70 | GLOADS);  // V(t) landed; K(t+1) in flight
+        else __builtin_amdgcn_s_waitcnt(0x0f70);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          i32x8 vop = lds_tr8x4<vrow_off(0, 0), vrow_off(0, 1), vrow_off(0, 2), vrow_off(0, 3)>(
+              vb + (unsigned)v_off[db]);
+          lds_wait8<0>(vop);
+          oacc[db] = mfma_fp8<FMT, kFmtE4M3>(vop, pw, oacc[db]);
+        }
+        lacc = mfma_fp8<kFmtE4M3, kFmtE4M3>(ones8, pw, lacc);
+        if (more) gload(t + 1, true);  // the V operand reads are done
+      }
+    }
+  } else {
   const int grp = wave >> 2;
   if (grp == 0) {
     dma_k(0, 0);
@@ -516,6 +632,7 @@ void attn_fwd_fp8(KParams p) {
       __builtin_amdgcn_s_barrier();
     }
   }
+  }  // ring pipeline
   __builtin_amdgcn_s_waitcnt(0x0f70);  // no direct load may land after the workgroup ends
 
   // ---- local+global, global-row items: merge the waves' partial (m, l, O) ----
