@@ -1,5 +1,7 @@
-"""Large-size cases (GPU): long sequences, long caches, wide row strides and
-many sequences, each compared with the fp64 oracles on sampled rows.
+"""Large-size cases (GPU): long sequences, long caches, wide row strides,
+many sequences, a distance-bias table over 81919 distances and FP8
+local+global at 32768 positions, each compared with the fp64 oracles on
+sampled rows.
 
 They exercise the index arithmetic at sizes beyond the workloads: 64-bit
 element offsets of long sequences, 32-bit buffer-descriptor extents of
@@ -113,3 +115,51 @@ def test_many_sequences(device):
     got = o[sel].float().cpu().numpy()
     ref = oracle.attention(inp["q"][sel], inp["k"][sel], inp["v"][sel], "causal")
     assert float(np.max(np.abs(got - ref))) <= TOL["bf16"]
+
+
+@pytest.mark.gpu
+def test_long_distance_bias_chunk(device):
+    """A bucketed distance-bias table over Sq + Skv - 1 = 81919 distances (a
+    4096-query chunk at the end of 77824 keys, causal), sampled rows of every
+    head, sequence-major tensors."""
+    import torch
+
+    B, Hq, Hkv, Sq, Skv, D = 1, 8, 2, 4096, 77824, 128
+    print(f"large: distance bias Sq={Sq} Skv={Skv}", flush=True)
+    inp = workloads.make_decode_inputs(B, Hq, Hkv, Sq, Skv, D, seed=75)
+    q, k, v = (bf16(inp[n + "_bits"], device).transpose(1, 2).contiguous().transpose(1, 2)
+               for n in ("q", "k", "v"))
+    table = workloads.make_distance_bias(Hq, Sq, Skv, seed=76)
+    o = attn.fwd_ex(q, k, v, mask="causal", dist_bias=torch.from_numpy(table).to(device))
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 128, 2048, 4094, 4095]
+    got = o[:, :, rows].float().cpu().numpy()
+    ref = oracle.cross_attention(inp["q"], inp["k"], inp["v"], "causal", rows=rows,
+                                 dist_bias=table)
+    err = float(np.max(np.abs(got - ref)))
+    print(f"max abs err {err:.3e}", flush=True)
+    assert err <= TOL["bf16"], err
+
+
+@pytest.mark.gpu
+def test_long_fp8_local_global(device):
+    """FP8 local + global at S = 32768 with 64 globals (the global rows' walks
+    span 32768 keys), sampled rows including every kind of row."""
+    import torch
+
+    B, Hq, Hkv, S, D = 1, 4, 4, 32768, 64
+    g = tuple(int(x) for x in np.linspace(0, S - 1, 64).astype(np.int64))
+    print(f"large: FP8 local+global S={S} globals={len(g)}", flush=True)
+    inp = workloads.make_inputs(B, Hq, Hkv, S, D, "fp8", seed=77)
+    q, k, v = workloads.to_torch(inp, "fp8", device)
+    o = attn.fwd(q, k, v, mask="local_global", window=256, global_idx=list(g))
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, 255, 256, 257, 16383, 16384, S - 1} | set(g[1:4]))
+    got = o[:, :, rows].float().cpu().numpy().astype(np.float64)
+    codes = (inp["q_codes"], inp["k_codes"], inp["v_codes"])
+    ref = oracle.fp8_attention(*codes, "local_global", 256, rows=rows, global_idx=g)
+    tol = oracle.fp8_tolerance(*codes, "local_global", 256, rows=rows, rounded_denominator=True,
+                               global_idx=g)
+    err = np.abs(got - ref)
+    print(f"max abs err {err.max():.3e}, worst error / tolerance {(err / tol).max():.3f}", flush=True)
+    assert np.all(err <= tol), float((err - tol).max())
