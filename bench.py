@@ -677,8 +677,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the kernel shards by key/value head, see DESIGN.md", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
+              "across GPUs the operation would shard by (batch, key/value head) with no "
+              "communication, which is not built", file=sys.stderr)
         return 2
 
     import workloads
