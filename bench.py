@@ -65,6 +65,10 @@ TRAFFIC_SUMMARIES = {
     "local_global_bf16_s8192": ("attn_fwd_bf16_local_global_s8192.md", KERNEL_SOURCES),
     "causal_gqa_fp8_s8192": ("attn_fwd_fp8_causal_gqa_s8192.md",
                              ("kernel_fp8.hip", "gfx950_ops.h", "attn_kernels.h", "attn_sched.h")),
+    "causal_mha_fp8_d64_s8192": ("attn_fwd_fp8_causal_mha_d64_s8192.md",
+                                 ("kernel_fp8.hip", "gfx950_ops.h", "attn_kernels.h", "attn_sched.h")),
+    "local_global_fp8_s8192": ("attn_fwd_fp8_local_global_s8192.md",
+                               ("kernel_fp8.hip", "gfx950_ops.h", "attn_kernels.h", "attn_sched.h")),
     "decode_gqa_bf16_b16_l8192": ("attn_decode_bf16_gqa_b16_l8192.md", DECODE_SOURCES),
     "decode_gqa_bf16_b8_sq4_l16384": ("attn_decode_bf16_ragged_b8_sq4_l16384.md", DECODE_SOURCES),
     "decode_window_gqa_bf16_b16_w4096_l32768": ("attn_decode_bf16_window_b16_w4096_l32768.md",
