@@ -73,6 +73,7 @@ TRAFFIC_SUMMARIES = {
     "decode_gqa_bf16_b8_sq4_l16384": ("attn_decode_bf16_ragged_b8_sq4_l16384.md", DECODE_SOURCES),
     "decode_window_gqa_bf16_b16_w4096_l32768": ("attn_decode_bf16_window_b16_w4096_l32768.md",
                                                 DECODE_SOURCES),
+    "decode_mqa_bf16_b4_l65536": ("attn_decode_bf16_mqa_b4_l65536.md", DECODE_SOURCES),
 }
 
 
